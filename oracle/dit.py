@@ -1,0 +1,381 @@
+"""Plain float64 implementation of one chunk's flow-matching DiT denoising pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Everything is numpy
+float64 on the host: no blocking, fusion or reordering beyond what each
+definition states, so that every function can be read against its definition.
+
+Page references are to HeyGen, "Avatar inference at scale":
+  [arch]  section "The underlying model architecture": a DiT trained with flow
+          matching, conditioned on rich reference tokens; long videos are made
+          chunk by chunk, the first chunk relying on the static reference only
+          and later chunks on boundary data from the previous segment.
+  [loop]  section "The streaming framework and pipeline loop": the reference is
+          encoded once per request; the audio-to-video stage runs a multi-step
+          diffusion pass per chunk, conditioned on the previous chunk's boundary
+          frames; the super-resolution stage upscales in a single step.
+  [mem]   section "Constant memory over duration": only the static reference
+          conditioning and a minimal anchor set persist between chunks.
+Readings the pages leave open (they give no block internals) are marked
+"reading:".
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "rms_norm", "modulate", "silu", "gelu_tanh", "linear", "timestep_features",
+    "conditioning", "block_modulation", "final_modulation", "rope_split",
+    "grid_positions", "rope_angles", "rope_apply", "qk_norm", "softmax",
+    "attention", "upsample2_tokens", "patch_input", "block_forward",
+    "context_pass", "dit_velocity", "euler", "schedule", "chunk_denoise",
+    "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone",
+]
+
+Weights = Dict[str, np.ndarray]
+
+
+def W(P: Weights, name: str) -> np.ndarray:
+    """Fetch a parameter as float64."""
+    return np.asarray(P[name], dtype=np.float64)
+
+
+# ------------------------------------------------------------------ primitives
+
+
+def rms_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """reading: RMSNorm over the last axis, x / sqrt(mean(x^2) + eps), no affine."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def modulate(u: np.ndarray, shift: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """reading: adaLN modulation u * (1 + scale) + shift, one vector per step."""
+    return u * (1.0 + scale) + shift
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x: np.ndarray) -> np.ndarray:
+    """reading: GELU, tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """y = x W^T + b with W stored [out, in]."""
+    return x @ w.T + b
+
+
+# ------------------------------------------------------------------ timestep conditioning
+
+
+def timestep_features(t: float, width: int = 256) -> np.ndarray:
+    """reading: sinusoid of s = 1000 t, [cos(s w_i) || sin(s w_i)], w_i = 10000^(-i/half)."""
+    half = width // 2
+    s = 1000.0 * float(t)
+    freqs = 10000.0 ** (-np.arange(half, dtype=np.float64) / half)
+    return np.concatenate([np.cos(s * freqs), np.sin(s * freqs)])
+
+
+def conditioning(P: Weights, t: float) -> np.ndarray:
+    """reading: c = SiLU(Linear(SiLU(Linear(phi(t))))); one global t per step."""
+    e = silu(linear(timestep_features(t), W(P, "t1.w"), W(P, "t1.b")))
+    return silu(linear(e, W(P, "t2.w"), W(P, "t2.b")))
+
+
+def block_modulation(P: Weights, l: int, c: np.ndarray) -> List[np.ndarray]:
+    """reading: Linear_{D->6D}(c) split into shift_msa, scale_msa, gate_msa,
+    shift_mlp, scale_mlp, gate_mlp (in that order)."""
+    m = linear(c, W(P, f"blk{l}.mod.w"), W(P, f"blk{l}.mod.b"))
+    return list(np.split(m, 6))
+
+
+def final_modulation(P: Weights, c: np.ndarray) -> List[np.ndarray]:
+    """reading: Linear_{D->2D}(c) split into shift_f, scale_f."""
+    m = linear(c, W(P, "fmod.w"), W(P, "fmod.b"))
+    return list(np.split(m, 2))
+
+
+# ------------------------------------------------------------------ 3D rotary positions
+
+
+def rope_split(dh: int) -> Tuple[int, int, int]:
+    """reading: head dims per axis (t, h, w): d_h = d_w = 2 floor(dh/6), d_t = rest."""
+    d_hw = 2 * (dh // 6)
+    return dh - 2 * d_hw, d_hw, d_hw
+
+
+def grid_positions(t0: int, frames: int, h: int, w: int) -> np.ndarray:
+    """(t, y, x) of every token of a frames x h x w grid, row-major; t = t0 + frame.
+
+    reading: positions are chunk-local; the boundary frame sits at t = -1 and the
+    reference frame at t = -2, each on its own (y, x) grid."""
+    f, y, x = np.meshgrid(np.arange(frames), np.arange(h), np.arange(w), indexing="ij")
+    return np.stack([f.ravel() + t0, y.ravel(), x.ravel()], axis=1).astype(np.int64)
+
+
+def rope_angles(pos: np.ndarray, dh: int, theta: float) -> np.ndarray:
+    """Angle of every rotated pair: [n, dh/2].
+
+    reading: pair i of an axis with d_a dims turns by p * theta^(-2i/d_a); the
+    first d_t/2 pairs follow t, the next d_h/2 follow y, the last d_w/2 follow x."""
+    parts = []
+    for axis, d in enumerate(rope_split(dh)):
+        i = np.arange(d // 2, dtype=np.float64)
+        inv = theta ** (-2.0 * i / d)
+        parts.append(pos[:, axis:axis + 1].astype(np.float64) * inv[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def rope_apply(x: np.ndarray, ang: np.ndarray) -> np.ndarray:
+    """Rotate adjacent pairs (2i, 2i+1) of every head: x [n, H, dh], ang [n, dh/2]."""
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def qk_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """reading: per-head RMSNorm over dh times a learned gamma shared by all heads."""
+    return rms_norm(x, eps) * gamma
+
+
+# ------------------------------------------------------------------ attention
+
+
+def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
+    m = np.max(s, axis=axis, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Per head softmax(q k^T / sqrt(dh)) v.  q [n, H, dh], k/v [m, H, dh] -> [n, H, dh]."""
+    n, H, dh = q.shape
+    out = np.empty((n, H, dh), dtype=np.float64)
+    for hh in range(H):
+        s = (q[:, hh, :] @ k[:, hh, :].T) / np.sqrt(dh)
+        out[:, hh, :] = softmax(s, axis=1) @ v[:, hh, :]
+    return out
+
+
+def _heads(x: np.ndarray, H: int) -> np.ndarray:
+    return x.reshape(x.shape[0], H, -1)
+
+
+# ------------------------------------------------------------------ inputs to the patch embed
+
+
+def upsample2_tokens(z: np.ndarray, frames: int, h: int, w: int) -> np.ndarray:
+    """Nearest 2x upsample in (y, x) of half-resolution latent tokens.
+
+    Tokens carry a (1, 2, 2) patch of channels laid out (c, dy, dx).  Upsampling the
+    pixel grid by 2 and re-patchifying gives token (f, y, x), channel (c, dy, dx) =
+    low-res token (f, y//2, x//2), channel (c, y%2, x%2), for every dy, dx.
+    reading: the super-resolution stage is conditioned on the low-resolution
+    latents by channel concatenation."""
+    hl, wl = h // 2, w // 2
+    C = z.shape[1]
+    zc = z.reshape(frames, hl, wl, C // 4, 2, 2)
+    out = np.empty((frames, h, w, C // 4, 2, 2), dtype=np.float64)
+    for y in range(h):
+        for x in range(w):
+            src = zc[:, y // 2, x // 2, :, y % 2, x % 2]            # [frames, C/4]
+            out[:, y, x, :, :, :] = src[:, :, None, None]
+    return out.reshape(frames * h * w, C)
+
+
+def patch_input(x: np.ndarray, cond: Optional[np.ndarray], C_c: int) -> np.ndarray:
+    """[x || cond]; context tokens (cond None) get a zero conditioning half."""
+    x = np.asarray(x, dtype=np.float64)
+    if C_c == 0:
+        return x
+    if cond is None:
+        cond = np.zeros((x.shape[0], C_c))
+    return np.concatenate([x, np.asarray(cond, dtype=np.float64)], axis=1)
+
+
+# ------------------------------------------------------------------ one DiT block
+
+
+def block_forward(P: Weights, cfg, l: int, h: np.ndarray, mod: Sequence[np.ndarray],
+                  pos: np.ndarray, ctx_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
+                  audio: Optional[np.ndarray], kv_only: bool = False):
+    """One DiT block over token states h [n, D].
+
+    Keys/values are the read-only context K/V (reference, then boundary), followed
+    by the block's own tokens.  Returns (h_out, k, v), with k normalised and rotated.
+    With kv_only the block stops after producing k and v (h_out is None).
+    reading: self-attention, then audio cross-attention (skipped without audio),
+    then the MLP, each pre-normed with a residual; adaLN shift/scale on the
+    self-attention and MLP inputs and gates on their outputs [arch, loop]."""
+    D, H, eps = cfg.D, cfg.H, cfg.eps
+    p = f"blk{l}."
+    sh1, sc1, g1, sh2, sc2, g2 = mod
+    u = modulate(rms_norm(h, eps), sh1, sc1)
+    qkv = linear(u, W(P, p + "qkv.w"), W(P, p + "qkv.b"))
+    q, k, v = (_heads(a, H) for a in np.split(qkv, 3, axis=1))
+    ang = rope_angles(pos, cfg.dh, cfg.rope_theta)
+    q = rope_apply(qk_norm(q, W(P, p + "gq"), eps), ang)
+    k = rope_apply(qk_norm(k, W(P, p + "gk"), eps), ang)
+    if kv_only:
+        return None, k, v
+    K = np.concatenate([kk for kk, _ in ctx_kv] + [k], axis=0)
+    V = np.concatenate([vv for _, vv in ctx_kv] + [v], axis=0)
+    o = attention(q, K, V).reshape(h.shape[0], D)
+    h = h + g1 * linear(o, W(P, p + "o.w"), W(P, p + "o.b"))
+    if audio is not None and audio.shape[0] > 0:
+        a = np.asarray(audio, dtype=np.float64)
+        uc = rms_norm(h, eps)
+        qc = qk_norm(_heads(linear(uc, W(P, p + "cq.w"), W(P, p + "cq.b")), H), W(P, p + "gcq"), eps)
+        kc = qk_norm(_heads(linear(a, W(P, p + "ck.w"), W(P, p + "ck.b")), H), W(P, p + "gck"), eps)
+        vc = _heads(linear(a, W(P, p + "cv.w"), W(P, p + "cv.b")), H)
+        oc = attention(qc, kc, vc).reshape(h.shape[0], D)
+        h = h + linear(oc, W(P, p + "co.w"), W(P, p + "co.b"))
+    u = modulate(rms_norm(h, eps), sh2, sc2)
+    y = linear(gelu_tanh(linear(u, W(P, p + "fc1.w"), W(P, p + "fc1.b"))),
+               W(P, p + "fc2.w"), W(P, p + "fc2.b"))
+    h = h + g2 * y
+    return h, k, v
+
+
+# ------------------------------------------------------------------ context K/V passes
+
+
+def context_pass(P: Weights, cfg, z: np.ndarray, pos: np.ndarray,
+                 prior: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]]):
+    """Per-block K/V of clean context tokens z [n, C_p] (reference or boundary).
+
+    reading: context tokens run through the same blocks at t = 0; they see the
+    earlier context segments (``prior[l]``: list of (K, V) per block) and
+    themselves, never the chunk; no audio.  Their K/V do not depend on the chunk
+    or the step, so they are computed once and kept read-only: the reference once
+    per request [loop], the boundary once per chunk [arch, loop]."""
+    c = conditioning(P, 0.0)
+    h = linear(patch_input(z, None, cfg.C_c), W(P, "pe.w"), W(P, "pe.b"))
+    out = []
+    for l in range(cfg.L):
+        mod = block_modulation(P, l, c)
+        last = l == cfg.L - 1
+        h_next, k, v = block_forward(P, cfg, l, h, mod, pos, list(prior[l]), None, kv_only=last)
+        out.append((k, v))
+        h = h_next
+    return out
+
+
+# ------------------------------------------------------------------ velocity and Euler
+
+
+def dit_velocity(P: Weights, cfg, x: np.ndarray, t: float, pos: np.ndarray,
+                 ctx: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]],
+                 audio: Optional[np.ndarray], cond: Optional[np.ndarray] = None) -> np.ndarray:
+    """Velocity v = DiT(x, t) for the chunk's latent tokens x [N, C_p] [arch].
+
+    ``ctx[l]`` lists the read-only (K, V) of block l's context segments."""
+    c = conditioning(P, t)
+    h = linear(patch_input(x, cond, cfg.C_c), W(P, "pe.w"), W(P, "pe.b"))
+    for l in range(cfg.L):
+        h, _, _ = block_forward(P, cfg, l, h, block_modulation(P, l, c), pos, list(ctx[l]), audio)
+    sh, sc = final_modulation(P, c)
+    u = modulate(rms_norm(h, cfg.eps), sh, sc)
+    return linear(u, W(P, "fin.w"), W(P, "fin.b"))
+
+
+def euler(x: np.ndarray, v: np.ndarray, t: float, t_next: float) -> np.ndarray:
+    """Flow-matching Euler update x + (t_next - t) v."""
+    return x + (float(t_next) - float(t)) * v
+
+
+def schedule(steps: int, t_start: float, t_end: float) -> np.ndarray:
+    """reading: linear schedule t_k = t_start + (t_end - t_start) k / steps, k = 0..steps."""
+    k = np.arange(steps + 1, dtype=np.float64)
+    return t_start + (t_end - t_start) * k / steps
+
+
+def chunk_denoise(P: Weights, cfg, x0: np.ndarray, ctx, audio, cond=None, grid=None,
+                  steps: Optional[int] = None, t_start=None, t_end=None, record=False):
+    """The multi-step diffusion pass over one chunk [loop]: Euler on the schedule.
+
+    Returns the final latent (and, with record, the list of per-step velocities)."""
+    g = grid if grid is not None else cfg.chunk
+    pos = grid_positions(0, g.frames, g.h, g.w)
+    S = cfg.steps if steps is None else steps
+    ts = schedule(S, cfg.t_start if t_start is None else t_start,
+                  cfg.t_end if t_end is None else t_end)
+    x = np.asarray(x0, dtype=np.float64)
+    vs = []
+    for k in range(S):
+        v = dit_velocity(P, cfg, x, ts[k], pos, ctx, audio, cond)
+        vs.append(v)
+        x = euler(x, v, ts[k], ts[k + 1])
+    return (x, vs) if record else x
+
+
+def last_frame(x: np.ndarray, frames: int, h: int, w: int) -> np.ndarray:
+    """Tokens of the last latent frame of a chunk (the boundary carried forward)."""
+    n = h * w
+    return np.asarray(x, dtype=np.float64)[(frames - 1) * n:frames * n]
+
+
+def ref_context(P: Weights, cfg, ref: np.ndarray, ref_grid):
+    """Reference K/V per block: the reference sees only itself."""
+    pos = grid_positions(ref_grid.t0, ref_grid.frames, ref_grid.h, ref_grid.w)
+    return context_pass(P, cfg, ref, pos, [[] for _ in range(cfg.L)])
+
+
+def bnd_context(P: Weights, cfg, ref_kv, bnd: np.ndarray, h: int, w: int):
+    """Boundary K/V per block: one frame at t = -1, seeing the reference and itself."""
+    pos = grid_positions(-1, 1, h, w)
+    return context_pass(P, cfg, bnd, pos, [[ref_kv[l]] for l in range(cfg.L)])
+
+
+def stream(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.ndarray):
+    """Chunked generation [arch, loop, mem]: reference K/V once, then per chunk the
+    boundary K/V from the previous chunk's last frame (none for chunk 0), then the
+    multi-step pass.  Returns the final latent of every chunk."""
+    g = cfg.chunk
+    ref_kv = ref_context(P, cfg, ref, cfg.ref)
+    outs = []
+    prev = None
+    for inp in chunks:
+        if prev is None:
+            ctx = [[ref_kv[l]] for l in range(cfg.L)]
+        else:
+            bkv = bnd_context(P, cfg, ref_kv, last_frame(prev, g.frames, g.h, g.w), g.h, g.w)
+            ctx = [[ref_kv[l], bkv[l]] for l in range(cfg.L)]
+        cond = None
+        if cfg.C_c > 0:
+            cond = (upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w)
+                    if cfg.cond_up == 2 else inp["cond"])
+        x = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond)
+        outs.append(x)
+        prev = x
+    return outs
+
+
+def standalone(P: Weights, cfg, inp: Dict[str, np.ndarray], record: bool = True):
+    """One self-contained chunk: reference K/V, the seeded boundary frame's K/V (if the
+    workload has one), then the chunk's multi-step pass.
+
+    Returns (x_final, velocities, ref_kv, bnd_kv)."""
+    g = cfg.chunk
+    ref_kv = ref_context(P, cfg, inp["ref"], cfg.ref)
+    bnd_kv = None
+    if cfg.bnd is not None:
+        bnd_kv = bnd_context(P, cfg, ref_kv, inp["bnd"], cfg.bnd.h, cfg.bnd.w)
+        ctx = [[ref_kv[l], bnd_kv[l]] for l in range(cfg.L)]
+    else:
+        ctx = [[ref_kv[l]] for l in range(cfg.L)]
+    cond = None
+    if cfg.C_c > 0:
+        cond = (upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w)
+                if cfg.cond_up == 2 else inp["cond"])
+    x, vs = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond, record=True)
+    return x, vs, ref_kv, bnd_kv
