@@ -1,0 +1,487 @@
+// libditchunk: host side of the C ABI (include/ditchunk.h).
+//
+// The handle borrows every device buffer (weights, state, workspace) from the caller
+// and validates all arguments on the host before any HIP call.  A call enqueues a
+// fixed kernel sequence on the handle's stream:
+//
+//   ref_kv_precompute / boundary_kv_carry (context pass at t = 0):
+//     modulation(0) -> patch input -> patch embed ->
+//     per block: RMSNorm+mod -> QKV -> QK-norm+RoPE (K, V written to the state) ->
+//                [not last block] attention over earlier context + self -> out-proj
+//                (gated residual) -> RMSNorm+mod -> FC1+GELU -> FC2 (gated residual)
+//   dit_chunk_step:
+//     modulation(t) -> patch input -> patch embed ->
+//     per block: RMSNorm+mod -> QKV -> QK-norm+RoPE -> attention over
+//                [ref | bnd | chunk] -> out-proj (gated residual) ->
+//                [audio] RMSNorm -> q_c -> q-norm; audio K/V -> k-norm; cross
+//                attention -> out (residual) ->
+//                RMSNorm+mod -> FC1+GELU -> FC2 (gated residual)
+//     final RMSNorm+mod -> final Linear with the Euler update fused into its epilogue.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ditchunk.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+int round64(long long x) { return (int)((x + 63) / 64 * 64); }
+
+// Buffer layout of the state and the workspace (byte offsets).
+struct Layout {
+  size_t elt = 0;
+  int cap_tok = 0, cap_ref = 0, cap_bnd = 0, cap_audio = 0, F = 0, C_in = 0, big_cols = 0;
+  // state
+  std::vector<size_t> kref, vref, kbnd, vbnd;
+  size_t state_total = 0;
+  // workspace
+  size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
+         va_raw = 0, ka = 0, vat = 0, mod = 0, tmp = 0;
+  size_t ws_total = 0;
+};
+
+int check_config(const dit_config* c) {
+  if (!c) return fail(DIT_EINVAL, "config is NULL");
+  if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype %d", c->dtype);
+  if (c->L < 1 || c->L > 256) return fail(DIT_EINVAL, "L=%d out of [1, 256]", c->L);
+  if (c->dh != 64 && c->dh != 128) return fail(DIT_EINVAL, "dh=%d (64 or 128)", c->dh);
+  if (c->H < 1 || c->D != c->H * c->dh) return fail(DIT_EINVAL, "D=%d != H*dh=%d*%d", c->D, c->H, c->dh);
+  if (c->D % 256 || c->D > 4096) return fail(DIT_EINVAL, "D=%d must be a multiple of 256, <= 4096", c->D);
+  if (c->mlp_ratio < 1 || c->mlp_ratio > 8) return fail(DIT_EINVAL, "mlp_ratio=%d", c->mlp_ratio);
+  if (c->c_p < 4 || c->c_p % 4) return fail(DIT_EINVAL, "c_p=%d must be a positive multiple of 4", c->c_p);
+  if (c->c_c < 0 || (c->c_p + c->c_c) % 64) return fail(DIT_EINVAL, "c_p+c_c=%d must be a multiple of 64", c->c_p + c->c_c);
+  if (c->cond_up != 1 && c->cond_up != 2) return fail(DIT_EINVAL, "cond_up=%d (1 or 2)", c->cond_up);
+  if (c->cond_up == 2 && c->c_c % 4) return fail(DIT_EINVAL, "cond_up=2 needs c_c multiple of 4");
+  if (c->d_a < 0 || c->d_a % 64) return fail(DIT_EINVAL, "d_a=%d must be a multiple of 64", c->d_a);
+  if (c->max_tokens < 1 || c->max_ref < 1 || c->max_bnd < 0 || c->max_audio < 0)
+    return fail(DIT_EINVAL, "capacities must be max_tokens>=1, max_ref>=1, max_bnd>=0, max_audio>=0");
+  if (c->max_tokens > (1 << 24) || c->max_ref > (1 << 24) || c->max_bnd > (1 << 24) || c->max_audio > 65536)
+    return fail(DIT_EINVAL, "capacity too large");
+  if (!(c->eps > 0) || !std::isfinite(c->eps)) return fail(DIT_EINVAL, "eps must be finite and > 0");
+  if (!(c->rope_theta > 1) || !std::isfinite(c->rope_theta)) return fail(DIT_EINVAL, "rope_theta must be finite and > 1");
+  return DIT_OK;
+}
+
+Layout make_layout(const dit_config* c) {
+  Layout L;
+  L.elt = c->dtype == DIT_BF16 ? 2 : 4;
+  const size_t D = c->D;
+  L.F = c->mlp_ratio * c->D;
+  L.C_in = c->c_p + c->c_c;
+  int mx = c->max_tokens;
+  if (c->max_ref > mx) mx = c->max_ref;
+  if (c->max_bnd > mx) mx = c->max_bnd;
+  L.cap_tok = round64(mx);
+  L.cap_ref = round64(c->max_ref);
+  L.cap_bnd = round64(c->max_bnd);
+  L.cap_audio = round64(c->max_audio > 0 ? c->max_audio : 1);
+  L.big_cols = 3 * c->D > L.F ? 3 * c->D : L.F;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t r = off; off += align256(bytes); return r; };
+  for (int l = 0; l < c->L; ++l) {
+    L.kref.push_back(take((size_t)L.cap_ref * D * L.elt));
+    L.vref.push_back(take((size_t)L.cap_ref * D * L.elt));
+    L.kbnd.push_back(take((size_t)L.cap_bnd * D * L.elt));
+    L.vbnd.push_back(take((size_t)L.cap_bnd * D * L.elt));
+  }
+  L.state_total = off;
+  off = 0;
+  const size_t T = L.cap_tok;
+  L.xin = take(T * L.C_in * L.elt);
+  L.h = take(T * D * 4);
+  L.u = take(T * D * L.elt);
+  L.big = take(T * L.big_cols * L.elt);
+  L.q = take(T * D * L.elt);
+  L.kc = take(T * D * L.elt);
+  L.vtc = take(T * D * L.elt);
+  L.o = take(T * D * L.elt);
+  const size_t A = L.cap_audio;
+  L.ain = take(A * (c->d_a > 0 ? c->d_a : 64) * L.elt);
+  L.ka_raw = take(A * D * L.elt);
+  L.va_raw = take(A * D * L.elt);
+  L.ka = take(A * D * L.elt);
+  L.vat = take(A * D * L.elt);
+  L.mod = take(((size_t)c->L * 6 * D + 2 * D) * 4);
+  L.tmp = take((256 + 2 * D) * 4);
+  L.ws_total = off;
+  return L;
+}
+
+constexpr int MAX_EVENT_PAIRS = 4096;
+
+}  // namespace
+
+namespace dit {
+int set_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+}  // namespace dit
+
+struct dit_handle {
+  dit_config cfg;
+  Layout lay;
+  std::vector<const void*> w;
+  char* state = nullptr;
+  char* ws = nullptr;
+  hipStream_t stream = nullptr;
+  bool has_ref = false;
+  int n_ref = 0, n_bnd = 0;
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created lazily
+  int ev_used = 0;
+  double flop_acc = 0.0;
+
+  const void* W(int i) const { return w[i]; }
+  const void* B(int l, int i) const { return w[DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT + i]; }
+  template <class P = void> P* S(size_t off) const { return reinterpret_cast<P*>(state + off); }
+  template <class P = void> P* X(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+};
+
+namespace {
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess) return fail(DIT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+int timed_begin(dit_handle* h, int* slot) {
+  *slot = -1;
+  if (!h->timing) return DIT_OK;
+  if (h->ev.empty()) {
+    h->ev.resize(2 * MAX_EVENT_PAIRS);
+    for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
+  }
+  if (h->ev_used >= MAX_EVENT_PAIRS) return DIT_OK;
+  *slot = h->ev_used++;
+  HIPCHK(hipEventRecord(h->ev[2 * *slot], h->stream));
+  return DIT_OK;
+}
+int timed_end(dit_handle* h, int slot, double flop) {
+  if (slot < 0) return DIT_OK;
+  HIPCHK(hipEventRecord(h->ev[2 * slot + 1], h->stream));
+  h->flop_acc += flop;
+  return DIT_OK;
+}
+
+// One context pass (reference or boundary) at t = 0: writes K (normed, rotated) and V
+// of every block into kdst[l] / vdst[l] (capacity cap).  prior_k/prior_v/prior_n: the
+// earlier context segment (reference) per block, or none.
+int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::vector<size_t>& kdst,
+                 const std::vector<size_t>& vdst, int cap, bool with_prior) {
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  const int D = c.D, F = L.F;
+  hipStream_t s = hd->stream;
+  float* mod = hd->X<float>(L.mod);
+  float* fmod = mod + (size_t)c.L * 6 * D;
+  std::vector<const void*> mw(c.L), mb(c.L);
+  for (int l = 0; l < c.L; ++l) { mw[l] = hd->B(l, DIT_WB_MOD_W); mb[l] = hd->B(l, DIT_WB_MOD_B); }
+  HIPCHK(modulation(c.dtype, D, c.L, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                    hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
+                    hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
+  HIPCHK(patch_input(c.dtype, z, n, c.c_p, nullptr, c.c_c, 0, g, hd->X(L.xin), s));
+  float* h = hd->X<float>(L.h);
+  GemmEpi e{};
+  e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = D;
+  HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, D, L.C_in, e, s));
+  for (int l = 0; l < c.L; ++l) {
+    const float* m = mod + (size_t)l * 6 * D;
+    const bool last = l == c.L - 1;
+    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
+    e = GemmEpi{};
+    e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
+    const char* big = hd->X<char>(L.big);
+    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, last ? nullptr : big, big + (size_t)D * L.elt,
+                       big + (size_t)2 * D * L.elt, 3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK),
+                       1, g, (float)c.eps, (float)c.rope_theta, hd->X(L.q), hd->S(kdst[l]),
+                       hd->S(vdst[l]), cap, s));
+    if (last) break;
+    AttnSeg seg[2];
+    int ns = 0;
+    if (with_prior) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
+    seg[ns++] = AttnSeg{hd->S(kdst[l]), hd->S(vdst[l]), n, cap};
+    int slot;
+    int rc = timed_begin(hd, &slot);
+    if (rc) return rc;
+    HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, seg, ns, s));
+    long long nkv = n + (with_prior ? hd->n_ref : 0);
+    if ((rc = timed_end(hd, slot, 4.0 * n * (double)nkv * D))) return rc;
+    e = GemmEpi{};
+    e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
+    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));
+    e = GemmEpi{};
+    e.kind = EPI_GELU; e.bias = hd->B(l, DIT_WB_FC1_B); e.out = hd->X(L.big); e.ldo = F;
+    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
+    e = GemmEpi{};
+    e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
+  }
+  return DIT_OK;
+}
+
+bool grid_ok(const dit_grid& g) { return g.frames >= 1 && g.h >= 1 && g.w >= 1; }
+long long grid_n(const dit_grid& g) { return (long long)g.frames * g.h * g.w; }
+
+}  // namespace
+
+extern "C" {
+
+int dit_weight_count(const dit_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return DIT_W_GLOBAL_COUNT + cfg->L * DIT_W_BLOCK_COUNT;
+}
+
+size_t dit_state_bytes(const dit_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return make_layout(cfg).state_total;
+}
+
+size_t dit_workspace_bytes(const dit_config* cfg) {
+  if (check_config(cfg)) return 0;
+  return make_layout(cfg).ws_total;
+}
+
+int dit_create(const dit_config* cfg, const void* const* weights, void* state, size_t state_bytes,
+               void* workspace, size_t workspace_bytes, void* hip_stream, dit_handle** out) {
+  if (!out) return fail(DIT_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!weights) return fail(DIT_EINVAL, "weights is NULL");
+  if (!state || !workspace) return fail(DIT_EINVAL, "state/workspace is NULL");
+  if (((uintptr_t)state & 255) || ((uintptr_t)workspace & 255))
+    return fail(DIT_EINVAL, "state/workspace must be 256-byte aligned");
+  Layout L = make_layout(cfg);
+  if (state_bytes < L.state_total)
+    return fail(DIT_EWORKSPACE, "state %zu bytes < required %zu", state_bytes, L.state_total);
+  if (workspace_bytes < L.ws_total)
+    return fail(DIT_EWORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, L.ws_total);
+  const int nw = DIT_W_GLOBAL_COUNT + cfg->L * DIT_W_BLOCK_COUNT;
+  for (int i = 0; i < nw; ++i) {
+    const int j = i < DIT_W_GLOBAL_COUNT ? -1 : (i - DIT_W_GLOBAL_COUNT) % DIT_W_BLOCK_COUNT;
+    const bool cross = j >= DIT_WB_CQ_W && j <= DIT_WB_CO_B;
+    if (!weights[i] && !(cross && cfg->d_a == 0)) return fail(DIT_EINVAL, "weight %d is NULL", i);
+    if (weights[i] && ((uintptr_t)weights[i] & 15)) return fail(DIT_EINVAL, "weight %d not 16-byte aligned", i);
+  }
+  dit_handle* h = new dit_handle();
+  h->cfg = *cfg;
+  h->lay = L;
+  h->w.assign(weights, weights + nw);
+  h->state = static_cast<char*>(state);
+  h->ws = static_cast<char*>(workspace);
+  h->stream = static_cast<hipStream_t>(hip_stream);
+  *out = h;
+  return DIT_OK;
+}
+
+int dit_destroy(dit_handle* h) {
+  if (!h) return DIT_OK;
+  for (auto& e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+  return DIT_OK;
+}
+
+int ref_kv_precompute(dit_handle* h, const float* ref, dit_grid grid) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (!ref) return fail(DIT_EINVAL, "ref is NULL");
+  if (!grid_ok(grid)) return fail(DIT_ESHAPE, "empty reference grid");
+  const long long n = grid_n(grid);
+  if (n > h->cfg.max_ref) return fail(DIT_ESHAPE, "reference tokens %lld > max_ref %d", n, h->cfg.max_ref);
+  h->has_ref = false;
+  h->n_bnd = 0;
+  RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
+  int rc = context_pass(h, ref, (int)n, g, h->lay.kref, h->lay.vref, h->lay.cap_ref, false);
+  if (rc) return rc;
+  h->n_ref = (int)n;
+  h->has_ref = true;
+  return DIT_OK;
+}
+
+int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (prev.frames == 0) {
+    h->n_bnd = 0;
+    return DIT_OK;
+  }
+  if (!x_prev) return fail(DIT_EINVAL, "x_prev is NULL");
+  if (!grid_ok(prev)) return fail(DIT_ESHAPE, "bad previous-chunk grid");
+  const long long n = (long long)prev.h * prev.w;
+  if (n > h->cfg.max_bnd) return fail(DIT_ESHAPE, "boundary tokens %lld > max_bnd %d", n, h->cfg.max_bnd);
+  if (!h->has_ref) return fail(DIT_ESTATE, "boundary_kv_carry before ref_kv_precompute");
+  h->n_bnd = 0;
+  const float* last = x_prev + (size_t)(prev.frames - 1) * n * h->cfg.c_p;
+  RopeGrid g{-1, 1, prev.h, prev.w};
+  int rc = context_pass(h, last, (int)n, g, h->lay.kbnd, h->lay.vbnd, h->lay.cap_bnd, true);
+  if (rc) return rc;
+  h->n_bnd = (int)n;
+  return DIT_OK;
+}
+
+int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
+                   dit_grid chunk, double t, double t_next, float* v_out) {
+  if (!hd) return fail(DIT_EINVAL, "handle is NULL");
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  if (!x) return fail(DIT_EINVAL, "x is NULL");
+  if (!std::isfinite(t) || !std::isfinite(t_next)) return fail(DIT_EINVAL, "t/t_next not finite");
+  if (!grid_ok(chunk)) return fail(DIT_ESHAPE, "empty chunk grid");
+  const long long nn = grid_n(chunk);
+  if (nn > c.max_tokens) return fail(DIT_ESHAPE, "chunk tokens %lld > max_tokens %d", nn, c.max_tokens);
+  if (c.c_c > 0 && !cond) return fail(DIT_EINVAL, "cond is NULL but c_c=%d", c.c_c);
+  if (c.c_c == 0 && cond) return fail(DIT_EINVAL, "cond given but c_c=0");
+  if (c.c_c > 0 && c.cond_up == 2 && (chunk.h % 2 || chunk.w % 2))
+    return fail(DIT_ESHAPE, "cond_up=2 needs even h and w");
+  if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
+  if (M > 0 && !audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
+  if (M > 0 && c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
+  if (!hd->has_ref) return fail(DIT_ESTATE, "dit_chunk_step before ref_kv_precompute");
+
+  const int n = (int)nn, D = c.D, F = L.F;
+  hipStream_t s = hd->stream;
+  RopeGrid g{chunk.t0, chunk.frames, chunk.h, chunk.w};
+  float* mod = hd->X<float>(L.mod);
+  float* fmod = mod + (size_t)c.L * 6 * D;
+  std::vector<const void*> mw(c.L), mb(c.L);
+  for (int l = 0; l < c.L; ++l) { mw[l] = hd->B(l, DIT_WB_MOD_W); mb[l] = hd->B(l, DIT_WB_MOD_B); }
+  HIPCHK(modulation(c.dtype, D, c.L, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                    hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
+                    hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
+  HIPCHK(patch_input(c.dtype, x, n, c.c_p, cond, c.c_c, c.c_c ? c.cond_up : 0, g, hd->X(L.xin), s));
+  const bool cross = M > 0 && c.d_a > 0;
+  if (cross)
+    HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g, hd->X(L.ain), s));
+  float* h = hd->X<float>(L.h);
+  GemmEpi e{};
+  e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = D;
+  HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, D, L.C_in, e, s));
+  const char* big = hd->X<char>(L.big);
+  for (int l = 0; l < c.L; ++l) {
+    const float* m = mod + (size_t)l * 6 * D;
+    // self-attention
+    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
+    e = GemmEpi{};
+    e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
+    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, big + (size_t)D * L.elt, big + (size_t)2 * D * L.elt,
+                       3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g, (float)c.eps,
+                       (float)c.rope_theta, hd->X(L.q), hd->X(L.kc), hd->X(L.vtc), L.cap_tok, s));
+    AttnSeg seg[3];
+    int ns = 0;
+    seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
+    if (hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
+    seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
+    int slot;
+    int rc = timed_begin(hd, &slot);
+    if (rc) return rc;
+    HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, seg, ns, s));
+    const double nkv = (double)n + hd->n_ref + hd->n_bnd;
+    if ((rc = timed_end(hd, slot, 4.0 * n * nkv * D))) return rc;
+    e = GemmEpi{};
+    e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
+    // audio cross-attention
+    if (cross) {
+      HIPCHK(rmsnorm_mod(c.dtype, h, n, D, nullptr, nullptr, (float)c.eps, hd->X(L.u), s));
+      e = GemmEpi{};
+      e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
+      HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+      HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
+                         nullptr, 0, g, (float)c.eps, (float)c.rope_theta, hd->X(L.q), nullptr,
+                         nullptr, L.cap_tok, s));
+      e = GemmEpi{};
+      e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CK_B); e.out = hd->X(L.ka_raw); e.ldo = D;
+      HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
+      e.bias = hd->B(l, DIT_WB_CV_B); e.out = hd->X(L.va_raw);
+      HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
+      HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
+                         hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, nullptr,
+                         hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
+      AttnSeg aseg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
+      HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, &aseg, 1, s));
+      e = GemmEpi{};
+      e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
+      HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));
+    }
+    // MLP
+    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));
+    e = GemmEpi{};
+    e.kind = EPI_GELU; e.bias = hd->B(l, DIT_WB_FC1_B); e.out = hd->X(L.big); e.ldo = F;
+    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
+    e = GemmEpi{};
+    e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
+    HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
+  }
+  // final layer + Euler
+  HIPCHK(rmsnorm_mod(c.dtype, h, n, D, fmod, fmod + D, (float)c.eps, hd->X(L.u), s));
+  e = GemmEpi{};
+  e.kind = EPI_EULER; e.bias = hd->W(DIT_W_FIN_B); e.out = x; e.ldo = c.c_p; e.v_out = v_out;
+  e.dt = (float)(t_next - t);
+  HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->W(DIT_W_FIN_W), D, n, c.c_p, D, e, s));
+  return DIT_OK;
+}
+
+int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_stream) {
+  if (n < 0) return fail(DIT_EINVAL, "n < 0");
+  if (n == 0) return DIT_OK;
+  if (!x || !v) return fail(DIT_EINVAL, "x or v is NULL");
+  if (!std::isfinite(dt)) return fail(DIT_EINVAL, "dt not finite");
+  if (((uintptr_t)x & 15) || ((uintptr_t)v & 15)) return fail(DIT_EINVAL, "x, v must be 16-byte aligned");
+  HIPCHK(euler(x, v, (float)dt, n, static_cast<hipStream_t>(hip_stream)));
+  return DIT_OK;
+}
+
+const char* dit_last_error(void) { return g_err.c_str(); }
+
+int dit_timing_enable(dit_handle* h, int enable) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  h->timing = enable != 0;
+  h->ev_used = 0;
+  h->flop_acc = 0.0;
+  return DIT_OK;
+}
+
+int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_flop) {
+  if (!h || !count || !total_ms) return fail(DIT_EINVAL, "NULL argument");
+  if (kind != DIT_TIME_ATTN) return fail(DIT_EINVAL, "kind %d", kind);
+  double ms = 0.0;
+  for (int i = 0; i < h->ev_used; ++i) {
+    HIPCHK(hipEventSynchronize(h->ev[2 * i + 1]));
+    float f = 0.f;
+    HIPCHK(hipEventElapsedTime(&f, h->ev[2 * i], h->ev[2 * i + 1]));
+    ms += f;
+  }
+  *count = h->ev_used;
+  *total_ms = ms;
+  if (total_flop) *total_flop = h->flop_acc;
+  h->ev_used = 0;
+  h->flop_acc = 0.0;
+  return DIT_OK;
+}
+
+}  // extern "C"

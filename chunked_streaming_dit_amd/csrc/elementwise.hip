@@ -1,0 +1,338 @@
+// Bandwidth-bound kernels: RMSNorm + adaLN modulate, per-head QK-norm + 3D RoPE with
+// K/V repacking into the attention layout, patch-embed input assembly (with the
+// nearest-2x conditioning upsample), the Euler update, and the timestep-conditioning
+// / modulation GEMVs.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+// ---------------------------------------------------------------- RMSNorm + modulate
+// One wave per row; each lane holds D/256 float4 groups in registers (D <= 4096).
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float* __restrict__ h, int n,
+                                                          int D, const float* __restrict__ shift,
+                                                          const float* __restrict__ scale,
+                                                          float eps, T* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const float* hr = h + (size_t)row * D;
+  const int iters = D >> 8;
+  f32x4 v[16];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < iters) {
+      v[i] = *reinterpret_cast<const f32x4*>(hr + i * 256 + lane * 4);
+      ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    }
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+  T* orow = out + (size_t)row * D;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (i < iters) {
+      const int c = i * 256 + lane * 4;
+      float o[4];
+      if (scale) {
+        f32x4 sc = *reinterpret_cast<const f32x4*>(scale + c);
+        f32x4 sh = *reinterpret_cast<const f32x4*>(shift + c);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = fmaf(v[i][r] * rs, 1.0f + sc[r], sh[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = v[i][r] * rs;
+      }
+      store4<T>(orow + c, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- QK-norm + RoPE + repack
+// Grid: (round_up(n, 64) / 64, H).  A workgroup owns 64 tokens x one head.  Each lane
+// holds one rotation pair (dims 2i, 2i+1); dh/2 lanes make one token, so a wave
+// handles 64/(dh/2) tokens at a time.  V rows are staged in LDS and written out
+// transposed ([dh, cap] per head) in the attention kernel's key order.
+template <class T, int DH>
+__global__ __launch_bounds__(256) void qknorm_rope_kernel(
+    int n, const T* __restrict__ q_in, const T* __restrict__ k_in, const T* __restrict__ v_in,
+    int ld_in, const T* __restrict__ gq, const T* __restrict__ gk, int rope, RopeGrid g,
+    float eps, float log2_theta, T* __restrict__ q_out, T* __restrict__ k_out,
+    T* __restrict__ vt_out, int cap, int D) {
+  constexpr int PAIRS = DH / 2;
+  constexpr int TPI = 64 / PAIRS;  // tokens per wave iteration
+  constexpr int VE = Vec<T>::n;
+  __shared__ T sv[64][DH + 2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int head = blockIdx.y;
+  const int tok0 = blockIdx.x * 64;
+  const int pair = lane % PAIRS;
+  const int sub = lane / PAIRS;
+
+  // Rotation frequency of this lane's pair: axis t for the first d_t/2 pairs, then y,
+  // then x; pair j of an axis with d_a dims turns at theta^(-2j/d_a).
+  const int d_hw = 2 * (DH / 6);
+  const int d_t = DH - 2 * d_hw;
+  int axis, j, d_a;
+  if (pair < d_t / 2) { axis = 0; j = pair; d_a = d_t; }
+  else if (pair < d_t / 2 + d_hw / 2) { axis = 1; j = pair - d_t / 2; d_a = d_hw; }
+  else { axis = 2; j = pair - d_t / 2 - d_hw / 2; d_a = d_hw; }
+  const float inv_freq = exp2f(-(2.0f * (float)j / (float)d_a) * log2_theta);
+  const float gq0 = gq ? to_f(gq[2 * pair]) : 0.f, gq1 = gq ? to_f(gq[2 * pair + 1]) : 0.f;
+  const float gk0 = gk ? to_f(gk[2 * pair]) : 0.f, gk1 = gk ? to_f(gk[2 * pair + 1]) : 0.f;
+  const int hw = g.h * g.w;
+
+  for (int it = wave * TPI + sub; it < 64; it += 4 * TPI) {
+    const int tok = tok0 + it;
+    const bool valid = tok < n;
+    float c = 1.f, s = 0.f;
+    if (rope && valid) {
+      const int f = tok / hw, rem = tok - f * hw;
+      const int y = rem / g.w, x = rem - y * g.w;
+      const int p = axis == 0 ? g.t0 + f : (axis == 1 ? y : x);
+      sincosf((float)p * inv_freq, &s, &c);
+    }
+    const size_t src = (size_t)tok * ld_in + head * DH + 2 * pair;
+    const size_t dst = (size_t)tok * D + head * DH + 2 * pair;
+    // q: norm + gamma + rotation (only valid tokens are written)
+    if (q_in) {
+      float x0 = 0.f, x1 = 0.f;
+      if (valid) { x0 = to_f(q_in[src]); x1 = to_f(q_in[src + 1]); }
+      float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+      for (int o = PAIRS / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
+      const float y0 = x0 * rs * gq0, y1 = x1 * rs * gq1;
+      if (valid) {
+        q_out[dst] = from_f<T>(y0 * c - y1 * s);
+        q_out[dst + 1] = from_f<T>(y0 * s + y1 * c);
+      }
+    }
+    if (k_in) {
+      float x0 = 0.f, x1 = 0.f;
+      if (valid) { x0 = to_f(k_in[src]); x1 = to_f(k_in[src + 1]); }
+      float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+      for (int o = PAIRS / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
+      const float y0 = x0 * rs * gk0, y1 = x1 * rs * gk1;
+      k_out[dst] = from_f<T>(valid ? y0 * c - y1 * s : 0.f);
+      k_out[dst + 1] = from_f<T>(valid ? y0 * s + y1 * c : 0.f);
+    }
+    if (v_in) {
+      T a = from_f<T>(0.f), b = from_f<T>(0.f);
+      if (valid) { a = v_in[src]; b = v_in[src + 1]; }
+      sv[it][2 * pair] = a;
+      sv[it][2 * pair + 1] = b;
+    }
+  }
+  if (!v_in) return;
+  __syncthreads();
+  // V^T: row d of this head gets the 64 tokens of the tile, 16 bytes per thread-chunk.
+  constexpr int CPR = 64 / VE;  // chunks per row
+  for (int c = tid; c < DH * CPR; c += 256) {
+    const int d = c / CPR, pos0 = (c % CPR) * VE;
+    typename Vec<T>::type out;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      const int p = pos0 + e;
+      int key = p;
+      if constexpr (sizeof(T) == 2) {  // MFMA operand order within each 16-key group
+        const int q16 = p & 15, gg = q16 >> 3, jj = q16 & 7;
+        key = (p & ~15) + 8 * (jj >> 2) + 4 * gg + (jj & 3);
+      }
+      out[e] = sv[key][d];
+    }
+    *reinterpret_cast<typename Vec<T>::type*>(vt_out + (size_t)(head * DH + d) * cap + tok0 + pos0) = out;
+  }
+}
+
+// ---------------------------------------------------------------- patch-embed input
+template <class T>
+__global__ void patch_input_kernel(const float* __restrict__ x, int n, int c_p,
+                                   const float* __restrict__ cond, int c_c, int mode, RopeGrid g,
+                                   T* __restrict__ xin) {
+  const int C = c_p + c_c;
+  const long long total = (long long)n * C;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int tok = (int)(i / C), ch = (int)(i - (long long)tok * C);
+    float v;
+    if (ch < c_p) {
+      v = x[(size_t)tok * c_p + ch];
+    } else {
+      const int cc = ch - c_p;
+      if (mode == 0) {
+        v = 0.f;
+      } else if (mode == 1) {
+        v = cond[(size_t)tok * c_c + cc];
+      } else {
+        // token (f, y, x), channel (c, dy, dx) <- half-res token (f, y/2, x/2),
+        // channel (c, y%2, x%2): nearest 2x upsample in pixel space, re-patchified.
+        const int hw = g.h * g.w;
+        const int f = tok / hw, rem = tok - f * hw;
+        const int y = rem / g.w, xx = rem - y * g.w;
+        const int hl = g.h / 2, wl = g.w / 2;
+        const int src_tok = (f * hl + y / 2) * wl + xx / 2;
+        const int src_ch = (cc / 4) * 4 + (y % 2) * 2 + (xx % 2);
+        v = cond[(size_t)src_tok * c_c + src_ch];
+      }
+    }
+    xin[i] = from_f<T>(v);
+  }
+}
+
+__global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dt,
+                             long long n) {
+  const long long n4 = n / 4;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    f32x4 a = reinterpret_cast<f32x4*>(x)[i];
+    f32x4 b = reinterpret_cast<const f32x4*>(v)[i];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = fmaf(dt, b[r], a[r]);
+    reinterpret_cast<f32x4*>(x)[i] = a;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const long long i = n4 * 4 + threadIdx.x;
+    x[i] = fmaf(dt, v[i], x[i]);
+  }
+}
+
+// ---------------------------------------------------------------- timestep conditioning
+// phi(t) = [cos(s w_i) || sin(s w_i)], s = 1000 t, w_i = 10000^(-i/128), in double.
+__global__ void timestep_features_kernel(double t, float* __restrict__ phi) {
+  const int i = threadIdx.x;  // 128 threads
+  const double s = 1000.0 * t;
+  const double w = pow(10000.0, -(double)i / 128.0);
+  phi[i] = (float)cos(s * w);
+  phi[128 + i] = (float)sin(s * w);
+}
+
+// y[r] = act(W[r, :] . x + b[r]) for r < R; one wave per output row.
+template <class T, int ACT>
+__global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
+                                                   const T* __restrict__ b, int R, int K,
+                                                   const float* __restrict__ x,
+                                                   float* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const T* wr = W + (size_t)r * K;
+  float acc = 0.f;
+  for (int k = lane * 4; k < K; k += 256) {
+    float w4[4];
+    load4<T>(wr + k, w4);
+    f32x4 x4 = *reinterpret_cast<const f32x4*>(x + k);
+    acc += w4[0] * x4[0] + w4[1] * x4[1] + w4[2] * x4[2] + w4[3] * x4[3];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    float v = acc + to_f(b[r]);
+    if (ACT) v = silu(v);
+    y[r] = v;
+  }
+}
+
+template <class T>
+hipError_t modulation_t(int D, int L, double t, const void* t1w, const void* t1b, const void* t2w,
+                        const void* t2b, const void* const* modw, const void* const* modb,
+                        const void* fmodw, const void* fmodb, float* tmp, float* mod_out,
+                        float* fmod_out, hipStream_t s) {
+  float* phi = tmp;            // [256]
+  float* e1 = tmp + 256;       // [D]
+  float* c = tmp + 256 + D;    // [D]
+  timestep_features_kernel<<<1, 128, 0, s>>>(t, phi);
+  auto G = [&](const void* w, const void* b, int R, int K, const float* x, float* y, int act) {
+    dim3 grid((R + 3) / 4);
+    if (act)
+      gemv_kernel<T, 1><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, y);
+    else
+      gemv_kernel<T, 0><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, y);
+  };
+  G(t1w, t1b, D, 256, phi, e1, 1);
+  G(t2w, t2b, D, D, e1, c, 1);
+  for (int l = 0; l < L; ++l) G(modw[l], modb[l], 6 * D, D, c, mod_out + (size_t)l * 6 * D, 0);
+  G(fmodw, fmodb, 2 * D, D, c, fmod_out, 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shift,
+                       const float* scale, float eps, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (D % 256 || D > 4096) return hipErrorInvalidValue;
+  dim3 grid((n + 3) / 4);
+  if (dtype == BF16)
+    rmsnorm_mod_kernel<bf16><<<grid, 256, 0, s>>>(h, n, D, shift, scale, eps, (bf16*)out);
+  else
+    rmsnorm_mod_kernel<float><<<grid, 256, 0, s>>>(h, n, D, shift, scale, eps, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
+                       const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
+                       RopeGrid g, float eps, float theta, void* q_out, void* k_out,
+                       void* vt_out, int cap, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int npad = (n + 63) / 64 * 64;
+  if (npad > cap && (k_in || v_in)) return hipErrorInvalidValue;
+  dim3 grid(npad / 64, H);
+  const float l2t = log2f(theta);
+  const int D = H * dh;
+#define QKR(T, DHV)                                                                          \
+  qknorm_rope_kernel<T, DHV><<<grid, 256, 0, s>>>(n, (const T*)q_in, (const T*)k_in,         \
+                                                  (const T*)v_in, ld_in, (const T*)gq,       \
+                                                  (const T*)gk, rope, g, eps, l2t, (T*)q_out, \
+                                                  (T*)k_out, (T*)vt_out, cap, D)
+  if (dtype == BF16 && dh == 128) QKR(bf16, 128);
+  else if (dtype == BF16 && dh == 64) QKR(bf16, 64);
+  else if (dtype == F32 && dh == 128) QKR(float, 128);
+  else if (dtype == F32 && dh == 64) QKR(float, 64);
+  else return hipErrorInvalidValue;
+#undef QKR
+  return hipGetLastError();
+}
+
+hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
+                       int cond_mode, RopeGrid g, void* xin, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long total = (long long)n * (c_p + c_c);
+  const int blocks = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  if (dtype == BF16)
+    patch_input_kernel<bf16><<<blocks, 256, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g, (bf16*)xin);
+  else
+    patch_input_kernel<float><<<blocks, 256, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g, (float*)xin);
+  return hipGetLastError();
+}
+
+hipError_t euler(float* x, const float* v, float dt, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  euler_kernel<<<(int)blocks, 256, 0, s>>>(x, v, dt, n);
+  return hipGetLastError();
+}
+
+hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const void* t1b,
+                      const void* t2w, const void* t2b, const void* const* modw,
+                      const void* const* modb, const void* fmodw, const void* fmodb, float* tmp,
+                      float* mod_out, float* fmod_out, hipStream_t s) {
+  if (D % 256) return hipErrorInvalidValue;
+  if (dtype == BF16)
+    return modulation_t<bf16>(D, L, t, t1w, t1b, t2w, t2b, modw, modb, fmodw, fmodb, tmp, mod_out,
+                              fmod_out, s);
+  return modulation_t<float>(D, L, t, t1w, t1b, t2w, t2b, modw, modb, fmodw, fmodb, tmp, mod_out,
+                             fmod_out, s);
+}
+
+}  // namespace dit

@@ -1,0 +1,83 @@
+// Host-side launchers of the device kernels (internal to libditchunk).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace dit {
+
+enum Dtype { F32 = 0, BF16 = 1 };
+
+// ---------------------------------------------------------------- GEMM (MFMA)
+// C = A W^T (+ bias), A [M, K] (lda), W [N, K] (ldw), fp32 accumulation, then:
+enum EpiKind {
+  EPI_BIAS = 0,   // out[M, N] (dtype)  = C + b
+  EPI_GELU = 1,   // out[M, N] (dtype)  = GELU_tanh(C + b)
+  EPI_RESID = 2,  // h[M, N]   (fp32)  += gate (.) (C + b)      (gate NULL: 1)
+  EPI_F32 = 3,    // out[M, N] (fp32)   = C + b
+  EPI_EULER = 4,  // v = C + b; x[M, N] (fp32) += dt v; v_out (fp32, optional) = v
+};
+struct GemmEpi {
+  int kind;
+  const void* bias;   // [N] dtype
+  void* out;          // EPI_BIAS/EPI_GELU/EPI_F32 output, EPI_RESID h, EPI_EULER x
+  int ldo;
+  const float* gate;  // EPI_RESID
+  float* v_out;       // EPI_EULER
+  float dt;           // EPI_EULER
+};
+hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                const GemmEpi& e, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+// K/V segment in the attention layout:
+//   k  [cap, ldk] row-major, head h at columns [h*dh, (h+1)*dh); rows >= n are zero.
+//   vt [H*dh, cap] (V transposed); columns >= n are zero.  For bf16 the keys of each
+//      aligned group of 16 are stored in MFMA operand order: key offset o sits at
+//      position 8*((o%8)/4) + 4*(o/8) + o%4.  fp32 keeps natural order.
+//   cap is a multiple of 64.
+struct AttnSeg {
+  const void* k;
+  const void* vt;
+  int n;
+  int cap;
+};
+enum { ATTN_MAX_SEGS = 3 };
+// o[nq, ldo] = softmax(q k^T / sqrt(dh)) v over the concatenated segments, per head.
+hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
+                     int ldk, const AttnSeg* segs, int nseg, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+// out[n, D] (dtype) = RMSNorm(h) * (1 + scale) + shift  (shift/scale NULL: plain RMSNorm)
+hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shift,
+                       const float* scale, float eps, void* out, hipStream_t s);
+
+// Per-head QK-norm (+ optional 3D RoPE) and K/V repacking.
+//   q_in/k_in/v_in: [n, ld_in] dtype (any may be NULL); gq/gk [dh] dtype.
+//   q_out [n, D] (plain), k_out [cap, D], vt_out [D, cap] (attention layout above).
+//   Rows/columns in [n, round_up(n, 64)) of k_out/vt_out are zeroed.
+//   rope: positions from the grid (t0 + f, y, x); rope == 0: no rotation.
+struct RopeGrid {
+  int t0, frames, h, w;
+};
+hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
+                       const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
+                       RopeGrid g, float eps, float theta, void* q_out, void* k_out,
+                       void* vt_out, int cap, hipStream_t s);
+
+// xin[n, c_p + c_c] (dtype) = [x rows (row_off..) || cond]; cond modes: 0 zero, 1 per-token
+// [n, c_c], 2 nearest-2x upsample of [frames*(h/2)*(w/2), c_c] on grid g.
+hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
+                       int cond_mode, RopeGrid g, void* xin, hipStream_t s);
+
+// x[i] += dt * v[i]
+hipError_t euler(float* x, const float* v, float dt, long long n, hipStream_t s);
+
+// Timestep conditioning c = SiLU(W2 SiLU(W1 phi(t) + b1) + b2) and per-block modulation
+// mod[l] = Wmod_l c + bmod_l ([6D]) and final fmod = Wf c + bf ([2D]).
+// tmp: fp32 scratch of 2*D floats.
+hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const void* t1b,
+                      const void* t2w, const void* t2b, const void* const* modw,
+                      const void* const* modb, const void* fmodw, const void* fmodb, float* tmp,
+                      float* mod_out, float* fmod_out, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,167 @@
+// Kernel-level entry points (include/ditchunk_ops.h): host validation, then one launch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "ditchunk.h"
+#include "ditchunk_ops.h"
+#include "kernels.h"
+
+using namespace dit;
+
+// Shared with ditchunk.cpp: the thread-local error message.
+extern "C" const char* dit_last_error(void);
+namespace dit {
+int set_error(int code, const char* msg);
+}
+
+namespace {
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  return dit::set_error(code, buf);
+}
+
+int hipchk(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DIT_OK;
+}
+
+bool dtype_ok(int d) { return d == DIT_F32 || d == DIT_BF16; }
+
+int gemm_args(int dtype, const void* A, const void* W, const void* b, int M, int N, int K) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (!A || !W || !b) return fail(DIT_EINVAL, "A, W and b must be non-NULL");
+  if (M < 0 || N < 1 || K < 1) return fail(DIT_ESHAPE, "M=%d N=%d K=%d", M, N, K);
+  if (K % 64) return fail(DIT_ESHAPE, "K=%d must be a multiple of 64", K);
+  if (N % 4) return fail(DIT_ESHAPE, "N=%d must be a multiple of 4", N);
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, int N, int K,
+                int act, void* out, void* stream) {
+  int rc = gemm_args(dtype, A, W, b, M, N, K);
+  if (rc) return rc;
+  if (!out) return fail(DIT_EINVAL, "out is NULL");
+  GemmEpi e{};
+  if (act == DITK_ACT_NONE) e.kind = EPI_BIAS;
+  else if (act == DITK_ACT_GELU) e.kind = EPI_GELU;
+  else if (act == DITK_OUT_F32) e.kind = EPI_F32;
+  else return fail(DIT_EINVAL, "act %d", act);
+  e.bias = b;
+  e.out = out;
+  e.ldo = N;
+  return hipchk(gemm(dtype, A, K, W, K, M, N, K, e, (hipStream_t)stream), "gemm");
+}
+
+int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b, const float* gate,
+                         int M, int N, int K, float* h, void* stream) {
+  int rc = gemm_args(dtype, A, W, b, M, N, K);
+  if (rc) return rc;
+  if (!h) return fail(DIT_EINVAL, "h is NULL");
+  GemmEpi e{};
+  e.kind = EPI_RESID;
+  e.bias = b;
+  e.out = h;
+  e.ldo = N;
+  e.gate = gate;
+  return hipchk(gemm(dtype, A, K, W, K, M, N, K, e, (hipStream_t)stream), "gemm");
+}
+
+int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* shift,
+                          const float* scale, double eps, void* out, void* stream) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (!h || !out) return fail(DIT_EINVAL, "h/out NULL");
+  if (!shift != !scale) return fail(DIT_EINVAL, "shift and scale must both be given or both NULL");
+  if (n < 0 || D < 256 || D % 256 || D > 4096) return fail(DIT_ESHAPE, "n=%d D=%d", n, D);
+  if (!(eps > 0) || !std::isfinite(eps)) return fail(DIT_EINVAL, "eps");
+  return hipchk(rmsnorm_mod(dtype, h, n, D, shift, scale, (float)eps, out, (hipStream_t)stream),
+                "rmsnorm_mod");
+}
+
+int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
+                     const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
+                     dit_grid grid, double eps, double theta, void* q_out, void* k_out,
+                     void* vt_out, int cap, void* stream) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
+  if (H < 1 || n < 0 || ld_in < H * dh) return fail(DIT_ESHAPE, "H=%d n=%d ld_in=%d", H, n, ld_in);
+  if ((q_in && (!q_out || !gq)) || (k_in && (!k_out || !gk)) || (v_in && !vt_out))
+    return fail(DIT_EINVAL, "missing output or gamma");
+  if ((k_in || v_in) && (cap % 64 || cap < (n + 63) / 64 * 64))
+    return fail(DIT_ESHAPE, "cap=%d must be a multiple of 64 >= n=%d", cap, n);
+  if (rope && (grid.frames < 1 || grid.h < 1 || grid.w < 1 || (long long)grid.frames * grid.h * grid.w < n))
+    return fail(DIT_ESHAPE, "grid does not cover n tokens");
+  if (!(eps > 0) || !(theta > 1)) return fail(DIT_EINVAL, "eps/theta");
+  RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
+  return hipchk(qknorm_rope(dtype, dh, H, n, q_in, k_in, v_in, ld_in, gq, gk, rope, g, (float)eps,
+                            (float)theta, q_out, k_out, vt_out, cap, (hipStream_t)stream),
+                "qknorm_rope");
+}
+
+int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
+                   const void* const* k, const void* const* vt, const int* n, const int* cap,
+                   void* o, void* stream) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
+  if (!q || !o || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
+  if (H < 1 || nq < 0 || nseg < 1 || nseg > ATTN_MAX_SEGS) return fail(DIT_ESHAPE, "H/nq/nseg");
+  AttnSeg seg[ATTN_MAX_SEGS];
+  long long total = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (n[i] < 0 || cap[i] % 64 || cap[i] < (n[i] + 63) / 64 * 64)
+      return fail(DIT_ESHAPE, "segment %d: n=%d cap=%d", i, n[i], cap[i]);
+    if (n[i] > 0 && (!k[i] || !vt[i])) return fail(DIT_EINVAL, "segment %d NULL", i);
+    seg[i] = AttnSeg{k[i], vt[i], n[i], cap[i]};
+    total += n[i];
+  }
+  if (total < 1) return fail(DIT_ESHAPE, "no keys");
+  const int D = H * dh;
+  return hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, (hipStream_t)stream),
+                "attention");
+}
+
+int ditk_modulation(int dtype, int D, int L, double t, const void* const* w, float* mod_out,
+                    float* fmod_out, float* tmp, void* stream) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (!w || !mod_out || !fmod_out || !tmp) return fail(DIT_EINVAL, "NULL argument");
+  if (D < 256 || D % 256 || L < 1) return fail(DIT_ESHAPE, "D=%d L=%d", D, L);
+  if (!std::isfinite(t)) return fail(DIT_EINVAL, "t not finite");
+  const void* mw[256];
+  const void* mb[256];
+  if (L > 256) return fail(DIT_ESHAPE, "L > 256");
+  for (int l = 0; l < L; ++l) {
+    mw[l] = w[DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT + DIT_WB_MOD_W];
+    mb[l] = w[DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT + DIT_WB_MOD_B];
+  }
+  return hipchk(modulation(dtype, D, L, t, w[DIT_W_T1_W], w[DIT_W_T1_B], w[DIT_W_T2_W],
+                           w[DIT_W_T2_B], mw, mb, w[DIT_W_FMOD_W], w[DIT_W_FMOD_B], tmp, mod_out,
+                           fmod_out, (hipStream_t)stream),
+                "modulation");
+}
+
+int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
+                     int cond_mode, dit_grid grid, void* xin, void* stream) {
+  if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if (!x || !xin || (cond_mode && !cond)) return fail(DIT_EINVAL, "NULL argument");
+  if (n < 0 || c_p < 1 || c_c < 0 || cond_mode < 0 || cond_mode > 2) return fail(DIT_ESHAPE, "shape");
+  if (cond_mode == 2 && (grid.h % 2 || grid.w % 2 || c_c % 4 ||
+                         (long long)grid.frames * grid.h * grid.w != n))
+    return fail(DIT_ESHAPE, "upsample grid");
+  RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
+  return hipchk(patch_input(dtype, x, n, c_p, cond, c_c, cond_mode, g, xin, (hipStream_t)stream),
+                "patch_input");
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+"""Python face of libditchunk: a handle class for the chunk step and thin op wrappers.
+
+Tensors must already live on the GPU, be contiguous and have the documented dtype;
+this module only checks that and passes pointers and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib as C
+
+__all__ = ["ChunkConfig", "DitChunk", "grid", "fm_euler_step", "ops", "torch_dtype"]
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def _dt_code(dtype: str) -> int:
+    return {"f32": C.DIT_F32, "bf16": C.DIT_BF16}[dtype]
+
+
+def grid(t0: int, frames: int, h: int, w: int) -> C.DitGrid:
+    return C.DitGrid(t0, frames, h, w)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype: Optional[torch.dtype] = None) -> None:
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    L: int
+    D: int
+    H: int
+    dh: int
+    mlp_ratio: int
+    c_p: int
+    c_c: int
+    cond_up: int
+    d_a: int
+    dtype: str
+    max_tokens: int
+    max_ref: int
+    max_bnd: int
+    max_audio: int
+    eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    def c_struct(self) -> C.DitConfig:
+        return C.DitConfig(self.L, self.D, self.H, self.dh, self.mlp_ratio, self.c_p, self.c_c,
+                           self.cond_up, self.d_a, _dt_code(self.dtype), self.max_tokens,
+                           self.max_ref, self.max_bnd, self.max_audio, self.eps, self.rope_theta)
+
+    def state_bytes(self) -> int:
+        cs = self.c_struct()
+        n = C.lib().dit_state_bytes(ctypes.byref(cs))
+        if n == 0:
+            raise C.DitError(C.DIT_EINVAL, C.last_error())
+        return n
+
+    def workspace_bytes(self) -> int:
+        cs = self.c_struct()
+        n = C.lib().dit_workspace_bytes(ctypes.byref(cs))
+        if n == 0:
+            raise C.DitError(C.DIT_EINVAL, C.last_error())
+        return n
+
+    def weight_names(self):
+        names = list(C.GLOBAL_ORDER)
+        for l in range(self.L):
+            names += [f"blk{l}.{b}" for b in C.BLOCK_ORDER]
+        return names
+
+
+class DitChunk:
+    """A libditchunk handle with its state and workspace allocated as torch tensors.
+
+    weights: name -> GPU tensor in the config's dtype (names of the ditchunk.h table:
+    "pe.w", ..., "blk{l}.qkv.w", ...); cross-attention entries may be absent when d_a == 0.
+    """
+
+    def __init__(self, cfg: ChunkConfig, weights: Dict[str, torch.Tensor],
+                 device: Optional[torch.device] = None):
+        self.cfg = cfg
+        self.device = device or torch.device("cuda", torch.cuda.current_device())
+        dt = torch_dtype(cfg.dtype)
+        names = cfg.weight_names()
+        ptrs = (C.P * len(names))()
+        self._weights = []
+        for i, nm in enumerate(names):
+            t = weights.get(nm)
+            if t is None:
+                ptrs[i] = None
+                continue
+            _dev(t, nm, dt)
+            self._weights.append(t)
+            ptrs[i] = t.data_ptr()
+        self.state = torch.empty(cfg.state_bytes(), dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device=self.device)
+        h = C.P()
+        cs = cfg.c_struct()
+        C.check(C.lib().dit_create(ctypes.byref(cs), ptrs, self.state.data_ptr(), self.state.numel(),
+                                   self.workspace.data_ptr(), self.workspace.numel(), _stream(),
+                                   ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            C.lib().dit_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def ref_kv_precompute(self, ref: torch.Tensor, g: C.DitGrid) -> None:
+        _dev(ref, "ref", torch.float32)
+        C.check(C.lib().ref_kv_precompute(self._h, ref.data_ptr(), g))
+
+    def boundary_kv_carry(self, x_prev: Optional[torch.Tensor], g: C.DitGrid) -> None:
+        _dev(x_prev, "x_prev", torch.float32)
+        C.check(C.lib().boundary_kv_carry(self._h, _ptr(x_prev), g))
+
+    def step(self, x: torch.Tensor, t: float, t_next: float, g: C.DitGrid,
+             cond: Optional[torch.Tensor] = None, audio: Optional[torch.Tensor] = None,
+             v_out: Optional[torch.Tensor] = None) -> None:
+        _dev(x, "x", torch.float32)
+        _dev(cond, "cond", torch.float32)
+        _dev(audio, "audio", torch.float32)
+        _dev(v_out, "v_out", torch.float32)
+        M = 0 if audio is None else audio.shape[0]
+        C.check(C.lib().dit_chunk_step(self._h, x.data_ptr(), _ptr(cond), _ptr(audio), M, g,
+                                       float(t), float(t_next), _ptr(v_out)))
+
+    def timing_enable(self, on: bool = True) -> None:
+        C.check(C.lib().dit_timing_enable(self._h, 1 if on else 0))
+
+    def timing_read(self) -> Tuple[int, float, float]:
+        """(launches, summed ms, summed algorithmic flop) of self-attention since the last read."""
+        n = ctypes.c_int()
+        ms = ctypes.c_double()
+        fl = ctypes.c_double()
+        C.check(C.lib().dit_timing_read(self._h, C.DIT_TIME_ATTN, ctypes.byref(n), ctypes.byref(ms),
+                                        ctypes.byref(fl)))
+        return n.value, ms.value, fl.value
+
+
+def fm_euler_step(x: torch.Tensor, v: torch.Tensor, dt: float) -> None:
+    _dev(x, "x", torch.float32)
+    _dev(v, "v", torch.float32)
+    if x.numel() != v.numel():
+        raise ValueError("x and v differ in size")
+    C.check(C.lib().fm_euler_step(x.data_ptr(), v.data_ptr(), float(dt), x.numel(), _stream()))
+
+
+class ops:
+    """Kernel-level entry points (ditchunk_ops.h)."""
+
+    @staticmethod
+    def linear(A, W, b, act: int, out, dtype: str) -> None:
+        M, K = A.shape
+        N = W.shape[0]
+        for t, n in ((A, "A"), (W, "W"), (b, "b"), (out, "out")):
+            _dev(t, n)
+        C.check(C.lib().ditk_linear(_dt_code(dtype), A.data_ptr(), W.data_ptr(), b.data_ptr(), M, N, K,
+                                    act, out.data_ptr(), _stream()))
+
+    @staticmethod
+    def linear_residual(A, W, b, gate, h, dtype: str) -> None:
+        M, K = A.shape
+        N = W.shape[0]
+        for t, n in ((A, "A"), (W, "W"), (b, "b"), (h, "h")):
+            _dev(t, n)
+        _dev(gate, "gate", torch.float32)
+        C.check(C.lib().ditk_linear_residual(_dt_code(dtype), A.data_ptr(), W.data_ptr(), b.data_ptr(),
+                                             _ptr(gate), M, N, K, h.data_ptr(), _stream()))
+
+    @staticmethod
+    def rmsnorm_modulate(h, shift, scale, eps, out, dtype: str) -> None:
+        _dev(h, "h", torch.float32)
+        _dev(out, "out")
+        n, D = h.shape
+        C.check(C.lib().ditk_rmsnorm_modulate(_dt_code(dtype), h.data_ptr(), n, D, _ptr(shift),
+                                              _ptr(scale), eps, out.data_ptr(), _stream()))
+
+    @staticmethod
+    def qknorm_rope(dtype: str, dh: int, H: int, n: int, q_in, k_in, v_in, ld_in: int, gq, gk,
+                    rope: bool, g: C.DitGrid, eps: float, theta: float, q_out, k_out, vt_out,
+                    cap: int) -> None:
+        C.check(C.lib().ditk_qknorm_rope(_dt_code(dtype), dh, H, n, _ptr(q_in), _ptr(k_in), _ptr(v_in),
+                                         ld_in, _ptr(gq), _ptr(gk), 1 if rope else 0, g, eps, theta,
+                                         _ptr(q_out), _ptr(k_out), _ptr(vt_out), cap, _stream()))
+
+    @staticmethod
+    def attention(dtype: str, dh: int, H: int, q, segs: Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]],
+                  o) -> None:
+        ns = len(segs)
+        kp = (C.P * ns)(*[s[0].data_ptr() for s in segs])
+        vp = (C.P * ns)(*[s[1].data_ptr() for s in segs])
+        nn = (ctypes.c_int * ns)(*[s[2] for s in segs])
+        cp = (ctypes.c_int * ns)(*[s[3] for s in segs])
+        C.check(C.lib().ditk_attention(_dt_code(dtype), dh, H, q.data_ptr(), q.shape[0], ns, kp, vp, nn,
+                                       cp, o.data_ptr(), _stream()))
+
+    @staticmethod
+    def modulation(dtype: str, cfg: ChunkConfig, weights: Dict[str, torch.Tensor], t: float,
+                   mod_out, fmod_out, tmp) -> None:
+        names = cfg.weight_names()
+        ptrs = (C.P * len(names))(*[(weights[n].data_ptr() if n in weights else None) for n in names])
+        C.check(C.lib().ditk_modulation(_dt_code(dtype), cfg.D, cfg.L, float(t), ptrs,
+                                        mod_out.data_ptr(), fmod_out.data_ptr(), tmp.data_ptr(),
+                                        _stream()))
+
+    @staticmethod
+    def patch_input(dtype: str, x, c_p: int, cond, c_c: int, mode: int, g: C.DitGrid, xin) -> None:
+        C.check(C.lib().ditk_patch_input(_dt_code(dtype), x.data_ptr(), x.shape[0], c_p, _ptr(cond), c_c,
+                                         mode, g, xin.data_ptr(), _stream()))

@@ -1,0 +1,219 @@
+/*
+ * ditchunk.h: C ABI of the chunked streaming DiT denoising step (MI355X, gfx950).
+ *
+ * What it computes.  HeyGen, "Avatar inference at scale":
+ *   - "The underlying model architecture": the generator is a diffusion
+ *     transformer trained with flow matching.  It is conditioned on rich
+ *     reference tokens, not on a compressed identity embedding.  Long videos are
+ *     made chunk by chunk: the first chunk relies on the static reference only,
+ *     and later chunks on boundary data from the previous segment.
+ *   - "The streaming framework and pipeline loop": the reference identity is
+ *     encoded once per request.  The audio-to-video stage then runs a multi-step
+ *     diffusion pass per chunk, conditioned on the previous chunk's boundary
+ *     frames.
+ *   - "Constant memory over duration": only the static reference conditioning
+ *     and a minimal set of anchor tensors persist between chunks, so peak memory
+ *     follows the chunk size, not the session length.
+ * Hence the call cadence:
+ *   ref_kv_precompute   once per request;
+ *   boundary_kv_carry   once per chunk (a zero-frame grid clears it for chunk 0);
+ *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
+ *   fm_euler_step       the bare Euler update, for callers with their own velocity.
+ *
+ * The block (readings of the pages, which give no internals): tokens are
+ * patchified latents [N, c_p] (fp32).  A patch-embed Linear feeds L blocks.
+ * Each block runs:
+ *   - RMSNorm + adaLN shift/scale, QKV, per-head QK-RMSNorm with gamma, and a 3D
+ *     RoPE over (t, y, x);
+ *   - self-attention whose keys are [reference K | boundary K | chunk K];
+ *   - a gated residual;
+ *   - RMSNorm, audio cross-attention (q and k per-head normed), and a residual;
+ *   - RMSNorm + adaLN, a GELU(tanh) MLP and a gated residual.
+ * A final RMSNorm + adaLN and a Linear give v [N, c_p].  Context tokens
+ * (reference, boundary) pass through the same blocks at t = 0: the reference
+ * sees only itself, and the boundary sees the reference and itself.  Their
+ * per-block K (normed, rotated) and V are kept resident, read-only, in the
+ * caller's state buffer.
+ *
+ * Ownership.  The caller owns ALL device memory:
+ *   - weights, state (dit_state_bytes), workspace (dit_workspace_bytes), and every
+ *     input and output buffer;
+ *   - the library borrows pointers and allocates nothing on the device.
+ * Every call is asynchronous on the handle's HIP stream.  A handle is not
+ * thread-safe; separate handles are independent.
+ *
+ * Errors.  Every int-returning call returns DIT_OK (0) or a negative code.
+ * Arguments and state are checked on the host before any HIP call; a failed
+ * check launches nothing and changes no state.  dit_last_error() gives a
+ * thread-local message for the last failure on the calling thread.
+ */
+#ifndef DITCHUNK_H
+#define DITCHUNK_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DIT_OK = 0,
+  DIT_EINVAL = -1,     /* null pointer, bad enum, non-finite t, inconsistent config */
+  DIT_ESHAPE = -2,     /* a size above the capacity fixed at create, or a bad grid  */
+  DIT_ESTATE = -3,     /* call order: e.g. a step before ref_kv_precompute          */
+  DIT_EWORKSPACE = -4, /* state or workspace smaller than required                  */
+  DIT_EHIP = -5        /* a HIP runtime call failed                                 */
+};
+
+enum { DIT_F32 = 0, DIT_BF16 = 1 };
+
+typedef struct dit_config {
+  int L;          /* DiT blocks                                                     */
+  int D;          /* hidden size; D == H * dh                                       */
+  int H;          /* heads                                                          */
+  int dh;         /* head dim: 64 or 128                                            */
+  int mlp_ratio;  /* MLP width = mlp_ratio * D                                      */
+  int c_p;        /* latent channels per token (x, v): 64                           */
+  int c_c;        /* conditioning channels concatenated after x (0: none); c_p+c_c
+                     must be a multiple of 64                                       */
+  int cond_up;    /* 1: cond is per token [N, c_c]; 2: cond is given at half (h, w)
+                     resolution [frames*(h/2)*(w/2), c_c] with (c, dy, dx) channel
+                     layout and is nearest-upsampled 2x                             */
+  int d_a;        /* audio feature dim (0: no audio cross-attention weights)        */
+  int dtype;      /* DIT_F32 or DIT_BF16: weights, activations and K/V              */
+  int max_tokens; /* capacity: chunk tokens N                                       */
+  int max_ref;    /* capacity: reference tokens                                     */
+  int max_bnd;    /* capacity: boundary tokens (one latent frame)                   */
+  int max_audio;  /* capacity: audio tokens M                                       */
+  double eps;     /* RMSNorm epsilon (1e-6)                                         */
+  double rope_theta; /* RoPE base (10000)                                           */
+} dit_config;
+
+/* Token grid: frames x h x w tokens, row-major over (frame, y, x).  Token (f, y, x)
+ * takes RoPE position (t0 + f, y, x). */
+typedef struct dit_grid {
+  int t0, frames, h, w;
+} dit_grid;
+
+typedef struct dit_handle dit_handle;
+
+/* Weight table order.  Every pointer is device memory in the config's dtype.
+ * Linear weights are [out, in] row-major (input-contiguous) with a bias [out].
+ * Global entries come first; then block l's entries start at
+ * DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT.  Cross-attention entries
+ * (DIT_WB_CQ_W .. DIT_WB_CO_B) may be NULL when d_a == 0. */
+enum {
+  DIT_W_PE_W = 0,   /* [D, c_p + c_c] patch embed                                    */
+  DIT_W_PE_B,       /* [D]                                                           */
+  DIT_W_T1_W,       /* [D, 256] timestep MLP layer 1 (input: sinusoid of 1000 t)     */
+  DIT_W_T1_B,
+  DIT_W_T2_W,       /* [D, D] timestep MLP layer 2                                   */
+  DIT_W_T2_B,
+  DIT_W_FMOD_W,     /* [2D, D] final adaLN (shift, scale)                            */
+  DIT_W_FMOD_B,
+  DIT_W_FIN_W,      /* [c_p, D] final Linear                                         */
+  DIT_W_FIN_B,
+  DIT_W_GLOBAL_COUNT
+};
+enum {
+  DIT_WB_MOD_W = 0, /* [6D, D] adaLN: shift_msa, scale_msa, gate_msa, shift_mlp,
+                       scale_mlp, gate_mlp                                           */
+  DIT_WB_MOD_B,
+  DIT_WB_QKV_W,     /* [3D, D] q | k | v, heads contiguous within each               */
+  DIT_WB_QKV_B,
+  DIT_WB_GQ,        /* [dh] QK-norm gamma for q                                      */
+  DIT_WB_GK,        /* [dh] QK-norm gamma for k                                      */
+  DIT_WB_O_W,       /* [D, D]                                                        */
+  DIT_WB_O_B,
+  DIT_WB_CQ_W,      /* [D, D] cross-attention query                                  */
+  DIT_WB_CQ_B,
+  DIT_WB_CK_W,      /* [D, d_a] cross-attention key                                  */
+  DIT_WB_CK_B,
+  DIT_WB_CV_W,      /* [D, d_a] cross-attention value                                */
+  DIT_WB_CV_B,
+  DIT_WB_GCQ,       /* [dh]                                                          */
+  DIT_WB_GCK,       /* [dh]                                                          */
+  DIT_WB_CO_W,      /* [D, D] cross-attention output                                 */
+  DIT_WB_CO_B,
+  DIT_WB_FC1_W,     /* [mlp_ratio*D, D]                                              */
+  DIT_WB_FC1_B,
+  DIT_WB_FC2_W,     /* [D, mlp_ratio*D]                                              */
+  DIT_WB_FC2_B,
+  DIT_W_BLOCK_COUNT
+};
+
+/* Number of entries of the weight table for this config (0 if the config is invalid). */
+int dit_weight_count(const dit_config* cfg);
+
+/* Bytes of the resident state: per block, K and V of max_ref reference tokens and
+ * max_bnd boundary tokens (rounded up to 64 tokens), plus a small modulation
+ * area.  0 if the config is invalid (see dit_last_error). */
+size_t dit_state_bytes(const dit_config* cfg);
+
+/* Bytes of per-call transients (activations of max(max_tokens, max_ref, max_bnd)
+ * tokens, audio K/V, attention partials).  0 if the config is invalid. */
+size_t dit_workspace_bytes(const dit_config* cfg);
+
+/* Create a handle.  weights: host array of dit_weight_count(cfg) device
+ * pointers (borrowed, must outlive the handle).  state/workspace: device
+ * buffers of at least the reported sizes, 256-byte aligned (borrowed).
+ * hip_stream: hipStream_t for every launch (NULL: the default stream).  No HIP
+ * call is made.  The new handle holds no reference and no boundary. */
+int dit_create(const dit_config* cfg, const void* const* weights, void* state,
+               size_t state_bytes, void* workspace, size_t workspace_bytes,
+               void* hip_stream, dit_handle** out);
+
+/* Destroy a handle (NULL is allowed).  Does not synchronise the stream. */
+int dit_destroy(dit_handle* h);
+
+/* Reference K/V: run the reference latent tokens ref [grid.frames*grid.h*grid.w,
+ * c_p] (fp32, device) through all blocks at t = 0, each token at position
+ * (grid.t0 + f, y, x), attending only to the reference, and store every block's
+ * K and V in the state.  Once per request.  Clears any boundary.
+ * Errors: EINVAL (null), ESHAPE (more than max_ref tokens, empty grid). */
+int ref_kv_precompute(dit_handle* h, const float* ref, dit_grid grid);
+
+/* Boundary K/V: take the last frame (frame prev.frames-1, h*w tokens) of the
+ * previous chunk's final latent x_prev [prev.frames*prev.h*prev.w, c_p] (fp32,
+ * device), run it through all blocks at t = 0 at positions (-1, y, x),
+ * attending to the reference and itself, and store its K and V in the state.
+ * prev.frames == 0 clears the boundary (first chunk: reference only).
+ * Errors: EINVAL (null x_prev with frames > 0), ESHAPE (h*w > max_bnd),
+ * ESTATE (no reference yet). */
+int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev);
+
+/* One denoising step of the chunk: v = DiT(x, t) and x += (t_next - t) v,
+ * with dt computed in double on the host and applied in fp32.
+ *   x     [N, c_p] fp32, device, updated in place; N = frames*h*w of chunk;
+ *         token (f, y, x) at position (chunk.t0 + f, y, x).
+ *   cond  fp32 conditioning (c_c > 0): [N, c_c] if cond_up == 1, else
+ *         [frames*(h/2)*(w/2), c_c]; must be NULL when c_c == 0.
+ *   audio [M, d_a] fp32 audio features (M == 0 or d_a == 0: no cross-attention).
+ *   v_out optional [N, c_p] fp32 copy of the velocity (NULL: not written).
+ * Errors: EINVAL (null x, non-finite t/t_next, cond/audio mismatch), ESHAPE
+ * (N > max_tokens, M > max_audio, odd h or w with cond_up == 2),
+ * ESTATE (no reference yet). */
+int dit_chunk_step(dit_handle* h, float* x, const float* cond, const float* audio, int M,
+                   dit_grid chunk, double t, double t_next, float* v_out);
+
+/* x[i] += (float)dt * v[i] for i < n (fp32, device) on hip_stream.
+ * Errors: EINVAL (null pointer with n > 0, non-finite dt, n < 0). */
+int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_stream);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* dit_last_error(void);
+
+/* Kernel timing on the handle's stream.  While enabled, each attention launch of
+ * dit_chunk_step, ref_kv_precompute and boundary_kv_carry is bracketed by a pair
+ * of HIP events (created lazily, at most 4096 pairs per window).
+ * dit_timing_read synchronises those events and returns the count and the summed
+ * milliseconds of the window, then opens a new window.
+ * kind: DIT_TIME_ATTN (self-attention launches). */
+enum { DIT_TIME_ATTN = 0, DIT_TIME_KINDS };
+int dit_timing_enable(dit_handle* h, int enable);
+int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_flop);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DITCHUNK_H */

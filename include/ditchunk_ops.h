@@ -1,0 +1,76 @@
+/*
+ * ditchunk_ops.h: kernel-level entry points of libditchunk.
+ *
+ * These expose the individual kernels that dit_chunk_step chains, so that each can be
+ * checked against its definition and timed on its own.  Conventions as in ditchunk.h:
+ *   - device pointers, dtype DIT_F32 or DIT_BF16 for "dtype" buffers, fp32 where stated;
+ *   - asynchronous on the given hipStream_t (NULL: default stream);
+ *   - arguments are validated on the host before any launch; failures return a
+ *     negative DIT_E* code and set dit_last_error().
+ * Linear weights are [out, in] row-major with a bias [out].
+ */
+#ifndef DITCHUNK_OPS_H
+#define DITCHUNK_OPS_H
+
+#include "ditchunk.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { DITK_ACT_NONE = 0, DITK_ACT_GELU = 1, DITK_OUT_F32 = 2 };
+
+/* out[M, N] = act(A W^T + b): A [M, K], W [N, K], b [N] (dtype).  act DITK_ACT_NONE
+ * or DITK_ACT_GELU (tanh form) store dtype; DITK_OUT_F32 stores fp32 without
+ * activation.  The Linear layers of the DiT block (QKV, cross q/k/v, FC1, patch embed).
+ * K must be a multiple of 64; N a multiple of 4. */
+int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, int N, int K,
+                int act, void* out, void* hip_stream);
+
+/* h[M, N] (fp32) += gate[N] (.) (A W^T + b); gate fp32, NULL means 1.  The gated
+ * residual of the adaLN DiT block (out-proj, cross out-proj, FC2). */
+int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b, const float* gate,
+                         int M, int N, int K, float* h, void* hip_stream);
+
+/* out[n, D] (dtype) = RMSNorm(h) (.) (1 + scale) + shift, h fp32 [n, D], shift/scale fp32
+ * [D] (both NULL: plain RMSNorm).  D a multiple of 256, <= 4096. */
+int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* shift,
+                          const float* scale, double eps, void* out, void* hip_stream);
+
+/* Per-head QK-RMSNorm with gamma [dh] (dtype), 3D RoPE (rope != 0) at positions
+ * (grid.t0 + f, y, x) of token f*h*w + y*w + x, and repacking into the attention layout:
+ *   q_out  [n, H*dh]              (plain, only if q_in)
+ *   k_out  [cap, H*dh]            (rows n..round_up(n,64)-1 zeroed; only if k_in)
+ *   vt_out [H*dh, cap]            V transposed (only if v_in); for bf16 the keys of each
+ *                                 aligned group of 16 are stored so that key offset o
+ *                                 sits at position 8*((o%8)/4) + 4*(o/8) + o%4; fp32
+ *                                 keeps natural order; columns n..round_up(n,64)-1 zeroed.
+ * q_in/k_in/v_in: [n, ld_in] (dtype), any may be NULL.  cap a multiple of 64, >= n. */
+int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
+                     const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
+                     dit_grid grid, double eps, double theta, void* q_out, void* k_out,
+                     void* vt_out, int cap, void* hip_stream);
+
+/* o[nq, H*dh] = softmax(q k^T / sqrt(dh)) v per head, keys the concatenation of nseg
+ * (1..3) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
+ * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype). */
+int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
+                   const void* const* k, const void* const* vt, const int* n, const int* cap,
+                   void* o, void* hip_stream);
+
+/* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
+ * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,
+ * scale_mlp, gate_mlp), fmod_out [2, D] (fp32: shift, scale).  tmp: fp32 scratch of
+ * 256 + 2 D floats. */
+int ditk_modulation(int dtype, int D, int L, double t, const void* const* weights,
+                    float* mod_out, float* fmod_out, float* tmp, void* hip_stream);
+
+/* xin[n, c_p + c_c] (dtype) = [x || cond]: cond_mode 0 zeros, 1 cond [n, c_c],
+ * 2 nearest-2x upsample of cond [frames*(h/2)*(w/2), c_c] on the token grid. */
+int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
+                     int cond_mode, dit_grid grid, void* xin, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DITCHUNK_OPS_H */

@@ -1,0 +1,58 @@
+"""Shared helpers of the GPU tests: device, uploads, the parity metric."""
+import numpy as np
+import pytest
+import torch
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def rel_err(g, o) -> float:
+    """max |g - o| / max |o| (max-abs normalised), g from the GPU, o from the oracle."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    assert np.isfinite(g).all(), "non-finite GPU output"
+    return float(np.abs(g - o).max() / max(np.abs(o).max(), 1e-30))
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def run_standalone_gpu(cfg, P, inp, dev, steps=None, record_v=True, weights=None, handle=None):
+    """One self-contained chunk on the GPU through the C ABI: reference K/V, the
+    boundary frame's K/V (if any), then the chunk's Euler steps.
+    Returns (x_final numpy, [v per step] numpy, handle)."""
+    import synth as S
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    W = weights if weights is not None else upload_weights(P, cfg.dtype, dev)
+    h = handle if handle is not None else DitChunk(chunk_config(cfg), W, dev)
+    h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    if cfg.bnd is not None:
+        b = cfg.bnd
+        h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(S.Grid(0, 1, b.h, b.w)))
+    else:
+        h.boundary_kv_carry(None, grid_of(S.Grid(0, 0, 0, 0)))
+    x = f32(inp["x_init"], dev)
+    cond = None
+    if cfg.C_c > 0:
+        cond = f32(inp["cond_lr"] if cfg.cond_up == 2 else inp["cond"], dev)
+    audio = f32(inp["audio"], dev) if cfg.M > 0 else None
+    S_ = cfg.steps if steps is None else steps
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S_ for k in range(S_ + 1)]
+    vs = []
+    v = torch.empty_like(x) if record_v else None
+    for k in range(S_):
+        h.step(x, ts[k], ts[k + 1], grid_of(cfg.chunk), cond=cond, audio=audio, v_out=v)
+        if record_v:
+            vs.append(to_np(v))
+    torch.cuda.synchronize()
+    return to_np(x), vs, h

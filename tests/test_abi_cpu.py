@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+sizes its buffers, and rejects bad arguments on the host before any HIP call.
+
+Fake (never dereferenced) device addresses stand in for buffers: every call below
+fails validation before it could launch anything.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+from chunked_streaming_dit_amd import _lib as C
+from chunked_streaming_dit_amd.workload import chunk_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000  # 256-byte aligned, never touched
+
+
+def _declared():
+    names = set()
+    for h in ("ditchunk.h", "ditchunk_ops.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.lib()
+    declared = _declared()
+    assert {"dit_chunk_step", "ref_kv_precompute", "boundary_kv_carry", "fm_euler_step",
+            "dit_create", "ditk_attention"} <= declared
+    for n in declared:
+        assert hasattr(lib, n), n
+    assert declared == set(C.EXPORTS)
+
+
+def _cs(cid=1, **kw):
+    cs = chunk_config(synth.CONFIGS[cid]).c_struct()
+    for k, v in kw.items():
+        setattr(cs, k, v)
+    return cs
+
+
+def test_sizes_and_weight_count():
+    lib = C.lib()
+    for cid in range(1, 6):
+        cs = _cs(cid)
+        cfg = synth.CONFIGS[cid]
+        assert lib.dit_weight_count(ctypes.byref(cs)) == 10 + 22 * cfg.L
+        sb = lib.dit_state_bytes(ctypes.byref(cs))
+        kv = cfg.L * 2 * cfg.D * (2 if cfg.dtype == "bf16" else 4) * (
+            (cfg.N_ref + 63) // 64 * 64 + (cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64)
+        assert kv <= sb <= kv + 4 * cfg.L * 256
+        assert lib.dit_workspace_bytes(ctypes.byref(cs)) > 0
+
+
+@pytest.mark.parametrize("field,value", [("D", 300), ("dh", 96), ("dtype", 7), ("L", 0),
+                                         ("cond_up", 3), ("c_c", 10), ("eps", 0.0),
+                                         ("rope_theta", float("inf")), ("max_tokens", 0)])
+def test_bad_config_rejected(field, value):
+    cs = _cs(1, **{field: value})
+    assert C.lib().dit_state_bytes(ctypes.byref(cs)) == 0
+    assert C.last_error()
+
+
+def _handle(cid=1):
+    cs = _cs(cid)
+    lib = C.lib()
+    n = lib.dit_weight_count(ctypes.byref(cs))
+    w = (C.P * n)(*([FAKE] * n))
+    h = C.P()
+    rc = lib.dit_create(ctypes.byref(cs), w, FAKE, lib.dit_state_bytes(ctypes.byref(cs)), FAKE + (1 << 20),
+                        lib.dit_workspace_bytes(ctypes.byref(cs)), None, ctypes.byref(h))
+    assert rc == C.DIT_OK, C.last_error()
+    return lib, cs, h
+
+
+def test_create_validation():
+    lib = C.lib()
+    cs = _cs(1)
+    n = lib.dit_weight_count(ctypes.byref(cs))
+    w = (C.P * n)(*([FAKE] * n))
+    h = C.P()
+    sb, wb = lib.dit_state_bytes(ctypes.byref(cs)), lib.dit_workspace_bytes(ctypes.byref(cs))
+    assert lib.dit_create(ctypes.byref(cs), w, FAKE, sb - 1, FAKE, wb, None, ctypes.byref(h)) == C.DIT_EWORKSPACE
+    assert lib.dit_create(ctypes.byref(cs), w, FAKE, sb, FAKE, wb - 1, None, ctypes.byref(h)) == C.DIT_EWORKSPACE
+    assert lib.dit_create(ctypes.byref(cs), w, FAKE + 8, sb, FAKE, wb, None, ctypes.byref(h)) == C.DIT_EINVAL
+    w2 = (C.P * n)(*([FAKE] * n))
+    w2[3] = None
+    assert lib.dit_create(ctypes.byref(cs), w2, FAKE, sb, FAKE, wb, None, ctypes.byref(h)) == C.DIT_EINVAL
+    assert lib.dit_create(ctypes.byref(cs), None, FAKE, sb, FAKE, wb, None, ctypes.byref(h)) == C.DIT_EINVAL
+    assert "NULL" in C.last_error()
+
+
+def test_call_order_and_shape_errors():
+    lib, cs, h = _handle(1)
+    g = C.DitGrid(0, 2, 8, 8)
+    # step before the reference exists
+    assert lib.dit_chunk_step(h, FAKE, None, FAKE, 16, g, 0.5, 0.45, None) == C.DIT_ESTATE
+    assert "ref_kv_precompute" in C.last_error()
+    assert lib.boundary_kv_carry(h, FAKE, C.DitGrid(0, 1, 4, 8)) == C.DIT_ESTATE
+    # argument errors win over state errors and never launch
+    assert lib.dit_chunk_step(h, None, None, None, 0, g, 0.5, 0.45, None) == C.DIT_EINVAL
+    assert lib.dit_chunk_step(h, FAKE, None, None, 0, g, float("nan"), 0.45, None) == C.DIT_EINVAL
+    assert lib.dit_chunk_step(h, FAKE, None, None, 0, C.DitGrid(0, 3, 8, 8), 0.5, 0.4, None) == C.DIT_ESHAPE
+    assert lib.dit_chunk_step(h, FAKE, None, None, 0, C.DitGrid(0, 0, 8, 8), 0.5, 0.4, None) == C.DIT_ESHAPE
+    assert lib.dit_chunk_step(h, FAKE, None, FAKE, 17, g, 0.5, 0.4, None) == C.DIT_ESHAPE
+    assert lib.dit_chunk_step(h, FAKE, None, None, 3, g, 0.5, 0.4, None) == C.DIT_EINVAL
+    assert lib.dit_chunk_step(h, FAKE, FAKE, None, 0, g, 0.5, 0.4, None) == C.DIT_EINVAL  # no cond channels
+    assert lib.ref_kv_precompute(h, None, C.DitGrid(-2, 1, 8, 8)) == C.DIT_EINVAL
+    assert lib.ref_kv_precompute(h, FAKE, C.DitGrid(-2, 1, 8, 9)) == C.DIT_ESHAPE
+    assert lib.boundary_kv_carry(h, FAKE, C.DitGrid(0, 1, 8, 8)) == C.DIT_ESHAPE  # 64 > max_bnd 32
+    assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 2, 4, 8)) == C.DIT_EINVAL
+    assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 0, 0, 0)) == C.DIT_OK      # clear: no launch
+    assert lib.dit_destroy(h) == C.DIT_OK
+    assert lib.dit_destroy(None) == C.DIT_OK
+
+
+def test_cond_and_audio_validation_sr_config():
+    lib, cs, h = _handle(4)
+    g = C.DitGrid(0, 5, 60, 104)
+    assert lib.dit_chunk_step(h, FAKE, None, None, 0, g, 1.0, 0.75, None) == C.DIT_EINVAL   # cond missing
+    assert lib.dit_chunk_step(h, FAKE, FAKE, None, 0, C.DitGrid(0, 1, 59, 104), 1.0, 0.75, None) == C.DIT_ESHAPE
+    assert lib.dit_chunk_step(h, FAKE, FAKE, FAKE, 1, g, 1.0, 0.75, None) == C.DIT_ESHAPE    # max_audio 0
+    lib.dit_destroy(h)
+
+
+def test_euler_and_ops_validation():
+    lib = C.lib()
+    assert lib.fm_euler_step(FAKE, FAKE, 0.1, 0, None) == C.DIT_OK
+    assert lib.fm_euler_step(None, FAKE, 0.1, 10, None) == C.DIT_EINVAL
+    assert lib.fm_euler_step(FAKE, FAKE, float("inf"), 10, None) == C.DIT_EINVAL
+    assert lib.fm_euler_step(FAKE, FAKE, 0.1, -1, None) == C.DIT_EINVAL
+    assert lib.fm_euler_step(FAKE + 4, FAKE, 0.1, 8, None) == C.DIT_EINVAL
+    assert lib.ditk_linear(1, FAKE, FAKE, FAKE, 10, 64, 100, 0, FAKE, None) == C.DIT_ESHAPE  # K % 64
+    assert lib.ditk_linear(1, FAKE, FAKE, FAKE, 10, 66, 128, 0, FAKE, None) == C.DIT_ESHAPE  # N % 4
+    assert lib.ditk_linear(5, FAKE, FAKE, FAKE, 10, 64, 128, 0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_linear(1, FAKE, FAKE, FAKE, 10, 64, 128, 9, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_rmsnorm_modulate(1, FAKE, 4, 300, None, None, 1e-6, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_rmsnorm_modulate(1, FAKE, 4, 256, FAKE, None, 1e-6, FAKE, None) == C.DIT_EINVAL
+    g = C.DitGrid(0, 1, 2, 2)
+    assert lib.ditk_qknorm_rope(1, 128, 2, 5, None, FAKE, None, 256, None, FAKE, 1, g, 1e-6, 1e4,
+                                None, FAKE, None, 64, None) == C.DIT_ESHAPE  # grid covers 4 < 5
+    assert lib.ditk_qknorm_rope(1, 128, 2, 65, None, FAKE, None, 256, None, FAKE, 0, g, 1e-6, 1e4,
+                                None, FAKE, None, 64, None) == C.DIT_ESHAPE  # cap < round_up(n)
+    k = (C.P * 1)(FAKE)
+    n = (ctypes.c_int * 1)(70)
+    cap = (ctypes.c_int * 1)(64)
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, FAKE, None) == C.DIT_ESHAPE
+    n[0] = 0
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, FAKE, None) == C.DIT_ESHAPE  # no keys

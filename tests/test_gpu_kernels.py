@@ -1,0 +1,249 @@
+"""Per-kernel parity: each HIP kernel, called through the C ABI, against the oracle's
+function for the same step on the same (already rounded) inputs.
+
+Shapes span several tiles and leave ragged tails (rows not a multiple of 64/128).
+Tolerance: max-abs-normalised error <= 1e-4 for fp32, <= 2e-2 for bf16.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from chunked_streaming_dit_amd import ChunkConfig, fm_euler_step, grid, ops, torch_dtype
+from tests.gpu_util import TOL, device, rel_err, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _arr(rng, shape, dtype, scale=1.0):
+    a = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return synth.round_bf16(a) if dtype == "bf16" else a
+
+
+def _dev(a, dtype, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch_dtype(dtype))
+
+
+LIN_SHAPES = [(1, 64, 64), (130, 192, 128), (777, 512, 256), (1000, 1536, 1536)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", LIN_SHAPES)
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_linear(dtype, M, N, K, act):
+    dev = device()
+    r = np.random.default_rng(M * 7 + N + K + act)
+    A, W, b = _arr(r, (M, K), dtype), _arr(r, (N, K), dtype, K ** -0.5), _arr(r, (N,), dtype, 0.5)
+    out = torch.empty((M, N), device=dev, dtype=torch.float32 if act == 2 else torch_dtype(dtype))
+    ops.linear(_dev(A, dtype, dev), _dev(W, dtype, dev), _dev(b, dtype, dev), act, out, dtype)
+    ref = O.linear(A.astype(np.float64), W.astype(np.float64), b.astype(np.float64))
+    if act == 1:
+        ref = O.gelu_tanh(ref)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(out), ref) <= TOL[dtype] / 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(130, 192, 128), (1000, 1536, 1536), (600, 512, 2048)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_linear_residual(dtype, M, N, K, gated):
+    dev = device()
+    r = np.random.default_rng(M + N + K)
+    A, W, b = _arr(r, (M, K), dtype), _arr(r, (N, K), dtype, K ** -0.5), _arr(r, (N,), dtype, 0.5)
+    h0 = r.standard_normal((M, N)).astype(np.float32)
+    gate = r.standard_normal(N).astype(np.float32) if gated else None
+    h = torch.from_numpy(h0).to(dev)
+    ops.linear_residual(_dev(A, dtype, dev), _dev(W, dtype, dev), _dev(b, dtype, dev),
+                        None if gate is None else torch.from_numpy(gate).to(dev), h, dtype)
+    y = O.linear(A.astype(np.float64), W.astype(np.float64), b.astype(np.float64))
+    ref = h0 + (y if gate is None else gate * y)
+    torch.cuda.synchronize()
+    # the residual dominates h; compare the update itself
+    assert rel_err(to_np(h) - h0, ref - h0) <= TOL[dtype] / 4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,D", [(1, 256), (37, 256), (301, 1536), (5, 3072)])
+@pytest.mark.parametrize("mod", [False, True])
+def test_rmsnorm_modulate(dtype, n, D, mod):
+    dev = device()
+    r = np.random.default_rng(n + D)
+    h = (r.standard_normal((n, D)) * 3 + 0.5).astype(np.float32)
+    sh, sc = r.standard_normal(D).astype(np.float32), r.standard_normal(D).astype(np.float32)
+    out = torch.empty((n, D), device=dev, dtype=torch_dtype(dtype))
+    ops.rmsnorm_modulate(torch.from_numpy(h).to(dev), torch.from_numpy(sh).to(dev) if mod else None,
+                         torch.from_numpy(sc).to(dev) if mod else None, 1e-6, out, dtype)
+    ref = O.rms_norm(h, 1e-6)
+    if mod:
+        ref = O.modulate(ref, sh.astype(np.float64), sc.astype(np.float64))
+    torch.cuda.synchronize()
+    assert rel_err(to_np(out), ref) <= TOL[dtype] / 4
+
+
+def _unpack_vt(vt, n, dtype):
+    """Inverse of the documented V^T key order: returns V [n, D]."""
+    cap = vt.shape[1]
+    pos = np.arange(cap)
+    key = pos.copy()
+    if dtype == "bf16":
+        q, g, j = pos & 15, (pos & 15) >> 3, pos & 7
+        key = (pos & ~15) + 8 * (j >> 2) + 4 * g + (j & 3)
+    v = np.zeros((cap, vt.shape[0]))
+    v[key] = vt.T
+    return v[:n], v[n:]
+
+
+def _pack_vt(v, cap, dtype):
+    n, D = v.shape
+    vp = np.zeros((cap, D), dtype=np.float32)
+    vp[:n] = v
+    pos = np.arange(cap)
+    key = pos.copy()
+    if dtype == "bf16":
+        g, j = (pos & 15) >> 3, pos & 7
+        key = (pos & ~15) + 8 * (j >> 2) + 4 * g + (j & 3)
+    return np.ascontiguousarray(vp[key].T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("rope", [False, True])
+def test_qknorm_rope(dtype, dh, rope):
+    dev = device()
+    H, n, cap = 3, 70, 128
+    D = H * dh
+    g = synth.Grid(-1, 3, 4, 6)  # 72 positions, 70 tokens used
+    r = np.random.default_rng(dh + rope)
+    qkv = _arr(r, (n, 3 * D), dtype, 2.0)
+    gq, gk = _arr(r, (dh,), dtype, 0.1) + 1, _arr(r, (dh,), dtype, 0.1) + 1
+    gq, gk = (synth.round_bf16(x) if dtype == "bf16" else x for x in (gq, gk))
+    td = torch_dtype(dtype)
+    q_out = torch.zeros((n, D), device=dev, dtype=td)
+    k_out = torch.full((cap, D), 7.0, device=dev, dtype=td)
+    vt_out = torch.full((D, cap), 7.0, device=dev, dtype=td)
+    qkv_d = _dev(qkv, dtype, dev)
+    ops.qknorm_rope(dtype, dh, H, n, qkv_d, qkv_d[:, D:], qkv_d[:, 2 * D:], 3 * D, _dev(gq, dtype, dev),
+                    _dev(gk, dtype, dev), rope, grid(g.t0, g.frames, g.h, g.w), 1e-6, 1e4,
+                    q_out, k_out, vt_out, cap)
+    # slices above are views with row stride 3D: pointers are offset, ld_in = 3D
+    pos = O.grid_positions(g.t0, g.frames, g.h, g.w)[:n]
+    ang = O.rope_angles(pos, dh, 1e4) if rope else np.zeros((n, dh // 2))
+    q64 = qkv.astype(np.float64)
+    qr = O.rope_apply(O.qk_norm(q64[:, :D].reshape(n, H, dh), gq.astype(np.float64), 1e-6), ang)
+    kr = O.rope_apply(O.qk_norm(q64[:, D:2 * D].reshape(n, H, dh), gk.astype(np.float64), 1e-6), ang)
+    torch.cuda.synchronize()
+    assert rel_err(to_np(q_out), qr.reshape(n, D)) <= TOL[dtype] / 4
+    k = to_np(k_out)
+    assert rel_err(k[:n], kr.reshape(n, D)) <= TOL[dtype] / 4
+    assert np.all(k[n:] == 0)
+    v, pad = _unpack_vt(to_np(vt_out), n, dtype)
+    assert np.array_equal(v, q64[:, 2 * D:])
+    assert np.all(pad == 0)
+
+
+def _attn_case(dtype, dh, H, nq, seg_ns, seed):
+    dev = device()
+    r = np.random.default_rng(seed)
+    D = H * dh
+    q = _arr(r, (nq, D), dtype, 2.0)
+    segs, ks, vs = [], [], []
+    keep = []
+    for n in seg_ns:
+        cap = max(64, (n + 63) // 64 * 64)
+        k = _arr(r, (n, D), dtype, 2.0)
+        v = _arr(r, (n, D), dtype)
+        kp = np.zeros((cap, D), dtype=np.float32)
+        kp[:n] = k
+        kd, vd = _dev(kp, dtype, dev), _dev(_pack_vt(v, cap, dtype), dtype, dev)
+        keep += [kd, vd]
+        segs.append((kd, vd, n, cap))
+        ks.append(k)
+        vs.append(v)
+    o = torch.empty((nq, D), device=dev, dtype=torch_dtype(dtype))
+    ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o)
+    K = np.concatenate(ks).astype(np.float64).reshape(-1, H, dh)
+    V = np.concatenate(vs).astype(np.float64).reshape(-1, H, dh)
+    ref = O.attention(q.astype(np.float64).reshape(nq, H, dh), K, V).reshape(nq, D)
+    torch.cuda.synchronize()
+    return rel_err(to_np(o), ref)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dh", [64, 128])
+@pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (1, [5]), (300, [64, 0, 200]),
+                                       (257, [1, 1, 1]), (128, [1000])])
+def test_attention(dtype, dh, nq, seg_ns):
+    err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + dh)
+    assert err <= TOL[dtype] / 4, err
+
+
+def test_attention_real_head_shape_bf16():
+    """One head group at the base-chunk shape: 12 heads of 128, keys 1560 | 1560 | 1000."""
+    err = _attn_case("bf16", 128, 12, 1000, [1560, 1560, 1000], 5)
+    assert err <= TOL["bf16"] / 4, err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_modulation(dtype):
+    dev = device()
+    cfg = synth.config(1, cid=201, L=2, D=256, H=2, dh=128, dtype=dtype)
+    P = synth.make_weights(cfg)
+    W = {k: _dev(v, dtype, dev) for k, v in P.items()}
+    cc = ChunkConfig(L=2, D=256, H=2, dh=128, mlp_ratio=4, c_p=64, c_c=0, cond_up=1, d_a=64,
+                     dtype=dtype, max_tokens=64, max_ref=64, max_bnd=0, max_audio=16)
+    for t in (0.0, 0.37, 1.0):
+        mod = torch.empty((2, 6 * 256), device=dev)
+        fmod = torch.empty(512, device=dev)
+        tmp = torch.empty(256 + 512, device=dev)
+        ops.modulation(dtype, cc, W, t, mod, fmod, tmp)
+        c = O.conditioning(P, t)
+        torch.cuda.synchronize()
+        for l in range(2):
+            ref = np.concatenate(O.block_modulation(P, l, c))
+            assert rel_err(to_np(mod[l]), ref) <= TOL["f32"], (t, l)
+        assert rel_err(to_np(fmod), np.concatenate(O.final_modulation(P, c))) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_patch_input_upsample(dtype):
+    dev = device()
+    frames, h, w, cp, cc = 3, 6, 10, 64, 64
+    n = frames * h * w
+    r = np.random.default_rng(3)
+    x = _arr(r, (n, cp), dtype)
+    z = _arr(r, (frames * (h // 2) * (w // 2), cc), dtype)
+    xin = torch.empty((n, cp + cc), device=dev, dtype=torch_dtype(dtype))
+    ops.patch_input(dtype, torch.from_numpy(x).to(dev), cp, torch.from_numpy(z).to(dev), cc, 2,
+                    grid(0, frames, h, w), xin)
+    ref = O.patch_input(x, O.upsample2_tokens(z, frames, h, w), cc)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(xin), ref)
+    xin0 = torch.empty((n, cp + cc), device=dev, dtype=torch_dtype(dtype))
+    ops.patch_input(dtype, torch.from_numpy(x).to(dev), cp, None, cc, 0, grid(0, frames, h, w), xin0)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(xin0), O.patch_input(x, None, cc))
+
+
+@pytest.mark.parametrize("lam", [0.0, -0.7])
+def test_fm_euler_step_closed_form(lam):
+    dev = device()
+    S, t0, t1 = 8, 1.0, 0.0
+    ts = O.schedule(S, t0, t1)
+    n = 1001
+    r = np.random.default_rng(4)
+    x0 = r.standard_normal(n).astype(np.float32)
+    c = r.standard_normal(n).astype(np.float32)
+    x = torch.from_numpy(x0).to(dev)
+    ct = torch.from_numpy(c).to(dev)
+    for k in range(S):
+        v = lam * x + ct  # the velocity is the test's input, uploaded each step
+        fm_euler_step(x, v.contiguous(), ts[k + 1] - ts[k])
+    d = (t1 - t0) / S
+    if lam == 0.0:
+        want = x0 + (t1 - t0) * c.astype(np.float64)
+    else:
+        gg = (1 + lam * d) ** S
+        want = gg * x0 + c * (gg - 1) / lam
+    torch.cuda.synchronize()
+    assert np.abs(to_np(x) - want).max() <= 1e-5

@@ -1,0 +1,108 @@
+"""End-to-end parity of the C-ABI path (ref_kv_precompute, boundary_kv_carry,
+dit_chunk_step) against the f64 oracle on the same seeded inputs.
+
+Compared: the velocity of every step and dx = x_S - x_0 (x itself is dominated by its
+exact initial value), max-abs normalised; <= 1e-4 for fp32, <= 2e-2 for bf16.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth import Grid
+from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu
+
+pytestmark = pytest.mark.gpu
+
+# Small variants that still span several 64/128 tiles with ragged tails.
+MINI_BF16 = synth.config(2, cid=202, L=2, D=256, H=2, dh=128, d_a=64, M=7,
+                         chunk=Grid(0, 3, 10, 13), ref=Grid(-2, 1, 10, 13), bnd=Grid(-1, 1, 10, 13),
+                         steps=2)
+MINI_F32 = dataclasses.replace(MINI_BF16, cid=203, dtype="f32")
+MINI_F32_DH64 = synth.config(1, cid=204, L=2, chunk=Grid(0, 3, 7, 9), ref=Grid(-2, 1, 7, 9),
+                             bnd=Grid(-1, 1, 5, 9), M=5, steps=2, t_start=0.9, t_end=0.3)
+MINI_SR = synth.config(4, cid=205, L=2, D=256, H=2, dh=128,
+                       chunk=Grid(0, 2, 12, 14), ref=Grid(-2, 1, 12, 14), bnd=Grid(-1, 1, 12, 14),
+                       steps=2)
+
+
+def _check(cfg, steps=None):
+    dev = device()
+    P = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, 0)
+    xg, vg, _ = run_standalone_gpu(cfg, P, inp, dev, steps=steps)
+    S = cfg.steps if steps is None else steps
+    g = cfg.chunk
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    ctx = [[ref_kv[l]] for l in range(cfg.L)]
+    if cfg.bnd is not None:
+        bkv = O.bnd_context(P, cfg, ref_kv, inp["bnd"], cfg.bnd.h, cfg.bnd.w)
+        ctx = [[ref_kv[l], bkv[l]] for l in range(cfg.L)]
+    cond = None
+    if cfg.C_c > 0:
+        cond = O.upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w) if cfg.cond_up == 2 else inp["cond"]
+    xo, vo = O.chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond, steps=S, record=True)
+    tol = TOL[cfg.dtype]
+    errs = [rel_err(a, b) for a, b in zip(vg, vo)]
+    dx = rel_err(xg - inp["x_init"], xo - inp["x_init"])
+    print(f"{cfg.name} cid={cfg.cid}: v errs {['%.2e' % e for e in errs]}, dx err {dx:.2e}")
+    assert max(errs) <= tol and dx <= tol, (errs, dx)
+
+
+def test_config1_tiny_fp32():
+    _check(synth.CONFIGS[1])
+
+
+def test_mini_fp32_dh128_multi_tile():
+    _check(MINI_F32)
+
+
+def test_mini_fp32_dh64_partial_boundary():
+    _check(MINI_F32_DH64)
+
+
+def test_mini_bf16_multi_tile():
+    _check(MINI_BF16)
+
+
+def test_mini_super_resolution_bf16():
+    _check(MINI_SR)
+
+
+def test_mini_stream_bf16():
+    """Chunked streaming: chunk 0 has no boundary; each later chunk's boundary is the
+    previous chunk's final last frame (carried on the GPU)."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(MINI_BF16, cid=206, bnd=None, n_chunks=3)
+    P = synth.make_weights(cfg)
+    chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
+    outs = O.stream(P, cfg, chunks, chunks[0]["ref"])
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(chunks[0]["ref"], dev), grid_of(cfg.ref))
+    g = cfg.chunk
+    ts = O.schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    prev = None
+    for c, inp in enumerate(chunks):
+        if prev is None:
+            h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+        else:
+            h.boundary_kv_carry(prev, grid_of(g))
+        x = f32(inp["x_init"], dev)
+        for k in range(cfg.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=f32(inp["audio"], dev))
+        prev = x
+        torch.cuda.synchronize()
+        err = rel_err(x.cpu().numpy() - inp["x_init"], outs[c] - inp["x_init"])
+        print(f"chunk {c}: dx err {err:.2e}")
+        assert err <= TOL["bf16"], (c, err)
+
+
+def test_config2_full_size_first_step():
+    """The base low-res chunk at its full shape (7800 tokens, keys 1560|1560|7800,
+    4 blocks, hidden 1536, 12x128 heads, 50 audio tokens): the first denoising step."""
+    _check(synth.CONFIGS[2], steps=1)
