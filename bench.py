@@ -1,0 +1,190 @@
+"""Benchmark of the chunked streaming DiT step on one MI355X.
+
+One bench step = one whole base low-res chunk job through the C ABI: the reference
+K/V pass (ref_kv_precompute), the boundary K/V pass from the previous chunk's last
+latent frame (boundary_kv_carry), then the 8 Euler denoising steps
+(dit_chunk_step: modulation, patch embed, 4 DiT blocks of self-attention over
+[reference | boundary | chunk] keys, audio cross-attention and adaLN MLP, final
+layer + Euler update).  Inputs are seeded synthetic tensors already resident in HBM.
+
+value = latent tokens x denoising steps / second (7800 x 8 per bench step; the
+context passes are included in the time).
+roofline = the self-attention kernel (the dominant kernel): algorithmic flop
+4 * N_q * N_kv * D per launch over its HIP-event-timed duration, against the
+bf16 dense MFMA peak.
+cpu_baseline = the f64 oracle timed on the host on a bounded sample (one DiT block of
+one denoising step at the full chunk shape, scaled to the 4-block step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT chunk-step latent tokens/sec and attention TFLOP/s (% bf16 MFMA peak), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+ATTN_SRC = os.path.join(ROOT, "chunked_streaming_dit_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_base_chunk_traffic.json")
+
+
+def _src_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or
+    None if it is missing or was taken on a different attention source."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("attention_src_sha256_16") != _src_hash(ATTN_SRC):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, P, inp, budget_s: float = 12.0):
+    """Time the oracle on one DiT block of one denoising step at the full chunk shape
+    (repeated up to L times while under the budget) and scale to the L-block step."""
+    import dataclasses
+
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    one = dataclasses.replace(cfg, L=1)
+    ref_kv = O.ref_context(P, one, inp["ref"], one.ref)
+    bkv = O.bnd_context(P, one, ref_kv, inp["bnd"], one.bnd.h, one.bnd.w)
+    ctx = [[ref_kv[0], bkv[0]]]
+    pos = O.grid_positions(0, cfg.chunk.frames, cfg.chunk.h, cfg.chunk.w)
+    times = []
+    while len(times) < cfg.L and sum(times) < budget_s:
+        t0 = time.perf_counter()
+        O.dit_velocity(P, one, inp["x_init"], 1.0, pos, ctx, inp["audio"])
+        times.append(time.perf_counter() - t0)
+    t_block = float(np.median(times))
+    t_step = t_block * cfg.L
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": cfg.N / t_step,
+        "unit": "latent tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(times)} x one DiT block of one denoising step at the full chunk shape "
+                   f"({cfg.N} tokens, {cfg.N_ref}+{cfg.N_bnd}+{cfg.N} keys, audio {cfg.M}), "
+                   f"median {t_block:.2f} s x {cfg.L} blocks; context passes excluded"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+
+    dev = torch.device("cuda", 0)
+    cfg = synth.CONFIGS[2]
+    P = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, 0)
+    W = upload_weights(P, cfg.dtype, dev)
+    h = DitChunk(chunk_config(cfg), W, dev)
+    ref = f32(inp["ref"], dev)
+    bnd = f32(inp["bnd"], dev)
+    x0 = f32(inp["x_init"], dev)
+    audio = f32(inp["audio"], dev)
+    x = torch.empty_like(x0)
+    S = cfg.steps
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S for k in range(S + 1)]
+    g_chunk = grid_of(cfg.chunk)
+    g_ref = grid_of(cfg.ref)
+    g_prev = grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w))
+
+    def step():
+        h.ref_kv_precompute(ref, g_ref)
+        h.boundary_kv_carry(bnd, g_prev)
+        x.copy_(x0)
+        for k in range(S):
+            h.step(x, ts[k], ts[k + 1], g_chunk, audio=audio)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    h.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_attn, attn_ms, attn_flop = h.timing_read()
+    h.timing_enable(False)
+    if not torch.isfinite(x).all():
+        print("bench.py: non-finite output", file=sys.stderr)
+        return 1
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = cfg.N * S / ((t1 - t0) / args.steps)
+    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    traffic = _traffic()
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "latent tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents/audio, N(0,1/fan_in) random-init weights)",
+        "config": {
+            "workload": ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
+                         "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
+                         "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = reference "
+                         "K/V + boundary K/V + 8 denoising steps"),
+            "tokens_per_step": cfg.N * S,
+            "attention_tflops": achieved,
+            "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+            "attention_launches": n_attn,
+            "attention_avg_launch_ms": attn_ms / max(n_attn, 1),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, P, inp)
+    print(json.dumps(line), flush=True)
+    h.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

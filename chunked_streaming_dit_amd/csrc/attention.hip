@@ -23,13 +23,30 @@ namespace {
 struct AttnArgs {
   const void* q;
   void* o;
-  int ldq, ldo, nq, ldk;
+  int ldq, ldo, nq, ldk, H;
   int nseg;
   float scale;  // log2(e) / sqrt(dh)
+  float thr;    // RESCALE_LOG2 / scale: lazy-rescale threshold in raw score units
   AttnSeg seg[ATTN_MAX_SEGS];
 };
 
 constexpr int BQ = 128;  // queries per workgroup
+constexpr float RESCALE_LOG2 = 8.0f;
+
+// Row-sum accumulation from the P^T operand vector.
+__device__ __forceinline__ float row_sum_add(bf16x8 p, float acc) {
+  typedef bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b2 q = {p[2 * i], p[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(q, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float row_sum_add(f32x4 p, float acc) {
+  return acc + p[0] + p[1] + p[2] + p[3];
+}
 constexpr int BKV = 64;  // keys per tile
 
 template <class T, int DH>
@@ -51,8 +68,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lg = lane >> 5;
-  const int head = blockIdx.y;
-  const int qrow = blockIdx.x * BQ + wave * 32 + l32;
+  // 1-D grid over (head, q-tile), head-major, remapped so that each XCD works through
+  // a contiguous range: the q-tiles of a head share that head's K/V in one L2.
+  const int nqt = (a.nq + BQ - 1) / BQ;
+  const int wi = xcd_remap(blockIdx.x, nqt * a.H);
+  const int head = wi / nqt;
+  const int qrow = (wi - head * nqt) * BQ + wave * 32 + l32;
   const bool qvalid = qrow < a.nq;
 
   // Q fragments (second MFMA operand): query qrow, dh = s*2VE + lg*VE + [0, VE).
@@ -168,38 +189,44 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * a.scale);
-    const float ms = m_new * a.scale;
-    float ls = 0.f;
+    // Lazy rescale: keep the running max unless a score exceeds it by more than
+    // RESCALE_LOG2 in the exp2 domain (then p stays <= 2^RESCALE_LOG2, which fp32
+    // sums and bf16 operands hold exactly as well as p <= 1).  The decision is
+    // wave-uniform; lanes l and l^32 hold the same query and the same max.
+    if (__any(mx > m_run + a.thr)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[d][r] *= alpha;
+      m_run = m_new;
+    }
+    const float ms = m_run * a.scale;
+    // P^T operands: elements [v*VE, v*VE+VE) of S[kb].  The row sum is taken from the
+    // converted operand values, i.e. from exactly the weights the second MFMA uses.
+    V pf[2][16 / VE];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(S[kb][r], a.scale, -ms));
-        S[kb][r] = p;
-        ls += p;
+      for (int v = 0; v < 16 / VE; ++v) {
+#pragma unroll
+        for (int j = 0; j < VE; ++j)
+          pf[kb][v][j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(S[kb][v * VE + j], a.scale, -ms)));
+        l_run = row_sum_add(pf[kb][v], l_run);
       }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) O[d][r] *= alpha;
 
-    // O^T += V^T P^T.  P^T operand: elements [v*VE, v*VE+VE) of S[kb]; the V^T
-    // vector at key offset 32 kb + v*2VE + lg*VE holds the same keys (stored order).
+    // O^T += V^T P^T; the V^T vector at key offset 32 kb + v*2VE + lg*VE holds the
+    // same keys as pf[kb][v] (stored order).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16 / VE; ++v) {
-        V pf;
-#pragma unroll
-        for (int j = 0; j < VE; ++j) pf[j] = from_f<T>(S[kb][v * VE + j]);
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
           V vf = as_vec<V>(ld16(sv + (d * 32 + l32) * VROWB + (kb * 32 + v * 2 * VE + lg * VE) * SZ));
-          O[d] = mfma32(vf, pf, O[d]);
+          O[d] = mfma32(vf, pf[kb][v], O[d]);
         }
       }
     }
@@ -241,9 +268,11 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.nq = nq;
   a.ldk = ldk;
   a.nseg = nseg;
+  a.H = H;
   a.scale = (float)(1.4426950408889634 / sqrt((double)dh));
+  a.thr = RESCALE_LOG2 / a.scale;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
-  dim3 grid((nq + BQ - 1) / BQ, H), block(256);
+  dim3 grid(((nq + BQ - 1) / BQ) * H), block(256);
   if (dtype == BF16 && dh == 128) attn_kernel<bf16, 128><<<grid, block, 0, s>>>(a);
   else if (dtype == BF16 && dh == 64) attn_kernel<bf16, 64><<<grid, block, 0, s>>>(a);
   else if (dtype == F32 && dh == 64) attn_kernel<float, 64><<<grid, block, 0, s>>>(a);

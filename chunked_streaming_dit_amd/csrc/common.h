@@ -57,11 +57,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// 1 + tanh(u) = 2 - 2 / (1 + e^{2u}) = 2 e^{2u} / (1 + e^{2u}); with e^{2u} from the
+// hardware exp2 this is x * e / (1 + e) (saturating to x or 0 when e overflows/underflows).
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float k1 = 0.044715f;
-  float u = k0 * (x + k1 * x * x * x);
-  return 0.5f * x * (1.0f + tanhf(u));
+  const float u = k0 * fmaf(k1 * x, x * x, x);
+  const float e = __builtin_amdgcn_exp2f(u * 2.8853900817779268f);  // e^{2u} = 2^{2u log2 e}
+  return isinf(e) ? x : x * e * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip (each with its own
+// L2).  Map dispatch index b to a logical index so that each XCD processes one
+// contiguous range of logical work items: neighbours in the logical order then share
+// an L2.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  constexpr int NXCD = 8;
+  const int x = b % NXCD, i = b / NXCD;
+  const int q = total / NXCD, r = total % NXCD;
+  return x * q + min(x, r) + i;
 }
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 

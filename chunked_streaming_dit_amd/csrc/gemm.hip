@@ -21,6 +21,71 @@ namespace {
 
 constexpr int ROWB = 128 + 16;  // LDS bytes per staged row (128 data + 16 pad)
 
+// Epilogue over a wave's (MB x 32) x (NB x 32) accumulator tile whose first row/column
+// are mw, nw: lane holds output row m = mw + 32 i + l32 and columns
+// n = nw + 32 j + 8 q + 4 lg + {0..3} in acc[i][j][4q .. 4q+3].
+template <class T, int MB, int NB, int EPI>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], int mw, int nw, int l32, int lg,
+                                         int M, int N, const GemmEpi& e) {
+  const T* bias = reinterpret_cast<const T*>(e.bias);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = mw + i * 32 + l32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nw + j * 32 + 8 * q + 4 * lg;
+        if (n >= N) continue;
+        float v[4], b[4];
+        load4<T>(bias + n, b);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + b[r];
+        if constexpr (EPI == EPI_BIAS) {
+          store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
+        } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
+          store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
+        } else if constexpr (EPI == EPI_F32) {
+          store4<float>(reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n, v);
+        } else if constexpr (EPI == EPI_RESID) {
+          float* hp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
+          float h[4], g[4] = {1.f, 1.f, 1.f, 1.f};
+          load4<float>(hp, h);
+          if (e.gate) load4<float>(e.gate + n, g);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] += g[r] * v[r];
+          store4<float>(hp, h);
+        } else {  // EPI_EULER
+          float* xp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
+          float x[4];
+          load4<float>(xp, x);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] = fmaf(e.dt, v[r], x[r]);
+          store4<float>(xp, x);
+          if (e.v_out) store4<float>(e.v_out + (size_t)m * e.ldo + n, v);
+        }
+      }
+    }
+  }
+}
+
+// Tile order: XCD-contiguous ranges of a grouped order in which GM consecutive
+// m-tiles share each W column block.
+__device__ __forceinline__ void tile_of(int b, int num_m, int num_n, int& tm, int& tn) {
+  constexpr int GM = 8;
+  const int pid = xcd_remap(b, num_m * num_n);
+  const int group = pid / (GM * num_n);
+  const int first_m = group * GM;
+  const int gsz = min(num_m - first_m, GM);
+  const int in_group = pid - group * GM * num_n;
+  tm = first_m + in_group % gsz;
+  tn = in_group / gsz;
+}
+
+
 template <class T, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int lda,
                                                    const T* __restrict__ W, int ldw, int M, int N,
@@ -38,16 +103,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int 
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lg = lane >> 5;
 
-  // Grouped tile order: GM consecutive m-tiles share each W column block.
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
-  constexpr int GM = 8;
-  const int pid = blockIdx.x;
-  const int group = pid / (GM * num_n);
-  const int first_m = group * GM;
-  const int gsz = min(num_m - first_m, GM);
-  const int in_group = pid - group * GM * num_n;
-  const int tm = first_m + in_group % gsz;
-  const int tn = in_group / gsz;
+  int tm, tn;
+  tile_of(blockIdx.x, num_m, num_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   u32x4 stage[CPT];
@@ -110,50 +168,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int 
     if (it + 1 < nk) sstore(buf ^ 1);
   }
 
-  // Epilogue: lane holds output row m = .. + l32, columns n = .. + 8q + 4lg + {0..3}.
-  const T* bias = reinterpret_cast<const T*>(e.bias);
-#pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    const int m = m0 + wm * WM + i * 32 + l32;
-    if (m >= M) continue;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WN + j * 32 + 8 * q + 4 * lg;
-        if (n >= N) continue;
-        float v[4], b[4];
-        load4<T>(bias + n, b);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + b[r];
-        if constexpr (EPI == EPI_BIAS) {
-          store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
-        } else if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
-          store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
-        } else if constexpr (EPI == EPI_F32) {
-          store4<float>(reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n, v);
-        } else if constexpr (EPI == EPI_RESID) {
-          float* hp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
-          float h[4], g[4] = {1.f, 1.f, 1.f, 1.f};
-          load4<float>(hp, h);
-          if (e.gate) load4<float>(e.gate + n, g);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] += g[r] * v[r];
-          store4<float>(hp, h);
-        } else {  // EPI_EULER
-          float* xp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
-          float x[4];
-          load4<float>(xp, x);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = fmaf(e.dt, v[r], x[r]);
-          store4<float>(xp, x);
-          if (e.v_out) store4<float>(e.v_out + (size_t)m * e.ldo + n, v);
-        }
-      }
-    }
-  }
+  epilogue<T, MB, NB, EPI>(acc, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }
 
 template <class T, int BM, int BN>
@@ -174,12 +189,146 @@ hipError_t launch_t(const void* A, int lda, const void* W, int ldw, int M, int N
   return hipGetLastError();
 }
 
+
+// bf16 GEMM for large tiles, 8 waves (2 x 4) per workgroup, 2 waves per SIMD.
+// Global -> LDS moves use direct-to-LDS loads (global_load_lds_dwordx4: each wave
+// instruction fills 1 KB = 8 rows of 128 bytes) into a 2-stage ring of unpadded
+// 128-byte rows.  The 16-byte chunk c of row r sits at chunk position
+// c ^ ((r >> 1) & 7), so that an MFMA fragment read (consecutive rows, same chunk)
+// spreads over all 64 LDS banks.  Loads for step k+1 are in flight while step k is
+// multiplied; one barrier per 64-wide K step.  Rows past M or N re-read the last valid
+// row (their outputs are never stored).  While one wave of a SIMD waits on LDS the
+// other issues MFMAs.
+constexpr int LDS_WM = 2, LDS_WN = 4, LDS_THREADS = 64 * LDS_WM * LDS_WN;
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __restrict__ A, int lda,
+                                                               const bf16* __restrict__ W, int ldw,
+                                                               int M, int N, int K, GemmEpi e) {
+  typedef bf16x8 V;
+  constexpr int NW = LDS_WM * LDS_WN;
+  constexpr int WM = BM / LDS_WM, WN = BN / LDS_WN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * 128;
+  constexpr int NLD = ROWS / (8 * NW);  // load instructions per wave per stage (8 rows each)
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && ROWS % (8 * NW) == 0 && BM % (8 * NW) == 0, "tile");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / LDS_WN, wn = wave % LDS_WN;
+  const int l32 = lane & 31, lg = lane >> 5;
+  const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, num_m, num_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Loader: instruction j of this wave fills tile rows 8 (NW j + wave) + [0, 8); the
+  // lane covers row r = 8 (NW j + wave) + lane/8 at chunk position lane & 7, i.e.
+  // source chunk (lane & 7) ^ ((r >> 1) & 7).  Byte offsets from the matrix base are
+  // 32-bit (matrices here are < 2 GB).
+  const int lsub = lane >> 3;
+  unsigned off[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int r = 8 * (NW * j + wave) + lsub;
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    if (8 * NW * j < BM)
+      off[j] = (unsigned)(min(m0 + r, M - 1) * lda + chunk * 8) * 2u;
+    else
+      off[j] = (unsigned)(min(n0 + r - BM, N - 1) * ldw + chunk * 8) * 2u;
+  }
+  const char* Ab = reinterpret_cast<const char*>(A);
+  const char* Wb = reinterpret_cast<const char*>(W);
+  auto issue = [&](int stage, int k0) {
+    char* dst = smem + stage * STAGE + wave * 8 * 128;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const char* base = (8 * NW * j < BM ? Ab : Wb) + (size_t)k0 * 2;
+      __builtin_amdgcn_global_load_lds((const void*)(base + off[j]), (void*)(dst + j * NW * 8 * 128), 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment rows: all offsets are multiples of 32 rows, so the swizzle term of every
+  // fragment this lane reads is the same: x = (l32 >> 1) & 7.
+  const int x = (l32 >> 1) & 7;
+  const int a_base = (wm * WM + l32) * 128;
+  const int w_base = (BM + wn * WN + l32) * 128;
+
+  const int nk = K / 64;
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < nk; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < nk) issue(buf ^ 1, (it + 1) * 64);
+    const char* st = smem + buf * STAGE;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int coff = ((2 * s + lg) ^ x) << 4;
+      V af[MB], wf[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[i] = as_vec<V>(ld16(st + a_base + i * 32 * 128 + coff));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wf[j] = as_vec<V>(ld16(st + w_base + j * 32 * 128 + coff));
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[j], af[i], acc[i][j]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  epilogue<bf16, MB, NB, EPI>(acc, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
+}
+
+template <int BM, int BN>
+hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+                      const GemmEpi& e, hipStream_t s) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  dim3 grid(tiles), block(LDS_THREADS);
+  const bf16* a = reinterpret_cast<const bf16*>(A);
+  const bf16* w = reinterpret_cast<const bf16*>(W);
+  switch (e.kind) {
+    case EPI_BIAS: gemm_lds_kernel<BM, BN, EPI_BIAS><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_GELU: gemm_lds_kernel<BM, BN, EPI_GELU><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_RESID: gemm_lds_kernel<BM, BN, EPI_RESID><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_F32: gemm_lds_kernel<BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_EULER: gemm_lds_kernel<BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                 const GemmEpi& e, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (dtype == BF16) {
+    if (M >= 256 && N >= 256 && N % 256 == 0) {
+      // Pick the tile height that minimises (waves of 256 workgroups) x tile area,
+      // i.e. the padded work of the last, partly filled wave; ties go to taller tiles.
+      const int cand[3] = {256, 192, 128};
+      int best = 256;
+      long long best_cost = -1;
+      for (int bm : cand) {
+        const long long tiles = (long long)((M + bm - 1) / bm) * (N / 256);
+        const long long cost = (tiles + 255) / 256 * (long long)bm;
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = bm; }
+      }
+      if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s);
+      if (best == 192) return launch_lds<192, 256>(A, lda, W, ldw, M, N, K, e, s);
+      return launch_lds<128, 256>(A, lda, W, ldw, M, N, K, e, s);
+    }
     if (M >= 512 && N >= 512) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
     return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
   }
