@@ -27,10 +27,15 @@ struct AttnArgs {
   int nseg;
   float scale;  // log2(e) / sqrt(dh)
   float thr;    // RESCALE_LOG2 / scale: lazy-rescale threshold in raw score units
+  int nsplit;   // key-range splits per (head, q-tile); > 1 writes partials
+  float* opart; // [nsplit, nq, H*DH] normalised partial outputs (nsplit > 1)
+  float* ml;    // [nsplit, nq, H, 2] (running max * scale, row sum) per partial
   AttnSeg seg[ATTN_MAX_SEGS];
 };
 
-constexpr int BQ = 128;  // queries per workgroup
+constexpr int AW = 8;          // waves per workgroup (32 queries each)
+constexpr int BQ = 32 * AW;    // queries per workgroup
+constexpr int NSLOT = 3;       // ring depth of the K and of the V^T tile rings
 constexpr float RESCALE_LOG2 = 8.0f;
 
 // Row-sum accumulation from the P^T operand vector.
@@ -49,31 +54,51 @@ __device__ __forceinline__ float row_sum_add(f32x4 p, float acc) {
 }
 constexpr int BKV = 64;  // keys per tile
 
+template <int N> __device__ __forceinline__ void wait_vm_lds() {
+  // s_waitcnt vmcnt(N) lgkmcnt(0); expcnt left at its maximum (7).
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// 16-byte chunk position of chunk c of row r in an unpadded LDS tile whose rows are RB
+// bytes: consecutive rows reading the same chunk spread over all 64 banks.
+template <int RB>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (RB >= 256) return c ^ (r & 15);
+  else return c ^ ((r >> 1) & 7);
+}
+
 template <class T, int DH>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
   constexpr int SZ = (int)sizeof(T);
   constexpr int QV = DH / (2 * VE);       // 16-byte vector steps over dh
-  constexpr int KROWB = DH * SZ + 16;     // LDS bytes per key row
-  constexpr int VROWB = BKV * SZ + 16;    // LDS bytes per V^T row
-  constexpr int CK = DH * SZ / 16;        // 16-byte chunks per key row
-  constexpr int CV = BKV * SZ / 16;       // 16-byte chunks per V^T row
-  constexpr int KCH = BKV * CK / 256;     // K chunks per thread per tile
-  constexpr int VCH = DH * CV / 256;      // V^T chunks per thread per tile
+  constexpr int RBK = DH * SZ;            // bytes per key row
+  constexpr int RBV = BKV * SZ;           // bytes per V^T row
+  constexpr int RPK = 1024 / RBK;         // key rows per 1-KB load instruction
+  constexpr int RPV = 1024 / RBV;         // V^T rows per 1-KB load instruction
+  constexpr int NLK = BKV * RBK / 1024 / AW;  // K load instructions per wave per tile
+  constexpr int NLV = DH * RBV / 1024 / AW;   // V^T load instructions per wave per tile
   constexpr int DB = DH / 32;             // 32-row blocks of dh
-  constexpr int STAGE = BKV * KROWB + DH * VROWB;
-  static_assert(BKV * CK % 256 == 0 && DH * CV % 256 == 0, "tile");
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  constexpr int KTILE = BKV * RBK, VTILE = DH * RBV;
+  static_assert(RBK >= 128 && RBV >= 128 && NLK >= 1 && NLV >= 1 &&
+                BKV * RBK == 1024 * AW * NLK && DH * RBV == 1024 * AW * NLV, "tile");
+  // LDS: NSLOT K slots and NSLOT V^T slots (separate rings, see the loop below).
+  __shared__ __attribute__((aligned(1024))) char smem[NSLOT * (KTILE + VTILE)];
+  char* const ks = smem;
+  char* const vs = smem + NSLOT * KTILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lg = lane >> 5;
   // 1-D grid over (head, q-tile), head-major, remapped so that each XCD works through
   // a contiguous range: the q-tiles of a head share that head's K/V in one L2.
+  // With nsplit > 1 the work item also names a contiguous part of the key tiles.
   const int nqt = (a.nq + BQ - 1) / BQ;
-  const int wi = xcd_remap(blockIdx.x, nqt * a.H);
-  const int head = wi / nqt;
-  const int qrow = (wi - head * nqt) * BQ + wave * 32 + l32;
+  const int wi = xcd_remap(blockIdx.x, nqt * a.H * a.nsplit);
+  const int hs = wi / nqt;                      // head * nsplit + split
+  const int head = hs / a.nsplit, split = hs - head * a.nsplit;
+  const int qrow = (wi - hs * nqt) * BQ + wave * 32 + l32;
   const bool qvalid = qrow < a.nq;
 
   // Q fragments (second MFMA operand): query qrow, dh = s*2VE + lg*VE + [0, VE).
@@ -89,50 +114,73 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // Flattened walk over the tiles of all segments.
-  int total = 0;
+  // Tiles of all segments in order: tile t lies in segment si at key offset base.
+  int c0 = 0, c1 = 0, c2 = 0;
+  if (a.nseg > 0) c0 = (a.seg[0].n + BKV - 1) / BKV;
+  if (a.nseg > 1) c1 = (a.seg[1].n + BKV - 1) / BKV;
+  if (a.nseg > 2) c2 = (a.seg[2].n + BKV - 1) / BKV;
+  const int ntiles = c0 + c1 + c2;
+  const int tb = (int)((long long)ntiles * split / a.nsplit);
+  const int total = (int)((long long)ntiles * (split + 1) / a.nsplit);  // tiles [tb, total)
+  auto locate = [&](int t, int& si, int& base) {
+    if (t < c0) { si = 0; base = t * BKV; }
+    else if (t < c0 + c1) { si = 1; base = (t - c0) * BKV; }
+    else { si = 2; base = (t - c0 - c1) * BKV; }
+  };
+  // Direct-to-LDS loads (global_load_lds_dwordx4): wave instruction g = wave + AW i fills
+  // 1 KB of a slot = rows [RP g, RP g + RP); the lane covers row RP g + lane/(64/RP) at
+  // chunk position lane % (64/RP), i.e. source chunk swz(row, position).
+  unsigned koff[NLK];
 #pragma unroll
-  for (int s = 0; s < ATTN_MAX_SEGS; ++s)
-    if (s < a.nseg) total += (a.seg[s].n + BKV - 1) / BKV;
-
-  u32x4 kst[KCH], vst[VCH];
-  auto gload = [&](int si, int base) {
-    const AttnSeg& sg = a.seg[si];
-    const char* kp = reinterpret_cast<const char*>(sg.k);
-    const char* vp = reinterpret_cast<const char*>(sg.vt);
+  for (int i = 0; i < NLK; ++i) {
+    const int g = wave + AW * i;
+    const int r = RPK * g + lane / (64 / RPK);
+    const int c = swz<RBK>(r, lane % (64 / RPK));
+    koff[i] = (unsigned)((r * a.ldk + head * DH) * SZ + c * 16);
+  }
+  int vrow[NLV], vchk[NLV];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CK, cc = c % CK;
-      kst[i] = ld16(kp + ((size_t)(base + r) * a.ldk + head * DH) * SZ + cc * 16);
-    }
+  for (int i = 0; i < NLV; ++i) {
+    const int g = wave + AW * i;
+    vrow[i] = RPV * g + lane / (64 / RPV);
+    vchk[i] = swz<RBV>(vrow[i], lane % (64 / RPV)) * 16;
+  }
+  auto load_k = [&](int t, int slot) {
+    int si, base;
+    locate(t, si, base);
+    const char* kp = reinterpret_cast<const char*>(a.seg[si].k) + (size_t)base * a.ldk * SZ;
+    char* dst = ks + slot * KTILE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / CV, cc = c % CV;
-      vst[i] = ld16(vp + ((size_t)(head * DH + r) * sg.cap + base) * SZ + cc * 16);
+    for (int i = 0; i < NLK; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(kp + koff[i]), (void*)(dst + i * AW * 1024), 16, 0, 0);
+  };
+  auto load_v = [&](int t, int slot) {
+    int si, base;
+    locate(t, si, base);
+    const unsigned cap = (unsigned)a.seg[si].cap;
+    const char* vp = reinterpret_cast<const char*>(a.seg[si].vt) + (size_t)base * SZ;
+    char* dst = vs + slot * VTILE + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const unsigned off = ((unsigned)(head * DH + vrow[i]) * cap) * SZ + vchk[i];
+      __builtin_amdgcn_global_load_lds((const void*)(vp + off), (void*)(dst + i * AW * 1024), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    char* sk = smem + buf * STAGE;
-    char* sv = sk + BKV * KROWB;
+  // S^T tile from a K slot: 2 blocks of 32 keys x 32 queries.  Lane: query l32,
+  // key = 32 kb + 8 (e/4) + 4 lg + e%4 for element e.
+  const int kx = l32;  // swizzle row term: fragment rows are l32 + multiples of 32
+  auto scores = [&](int slot, f32x16 (&S)[2]) {
+    const char* sk = ks + slot * KTILE;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      st16(sk + (c / CK) * KROWB + (c % CK) * 16, kst[i]);
-    }
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int c = tid + 256 * i;
-      st16(sv + (c / CV) * VROWB + (c % CV) * 16, vst[i]);
-    }
-  };
-  auto advance = [&](int& si, int& base) {
-    base += BKV;
-    if (base >= a.seg[si].n) {
-      base = 0;
-      ++si;
-      while (si < a.nseg && a.seg[si].n == 0) ++si;
+      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < QV; ++s) {
+        const int pos = swz<RBK>(kx, 2 * s + lg);
+        V kf = as_vec<V>(ld16(sk + (kb * 32 + l32) * RBK + pos * 16));
+        S[kb] = mfma32(kf, qf[s], S[kb]);
+      }
     }
   };
 
@@ -142,37 +190,44 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) O[d][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  f32x16 Sc[2], Sn[2];  // scores of the current and of the next tile
 
-  int si = 0, base = 0;
-  while (si < a.nseg && a.seg[si].n == 0) ++si;
-  int nsi = si, nbase = base;
-  if (total > 0) {
-    gload(si, base);
-    sstore(0);
-    advance(nsi, nbase);
-  }
-
-  for (int t = 0; t < total; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < total;
-    if (more) gload(nsi, nbase);
+  // Software pipeline over tiles.  Iteration t computes the scores of tile t+1 (MFMA)
+  // before the softmax of tile t (VALU), then O += V_t P_t.  K and V^T have separate
+  // NSLOT-slot rings (tile i in slot i % NSLOT).  Right after the barrier at its top,
+  // iteration t starts loading K tile t+3 and V tile t+2 (into the slots read during
+  // iteration t-1), so every tile is requested about two iterations before use; at
+  // its end it waits only for the older loads (K t+2, V t+1), keeping the new ones in
+  // flight (loads complete in issue order).
+  static_assert(NSLOT == 3, "the waits below assume a 3-deep ring");
+  auto wait_keep = [&](int keep) {  // s_waitcnt vmcnt(keep) lgkmcnt(0)
+    if (keep >= NLK + NLV) wait_vm_lds<NLK + NLV>();
+    else if (keep >= NLK && keep >= NLV) wait_vm_lds<(NLK > NLV ? NLK : NLV)>();
+    else if (keep >= NLK || keep >= NLV) wait_vm_lds<(NLK < NLV ? NLK : NLV)>();
+    else wait_vm_lds<0>();
+  };
+  if (total > tb) {
+    load_k(tb, tb % NSLOT);
+    if (total > tb + 1) load_k(tb + 1, (tb + 1) % NSLOT);
+    load_v(tb, tb % NSLOT);
+    int later = 0;
+    if (total > tb + 2) { load_k(tb + 2, (tb + 2) % NSLOT); later += NLK; }
+    if (total > tb + 1) { load_v(tb + 1, (tb + 1) % NSLOT); later += NLV; }
+    wait_keep(later);
     __syncthreads();
-    const char* sk = smem + buf * STAGE;
-    const char* sv = sk + BKV * KROWB;
+    scores(tb % NSLOT, Sc);
+  }
+  for (int t = tb; t < total; ++t) {
+    const bool has1 = t + 1 < total, has2 = t + 2 < total, has3 = t + 3 < total;
+    // Every wave has finished iteration t-1 (or the prologue's scores of tile tb), so
+    // the slots refilled below are no longer read by anyone.
+    __syncthreads();
+    if (has3) load_k(t + 3, (t + 3) % NSLOT);
+    if (has2) load_v(t + 2, (t + 2) % NSLOT);
+    if (has1) scores((t + 1) % NSLOT, Sn);
 
-    // S^T tile: 2 blocks of 32 keys x 32 queries.  Lane: query l32,
-    // key = 32 kb + 8 (e/4) + 4 lg + e%4 for element e.
-    f32x16 S[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < QV; ++s) {
-        V kf = as_vec<V>(ld16(sk + (kb * 32 + l32) * KROWB + s * 32 + lg * 16));
-        S[kb] = mfma32(kf, qf[s], S[kb]);
-      }
-    }
+    int si, base;
+    locate(t, si, base);
     const int seg_n = a.seg[si].n;
     if (base + BKV > seg_n) {  // ragged tail of a segment: mask keys >= n
 #pragma unroll
@@ -180,14 +235,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = base + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (key >= seg_n) S[kb][r] = -INFINITY;
+          if (key >= seg_n) Sc[kb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescale: keep the running max unless a score exceeds it by more than
     // RESCALE_LOG2 in the exp2 domain (then p stays <= 2^RESCALE_LOG2, which fp32
@@ -204,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float ms = m_run * a.scale;
-    // P^T operands: elements [v*VE, v*VE+VE) of S[kb].  The row sum is taken from the
+    // P^T operands: elements [v*VE, v*VE+VE) of Sc[kb].  The row sum is taken from the
     // converted operand values, i.e. from exactly the weights the second MFMA uses.
     V pf[2][16 / VE];
 #pragma unroll
@@ -213,36 +268,50 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       for (int v = 0; v < 16 / VE; ++v) {
 #pragma unroll
         for (int j = 0; j < VE; ++j)
-          pf[kb][v][j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(S[kb][v * VE + j], a.scale, -ms)));
+          pf[kb][v][j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(Sc[kb][v * VE + j], a.scale, -ms)));
         l_run = row_sum_add(pf[kb][v], l_run);
       }
-
     // O^T += V^T P^T; the V^T vector at key offset 32 kb + v*2VE + lg*VE holds the
     // same keys as pf[kb][v] (stored order).
+    const char* sv = vs + (t % NSLOT) * VTILE;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int v = 0; v < 16 / VE; ++v) {
+        const int chunk = (kb * 32 + v * 2 * VE + lg * VE) * SZ / 16;
+        const int pos = swz<RBV>(l32, chunk);
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          V vf = as_vec<V>(ld16(sv + (d * 32 + l32) * VROWB + (kb * 32 + v * 2 * VE + lg * VE) * SZ));
+          V vf = as_vec<V>(ld16(sv + (d * 32 + l32) * RBV + pos * 16));
           O[d] = mfma32(vf, pf[kb][v], O[d]);
         }
       }
     }
-    if (more) {
-      sstore(buf ^ 1);
-      si = nsi;
-      base = nbase;
-      advance(nsi, nbase);
-    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Sc[kb] = Sn[kb];
+    // this wave's loads of K tile t+2 and V tile t+1 have landed (this iteration's stay)
+    wait_keep((has3 ? NLK : 0) + (has2 ? NLV : 0));
   }
 
   // Normalise and store: lane holds query qrow, dh = 32 d + 8 q + 4 lg + [0, 4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
-  const float inv = 1.0f / l_tot;
-  T* op = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * DH;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (a.nsplit == 1) {
+    T* op = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * DH;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = O[d][4 * q + r] * inv;
+        store4<T>(op + d * 32 + 8 * q + 4 * lg, v);
+      }
+    return;
+  }
+  const int D = a.H * DH;
+  float* op = a.opart + ((size_t)split * a.nq + qrow) * D + head * DH;
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -250,16 +319,68 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = O[d][4 * q + r] * inv;
-      store4<T>(op + d * 32 + 8 * q + 4 * lg, v);
+      store4<float>(op + d * 32 + 8 * q + 4 * lg, v);
     }
+  if (lg == 0) {
+    float* mp = a.ml + (((size_t)split * a.nq + qrow) * a.H + head) * 2;
+    mp[0] = l_tot > 0.f ? m_run * a.scale : -INFINITY;
+    mp[1] = l_tot;
+  }
+}
+
+// Merge key-range partials: o = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - max m).
+// One thread per (query, head, 4 consecutive dh).
+template <class T, int DH>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
+                                                           const float* __restrict__ ml, int nsplit,
+                                                           int nq, int H, T* __restrict__ o, int ldo) {
+  const int D = H * DH;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)nq * D / 4) return;
+  const int qrow = (int)(i / (D / 4));
+  const int c = (int)(i - (long long)qrow * (D / 4)) * 4;
+  const int head = c / DH;
+  float mmax = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) mmax = fmaxf(mmax, ml[(((size_t)sp * nq + qrow) * H + head) * 2]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, wsum = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float* mp = ml + (((size_t)sp * nq + qrow) * H + head) * 2;
+    const float w = mp[1] > 0.f ? mp[1] * __builtin_amdgcn_exp2f(mp[0] - mmax) : 0.f;
+    float v[4];
+    load4<float>(opart + ((size_t)sp * nq + qrow) * D + c, v);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = fmaf(w, v[r], acc[r]);
+    wsum += w;
+  }
+  const float inv = 1.0f / wsum;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] *= inv;
+  store4<T>(o + (size_t)qrow * ldo + c, acc);
 }
 
 }  // namespace
 
+// Key-range splits for a launch: the smallest estimated time, counting waves of
+// `slots` concurrent workgroups and a small fixed cost for the merge pass.  Splitting
+// needs at least 2 tiles per split and partial storage for nsplit * nq rows.
+int attention_splits(int nq, int H, int total_keys_tiles, int partial_rows, int slots) {
+  const int nqt = (nq + BQ - 1) / BQ;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int ns = 1; ns <= 4; ++ns) {
+    if (ns > 1 && (total_keys_tiles < 2 * ns || (long long)ns * nq > partial_rows)) break;
+    const long long items = (long long)nqt * H * ns;
+    const double cost = (double)((items + slots - 1) / slots) / ns + (ns > 1 ? 0.05 : 0.0);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = ns; }
+  }
+  return best;
+}
+
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, hipStream_t s) {
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
+  if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
   AttnArgs a;
   a.q = q;
   a.o = o;
@@ -271,14 +392,50 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.H = H;
   a.scale = (float)(1.4426950408889634 / sqrt((double)dh));
   a.thr = RESCALE_LOG2 / a.scale;
+  a.nsplit = sp.nsplit;
+  a.opart = sp.opart;
+  a.ml = sp.ml;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
-  dim3 grid(((nq + BQ - 1) / BQ) * H), block(256);
+  dim3 grid(((nq + BQ - 1) / BQ) * H * sp.nsplit), block(64 * AW);
   if (dtype == BF16 && dh == 128) attn_kernel<bf16, 128><<<grid, block, 0, s>>>(a);
   else if (dtype == BF16 && dh == 64) attn_kernel<bf16, 64><<<grid, block, 0, s>>>(a);
   else if (dtype == F32 && dh == 64) attn_kernel<float, 64><<<grid, block, 0, s>>>(a);
-  else if (dtype == F32 && dh == 128) attn_kernel<float, 128><<<grid, block, 0, s>>>(a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
+                             hipStream_t s) {
+  if (nq <= 0 || sp.nsplit <= 1) return hipSuccess;
+  const long long n4 = (long long)nq * H * dh / 4;
+  dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+  if (dtype == BF16 && dh == 128)
+    attn_combine_kernel<bf16, 128><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (bf16*)o, ldo);
+  else if (dtype == BF16 && dh == 64)
+    attn_combine_kernel<bf16, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (bf16*)o, ldo);
+  else if (dtype == F32 && dh == 64)
+    attn_combine_kernel<float, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (float*)o, ldo);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+int attention_key_tiles(const AttnSeg* segs, int nseg) {
+  int t = 0;
+  for (int i = 0; i < nseg; ++i) t += (segs[i].n + BKV - 1) / BKV;
+  return t;
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
 }
 
 }  // namespace dit

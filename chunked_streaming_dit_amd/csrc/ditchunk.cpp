@@ -57,7 +57,8 @@ struct Layout {
   size_t state_total = 0;
   // workspace
   size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
-         va_raw = 0, ka = 0, vat = 0, mod = 0, tmp = 0;
+         va_raw = 0, ka = 0, vat = 0, mod = 0, tmp = 0, opart = 0, ml = 0;
+  int part_rows = 0;  // rows of key-range attention partials (split count x queries)
   size_t ws_total = 0;
 };
 
@@ -66,6 +67,7 @@ int check_config(const dit_config* c) {
   if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return fail(DIT_EINVAL, "dtype %d", c->dtype);
   if (c->L < 1 || c->L > 256) return fail(DIT_EINVAL, "L=%d out of [1, 256]", c->L);
   if (c->dh != 64 && c->dh != 128) return fail(DIT_EINVAL, "dh=%d (64 or 128)", c->dh);
+  if (c->dtype == DIT_F32 && c->dh != 64) return fail(DIT_EINVAL, "fp32 supports dh=64 only");
   if (c->H < 1 || c->D != c->H * c->dh) return fail(DIT_EINVAL, "D=%d != H*dh=%d*%d", c->D, c->H, c->dh);
   if (c->D % 256 || c->D > 4096) return fail(DIT_EINVAL, "D=%d must be a multiple of 256, <= 4096", c->D);
   if (c->mlp_ratio < 1 || c->mlp_ratio > 8) return fail(DIT_EINVAL, "mlp_ratio=%d", c->mlp_ratio);
@@ -124,6 +126,9 @@ Layout make_layout(const dit_config* c) {
   L.vat = take(A * D * L.elt);
   L.mod = take(((size_t)c->L * 6 * D + 2 * D) * 4);
   L.tmp = take((256 + 2 * D) * 4);
+  L.part_rows = 2 * L.cap_tok;
+  L.opart = take((size_t)L.part_rows * D * 4);
+  L.ml = take((size_t)L.part_rows * c->H * 2 * 4);
   L.ws_total = off;
   return L;
 }
@@ -187,6 +192,26 @@ int timed_end(dit_handle* h, int slot, double flop) {
   return DIT_OK;
 }
 
+// Self-attention launch: picks the key-range split, times the main kernel when timing is
+// on (the flop count is the method's 4 n_q n_kv D), then merges partials if split.
+int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed) {
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  AttnSplit sp{1, hd->X<float>(L.opart), hd->X<float>(L.ml)};
+  sp.nsplit = attention_splits(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
+  int slot = -1, rc;
+  if (timed && (rc = timed_begin(hd, &slot))) return rc;
+  HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
+                   hd->stream));
+  if (timed) {
+    double nkv = 0;
+    for (int i = 0; i < ns; ++i) nkv += seg[i].n;
+    if ((rc = timed_end(hd, slot, 4.0 * n * nkv * c.D))) return rc;
+  }
+  HIPCHK(attention_combine(c.dtype, c.dh, c.H, n, sp, hd->X(L.o), c.D, hd->stream));
+  return DIT_OK;
+}
+
 // One context pass (reference or boundary) at t = 0: writes K (normed, rotated) and V
 // of every block into kdst[l] / vdst[l] (capacity cap).  prior_k/prior_v/prior_n: the
 // earlier context segment (reference) per block, or none.
@@ -225,12 +250,8 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
     int ns = 0;
     if (with_prior) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     seg[ns++] = AttnSeg{hd->S(kdst[l]), hd->S(vdst[l]), n, cap};
-    int slot;
-    int rc = timed_begin(hd, &slot);
+    int rc = run_attention(hd, n, seg, ns, true);
     if (rc) return rc;
-    HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, seg, ns, s));
-    long long nkv = n + (with_prior ? hd->n_ref : 0);
-    if ((rc = timed_end(hd, slot, 4.0 * n * (double)nkv * D))) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
     HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
@@ -396,12 +417,8 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
     seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     if (hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
-    int slot;
-    int rc = timed_begin(hd, &slot);
+    int rc = run_attention(hd, n, seg, ns, true);
     if (rc) return rc;
-    HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, seg, ns, s));
-    const double nkv = (double)n + hd->n_ref + hd->n_bnd;
-    if ((rc = timed_end(hd, slot, 4.0 * n * nkv * D))) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
     HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
@@ -423,7 +440,7 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
                          hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, nullptr,
                          hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
       AttnSeg aseg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
-      HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), D, hd->X(L.o), D, n, D, &aseg, 1, s));
+      if (int rc2 = run_attention(hd, n, &aseg, 1, false)) return rc2;
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
       HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));

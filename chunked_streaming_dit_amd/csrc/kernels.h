@@ -42,9 +42,24 @@ struct AttnSeg {
   int cap;
 };
 enum { ATTN_MAX_SEGS = 3 };
+// Key-range split: nsplit > 1 makes attention() write normalised partial outputs
+// opart [nsplit, nq, H*dh] and (max * log2e/sqrt(dh), row sum) pairs ml [nsplit, nq, H, 2]
+// (fp32), which attention_combine() merges into o.
+struct AttnSplit {
+  int nsplit;
+  float* opart;
+  float* ml;
+};
 // o[nq, ldo] = softmax(q k^T / sqrt(dh)) v over the concatenated segments, per head.
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, hipStream_t s);
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s);
+hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
+                             hipStream_t s);
+// Splits minimising the estimated time for nq queries, H heads, key_tiles 64-key tiles,
+// partial storage of partial_rows rows and `slots` concurrent workgroups.
+int attention_splits(int nq, int H, int key_tiles, int partial_rows, int slots);
+int attention_key_tiles(const AttnSeg* segs, int nseg);
+int device_cus();
 
 // ---------------------------------------------------------------- elementwise
 // out[n, D] (dtype) = RMSNorm(h) * (1 + scale) + shift  (shift/scale NULL: plain RMSNorm)

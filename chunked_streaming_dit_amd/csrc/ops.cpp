@@ -112,10 +112,11 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   void* o, void* stream) {
+                   int nsplit, float* partial, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
   if (!q || !o || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
+  if (dtype == DIT_F32 && dh != 64) return fail(DIT_EINVAL, "fp32 attention supports dh=64 only");
   if (H < 1 || nq < 0 || nseg < 1 || nseg > ATTN_MAX_SEGS) return fail(DIT_ESHAPE, "H/nq/nseg");
   AttnSeg seg[ATTN_MAX_SEGS];
   long long total = 0;
@@ -127,9 +128,14 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
     total += n[i];
   }
   if (total < 1) return fail(DIT_ESHAPE, "no keys");
+  if (nsplit < 1 || nsplit > 8) return fail(DIT_EINVAL, "nsplit=%d out of [1, 8]", nsplit);
+  if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   const int D = H * dh;
-  return hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, (hipStream_t)stream),
-                "attention");
+  AttnSplit sp{nsplit, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
+  int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, (hipStream_t)stream),
+                  "attention");
+  if (rc) return rc;
+  return hipchk(attention_combine(dtype, dh, H, nq, sp, o, D, (hipStream_t)stream), "attention_combine");
 }
 
 int ditk_modulation(int dtype, int D, int L, double t, const void* const* w, float* mod_out,

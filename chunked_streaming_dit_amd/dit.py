@@ -215,14 +215,14 @@ class ops:
 
     @staticmethod
     def attention(dtype: str, dh: int, H: int, q, segs: Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]],
-                  o) -> None:
+                  o, nsplit: int = 1, partial: Optional[torch.Tensor] = None) -> None:
         ns = len(segs)
         kp = (C.P * ns)(*[s[0].data_ptr() for s in segs])
         vp = (C.P * ns)(*[s[1].data_ptr() for s in segs])
         nn = (ctypes.c_int * ns)(*[s[2] for s in segs])
         cp = (ctypes.c_int * ns)(*[s[3] for s in segs])
         C.check(C.lib().ditk_attention(_dt_code(dtype), dh, H, q.data_ptr(), q.shape[0], ns, kp, vp, nn,
-                                       cp, o.data_ptr(), _stream()))
+                                       cp, nsplit, _ptr(partial), o.data_ptr(), _stream()))
 
     @staticmethod
     def modulation(dtype: str, cfg: ChunkConfig, weights: Dict[str, torch.Tensor], t: float,

@@ -53,10 +53,13 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 /* o[nq, H*dh] = softmax(q k^T / sqrt(dh)) v per head, keys the concatenation of nseg
  * (1..3) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
- * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype). */
+ * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
+ * nsplit (1..8) splits the key tiles into contiguous parts computed by separate
+ * workgroups and merged afterwards; nsplit > 1 needs partial: fp32 scratch of
+ * nsplit * nq * (H*dh + 2*H) floats (NULL allowed for nsplit == 1). */
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   void* o, void* hip_stream);
+                   int nsplit, float* partial, void* o, void* hip_stream);
 
 /* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
  * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,

@@ -149,6 +149,10 @@ def test_euler_and_ops_validation():
     k = (C.P * 1)(FAKE)
     n = (ctypes.c_int * 1)(70)
     cap = (ctypes.c_int * 1)(64)
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_ESHAPE
+    n[0] = 40
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_EINVAL
     n[0] = 0
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, FAKE, None) == C.DIT_ESHAPE  # no keys
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_ESHAPE  # no keys

@@ -142,7 +142,7 @@ def test_qknorm_rope(dtype, dh, rope):
     assert np.all(pad == 0)
 
 
-def _attn_case(dtype, dh, H, nq, seg_ns, seed):
+def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1):
     dev = device()
     r = np.random.default_rng(seed)
     D = H * dh
@@ -161,7 +161,8 @@ def _attn_case(dtype, dh, H, nq, seg_ns, seed):
         ks.append(k)
         vs.append(v)
     o = torch.empty((nq, D), device=dev, dtype=torch_dtype(dtype))
-    ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o)
+    part = torch.empty(nsplit * nq * (D + 2 * H), device=dev) if nsplit > 1 else None
+    ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part)
     K = np.concatenate(ks).astype(np.float64).reshape(-1, H, dh)
     V = np.concatenate(vs).astype(np.float64).reshape(-1, H, dh)
     ref = O.attention(q.astype(np.float64).reshape(nq, H, dh), K, V).reshape(nq, D)
@@ -174,7 +175,18 @@ def _attn_case(dtype, dh, H, nq, seg_ns, seed):
 @pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (1, [5]), (300, [64, 0, 200]),
                                        (257, [1, 1, 1]), (128, [1000])])
 def test_attention(dtype, dh, nq, seg_ns):
+    if dtype == "f32" and dh == 128:
+        pytest.skip("fp32 attention is built for dh=64 only (the fp32 workload's head size)")
     err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + dh)
+    assert err <= TOL[dtype] / 4, err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("nsplit", [2, 3, 8])
+@pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (300, [64, 0, 200]), (40, [130])])
+def test_attention_key_split(dtype, nsplit, nq, seg_ns):
+    """Key tiles split over workgroups and merged; includes splits with no tiles."""
+    err = _attn_case(dtype, 64, 2, nq, seg_ns, nq + sum(seg_ns) + nsplit, nsplit)
     assert err <= TOL[dtype] / 4, err
 
 

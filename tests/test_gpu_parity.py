@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 MINI_BF16 = synth.config(2, cid=202, L=2, D=256, H=2, dh=128, d_a=64, M=7,
                          chunk=Grid(0, 3, 10, 13), ref=Grid(-2, 1, 10, 13), bnd=Grid(-1, 1, 10, 13),
                          steps=2)
-MINI_F32 = dataclasses.replace(MINI_BF16, cid=203, dtype="f32")
+MINI_F32 = dataclasses.replace(MINI_BF16, cid=203, dtype="f32", H=4, dh=64)
 MINI_F32_DH64 = synth.config(1, cid=204, L=2, chunk=Grid(0, 3, 7, 9), ref=Grid(-2, 1, 7, 9),
                              bnd=Grid(-1, 1, 5, 9), M=5, steps=2, t_start=0.9, t_end=0.3)
 MINI_SR = synth.config(4, cid=205, L=2, D=256, H=2, dh=128,
@@ -56,7 +56,7 @@ def test_config1_tiny_fp32():
     _check(synth.CONFIGS[1])
 
 
-def test_mini_fp32_dh128_multi_tile():
+def test_mini_fp32_multi_tile():
     _check(MINI_F32)
 
 
