@@ -68,7 +68,9 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ ((r >> 1) & 7);
 }
 
-template <class T, int DH>
+// KIND only names the launch site in profiles (0: self-attention over the segmented
+// keys, 1: audio cross-attention); the code is the same.
+template <class T, int DH, int KIND>
 __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
@@ -377,7 +379,8 @@ int attention_splits(int nq, int H, int total_keys_tiles, int partial_rows, int 
 }
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s) {
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s,
+                     int kind) {
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
   if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
@@ -397,10 +400,19 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.ml = sp.ml;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
   dim3 grid(((nq + BQ - 1) / BQ) * H * sp.nsplit), block(64 * AW);
-  if (dtype == BF16 && dh == 128) attn_kernel<bf16, 128><<<grid, block, 0, s>>>(a);
-  else if (dtype == BF16 && dh == 64) attn_kernel<bf16, 64><<<grid, block, 0, s>>>(a);
-  else if (dtype == F32 && dh == 64) attn_kernel<float, 64><<<grid, block, 0, s>>>(a);
-  else return hipErrorInvalidValue;
+  const bool cross = kind == ATTN_CROSS;
+  if (dtype == BF16 && dh == 128) {
+    if (cross) attn_kernel<bf16, 128, 1><<<grid, block, 0, s>>>(a);
+    else attn_kernel<bf16, 128, 0><<<grid, block, 0, s>>>(a);
+  } else if (dtype == BF16 && dh == 64) {
+    if (cross) attn_kernel<bf16, 64, 1><<<grid, block, 0, s>>>(a);
+    else attn_kernel<bf16, 64, 0><<<grid, block, 0, s>>>(a);
+  } else if (dtype == F32 && dh == 64) {
+    if (cross) attn_kernel<float, 64, 1><<<grid, block, 0, s>>>(a);
+    else attn_kernel<float, 64, 0><<<grid, block, 0, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -194,7 +194,7 @@ int timed_end(dit_handle* h, int slot, double flop) {
 
 // Self-attention launch: picks the key-range split, times the main kernel when timing is
 // on (the flop count is the method's 4 n_q n_kv D), then merges partials if split.
-int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed) {
+int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed, int kind) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   AttnSplit sp{1, hd->X<float>(L.opart), hd->X<float>(L.ml)};
@@ -202,7 +202,7 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed)
   int slot = -1, rc;
   if (timed && (rc = timed_begin(hd, &slot))) return rc;
   HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
-                   hd->stream));
+                   hd->stream, kind));
   if (timed) {
     double nkv = 0;
     for (int i = 0; i < ns; ++i) nkv += seg[i].n;
@@ -250,7 +250,7 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
     int ns = 0;
     if (with_prior) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     seg[ns++] = AttnSeg{hd->S(kdst[l]), hd->S(vdst[l]), n, cap};
-    int rc = run_attention(hd, n, seg, ns, true);
+    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
     if (rc) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
@@ -417,7 +417,7 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
     seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     if (hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
-    int rc = run_attention(hd, n, seg, ns, true);
+    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
     if (rc) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
@@ -440,7 +440,7 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
                          hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, nullptr,
                          hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
       AttnSeg aseg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
-      if (int rc2 = run_attention(hd, n, &aseg, 1, false)) return rc2;
+      if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS)) return rc2;
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
       HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));

@@ -51,8 +51,10 @@ struct AttnSplit {
   float* ml;
 };
 // o[nq, ldo] = softmax(q k^T / sqrt(dh)) v over the concatenated segments, per head.
+enum { ATTN_SELF = 0, ATTN_CROSS = 1 };
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s);
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s,
+                     int kind = ATTN_SELF);
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
                              hipStream_t s);
 // Splits minimising the estimated time for nq queries, H heads, key_tiles 64-key tiles,

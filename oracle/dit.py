@@ -30,7 +30,7 @@ __all__ = [
     "grid_positions", "rope_angles", "rope_apply", "qk_norm", "softmax",
     "attention", "upsample2_tokens", "patch_input", "block_forward",
     "context_pass", "dit_velocity", "euler", "schedule", "chunk_denoise",
-    "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone",
+    "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone", "velocity_rows",
 ]
 
 Weights = Dict[str, np.ndarray]
@@ -379,3 +379,46 @@ def standalone(P: Weights, cfg, inp: Dict[str, np.ndarray], record: bool = True)
                 if cfg.cond_up == 2 else inp["cond"])
     x, vs = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond, record=True)
     return x, vs, ref_kv, bnd_kv
+
+
+def velocity_rows(P: Weights, cfg, x: np.ndarray, t: float, pos: np.ndarray,
+                  ctx: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]],
+                  audio: Optional[np.ndarray], rows: np.ndarray,
+                  cond: Optional[np.ndarray] = None) -> np.ndarray:
+    """dit_velocity(...)[rows] for a single-block model (cfg.L == 1), computing the
+    query-side path only for the requested rows.
+
+    With one block, a row's velocity depends on the other tokens only through that
+    block's keys and values, so K and V are formed for every token while queries,
+    attention, MLP and the final layer run for the requested rows alone.  This makes
+    sampled checks affordable at full token counts."""
+    assert cfg.L == 1, "row-restricted evaluation is exact only for one block"
+    D, H, eps = cfg.D, cfg.H, cfg.eps
+    c = conditioning(P, t)
+    sh1, sc1, g1, sh2, sc2, g2 = block_modulation(P, 0, c)
+    h_all = linear(patch_input(x, cond, cfg.C_c), W(P, "pe.w"), W(P, "pe.b"))
+    u_all = modulate(rms_norm(h_all, eps), sh1, sc1)
+    wqkv, bqkv = W(P, "blk0.qkv.w"), W(P, "blk0.qkv.b")
+    ang_all = rope_angles(pos, cfg.dh, cfg.rope_theta)
+    k = rope_apply(qk_norm(_heads(linear(u_all, wqkv[D:2 * D], bqkv[D:2 * D]), H), W(P, "blk0.gk"), eps),
+                   ang_all)
+    v = _heads(linear(u_all, wqkv[2 * D:], bqkv[2 * D:]), H)
+    h = h_all[rows]
+    q = rope_apply(qk_norm(_heads(linear(u_all[rows], wqkv[:D], bqkv[:D]), H), W(P, "blk0.gq"), eps),
+                   ang_all[rows])
+    K = np.concatenate([kk for kk, _ in ctx[0]] + [k], axis=0)
+    V = np.concatenate([vv for _, vv in ctx[0]] + [v], axis=0)
+    o = attention(q, K, V).reshape(len(rows), D)
+    h = h + g1 * linear(o, W(P, "blk0.o.w"), W(P, "blk0.o.b"))
+    if audio is not None and audio.shape[0] > 0:
+        a = np.asarray(audio, dtype=np.float64)
+        qc = qk_norm(_heads(linear(rms_norm(h, eps), W(P, "blk0.cq.w"), W(P, "blk0.cq.b")), H),
+                     W(P, "blk0.gcq"), eps)
+        kc = qk_norm(_heads(linear(a, W(P, "blk0.ck.w"), W(P, "blk0.ck.b")), H), W(P, "blk0.gck"), eps)
+        vc = _heads(linear(a, W(P, "blk0.cv.w"), W(P, "blk0.cv.b")), H)
+        h = h + linear(attention(qc, kc, vc).reshape(len(rows), D), W(P, "blk0.co.w"), W(P, "blk0.co.b"))
+    u = modulate(rms_norm(h, eps), sh2, sc2)
+    h = h + g2 * linear(gelu_tanh(linear(u, W(P, "blk0.fc1.w"), W(P, "blk0.fc1.b"))),
+                        W(P, "blk0.fc2.w"), W(P, "blk0.fc2.b"))
+    shf, scf = final_modulation(P, c)
+    return linear(modulate(rms_norm(h, eps), shf, scf), W(P, "fin.w"), W(P, "fin.b"))

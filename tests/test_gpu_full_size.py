@@ -1,0 +1,178 @@
+"""Parity and properties at the workloads' full sizes, through the C ABI.
+
+- Streaming sequence (6 chunks of the base shape): oracle parity of the first
+  step of chunk 0 (no boundary) and of chunk 1 (boundary K/V carried from the GPU's
+  chunk-0 latent); a resumed handle reproduces a chunk bit for bit; device memory
+  does not grow with the number of chunks.
+- Super-resolution and large base chunks: the launch shapes of the full workloads
+  (tokens, keys, hidden size, heads, audio) with one block, the oracle evaluated on
+  sampled query rows (first, last and ragged-tail tiles plus random rows); and the
+  full-depth models run end to end with a zero final projection, where the velocity
+  must equal the final bias exactly (closed-form Euler trajectory), and repeat
+  bit for bit.
+Tolerance as elsewhere: max-abs-normalised error <= 2e-2 for bf16.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from synth import Grid
+from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _handle(cfg, P, dev):
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, upload_weights
+    return DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+
+
+def _run_chunk(h, cfg, x, audio, prev, v0=None):
+    """Boundary from prev (None: first chunk), then the chunk's Euler steps on x in
+    place; v0 (optional) receives the first step's velocity."""
+    from chunked_streaming_dit_amd.workload import grid_of
+    g = cfg.chunk
+    if prev is None:
+        h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+    else:
+        h.boundary_kv_carry(prev, grid_of(g))
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
+    for k in range(cfg.steps):
+        h.step(x, ts[k], ts[k + 1], grid_of(g), audio=audio, v_out=v0 if k == 0 else None)
+
+
+def test_config3_stream_full_size():
+    from chunked_streaming_dit_amd.workload import f32, grid_of
+    dev = device()
+    cfg = synth.CONFIGS[3]
+    g = cfg.chunk
+    P = synth.make_weights(cfg)
+    chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
+    h = _handle(cfg, P, dev)
+    # every device buffer of the session exists before the first chunk
+    xs = [f32(inp["x_init"], dev) for inp in chunks]
+    auds = [f32(inp["audio"], dev) for inp in chunks]
+    v_first = [torch.empty_like(xs[0]) for _ in range(2)]
+    x_resume = f32(chunks[3]["x_init"], dev)
+    h.ref_kv_precompute(f32(chunks[0]["ref"], dev), grid_of(cfg.ref))
+    torch.cuda.synchronize()
+    mem = []
+    prev = None
+    for c in range(cfg.n_chunks):
+        _run_chunk(h, cfg, xs[c], auds[c], prev, v_first[c] if c < 2 else None)
+        torch.cuda.synchronize()
+        mem.append((torch.cuda.memory_allocated(dev), torch.cuda.max_memory_allocated(dev)))
+        prev = xs[c]
+    # constant device memory over the session: nothing is allocated after chunk 0
+    assert all(m == mem[0] for m in mem), mem
+    for x in xs:
+        assert torch.isfinite(x).all()
+
+    # resume: a fresh handle given the reference and chunk 2's final latent reproduces chunk 3
+    h2 = _handle(cfg, P, dev)
+    h2.ref_kv_precompute(f32(chunks[0]["ref"], dev), grid_of(cfg.ref))
+    _run_chunk(h2, cfg, x_resume, auds[3], xs[2])
+    torch.cuda.synchronize()
+    assert torch.equal(x_resume, xs[3])
+
+    # oracle: first step of chunk 0 (reference only) and of chunk 1 (boundary from the
+    # GPU's chunk-0 final latent)
+    pos = O.grid_positions(0, g.frames, g.h, g.w)
+    ref_kv = O.ref_context(P, cfg, chunks[0]["ref"], cfg.ref)
+    vo0 = O.dit_velocity(P, cfg, chunks[0]["x_init"], cfg.t_start, pos, [[kv] for kv in ref_kv],
+                         chunks[0]["audio"])
+    e0 = rel_err(to_np(v_first[0]), vo0)
+    x0_gpu = to_np(xs[0])
+    bkv = O.bnd_context(P, cfg, ref_kv, O.last_frame(x0_gpu, g.frames, g.h, g.w), g.h, g.w)
+    vo1 = O.dit_velocity(P, cfg, chunks[1]["x_init"], cfg.t_start, pos,
+                         [[ref_kv[l], bkv[l]] for l in range(cfg.L)], chunks[1]["audio"])
+    e1 = rel_err(to_np(v_first[1]), vo1)
+    print(f"stream: chunk0 v err {e0:.2e}, chunk1 v err {e1:.2e}")
+    assert e0 <= TOL["bf16"] and e1 <= TOL["bf16"], (e0, e1)
+
+
+def _sample_rows(n, seed):
+    r = np.random.default_rng(seed)
+    tail = np.arange(max(0, n - 64), n)
+    return np.unique(np.concatenate([np.arange(64), tail, r.choice(n, 128, replace=False)]))
+
+
+@pytest.mark.parametrize("base", [4, 5])
+def test_full_shape_one_block_sampled_rows(base):
+    """One block at the full launch shape; the oracle evaluates sampled query rows."""
+    dev = device()
+    cfg = dataclasses.replace(synth.CONFIGS[base], L=1, cid=40 + base, steps=1)
+    P = synth.make_weights(cfg, threads=16)
+    inp = synth.make_inputs(cfg, 0)
+    _, vg, h = run_standalone_gpu(cfg, P, inp, dev, steps=1)
+    h.close()
+    g = cfg.chunk
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    bkv = O.bnd_context(P, cfg, ref_kv, inp["bnd"], cfg.bnd.h, cfg.bnd.w)
+    cond = O.upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w) if cfg.C_c else None
+    rows = _sample_rows(cfg.N, base)
+    vo = O.velocity_rows(P, cfg, inp["x_init"], cfg.t_start, O.grid_positions(0, g.frames, g.h, g.w),
+                         [[ref_kv[0], bkv[0]]], inp.get("audio"), rows, cond)
+    err = rel_err(vg[0][rows], vo)
+    print(f"config {base} one-block full shape, {len(rows)} sampled rows: v err {err:.2e}")
+    assert err <= TOL["bf16"], err
+
+
+def _device_weights(cfg, dev, seed):
+    """Seeded N(0, 1/fan_in) weights drawn on the device (no host copy of 10+ GB)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    W = {}
+    for name, (shape, fan_in, kind) in synth.weight_catalogue(cfg).items():
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        t = 1.0 + 0.1 * t if kind == "g" else t / fan_in ** 0.5
+        W[name] = t.to(torch.bfloat16)
+    return W
+
+
+@pytest.mark.parametrize("base", [4, 5])
+def test_full_depth_constant_velocity_and_repeatability(base):
+    """All blocks at full size with a zero final projection: v must be exactly the final
+    bias at every step and x follows x_0 + (t_end - t_start) b exactly up to fp32
+    rounding; a repeated step is bit-identical."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of
+    dev = device()
+    cfg = synth.CONFIGS[base]
+    W = _device_weights(cfg, dev, 1000 + base)
+    W["fin.w"].zero_()
+    inp = synth.make_inputs(cfg, 0)
+    h = DitChunk(chunk_config(cfg), W, dev)
+    h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+    cond = f32(inp["cond_lr"], dev) if cfg.C_c else None
+    audio = f32(inp["audio"], dev) if cfg.M else None
+    x = f32(inp["x_init"], dev)
+    v = torch.empty_like(x)
+    S = min(cfg.steps, 2)
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(S + 1)]
+    b = W["fin.b"].float()
+    for k in range(S):
+        h.step(x, ts[k], ts[k + 1], grid_of(cfg.chunk), cond=cond, audio=audio, v_out=v)
+        torch.cuda.synchronize()
+        assert torch.equal(v, b.expand_as(v))
+    want = torch.from_numpy(inp["x_init"]).double() + (ts[S] - ts[0]) * b.double().cpu()
+    assert (x.double().cpu() - want).abs().max().item() <= 1e-6
+    # repeatability with the real final projection restored
+    W2 = dict(W)
+    W2["fin.w"] = torch.randn(W["fin.w"].shape, device=dev).mul_(cfg.D ** -0.5).to(torch.bfloat16)
+    h2 = DitChunk(chunk_config(cfg), W2, dev)
+    h2.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    h2.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+    outs = []
+    for _ in range(2):
+        x = f32(inp["x_init"], dev)
+        h2.step(x, ts[0], ts[1], grid_of(cfg.chunk), cond=cond, audio=audio, v_out=v)
+        torch.cuda.synchronize()
+        outs.append(v.clone())
+    assert torch.isfinite(outs[0]).all() and torch.equal(outs[0], outs[1])

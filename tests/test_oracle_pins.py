@@ -435,3 +435,19 @@ def test_conditioning_structure_special_case():
     P["t1.b"] = np.zeros(D)
     t = 0.123
     assert abs(O.conditioning(P, t)[0] - O.silu(O.silu(np.cos(123.0)))) < 1e-15
+
+
+@pytest.mark.parametrize("sr", [False, True])
+def test_velocity_rows_equals_full_velocity_one_block(sr):
+    """The row-restricted single-block evaluation equals the full computation's rows."""
+    cfg = dataclasses.replace(TINY_SR if sr else TINY, L=1)
+    P, inp = synth.make_weights(cfg), synth.make_inputs(cfg, 0)
+    _, _, ctx = _ctx(P, cfg, inp)
+    g = cfg.chunk
+    cond = O.upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w) if sr else None
+    audio = None if sr else inp["audio"]
+    pos = _pos(g)
+    full = O.dit_velocity(P, cfg, inp["x_init"], 0.55, pos, ctx, audio, cond)
+    rows = np.array([0, 3, cfg.N - 1, 5])
+    part = O.velocity_rows(P, cfg, inp["x_init"], 0.55, pos, ctx, audio, rows, cond)
+    assert np.abs(part - full[rows]).max() <= 1e-13 * np.abs(full).max()
