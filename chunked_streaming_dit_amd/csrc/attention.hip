@@ -219,14 +219,18 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     __syncthreads();
     scores(tb % NSLOT, Sc);
   }
-  for (int t = tb; t < total; ++t) {
-    const bool has1 = t + 1 < total, has2 = t + 2 < total, has3 = t + 3 < total;
+  // One iteration.  The softmax exponentials / P^T conversion / P V MFMAs of tile t and
+  // the score MFMAs of tile t+1 form one branch-free block that the scheduler
+  // interleaves (MFMA, LDS read, VALU), so the VALU softmax of one tile runs under the
+  // MFMAs of the other.  For the last tile the scores of a (stale) slot are computed and
+  // dropped, which keeps the block free of branches; the slot address stays in LDS.
+  auto body = [&](int t, f32x16 (&S)[2], f32x16 (&Snext)[2]) {
+    const bool has2 = t + 2 < total, has3 = t + 3 < total;
     // Every wave has finished iteration t-1 (or the prologue's scores of tile tb), so
     // the slots refilled below are no longer read by anyone.
     __syncthreads();
     if (has3) load_k(t + 3, (t + 3) % NSLOT);
     if (has2) load_v(t + 2, (t + 2) % NSLOT);
-    if (has1) scores((t + 1) % NSLOT, Sn);
 
     int si, base;
     locate(t, si, base);
@@ -237,14 +241,14 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = base + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (key >= seg_n) Sc[kb][r] = -INFINITY;
+          if (key >= seg_n) S[kb][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, Sc[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     // Lazy rescale: keep the running max unless a score exceeds it by more than
     // RESCALE_LOG2 in the exp2 domain (then p stays <= 2^RESCALE_LOG2, which fp32
@@ -261,39 +265,66 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float ms = m_run * a.scale;
-    // P^T operands: elements [v*VE, v*VE+VE) of Sc[kb].  The row sum is taken from the
-    // converted operand values, i.e. from exactly the weights the second MFMA uses.
-    V pf[2][16 / VE];
+    const char* sv = vs + (t % NSLOT) * VTILE;
+    const char* sk = ks + ((t + 1) % NSLOT) * KTILE;
+    // Softmax of tile t, P V of tile t and the scores of tile t+1, in NU phases.  Unit u
+    // = (kb, v) covers keys [32 kb + v*2VE, +2VE) of tile t: VE exponentials per lane
+    // (P^T operand elements [v*VE, v*VE+VE) of S[kb]), their row-sum contribution and
+    // DB P V MFMAs with the V^T vector holding the same keys (stored order).  Phase u
+    // first requests the K fragments of phase u+1 (scores of tile t+1, KPU fragments per
+    // phase), then exponentiates, then issues its score and P V MFMAs; the scheduling
+    // barrier keeps that order so LDS latency hides under the exponentials.  For the last
+    // tile the scores of a stale slot are computed and dropped, which keeps the block
+    // free of branches (the slot lies inside LDS).  The row sum is taken from the
+    // converted operand values, i.e. from exactly the weights the MFMA uses.
+    constexpr int UPK = 16 / VE;       // units per 32-key block
+    constexpr int NU = 2 * UPK;        // units (phases) per tile
+    constexpr int KPU = 2 * QV / NU;   // score fragments per phase
+    V kf[2][KPU];
+    auto kread = [&](int u, int set) {
+#pragma unroll
+      for (int i = 0; i < KPU; ++i) {
+        const int f = u * KPU + i, skb = f / QV, st = f % QV;
+        const int pos = swz<RBK>(l32, 2 * st + lg);
+        kf[set][i] = as_vec<V>(ld16(sk + (skb * 32 + l32) * RBK + pos * 16));
+      }
+    };
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16 / VE; ++v) {
+      for (int r = 0; r < 16; ++r) Snext[kb][r] = 0.f;
+    kread(0, 0);
 #pragma unroll
-        for (int j = 0; j < VE; ++j)
-          pf[kb][v][j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(Sc[kb][v * VE + j], a.scale, -ms)));
-        l_run = row_sum_add(pf[kb][v], l_run);
+    for (int u = 0; u < NU; ++u) {
+      if (u + 1 < NU) kread(u + 1, (u + 1) & 1);
+      const int kb = u / UPK, v = u % UPK;
+      V pf;
+#pragma unroll
+      for (int j = 0; j < VE; ++j)
+        pf[j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(S[kb][v * VE + j], a.scale, -ms)));
+      l_run = row_sum_add(pf, l_run);
+      const int pos = swz<RBV>(l32, (kb * 32 + v * 2 * VE + lg * VE) * SZ / 16);
+      V vf[DB];
+#pragma unroll
+      for (int d = 0; d < DB; ++d) vf[d] = as_vec<V>(ld16(sv + (d * 32 + l32) * RBV + pos * 16));
+#pragma unroll
+      for (int i = 0; i < KPU; ++i) {
+        const int f = u * KPU + i, skb = f / QV, st = f % QV;
+        Snext[skb] = mfma32(kf[u & 1][i], qf[st], Snext[skb]);
       }
-    // O^T += V^T P^T; the V^T vector at key offset 32 kb + v*2VE + lg*VE holds the
-    // same keys as pf[kb][v] (stored order).
-    const char* sv = vs + (t % NSLOT) * VTILE;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16 / VE; ++v) {
-        const int chunk = (kb * 32 + v * 2 * VE + lg * VE) * SZ / 16;
-        const int pos = swz<RBV>(l32, chunk);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          V vf = as_vec<V>(ld16(sv + (d * 32 + l32) * RBV + pos * 16));
-          O[d] = mfma32(vf, pf[kb][v], O[d]);
-        }
-      }
+      for (int d = 0; d < DB; ++d) O[d] = mfma32(vf[d], pf, O[d]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) Sc[kb] = Sn[kb];
     // this wave's loads of K tile t+2 and V tile t+1 have landed (this iteration's stay)
     wait_keep((has3 ? NLK : 0) + (has2 ? NLV : 0));
+  };
+  int t = tb;
+  for (; t + 1 < total; t += 2) {
+    body(t, Sc, Sn);
+    body(t + 1, Sn, Sc);
   }
+  if (t < total) body(t, Sc, Sn);
 
   // Normalise and store: lane holds query qrow, dh = 32 d + 8 q + 4 lg + [0, 4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);

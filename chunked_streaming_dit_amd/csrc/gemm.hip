@@ -271,18 +271,33 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     const int buf = it & 1;
     if (it + 1 < nk) issue(buf ^ 1, (it + 1) * 64);
     const char* st = smem + buf * STAGE;
+    // Fragments of sub-step s+1 are requested before sub-step s multiplies and the
+    // scheduler is asked to interleave them one per MFMA, so LDS latency hides under
+    // the MFMAs of the same wave as well as under the other wave of the SIMD.
+    V af[2][MB], wf[2][NB];
+    auto frags = [&](int s, int set) {
+      const int coff = ((2 * s + lg) ^ x) << 4;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[set][i] = as_vec<V>(ld16(st + a_base + i * 32 * 128 + coff));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wf[set][j] = as_vec<V>(ld16(st + w_base + j * 32 * 128 + coff));
+    };
+    frags(0, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int coff = ((2 * s + lg) ^ x) << 4;
-      V af[MB], wf[NB];
-#pragma unroll
-      for (int i = 0; i < MB; ++i) af[i] = as_vec<V>(ld16(st + a_base + i * 32 * 128 + coff));
-#pragma unroll
-      for (int j = 0; j < NB; ++j) wf[j] = as_vec<V>(ld16(st + w_base + j * 32 * 128 + coff));
+      if (s < 3) frags(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[j], af[i], acc[i][j]);
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[s & 1][j], af[s & 1][i], acc[i][j]);
+      if (s < 3) {
+#pragma unroll
+        for (int q = 0; q < MB + NB; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, MB * NB - (MB + NB), 0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
