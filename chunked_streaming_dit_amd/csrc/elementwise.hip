@@ -55,91 +55,111 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------- QK-norm + RoPE + repack
-// Grid: (round_up(n, 64) / 64, H).  A workgroup owns 64 tokens x one head.  Each lane
-// holds one rotation pair (dims 2i, 2i+1); dh/2 lanes make one token, so a wave
-// handles 64/(dh/2) tokens at a time.  V rows are staged in LDS and written out
-// transposed ([dh, cap] per head) in the attention kernel's key order.
+// Grid: (round_up(n, 64) / 64, H).  A workgroup owns 64 tokens x one head.  A lane moves
+// one 16-byte vector (VE elements, VE/2 rotation pairs) of a head row, so a row of dh
+// elements is LPR = dh/VE lanes and a wave handles 64/LPR tokens at a time.  The row's
+// sum of squares is reduced over its LPR lanes.  V rows are staged in LDS and written
+// out transposed ([dh, cap] per head) in the attention kernel's key order.
 template <class T, int DH>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     int n, const T* __restrict__ q_in, const T* __restrict__ k_in, const T* __restrict__ v_in,
     int ld_in, const T* __restrict__ gq, const T* __restrict__ gk, int rope, RopeGrid g,
     float eps, float log2_theta, T* __restrict__ q_out, T* __restrict__ k_out,
     T* __restrict__ vt_out, int cap, int D) {
-  constexpr int PAIRS = DH / 2;
-  constexpr int TPI = 64 / PAIRS;  // tokens per wave iteration
+  typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
-  __shared__ T sv[64][DH + 2];
+  constexpr int LPR = DH / VE;      // lanes per head row
+  constexpr int TPW = 64 / LPR;     // tokens per wave step
+  constexpr int NP = VE / 2;        // rotation pairs per lane
+  __shared__ __attribute__((aligned(16))) T sv[64][DH + 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int head = blockIdx.y;
   const int tok0 = blockIdx.x * 64;
-  const int pair = lane % PAIRS;
-  const int sub = lane / PAIRS;
+  const int c = lane % LPR;           // vector index within the row
+  const int sub = lane / LPR;         // token within the wave step
 
-  // Rotation frequency of this lane's pair: axis t for the first d_t/2 pairs, then y,
-  // then x; pair j of an axis with d_a dims turns at theta^(-2j/d_a).
+  // Rotation frequency of each of this lane's pairs: axis t for the first d_t/2 pairs,
+  // then y, then x; pair j of an axis with d_a dims turns at theta^(-2j/d_a).
   const int d_hw = 2 * (DH / 6);
   const int d_t = DH - 2 * d_hw;
-  int axis, j, d_a;
-  if (pair < d_t / 2) { axis = 0; j = pair; d_a = d_t; }
-  else if (pair < d_t / 2 + d_hw / 2) { axis = 1; j = pair - d_t / 2; d_a = d_hw; }
-  else { axis = 2; j = pair - d_t / 2 - d_hw / 2; d_a = d_hw; }
-  const float inv_freq = exp2f(-(2.0f * (float)j / (float)d_a) * log2_theta);
-  const float gq0 = gq ? to_f(gq[2 * pair]) : 0.f, gq1 = gq ? to_f(gq[2 * pair + 1]) : 0.f;
-  const float gk0 = gk ? to_f(gk[2 * pair]) : 0.f, gk1 = gk ? to_f(gk[2 * pair + 1]) : 0.f;
+  int axis[NP];
+  float inv_freq[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pair = c * NP + i;
+    int j, d_a;
+    if (pair < d_t / 2) { axis[i] = 0; j = pair; d_a = d_t; }
+    else if (pair < d_t / 2 + d_hw / 2) { axis[i] = 1; j = pair - d_t / 2; d_a = d_hw; }
+    else { axis[i] = 2; j = pair - d_t / 2 - d_hw / 2; d_a = d_hw; }
+    inv_freq[i] = exp2f(-(2.0f * (float)j / (float)d_a) * log2_theta);
+  }
+  float gqv[VE], gkv[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    gqv[e] = gq ? to_f(gq[c * VE + e]) : 0.f;
+    gkv[e] = gk ? to_f(gk[c * VE + e]) : 0.f;
+  }
   const int hw = g.h * g.w;
 
-  for (int it = wave * TPI + sub; it < 64; it += 4 * TPI) {
+  // Normalise (per-head RMS over LPR lanes), scale by gamma and rotate one row vector.
+  auto norm_rot = [&](V x, const float (&gam)[VE], const float (&cs)[NP], const float (&sn)[NP]) {
+    float f[VE], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) { f[e] = to_f(x[e]); ss += f[e] * f[e]; }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
+    V out;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const float y0 = f[2 * i] * rs * gam[2 * i], y1 = f[2 * i + 1] * rs * gam[2 * i + 1];
+      out[2 * i] = from_f<T>(y0 * cs[i] - y1 * sn[i]);
+      out[2 * i + 1] = from_f<T>(y0 * sn[i] + y1 * cs[i]);
+    }
+    return out;
+  };
+
+  for (int it = wave * TPW + sub; it < 64; it += 4 * TPW) {
     const int tok = tok0 + it;
     const bool valid = tok < n;
-    float c = 1.f, s = 0.f;
+    float cs[NP], sn[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) { cs[i] = 1.f; sn[i] = 0.f; }
     if (rope && valid) {
       const int f = tok / hw, rem = tok - f * hw;
       const int y = rem / g.w, x = rem - y * g.w;
-      const int p = axis == 0 ? g.t0 + f : (axis == 1 ? y : x);
-      sincosf((float)p * inv_freq, &s, &c);
+      const int pv[3] = {g.t0 + f, y, x};
+#pragma unroll
+      for (int i = 0; i < NP; ++i) sincosf((float)pv[axis[i]] * inv_freq[i], &sn[i], &cs[i]);
     }
-    const size_t src = (size_t)tok * ld_in + head * DH + 2 * pair;
-    const size_t dst = (size_t)tok * D + head * DH + 2 * pair;
-    // q: norm + gamma + rotation (only valid tokens are written)
+    const size_t src = (size_t)tok * ld_in + head * DH + c * VE;
+    const size_t dst = (size_t)tok * D + head * DH + c * VE;
+    V zero;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) zero[e] = from_f<T>(0.f);
     if (q_in) {
-      float x0 = 0.f, x1 = 0.f;
-      if (valid) { x0 = to_f(q_in[src]); x1 = to_f(q_in[src + 1]); }
-      float ss = x0 * x0 + x1 * x1;
-#pragma unroll
-      for (int o = PAIRS / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
-      const float y0 = x0 * rs * gq0, y1 = x1 * rs * gq1;
-      if (valid) {
-        q_out[dst] = from_f<T>(y0 * c - y1 * s);
-        q_out[dst + 1] = from_f<T>(y0 * s + y1 * c);
-      }
+      const V x = valid ? as_vec<V>(ld16(q_in + src)) : zero;
+      const V y = norm_rot(x, gqv, cs, sn);
+      if (valid) st16(q_out + dst, __builtin_bit_cast(u32x4, y));
     }
-    if (k_in) {
-      float x0 = 0.f, x1 = 0.f;
-      if (valid) { x0 = to_f(k_in[src]); x1 = to_f(k_in[src + 1]); }
-      float ss = x0 * x0 + x1 * x1;
-#pragma unroll
-      for (int o = PAIRS / 2; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-      const float rs = 1.0f / sqrtf(ss / (float)DH + eps);
-      const float y0 = x0 * rs * gk0, y1 = x1 * rs * gk1;
-      k_out[dst] = from_f<T>(valid ? y0 * c - y1 * s : 0.f);
-      k_out[dst + 1] = from_f<T>(valid ? y0 * s + y1 * c : 0.f);
+    if (k_in) {  // rows past n are written as zeros (x = 0 normalises to 0)
+      const V x = valid ? as_vec<V>(ld16(k_in + src)) : zero;
+      const V y = norm_rot(x, gkv, cs, sn);
+      st16(k_out + dst, __builtin_bit_cast(u32x4, y));
     }
     if (v_in) {
-      T a = from_f<T>(0.f), b = from_f<T>(0.f);
-      if (valid) { a = v_in[src]; b = v_in[src + 1]; }
-      sv[it][2 * pair] = a;
-      sv[it][2 * pair + 1] = b;
+      const V x = valid ? as_vec<V>(ld16(v_in + src)) : zero;
+      *reinterpret_cast<V*>(&sv[it][c * VE]) = x;
     }
   }
   if (!v_in) return;
   __syncthreads();
   // V^T: row d of this head gets the 64 tokens of the tile, 16 bytes per thread-chunk.
   constexpr int CPR = 64 / VE;  // chunks per row
-  for (int c = tid; c < DH * CPR; c += 256) {
-    const int d = c / CPR, pos0 = (c % CPR) * VE;
-    typename Vec<T>::type out;
+  for (int cc = tid; cc < DH * CPR; cc += 256) {
+    const int d = cc / CPR, pos0 = (cc % CPR) * VE;
+    V out;
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       const int p = pos0 + e;
@@ -150,7 +170,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
       }
       out[e] = sv[key][d];
     }
-    *reinterpret_cast<typename Vec<T>::type*>(vt_out + (size_t)(head * DH + d) * cap + tok0 + pos0) = out;
+    *reinterpret_cast<V*>(vt_out + (size_t)(head * DH + d) * cap + tok0 + pos0) = out;
   }
 }
 
