@@ -50,6 +50,60 @@ def _traffic():
     return d.get("hbm_bytes_per_launch")
 
 
+COPY_PROBE_BYTES = 256 << 20
+
+
+def copy_probe(reps: int = 3) -> None:
+    """A plain device copy of COPY_PROBE_BYTES, the known-size kernel that calibrates
+    the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    dev = torch.device("cuda", 0)
+    a = torch.empty(COPY_PROBE_BYTES // 4, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+def _counter_means(path: str, counter: str, match) -> tuple:
+    """(mean counter value, dispatches) over the dispatches of a rocprofv3 counter CSV
+    whose kernel name satisfies match."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    if not vals:
+        raise SystemExit(f"bench.py: no {counter} rows matched in {path}")
+    return sum(vals) / len(vals), len(vals)
+
+
+def _is_self_attention(name: str) -> bool:
+    """attn_kernel<T, DH, KIND> with KIND 0 (self-attention; 1 is the audio cross-attention),
+    demangled or mangled."""
+    import re
+    return re.search(r"attn_kernel(<[^<>]*,\s*0>|I\w*Li0EE)", name) is not None
+
+
+def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv) -> dict:
+    """HBM bytes per self-attention launch from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, in KiB per dispatch, over the bench and over copy_probe), each counter
+    scaled so that the copy reads COPY_PROBE_BYTES and writes COPY_PROBE_BYTES."""
+    kib = COPY_PROBE_BYTES / 1024
+    cf, _ = _counter_means(copy_fetch_csv, "FETCH_SIZE", lambda n: "copy" in n.lower())
+    cw, _ = _counter_means(copy_write_csv, "WRITE_SIZE", lambda n: "copy" in n.lower())
+    f, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_self_attention)
+    w, nw = _counter_means(write_csv, "WRITE_SIZE", _is_self_attention)
+    sf, sw = kib / cf, kib / cw
+    return {
+        "attention_src_sha256_16": _src_hash(ATTN_SRC),
+        "hbm_bytes_per_launch": (f * sf + w * sw) * 1024,
+        "fetch_bytes_per_launch": f * sf * 1024,
+        "write_bytes_per_launch": w * sw * 1024,
+        "fetch_scale": sf,
+        "write_scale": sw,
+        "dispatches": [nf, nw],
+    }
+
+
 def cpu_baseline(cfg, P, inp, budget_s: float = 12.0):
     """Time the oracle on one DiT block of one denoising step at the full chunk shape
     (repeated up to L times while under the budget) and scale to the L-block step."""
@@ -90,7 +144,21 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 256 MiB calibration copy (for the traffic counters)")
+    ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the attention traffic file from rocprofv3 counter CSVs")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return 0
+    if args.reduce_traffic:
+        d = reduce_traffic(*args.reduce_traffic)
+        with open(TRAFFIC_FILE, "w") as fh:
+            json.dump(d, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(d))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
