@@ -66,9 +66,9 @@ _SIGS = {
     "ditk_linear": (I, [I, P, P, P, I, I, I, I, P, P]),
     "ditk_linear_residual": (I, [I, P, P, P, P, I, I, I, P, P]),
     "ditk_rmsnorm_modulate": (I, [I, P, I, I, P, P, Dbl, P, P]),
-    "ditk_qknorm_rope": (I, [I, I, I, I, P, P, P, I, P, P, I, DitGrid, Dbl, Dbl, P, P, P, I, P]),
+    "ditk_qknorm_rope": (I, [I, I, I, I, P, P, P, I, P, P, I, DitGrid, Dbl, Dbl, Dbl, P, P, P, I, P]),
     "ditk_attention": (I, [I, I, I, P, I, I, ctypes.POINTER(P), ctypes.POINTER(P),
-                           ctypes.POINTER(I), ctypes.POINTER(I), I, P, P, P]),
+                           ctypes.POINTER(I), ctypes.POINTER(I), I, P, I, P, P]),
     "ditk_modulation": (I, [I, I, I, Dbl, ctypes.POINTER(P), P, P, P, P]),
     "ditk_patch_input": (I, [I, P, I, I, P, I, I, DitGrid, P, P]),
 }

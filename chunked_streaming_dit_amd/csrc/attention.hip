@@ -1,16 +1,17 @@
 // Flash attention over segmented keys: [reference | boundary | chunk] (self-attention)
 // or [audio] (cross-attention), one head per grid row.
 //
-// Per workgroup: 128 queries of one head (4 waves x 32 queries).  Key/value tiles of
-// 64 keys are staged in LDS (double-buffered, one barrier per tile; the next tile is
-// fetched into registers while the current one is used).  Each wave computes the
-// transposed score tile S^T = K Q^T with 32x32 MFMAs, so that a lane holds scores of
-// ONE query for 32 keys: the online-softmax row max needs one cross-lane exchange
-// (lanes l and l^32), the row sum none until the end, and the rescale of the output
-// accumulator O^T = V^T P^T touches only the lane's own registers.  The exponentiated
-// scores feed the second MFMA directly from registers (no LDS round trip); the key
-// order they are held in is matched by the stored order of V^T (see kernels.h).
-// Softmax statistics and accumulation are fp32; exp2 with log2(e)/sqrt(dh) folded in.
+// Per workgroup: 256 queries of one head (8 waves x 32 queries).  Key and V^T tiles of
+// 64 keys are brought into LDS by direct-to-LDS transfers through two 3-slot rings, each
+// tile requested about two tiles ahead of its use; one workgroup barrier per tile.  Each
+// wave computes the transposed score tile S^T = K Q^T with 32x32 MFMAs, so that a lane
+// holds scores of ONE query for 32 keys: the online-softmax row max needs one
+// cross-lane exchange (lanes l and l^32), the row sum none until the end, and the
+// rescale of the output accumulator O^T = V^T P^T touches only the lane's own
+// registers.  The exponentiated scores feed the second MFMA directly from registers (no
+// LDS round trip); the key order they are held in is matched by the stored order of V^T
+// (see kernels.h).  Softmax statistics and accumulation are fp32; the softmax is taken
+// in base 2 with log2(e)/sqrt(dh) folded into q (given pre-scaled, or applied here).
 #include <math.h>
 
 #include "common.h"
@@ -25,7 +26,7 @@ struct AttnArgs {
   void* o;
   int ldq, ldo, nq, ldk, H;
   int nseg;
-  float scale;  // log2(e) / sqrt(dh)
+  float scale;  // log2(e) / sqrt(dh), or 1 when q comes pre-scaled
   float thr;    // RESCALE_LOG2 / scale: lazy-rescale threshold in raw score units
   int nsplit;   // key-range splits per (head, q-tile); > 1 writes partials
   float* opart; // [nsplit, nq, H*DH] normalised partial outputs (nsplit > 1)
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     if (total > tb + 2) { load_k(tb + 2, (tb + 2) % NSLOT); later += NLK; }
     if (total > tb + 1) { load_v(tb + 1, (tb + 1) % NSLOT); later += NLV; }
     wait_keep(later);
-    __syncthreads();
+    lds_barrier();
     scores(tb % NSLOT, Sc);
   }
   // One iteration.  The softmax exponentials / P^T conversion / P V MFMAs of tile t and
@@ -227,8 +228,10 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   auto body = [&](int t, f32x16 (&S)[2], f32x16 (&Snext)[2]) {
     const bool has2 = t + 2 < total, has3 = t + 3 < total;
     // Every wave has finished iteration t-1 (or the prologue's scores of tile tb), so
-    // the slots refilled below are no longer read by anyone.
-    __syncthreads();
+    // the slots refilled below are no longer read by anyone.  Each wave's own older
+    // transfers have landed (wait_keep at the end of the previous iteration, or the
+    // prologue's wait); the newest ones stay in flight across this barrier.
+    lds_barrier();
     if (has3) load_k(t + 3, (t + 3) % NSLOT);
     if (has2) load_v(t + 2, (t + 2) % NSLOT);
 
@@ -410,8 +413,8 @@ int attention_splits(int nq, int H, int total_keys_tiles, int partial_rows, int 
 }
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s,
-                     int kind) {
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
+                     hipStream_t s, int kind) {
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
   if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
@@ -424,7 +427,7 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.ldk = ldk;
   a.nseg = nseg;
   a.H = H;
-  a.scale = (float)(1.4426950408889634 / sqrt((double)dh));
+  a.scale = q_prescaled ? 1.0f : attention_q_scale(dh);
   a.thr = RESCALE_LOG2 / a.scale;
   a.nsplit = sp.nsplit;
   a.opart = sp.opart;

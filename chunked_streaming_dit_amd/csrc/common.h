@@ -102,4 +102,13 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* p, const float v[
   *reinterpret_cast<b4*>(p) = r;
 }
 
+
+// Workgroup barrier that keeps direct-to-LDS loads in flight.  __syncthreads() carries
+// a workgroup fence, which the compiler implements by draining every outstanding
+// memory operation (vmcnt(0)), including global_load_lds transfers issued for later
+// tiles.  Callers of this barrier instead wait explicitly (vmcnt(N) for their own
+// older transfers, lgkmcnt(0) for their LDS reads) before it; the memory clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 }  // namespace dit

@@ -202,7 +202,7 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
   int slot = -1, rc;
   if (timed && (rc = timed_begin(hd, &slot))) return rc;
   HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
-                   hd->stream, kind));
+                   true, hd->stream, kind));
   if (timed) {
     double nkv = 0;
     for (int i = 0; i < ns; ++i) nkv += seg[i].n;
@@ -243,7 +243,8 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
     const char* big = hd->X<char>(L.big);
     HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, last ? nullptr : big, big + (size_t)D * L.elt,
                        big + (size_t)2 * D * L.elt, 3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK),
-                       1, g, (float)c.eps, (float)c.rope_theta, hd->X(L.q), hd->S(kdst[l]),
+                       1, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q),
+                       hd->S(kdst[l]),
                        hd->S(vdst[l]), cap, s));
     if (last) break;
     AttnSeg seg[2];
@@ -411,7 +412,8 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
     HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
     HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, big + (size_t)D * L.elt, big + (size_t)2 * D * L.elt,
                        3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g, (float)c.eps,
-                       (float)c.rope_theta, hd->X(L.q), hd->X(L.kc), hd->X(L.vtc), L.cap_tok, s));
+                       (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q), hd->X(L.kc),
+                       hd->X(L.vtc), L.cap_tok, s));
     AttnSeg seg[3];
     int ns = 0;
     seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
@@ -429,16 +431,16 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
       e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
       HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
       HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
-                         nullptr, 0, g, (float)c.eps, (float)c.rope_theta, hd->X(L.q), nullptr,
-                         nullptr, L.cap_tok, s));
+                         nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
+                         hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
       e = GemmEpi{};
       e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CK_B); e.out = hd->X(L.ka_raw); e.ldo = D;
       HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
       e.bias = hd->B(l, DIT_WB_CV_B); e.out = hd->X(L.va_raw);
       HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
       HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
-                         hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, nullptr,
-                         hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
+                         hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, 1.0f,
+                         nullptr, hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
       AttnSeg aseg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
       if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS)) return rc2;
       e = GemmEpi{};

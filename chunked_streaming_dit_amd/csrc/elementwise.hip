@@ -64,7 +64,7 @@ template <class T, int DH>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     int n, const T* __restrict__ q_in, const T* __restrict__ k_in, const T* __restrict__ v_in,
     int ld_in, const T* __restrict__ gq, const T* __restrict__ gk, int rope, RopeGrid g,
-    float eps, float log2_theta, T* __restrict__ q_out, T* __restrict__ k_out,
+    float eps, float log2_theta, float q_scale, T* __restrict__ q_out, T* __restrict__ k_out,
     T* __restrict__ vt_out, int cap, int D) {
   typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   float gqv[VE], gkv[VE];
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
-    gqv[e] = gq ? to_f(gq[c * VE + e]) : 0.f;
+    gqv[e] = gq ? to_f(gq[c * VE + e]) * q_scale : 0.f;  // q_out carries q_scale
     gkv[e] = gk ? to_f(gk[c * VE + e]) : 0.f;
   }
   const int hw = g.h * g.w;
@@ -300,8 +300,8 @@ hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shi
 
 hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
                        const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
-                       RopeGrid g, float eps, float theta, void* q_out, void* k_out,
-                       void* vt_out, int cap, hipStream_t s) {
+                       RopeGrid g, float eps, float theta, float q_scale, void* q_out,
+                       void* k_out, void* vt_out, int cap, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int npad = (n + 63) / 64 * 64;
   if (npad > cap && (k_in || v_in)) return hipErrorInvalidValue;
@@ -311,7 +311,7 @@ hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const 
 #define QKR(T, DHV)                                                                          \
   qknorm_rope_kernel<T, DHV><<<grid, 256, 0, s>>>(n, (const T*)q_in, (const T*)k_in,         \
                                                   (const T*)v_in, ld_in, (const T*)gq,       \
-                                                  (const T*)gk, rope, g, eps, l2t, (T*)q_out, \
+                                                  (const T*)gk, rope, g, eps, l2t, q_scale, (T*)q_out, \
                                                   (T*)k_out, (T*)vt_out, cap, D)
   if (dtype == BF16 && dh == 128) QKR(bf16, 128);
   else if (dtype == BF16 && dh == 64) QKR(bf16, 64);

@@ -43,7 +43,8 @@ struct AttnSeg {
 };
 enum { ATTN_MAX_SEGS = 3 };
 // Key-range split: nsplit > 1 makes attention() write normalised partial outputs
-// opart [nsplit, nq, H*dh] and (max * log2e/sqrt(dh), row sum) pairs ml [nsplit, nq, H, 2]
+// opart [nsplit, nq, H*dh] and (running max of the exp2-domain logits, row sum) pairs
+// ml [nsplit, nq, H, 2]
 // (fp32), which attention_combine() merges into o.
 struct AttnSplit {
   int nsplit;
@@ -51,10 +52,15 @@ struct AttnSplit {
   float* ml;
 };
 // o[nq, ldo] = softmax(q k^T / sqrt(dh)) v over the concatenated segments, per head.
+// q_prescaled: q holds q * log2(e)/sqrt(dh) (as written by qknorm_rope with that
+// q_scale), the form the kernels consume; otherwise the kernel scales q itself (for
+// bf16 with dh = 128 that rounds the scaled q to bf16 a second time).
 enum { ATTN_SELF = 0, ATTN_CROSS = 1 };
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
-                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, hipStream_t s,
-                     int kind = ATTN_SELF);
+                     int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
+                     hipStream_t s, int kind = ATTN_SELF);
+// log2(e) / sqrt(dh): the q scale of the exp2-domain logits.
+inline float attention_q_scale(int dh) { return (float)(1.4426950408889634 / __builtin_sqrt((double)dh)); }
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
                              hipStream_t s);
 // Splits minimising the estimated time for nq queries, H heads, key_tiles 64-key tiles,
@@ -70,7 +76,7 @@ hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shi
 
 // Per-head QK-norm (+ optional 3D RoPE) and K/V repacking.
 //   q_in/k_in/v_in: [n, ld_in] dtype (any may be NULL); gq/gk [dh] dtype.
-//   q_out [n, D] (plain), k_out [cap, D], vt_out [D, cap] (attention layout above).
+//   q_out [n, D] (times q_scale), k_out [cap, D], vt_out [D, cap] (attention layout above).
 //   Rows/columns in [n, round_up(n, 64)) of k_out/vt_out are zeroed.
 //   rope: positions from the grid (t0 + f, y, x); rope == 0: no rotation.
 struct RopeGrid {
@@ -78,8 +84,8 @@ struct RopeGrid {
 };
 hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
                        const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
-                       RopeGrid g, float eps, float theta, void* q_out, void* k_out,
-                       void* vt_out, int cap, hipStream_t s);
+                       RopeGrid g, float eps, float theta, float q_scale, void* q_out,
+                       void* k_out, void* vt_out, int cap, hipStream_t s);
 
 // xin[n, c_p + c_c] (dtype) = [x rows (row_off..) || cond]; cond modes: 0 zero, 1 per-token
 // [n, c_c], 2 nearest-2x upsample of [frames*(h/2)*(w/2), c_c] on grid g.

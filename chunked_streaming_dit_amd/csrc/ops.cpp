@@ -92,8 +92,8 @@ int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* 
 
 int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
                      const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
-                     dit_grid grid, double eps, double theta, void* q_out, void* k_out,
-                     void* vt_out, int cap, void* stream) {
+                     dit_grid grid, double eps, double theta, double q_scale, void* q_out,
+                     void* k_out, void* vt_out, int cap, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
   if (H < 1 || n < 0 || ld_in < H * dh) return fail(DIT_ESHAPE, "H=%d n=%d ld_in=%d", H, n, ld_in);
@@ -104,15 +104,17 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
   if (rope && (grid.frames < 1 || grid.h < 1 || grid.w < 1 || (long long)grid.frames * grid.h * grid.w < n))
     return fail(DIT_ESHAPE, "grid does not cover n tokens");
   if (!(eps > 0) || !(theta > 1)) return fail(DIT_EINVAL, "eps/theta");
+  if (!(q_scale > 0) || !std::isfinite(q_scale)) return fail(DIT_EINVAL, "q_scale");
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
   return hipchk(qknorm_rope(dtype, dh, H, n, q_in, k_in, v_in, ld_in, gq, gk, rope, g, (float)eps,
-                            (float)theta, q_out, k_out, vt_out, cap, (hipStream_t)stream),
+                            (float)theta, (float)q_scale, q_out, k_out, vt_out, cap,
+                            (hipStream_t)stream),
                 "qknorm_rope");
 }
 
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, void* o, void* stream) {
+                   int nsplit, float* partial, int q_prescaled, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
   if (!q || !o || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
@@ -132,7 +134,8 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   const int D = H * dh;
   AttnSplit sp{nsplit, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
-  int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, (hipStream_t)stream),
+  int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, q_prescaled != 0,
+                            (hipStream_t)stream),
                   "attention");
   if (rc) return rc;
   return hipchk(attention_combine(dtype, dh, H, nq, sp, o, D, (hipStream_t)stream), "attention_combine");

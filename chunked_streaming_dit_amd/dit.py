@@ -208,21 +208,24 @@ class ops:
     @staticmethod
     def qknorm_rope(dtype: str, dh: int, H: int, n: int, q_in, k_in, v_in, ld_in: int, gq, gk,
                     rope: bool, g: C.DitGrid, eps: float, theta: float, q_out, k_out, vt_out,
-                    cap: int) -> None:
+                    cap: int, q_scale: float = 1.0) -> None:
         C.check(C.lib().ditk_qknorm_rope(_dt_code(dtype), dh, H, n, _ptr(q_in), _ptr(k_in), _ptr(v_in),
                                          ld_in, _ptr(gq), _ptr(gk), 1 if rope else 0, g, eps, theta,
-                                         _ptr(q_out), _ptr(k_out), _ptr(vt_out), cap, _stream()))
+                                         q_scale, _ptr(q_out), _ptr(k_out), _ptr(vt_out), cap,
+                                         _stream()))
 
     @staticmethod
     def attention(dtype: str, dh: int, H: int, q, segs: Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]],
-                  o, nsplit: int = 1, partial: Optional[torch.Tensor] = None) -> None:
+                  o, nsplit: int = 1, partial: Optional[torch.Tensor] = None,
+                  q_prescaled: bool = False) -> None:
         ns = len(segs)
         kp = (C.P * ns)(*[s[0].data_ptr() for s in segs])
         vp = (C.P * ns)(*[s[1].data_ptr() for s in segs])
         nn = (ctypes.c_int * ns)(*[s[2] for s in segs])
         cp = (ctypes.c_int * ns)(*[s[3] for s in segs])
         C.check(C.lib().ditk_attention(_dt_code(dtype), dh, H, q.data_ptr(), q.shape[0], ns, kp, vp, nn,
-                                       cp, nsplit, _ptr(partial), o.data_ptr(), _stream()))
+                                       cp, nsplit, _ptr(partial), 1 if q_prescaled else 0, o.data_ptr(),
+                                       _stream()))
 
     @staticmethod
     def modulation(dtype: str, cfg: ChunkConfig, weights: Dict[str, torch.Tensor], t: float,

@@ -39,7 +39,9 @@ int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* 
 
 /* Per-head QK-RMSNorm with gamma [dh] (dtype), 3D RoPE (rope != 0) at positions
  * (grid.t0 + f, y, x) of token f*h*w + y*w + x, and repacking into the attention layout:
- *   q_out  [n, H*dh]              (plain, only if q_in)
+ *   q_out  [n, H*dh]              q_scale times the normalised, rotated q (only if q_in);
+ *                                 q_scale = log2(e)/sqrt(dh) gives the pre-scaled q that
+ *                                 ditk_attention takes with q_prescaled != 0
  *   k_out  [cap, H*dh]            (rows n..round_up(n,64)-1 zeroed; only if k_in)
  *   vt_out [H*dh, cap]            V transposed (only if v_in); for bf16 the keys of each
  *                                 aligned group of 16 are stored so that key offset o
@@ -48,18 +50,22 @@ int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* 
  * q_in/k_in/v_in: [n, ld_in] (dtype), any may be NULL.  cap a multiple of 64, >= n. */
 int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
                      const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
-                     dit_grid grid, double eps, double theta, void* q_out, void* k_out,
-                     void* vt_out, int cap, void* hip_stream);
+                     dit_grid grid, double eps, double theta, double q_scale, void* q_out,
+                     void* k_out, void* vt_out, int cap, void* hip_stream);
 
 /* o[nq, H*dh] = softmax(q k^T / sqrt(dh)) v per head, keys the concatenation of nseg
  * (1..3) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
  * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
  * nsplit (1..8) splits the key tiles into contiguous parts computed by separate
  * workgroups and merged afterwards; nsplit > 1 needs partial: fp32 scratch of
- * nsplit * nq * (H*dh + 2*H) floats (NULL allowed for nsplit == 1). */
+ * nsplit * nq * (H*dh + 2*H) floats (NULL allowed for nsplit == 1).
+ * q_prescaled != 0: q holds q * log2(e)/sqrt(dh) (ditk_qknorm_rope with that q_scale;
+ * the softmax is then taken in base 2 on q k^T directly).  q_prescaled == 0: plain q,
+ * scaled inside the kernel (for bf16 with dh = 128 this rounds the scaled q to bf16
+ * once more, i.e. slightly less accurate than the pre-scaled form). */
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, void* o, void* hip_stream);
+                   int nsplit, float* partial, int q_prescaled, void* o, void* hip_stream);
 
 /* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
  * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,

@@ -143,16 +143,19 @@ def test_euler_and_ops_validation():
     assert lib.ditk_rmsnorm_modulate(1, FAKE, 4, 256, FAKE, None, 1e-6, FAKE, None) == C.DIT_EINVAL
     g = C.DitGrid(0, 1, 2, 2)
     assert lib.ditk_qknorm_rope(1, 128, 2, 5, None, FAKE, None, 256, None, FAKE, 1, g, 1e-6, 1e4,
-                                None, FAKE, None, 64, None) == C.DIT_ESHAPE  # grid covers 4 < 5
+                                1.0, None, FAKE, None, 64, None) == C.DIT_ESHAPE  # grid covers 4 < 5
     assert lib.ditk_qknorm_rope(1, 128, 2, 65, None, FAKE, None, 256, None, FAKE, 0, g, 1e-6, 1e4,
-                                None, FAKE, None, 64, None) == C.DIT_ESHAPE  # cap < round_up(n)
+                                1.0, None, FAKE, None, 64, None) == C.DIT_ESHAPE  # cap < round_up(n)
+    g2 = C.DitGrid(0, 1, 4, 4)
+    assert lib.ditk_qknorm_rope(1, 128, 2, 5, None, FAKE, None, 256, None, FAKE, 0, g2, 1e-6, 1e4,
+                                0.0, None, FAKE, None, 64, None) == C.DIT_EINVAL  # q_scale <= 0
     k = (C.P * 1)(FAKE)
     n = (ctypes.c_int * 1)(70)
     cap = (ctypes.c_int * 1)(64)
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, FAKE, None) == C.DIT_ESHAPE
     n[0] = 40
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, FAKE, None) == C.DIT_EINVAL
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, FAKE, None) == C.DIT_EINVAL
-    assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, 0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, 0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, FAKE, None) == C.DIT_EINVAL
     n[0] = 0
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, FAKE, None) == C.DIT_ESHAPE  # no keys
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, FAKE, None) == C.DIT_ESHAPE  # no keys
