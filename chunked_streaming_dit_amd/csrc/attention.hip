@@ -55,11 +55,6 @@ __device__ __forceinline__ float row_sum_add(f32x4 p, float acc) {
 }
 constexpr int BKV = 64;  // keys per tile
 
-template <int N> __device__ __forceinline__ void wait_vm_lds() {
-  // s_waitcnt vmcnt(N) lgkmcnt(0); expcnt left at its maximum (7).
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
 
 // 16-byte chunk position of chunk c of row r in an unpadded LDS tile whose rows are RB
 // bytes: consecutive rows reading the same chunk spread over all 64 banks.

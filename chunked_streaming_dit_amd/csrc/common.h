@@ -111,4 +111,10 @@ template <> __device__ __forceinline__ void store4<bf16>(bf16* p, const float v[
 // keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0); expcnt left at its maximum (7).
+template <int N> __device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 }  // namespace dit

@@ -21,27 +21,71 @@ namespace {
 
 constexpr int ROWB = 128 + 16;  // LDS bytes per staged row (128 data + 16 pad)
 
+// Bias of a wave's NB x 32 columns, loaded into registers before the K loop so that its
+// latency hides under it: lane columns n = nw + 32 j + 8 q + 4 lg + {0..3} in [j][q][0..3].
+template <int NB, int EPI>
+struct EpiCols {
+  float b[NB][4][4];
+};
+template <class T, int NB, int EPI>
+__device__ __forceinline__ void epi_cols_load(EpiCols<NB, EPI>& c, int nw, int lg, int N, const GemmEpi& e) {
+  const T* bias = reinterpret_cast<const T*>(e.bias);
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = nw + j * 32 + 8 * q + 4 * lg;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c.b[j][q][r] = 0.f;
+      if (n < N) load4<T>(bias + n, c.b[j][q]);
+    }
+}
+
 // Epilogue over a wave's (MB x 32) x (NB x 32) accumulator tile whose first row/column
 // are mw, nw: lane holds output row m = mw + 32 i + l32 and columns
-// n = nw + 32 j + 8 q + 4 lg + {0..3} in acc[i][j][4q .. 4q+3].
+// n = nw + 32 j + 8 q + 4 lg + {0..3} in acc[i][j][4q .. 4q+3].  The residual gate is
+// read before any store, and per 32-row block the values read back from the destination
+// (residual h, latent x) are all requested before any store of that block, so their
+// latencies overlap instead of adding up.
 template <class T, int MB, int NB, int EPI>
-__device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], int mw, int nw, int l32, int lg,
-                                         int M, int N, const GemmEpi& e) {
-  const T* bias = reinterpret_cast<const T*>(e.bias);
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const EpiCols<NB, EPI>& c, int mw,
+                                         int nw, int l32, int lg, int M, int N, const GemmEpi& e) {
+  float gate[EPI == EPI_RESID ? NB : 1][4][4];
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nw + j * 32 + 8 * q + 4 * lg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gate[j][q][r] = 1.f;
+        if (e.gate && n < N) load4<float>(e.gate + n, gate[j][q]);
+      }
+  }
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int m = mw + i * 32 + l32;
     if (m >= M) continue;
+    float* dst32 = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo;
+    float old[EPI == EPI_RESID || EPI == EPI_EULER ? NB : 1][4][4];
+    if constexpr (EPI == EPI_RESID || EPI == EPI_EULER) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nw + j * 32 + 8 * q + 4 * lg;
+          if (n < N) load4<float>(dst32 + n, old[j][q]);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = nw + j * 32 + 8 * q + 4 * lg;
         if (n >= N) continue;
-        float v[4], b[4];
-        load4<T>(bias + n, b);
+        float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + b[r];
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + c.b[j][q][r];
         if constexpr (EPI == EPI_BIAS) {
           store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
         } else if constexpr (EPI == EPI_GELU) {
@@ -49,22 +93,17 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], int mw, in
           for (int r = 0; r < 4; ++r) v[r] = gelu_tanh(v[r]);
           store4<T>(reinterpret_cast<T*>(e.out) + (size_t)m * e.ldo + n, v);
         } else if constexpr (EPI == EPI_F32) {
-          store4<float>(reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n, v);
+          store4<float>(dst32 + n, v);
         } else if constexpr (EPI == EPI_RESID) {
-          float* hp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
-          float h[4], g[4] = {1.f, 1.f, 1.f, 1.f};
-          load4<float>(hp, h);
-          if (e.gate) load4<float>(e.gate + n, g);
+          float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] += g[r] * v[r];
-          store4<float>(hp, h);
+          for (int r = 0; r < 4; ++r) h[r] = old[j][q][r] + gate[j][q][r] * v[r];
+          store4<float>(dst32 + n, h);
         } else {  // EPI_EULER
-          float* xp = reinterpret_cast<float*>(e.out) + (size_t)m * e.ldo + n;
           float x[4];
-          load4<float>(xp, x);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] = fmaf(e.dt, v[r], x[r]);
-          store4<float>(xp, x);
+          for (int r = 0; r < 4; ++r) x[r] = fmaf(e.dt, v[r], old[j][q][r]);
+          store4<float>(dst32 + n, x);
           if (e.v_out) store4<float>(e.v_out + (size_t)m * e.ldo + n, v);
         }
       }
@@ -134,6 +173,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int 
     }
   };
 
+  EpiCols<NB, EPI> cols;
+  epi_cols_load<T, NB, EPI>(cols, n0 + wn * WN, lg, N, e);
   f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -168,7 +209,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int 
     if (it + 1 < nk) sstore(buf ^ 1);
   }
 
-  epilogue<T, MB, NB, EPI>(acc, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
+  epilogue<T, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }
 
 template <class T, int BM, int BN>
@@ -249,6 +290,8 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     }
   };
 
+  EpiCols<NB, EPI> cols;
+  epi_cols_load<bf16, NB, EPI>(cols, n0 + wn * WN, lg, N, e);
   f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -302,7 +345,7 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  epilogue<bf16, MB, NB, EPI>(acc, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
+  epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }
 
 template <int BM, int BN>
