@@ -58,6 +58,7 @@ _SIGS = {
     "dit_destroy": (I, [P]),
     "ref_kv_precompute": (I, [P, P, DitGrid]),
     "boundary_kv_carry": (I, [P, P, DitGrid]),
+    "interp_anchor_kv": (I, [P, P, DitGrid, I]),
     "dit_chunk_step": (I, [P, P, P, P, I, DitGrid, Dbl, Dbl, P]),
     "fm_euler_step": (I, [P, P, Dbl, ctypes.c_longlong, P]),
     "dit_last_error": (ctypes.c_char_p, []),

@@ -113,17 +113,20 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   }
 
   // Tiles of all segments in order: tile t lies in segment si at key offset base.
-  int c0 = 0, c1 = 0, c2 = 0;
-  if (a.nseg > 0) c0 = (a.seg[0].n + BKV - 1) / BKV;
-  if (a.nseg > 1) c1 = (a.seg[1].n + BKV - 1) / BKV;
-  if (a.nseg > 2) c2 = (a.seg[2].n + BKV - 1) / BKV;
-  const int ntiles = c0 + c1 + c2;
+  // Tile counts of the segments, and prefix sums e1 <= e2 <= e3 = ntiles.
+  int c[ATTN_MAX_SEGS];
+#pragma unroll
+  for (int i = 0; i < ATTN_MAX_SEGS; ++i) c[i] = i < a.nseg ? (a.seg[i].n + BKV - 1) / BKV : 0;
+  static_assert(ATTN_MAX_SEGS == 4, "segment walk below");
+  const int e1 = c[0], e2 = e1 + c[1], e3 = e2 + c[2];
+  const int ntiles = e3 + c[3];
   const int tb = (int)((long long)ntiles * split / a.nsplit);
   const int total = (int)((long long)ntiles * (split + 1) / a.nsplit);  // tiles [tb, total)
   auto locate = [&](int t, int& si, int& base) {
-    if (t < c0) { si = 0; base = t * BKV; }
-    else if (t < c0 + c1) { si = 1; base = (t - c0) * BKV; }
-    else { si = 2; base = (t - c0 - c1) * BKV; }
+    if (t < e1) { si = 0; base = t * BKV; }
+    else if (t < e2) { si = 1; base = (t - e1) * BKV; }
+    else if (t < e3) { si = 2; base = (t - e2) * BKV; }
+    else { si = 3; base = (t - e3) * BKV; }
   };
   // Direct-to-LDS loads (global_load_lds_dwordx4): wave instruction g = wave + AW i fills
   // 1 KB of a slot = rows [RP g, RP g + RP); the lane covers row RP g + lane/(64/RP) at

@@ -4,7 +4,7 @@
 // and validates all arguments on the host before any HIP call.  A call enqueues a
 // fixed kernel sequence on the handle's stream:
 //
-//   ref_kv_precompute / boundary_kv_carry (context pass at t = 0):
+//   ref_kv_precompute / boundary_kv_carry / interp_anchor_kv (context pass at t = 0):
 //     modulation(0) -> patch input -> patch embed ->
 //     per block: RMSNorm+mod -> QKV -> QK-norm+RoPE (K, V written to the state) ->
 //                [not last block] attention over earlier context + self -> out-proj
@@ -12,7 +12,7 @@
 //   dit_chunk_step:
 //     modulation(t) -> patch input -> patch embed ->
 //     per block: RMSNorm+mod -> QKV -> QK-norm+RoPE -> attention over
-//                [ref | bnd | chunk] -> out-proj (gated residual) ->
+//                [ref | bnd | anchor | chunk] -> out-proj (gated residual) ->
 //                [audio] RMSNorm -> q_c -> q-norm; audio K/V -> k-norm; cross
 //                attention -> out (residual) ->
 //                RMSNorm+mod -> FC1+GELU -> FC2 (gated residual)
@@ -53,7 +53,7 @@ struct Layout {
   size_t elt = 0;
   int cap_tok = 0, cap_ref = 0, cap_bnd = 0, cap_audio = 0, F = 0, C_in = 0, big_cols = 0;
   // state
-  std::vector<size_t> kref, vref, kbnd, vbnd;
+  std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc;
   size_t state_total = 0;
   // workspace
   size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
@@ -106,6 +106,8 @@ Layout make_layout(const dit_config* c) {
     L.vref.push_back(take((size_t)L.cap_ref * D * L.elt));
     L.kbnd.push_back(take((size_t)L.cap_bnd * D * L.elt));
     L.vbnd.push_back(take((size_t)L.cap_bnd * D * L.elt));
+    L.kanc.push_back(take((size_t)L.cap_bnd * D * L.elt));
+    L.vanc.push_back(take((size_t)L.cap_bnd * D * L.elt));
   }
   L.state_total = off;
   off = 0;
@@ -152,7 +154,7 @@ struct dit_handle {
   char* ws = nullptr;
   hipStream_t stream = nullptr;
   bool has_ref = false;
-  int n_ref = 0, n_bnd = 0;
+  int n_ref = 0, n_bnd = 0, n_anc = 0;
   // timing
   bool timing = false;
   std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created lazily
@@ -212,11 +214,12 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
   return DIT_OK;
 }
 
-// One context pass (reference or boundary) at t = 0: writes K (normed, rotated) and V
-// of every block into kdst[l] / vdst[l] (capacity cap).  prior_k/prior_v/prior_n: the
-// earlier context segment (reference) per block, or none.
+// One context pass (reference, boundary or interpolation anchor) at t = 0: writes K
+// (normed, rotated) and V of every block into kdst[l] / vdst[l] (capacity cap).  The
+// tokens attend to the earlier context segments and themselves: nprior 0 (reference:
+// itself only), 1 (boundary: reference), 2 (anchor: reference and, if held, boundary).
 int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::vector<size_t>& kdst,
-                 const std::vector<size_t>& vdst, int cap, bool with_prior) {
+                 const std::vector<size_t>& vdst, int cap, int nprior) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   const int D = c.D, F = L.F;
@@ -247,9 +250,10 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
                        hd->S(kdst[l]),
                        hd->S(vdst[l]), cap, s));
     if (last) break;
-    AttnSeg seg[2];
+    AttnSeg seg[3];
     int ns = 0;
-    if (with_prior) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
+    if (nprior >= 1) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
+    if (nprior >= 2 && hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->S(kdst[l]), hd->S(vdst[l]), n, cap};
     int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
     if (rc) return rc;
@@ -337,8 +341,9 @@ int ref_kv_precompute(dit_handle* h, const float* ref, dit_grid grid) {
   if (n > h->cfg.max_ref) return fail(DIT_ESHAPE, "reference tokens %lld > max_ref %d", n, h->cfg.max_ref);
   h->has_ref = false;
   h->n_bnd = 0;
+  h->n_anc = 0;
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
-  int rc = context_pass(h, ref, (int)n, g, h->lay.kref, h->lay.vref, h->lay.cap_ref, false);
+  int rc = context_pass(h, ref, (int)n, g, h->lay.kref, h->lay.vref, h->lay.cap_ref, 0);
   if (rc) return rc;
   h->n_ref = (int)n;
   h->has_ref = true;
@@ -349,6 +354,7 @@ int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev) {
   if (!h) return fail(DIT_EINVAL, "handle is NULL");
   if (prev.frames == 0) {
     h->n_bnd = 0;
+    h->n_anc = 0;
     return DIT_OK;
   }
   if (!x_prev) return fail(DIT_EINVAL, "x_prev is NULL");
@@ -357,11 +363,31 @@ int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev) {
   if (n > h->cfg.max_bnd) return fail(DIT_ESHAPE, "boundary tokens %lld > max_bnd %d", n, h->cfg.max_bnd);
   if (!h->has_ref) return fail(DIT_ESTATE, "boundary_kv_carry before ref_kv_precompute");
   h->n_bnd = 0;
+  h->n_anc = 0;  // an anchor's K/V depend on the boundary they were computed with
   const float* last = x_prev + (size_t)(prev.frames - 1) * n * h->cfg.c_p;
   RopeGrid g{-1, 1, prev.h, prev.w};
-  int rc = context_pass(h, last, (int)n, g, h->lay.kbnd, h->lay.vbnd, h->lay.cap_bnd, true);
+  int rc = context_pass(h, last, (int)n, g, h->lay.kbnd, h->lay.vbnd, h->lay.cap_bnd, 1);
   if (rc) return rc;
   h->n_bnd = (int)n;
+  return DIT_OK;
+}
+
+int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_pos) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (next.frames == 0) {
+    h->n_anc = 0;
+    return DIT_OK;
+  }
+  if (!x_next) return fail(DIT_EINVAL, "x_next is NULL");
+  if (!grid_ok(next)) return fail(DIT_ESHAPE, "bad next-chunk grid");
+  const long long n = (long long)next.h * next.w;
+  if (n > h->cfg.max_bnd) return fail(DIT_ESHAPE, "anchor tokens %lld > max_bnd %d", n, h->cfg.max_bnd);
+  if (!h->has_ref) return fail(DIT_ESTATE, "interp_anchor_kv before ref_kv_precompute");
+  h->n_anc = 0;
+  RopeGrid g{t_pos, 1, next.h, next.w};  // frame 0 of the next chunk, placed at t = t_pos
+  int rc = context_pass(h, x_next, (int)n, g, h->lay.kanc, h->lay.vanc, h->lay.cap_bnd, 2);
+  if (rc) return rc;
+  h->n_anc = (int)n;
   return DIT_OK;
 }
 
@@ -414,10 +440,11 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
                        3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g, (float)c.eps,
                        (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q), hd->X(L.kc),
                        hd->X(L.vtc), L.cap_tok, s));
-    AttnSeg seg[3];
+    AttnSeg seg[ATTN_MAX_SEGS];
     int ns = 0;
     seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     if (hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
+    if (hd->n_anc > 0) seg[ns++] = AttnSeg{hd->S(L.kanc[l]), hd->S(L.vanc[l]), hd->n_anc, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
     int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
     if (rc) return rc;

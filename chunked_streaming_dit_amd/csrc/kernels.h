@@ -41,7 +41,7 @@ struct AttnSeg {
   int n;
   int cap;
 };
-enum { ATTN_MAX_SEGS = 3 };
+enum { ATTN_MAX_SEGS = 4 };  // reference | boundary | anchor | chunk
 // Key-range split: nsplit > 1 makes attention() write normalised partial outputs
 // opart [nsplit, nq, H*dh] and (running max of the exp2-domain logits, row sum) pairs
 // ml [nsplit, nq, H, 2]

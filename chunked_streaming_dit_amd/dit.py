@@ -143,6 +143,12 @@ class DitChunk:
         _dev(x_prev, "x_prev", torch.float32)
         C.check(C.lib().boundary_kv_carry(self._h, _ptr(x_prev), g))
 
+    def interp_anchor_kv(self, x_next: Optional[torch.Tensor], g: C.DitGrid, t_pos: int) -> None:
+        """Anchor K/V of an interpolation chunk from frame 0 of the next chunk's final
+        latent x_next (grid g), placed at time position t_pos; g.frames == 0 clears it."""
+        _dev(x_next, "x_next", torch.float32)
+        C.check(C.lib().interp_anchor_kv(self._h, _ptr(x_next), g, int(t_pos)))
+
     def step(self, x: torch.Tensor, t: float, t_next: float, g: C.DitGrid,
              cond: Optional[torch.Tensor] = None, audio: Optional[torch.Tensor] = None,
              v_out: Optional[torch.Tensor] = None) -> None:

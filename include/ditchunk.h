@@ -17,6 +17,8 @@
  * Hence the call cadence:
  *   ref_kv_precompute   once per request;
  *   boundary_kv_carry   once per chunk (a zero-frame grid clears it for chunk 0);
+ *   interp_anchor_kv    once per interpolation chunk (see below; cleared for
+ *                       ordinary chunks);
  *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
  *   fm_euler_step       the bare Euler update, for callers with their own velocity.
  *
@@ -25,13 +27,15 @@
  * Each block runs:
  *   - RMSNorm + adaLN shift/scale, QKV, per-head QK-RMSNorm with gamma, and a 3D
  *     RoPE over (t, y, x);
- *   - self-attention whose keys are [reference K | boundary K | chunk K];
+ *   - self-attention whose keys are [reference K | boundary K | anchor K | chunk K]
+ *     (boundary and anchor when held);
  *   - a gated residual;
  *   - RMSNorm, audio cross-attention (q and k per-head normed), and a residual;
  *   - RMSNorm + adaLN, a GELU(tanh) MLP and a gated residual.
  * A final RMSNorm + adaLN and a Linear give v [N, c_p].  Context tokens
- * (reference, boundary) pass through the same blocks at t = 0: the reference
- * sees only itself, and the boundary sees the reference and itself.  Their
+ * (reference, boundary, anchor) pass through the same blocks at t = 0: the
+ * reference sees only itself, the boundary sees the reference and itself, and the
+ * anchor sees the reference, the boundary and itself.  Their
  * per-block K (normed, rotated) and V are kept resident, read-only, in the
  * caller's state buffer.
  *
@@ -145,9 +149,9 @@ enum {
 /* Number of entries of the weight table for this config (0 if the config is invalid). */
 int dit_weight_count(const dit_config* cfg);
 
-/* Bytes of the resident state: per block, K and V of max_ref reference tokens and
- * max_bnd boundary tokens (rounded up to 64 tokens), plus a small modulation
- * area.  0 if the config is invalid (see dit_last_error). */
+/* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
+ * max_bnd boundary tokens and of max_bnd interpolation-anchor tokens (each rounded
+ * up to 64 tokens).  0 if the config is invalid (see dit_last_error). */
 size_t dit_state_bytes(const dit_config* cfg);
 
 /* Bytes of per-call transients (activations of max(max_tokens, max_ref, max_bnd)
@@ -169,7 +173,7 @@ int dit_destroy(dit_handle* h);
 /* Reference K/V: run the reference latent tokens ref [grid.frames*grid.h*grid.w,
  * c_p] (fp32, device) through all blocks at t = 0, each token at position
  * (grid.t0 + f, y, x), attending only to the reference, and store every block's
- * K and V in the state.  Once per request.  Clears any boundary.
+ * K and V in the state.  Once per request.  Clears any boundary and anchor.
  * Errors: EINVAL (null), ESHAPE (more than max_ref tokens, empty grid). */
 int ref_kv_precompute(dit_handle* h, const float* ref, dit_grid grid);
 
@@ -181,6 +185,24 @@ int ref_kv_precompute(dit_handle* h, const float* ref, dit_grid grid);
  * Errors: EINVAL (null x_prev with frames > 0), ESHAPE (h*w > max_bnd),
  * ESTATE (no reference yet). */
 int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev);
+
+/* Interpolation anchor K/V (HeyGen, "Avatar inference at scale", section "Boundary
+ * continuity and chunk consistency": ordinary N-chunks make the timeline, and an
+ * interpolation chunk between N_k and N_k+1, generated after both, smooths the
+ * transition using the last frame of N_k and an early frame of N_k+1 as anchors;
+ * the order is N0, N1, I0, N2, I1, ...).  Reading: both anchors are context
+ * segments.  The boundary (boundary_kv_carry on N_k's final latent) is the first;
+ * this call makes the second from frame 0 (h*w tokens) of N_k+1's final latent
+ * x_next [next.frames*next.h*next.w, c_p] (fp32, device), run through all blocks at
+ * t = 0 at positions (t_pos, y, x), usually t_pos = the interpolation chunk's frame
+ * count, attending to the reference, the boundary (if held) and itself.  Anchors
+ * are never denoised, so they yield no predictions to discard.  Until cleared,
+ * dit_chunk_step attends to [reference | boundary | anchor | chunk].
+ * next.frames == 0 clears the anchor; boundary_kv_carry and ref_kv_precompute also
+ * clear it (its K/V depend on the boundary).
+ * Errors: EINVAL (null x_next with frames > 0), ESHAPE (h*w > max_bnd),
+ * ESTATE (no reference yet). */
+int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_pos);
 
 /* One denoising step of the chunk: v = DiT(x, t) and x += (t_next - t) v,
  * with dt computed in double on the host and applied in fp32.
@@ -204,7 +226,8 @@ int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_st
 const char* dit_last_error(void);
 
 /* Kernel timing on the handle's stream.  While enabled, each attention launch of
- * dit_chunk_step, ref_kv_precompute and boundary_kv_carry is bracketed by a pair
+ * dit_chunk_step, ref_kv_precompute, boundary_kv_carry and interp_anchor_kv is
+ * bracketed by a pair
  * of HIP events (created lazily, at most 4096 pairs per window).
  * dit_timing_read synchronises those events and returns the count and the summed
  * milliseconds of the window, then opens a new window.

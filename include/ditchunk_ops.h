@@ -54,7 +54,7 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
                      void* k_out, void* vt_out, int cap, void* hip_stream);
 
 /* o[nq, H*dh] = softmax(q k^T / sqrt(dh)) v per head, keys the concatenation of nseg
- * (1..3) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
+ * (1..4) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
  * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
  * nsplit (1..8) splits the key tiles into contiguous parts computed by separate
  * workgroups and merged afterwards; nsplit > 1 needs partial: fp32 scratch of

@@ -13,10 +13,15 @@ The pages give no block internals, so every constant below (norm type, RoPE
 split, modulation order, GELU form, schedule) is a stated reading, chosen as the
 plainest one consistent with them.
 
+The boundary continuity section adds interpolation (I) chunks between ordinary
+N-chunks, anchored on the neighbouring N-chunks' frames (anchor_context,
+interp_stream).
+
 Parity status: every function is pinned by a CPU test (brute-force attention,
-softmax normalisation, masked-joint vs cached-KV equivalence, chunked ==
-unchunked, closed-form Euler, constant-velocity model, uniform attention, RoPE
-and RMSNorm identities, zero-gate identity, key-permutation invariance).  Against
+softmax normalisation, masked-joint vs cached-KV equivalence with and without
+the interpolation anchor, chunked == unchunked, closed-form Euler,
+constant-velocity model, uniform attention, RoPE and RMSNorm identities,
+zero-gate identity, key-permutation and time-shift invariance).  Against
 the pages themselves parity is unpinned: they print no values.
 """
 from .dit import *  # noqa: F401,F403

@@ -30,7 +30,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = C.lib()
     declared = _declared()
-    assert {"dit_chunk_step", "ref_kv_precompute", "boundary_kv_carry", "fm_euler_step",
+    assert {"dit_chunk_step", "ref_kv_precompute", "boundary_kv_carry", "interp_anchor_kv", "fm_euler_step",
             "dit_create", "ditk_attention"} <= declared
     for n in declared:
         assert hasattr(lib, n), n
@@ -51,9 +51,10 @@ def test_sizes_and_weight_count():
         cfg = synth.CONFIGS[cid]
         assert lib.dit_weight_count(ctypes.byref(cs)) == 10 + 22 * cfg.L
         sb = lib.dit_state_bytes(ctypes.byref(cs))
+        # per block K and V of the reference, the boundary and the interpolation anchor
         kv = cfg.L * 2 * cfg.D * (2 if cfg.dtype == "bf16" else 4) * (
-            (cfg.N_ref + 63) // 64 * 64 + (cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64)
-        assert kv <= sb <= kv + 4 * cfg.L * 256
+            (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64))
+        assert kv <= sb <= kv + 6 * cfg.L * 256
         assert lib.dit_workspace_bytes(ctypes.byref(cs)) > 0
 
 
@@ -115,6 +116,14 @@ def test_call_order_and_shape_errors():
     assert lib.boundary_kv_carry(h, FAKE, C.DitGrid(0, 1, 8, 8)) == C.DIT_ESHAPE  # 64 > max_bnd 32
     assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 2, 4, 8)) == C.DIT_EINVAL
     assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 0, 0, 0)) == C.DIT_OK      # clear: no launch
+    # interpolation anchor: same checks as the boundary
+    assert lib.interp_anchor_kv(h, FAKE, C.DitGrid(0, 2, 4, 8), 2) == C.DIT_ESTATE
+    assert "ref_kv_precompute" in C.last_error()
+    assert lib.interp_anchor_kv(h, FAKE, C.DitGrid(0, 1, 8, 8), 2) == C.DIT_ESHAPE  # 64 > max_bnd 32
+    assert lib.interp_anchor_kv(h, None, C.DitGrid(0, 2, 4, 8), 2) == C.DIT_EINVAL
+    assert lib.interp_anchor_kv(h, FAKE, C.DitGrid(0, 1, 0, 8), 2) == C.DIT_ESHAPE
+    assert lib.interp_anchor_kv(h, None, C.DitGrid(0, 0, 0, 0), 2) == C.DIT_OK     # clear: no launch
+    assert lib.interp_anchor_kv(None, FAKE, C.DitGrid(0, 1, 4, 8), 2) == C.DIT_EINVAL
     assert lib.dit_destroy(h) == C.DIT_OK
     assert lib.dit_destroy(None) == C.DIT_OK
 

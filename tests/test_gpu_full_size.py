@@ -123,6 +123,39 @@ def test_full_shape_one_block_sampled_rows(base):
     assert err <= TOL["bf16"], err
 
 
+def test_interp_chunk_full_shape_one_block_sampled_rows():
+    """An interpolation chunk at the base-chunk shape with one block: keys
+    [reference 1560 | boundary 1560 | anchor 1560 at t = 5 | chunk 7800]; the oracle
+    evaluates sampled query rows of the first step's velocity."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(synth.CONFIGS[2], L=1, cid=52, steps=1)
+    P = synth.make_weights(cfg, threads=16)
+    inp = synth.make_inputs(cfg, 0)
+    anchor = synth.make_inputs(cfg, 1)["bnd"]  # frame 0 of the "next" chunk
+    g = cfg.chunk
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, g.h, g.w)))
+    h.interp_anchor_kv(f32(anchor, dev), grid_of(Grid(0, 1, g.h, g.w)), g.frames)
+    x = f32(inp["x_init"], dev)
+    v = torch.empty_like(x)
+    h.step(x, cfg.t_start, cfg.t_end, grid_of(g), audio=f32(inp["audio"], dev), v_out=v)
+    torch.cuda.synchronize()
+    vg = to_np(v)
+    h.close()
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    bkv = O.bnd_context(P, cfg, ref_kv, inp["bnd"], g.h, g.w)
+    akv = O.anchor_context(P, cfg, ref_kv, bkv, anchor, g.h, g.w, g.frames)
+    rows = _sample_rows(cfg.N, 52)
+    vo = O.velocity_rows(P, cfg, inp["x_init"], cfg.t_start, O.grid_positions(0, g.frames, g.h, g.w),
+                         [[ref_kv[0], bkv[0], akv[0]]], inp["audio"], rows)
+    err = rel_err(vg[rows], vo)
+    print(f"interpolation chunk one-block full shape, {len(rows)} sampled rows: v err {err:.2e}")
+    assert err <= TOL["bf16"], err
+
+
 def _device_weights(cfg, dev, seed):
     """Seeded N(0, 1/fan_in) weights drawn on the device (no host copy of 10+ GB)."""
     gen = torch.Generator(device=dev)

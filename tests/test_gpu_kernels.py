@@ -183,7 +183,8 @@ def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dh", [64, 128])
 @pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (1, [5]), (300, [64, 0, 200]),
-                                       (257, [1, 1, 1]), (128, [1000])])
+                                       (257, [1, 1, 1]), (128, [1000]), (200, [70, 33, 65, 129]),
+                                       (70, [64, 0, 1, 200])])
 @pytest.mark.parametrize("prescaled", [True, False])
 def test_attention(dtype, dh, nq, seg_ns, prescaled):
     if dtype == "f32" and dh == 128:
@@ -197,7 +198,8 @@ def test_attention(dtype, dh, nq, seg_ns, prescaled):
 
 @pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 64), ("bf16", 128)])
 @pytest.mark.parametrize("nsplit", [2, 3, 8])
-@pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (300, [64, 0, 200]), (40, [130])])
+@pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (300, [64, 0, 200]), (40, [130]),
+                                       (90, [70, 33, 65, 129])])
 def test_attention_key_split(dtype, dh, nsplit, nq, seg_ns):
     """Key tiles split over workgroups and merged; includes splits with no tiles."""
     err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + nsplit, nsplit, prescaled=True)

@@ -102,6 +102,52 @@ def test_mini_stream_bf16():
         assert err <= TOL["bf16"], (c, err)
 
 
+@pytest.mark.parametrize("base", ["bf16", "f32"])
+def test_mini_interp_stream(base):
+    """N- and I-chunks in the order N0, N1, I0, N2, I1: I_k attends to
+    [reference | N_k's last frame at t = -1 | N_k+1's first frame at t = frames | chunk];
+    the boundary call before each N-chunk clears the anchor."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(MINI_BF16 if base == "bf16" else MINI_F32, cid=207 if base == "bf16" else 208,
+                              bnd=None)
+    P = synth.make_weights(cfg)
+    n_in = [synth.make_inputs(cfg, c) for c in range(3)]
+    i_in = [synth.make_inputs(cfg, 100 + k) for k in range(2)]
+    n_ref, i_ref = O.interp_stream(P, cfg, n_in, i_in, n_in[0]["ref"])
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(n_in[0]["ref"], dev), grid_of(cfg.ref))
+    g = cfg.chunk
+    ts = O.schedule(cfg.steps, cfg.t_start, cfg.t_end)
+
+    def denoise(inp):
+        x = f32(inp["x_init"], dev)
+        for k in range(cfg.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=f32(inp["audio"], dev))
+        return x
+
+    n_gpu, i_gpu = [], []
+    for c in range(3):
+        if c == 0:
+            h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+        else:
+            h.boundary_kv_carry(n_gpu[-1], grid_of(g))  # also clears the anchor
+        n_gpu.append(denoise(n_in[c]))
+        if c >= 1:
+            k = c - 1
+            h.boundary_kv_carry(n_gpu[k], grid_of(g))
+            h.interp_anchor_kv(n_gpu[k + 1], grid_of(g), g.frames)
+            i_gpu.append(denoise(i_in[k]))
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    for name, got, want, inps in (("N", n_gpu, n_ref, n_in), ("I", i_gpu, i_ref, i_in)):
+        for k, (a, b) in enumerate(zip(got, want)):
+            err = rel_err(a.cpu().numpy() - inps[k]["x_init"], b - inps[k]["x_init"])
+            print(f"{name}{k}: dx err {err:.2e}")
+            assert err <= tol, (name, k, err)
+
+
 def test_config2_full_size_first_step():
     """The base low-res chunk at its full shape (7800 tokens, keys 1560|1560|7800,
     4 blocks, hidden 1536, 12x128 heads, 50 audio tokens): the first denoising step."""

@@ -222,10 +222,11 @@ def _pos(g):
 
 
 def joint_velocity(P, cfg, segs, audio, t, L=None):
-    """Monolithic form: one sequence [ref; bnd; chunk] with a per-token timestep
-    (0 for context tokens) and a block-causal mask (ref sees ref, bnd sees ref and
-    bnd, chunk sees everything); audio only for chunk rows; every block runs on
-    every token.  segs: list of (tokens [n, C_in], positions, seg_id, t)."""
+    """Monolithic form: one sequence [ref; bnd; (anchor;) chunk] with a per-token
+    timestep (0 for context tokens) and a block-causal mask (a segment sees the
+    segments with ids up to its own; the chunk, the highest id, sees everything);
+    audio only for chunk rows; every block runs on every token.
+    segs: list of (tokens [n, C_in], positions, seg_id, t)."""
     L = cfg.L if L is None else L
     D, H, dh, eps = cfg.D, cfg.H, cfg.dh, cfg.eps
     X = np.concatenate([s[0] for s in segs])
@@ -233,7 +234,7 @@ def joint_velocity(P, cfg, segs, audio, t, L=None):
     seg = np.concatenate([np.full(len(s[0]), s[2]) for s in segs])
     tt = np.concatenate([np.full(len(s[0]), s[3]) for s in segs])
     n = len(X)
-    is_chunk = seg == 2
+    is_chunk = seg == seg.max()
     h = X @ O.W(P, "pe.w").T + O.W(P, "pe.b")
     cvec = {tv: O.conditioning(P, tv) for tv in set(tt.tolist())}
     allowed = seg[None, :] <= seg[:, None]
@@ -392,6 +393,78 @@ def test_p10_zero_gates_are_identity(tiny):
     out, _, _ = O.block_forward(P, cfg, 1, h, O.block_modulation(P, 1, np.ones(D)), _pos(cfg.chunk),
                                 ctx[1], inp["audio"])
     assert np.array_equal(out, h)
+
+
+# ---------------------------------------------------------------- interpolation chunks
+
+
+def _anchor_pos(cfg):
+    g = cfg.chunk
+    return O.grid_positions(g.frames, 1, g.h, g.w)
+
+
+def test_interp_cached_context_equals_joint_masked(tiny):
+    """An I-chunk's cached [ref | bnd | anchor] K/V give the velocity of the monolithic
+    block-causal sequence [ref; bnd; anchor; chunk] (anchor at t = frames, seeing
+    ref, bnd and itself)."""
+    P, inp = tiny
+    cfg = TINY
+    anchor = synth.make_inputs(TINY, 5)["bnd"]  # any frame of the grid's h x w size
+    ref_kv, bnd_kv, _ = _ctx(P, cfg, inp)
+    akv = O.anchor_context(P, cfg, ref_kv, bnd_kv, anchor, cfg.chunk.h, cfg.chunk.w, cfg.chunk.frames)
+    ctx = [[ref_kv[l], bnd_kv[l], akv[l]] for l in range(cfg.L)]
+    t = 0.41
+    v = O.dit_velocity(P, cfg, inp["x_init"], t, _pos(cfg.chunk), ctx, inp["audio"])
+    segs = [(inp["ref"], _pos(cfg.ref), 0, 0.0), (inp["bnd"], _pos(cfg.bnd), 1, 0.0),
+            (anchor, _anchor_pos(cfg), 2, 0.0), (inp["x_init"], _pos(cfg.chunk), 3, t)]
+    vj = joint_velocity(P, cfg, segs, inp["audio"].astype(np.float64), t)
+    assert np.abs(v - vj).max() <= 1e-12 * np.abs(vj).max()
+    # the anchor matters: without it the velocity differs
+    v_no = O.dit_velocity(P, cfg, inp["x_init"], t, _pos(cfg.chunk), [c[:2] for c in ctx], inp["audio"])
+    assert np.abs(v - v_no).max() > 1e-6 * np.abs(v).max()
+
+
+def test_interp_time_shift_invariance(tiny):
+    """Shifting every time coordinate (reference, boundary, anchor, chunk) together
+    leaves an I-chunk's velocity unchanged."""
+    P, inp = tiny
+    cfg = TINY
+    anchor = synth.make_inputs(TINY, 5)["bnd"]
+    def vel(shift):
+        sh = np.array([shift, 0, 0])
+        rkv = O.context_pass(P, cfg, inp["ref"], _pos(cfg.ref) + sh, [[] for _ in range(cfg.L)])
+        bkv = O.context_pass(P, cfg, inp["bnd"], _pos(cfg.bnd) + sh, [[rkv[l]] for l in range(cfg.L)])
+        akv = O.context_pass(P, cfg, anchor, _anchor_pos(cfg) + sh, [[rkv[l], bkv[l]] for l in range(cfg.L)])
+        ctx = [[rkv[l], bkv[l], akv[l]] for l in range(cfg.L)]
+        return O.dit_velocity(P, cfg, inp["x_init"], 0.3, _pos(cfg.chunk) + sh, ctx, inp["audio"])
+    v0, v1 = vel(0), vel(-9)
+    assert np.abs(v0 - v1).max() <= 1e-11 * np.abs(v0).max()
+
+
+def test_interp_stream_schedule_and_anchor_frames(tiny):
+    """N0, N1, I0, N2, I1: the N-chunks equal stream(); I_k equals one chunk whose
+    boundary is N_k's last frame and whose anchor is N_k+1's first frame (rows picked
+    here by their grid coordinates), placed at t = frames."""
+    P, _ = tiny
+    cfg = dataclasses.replace(TINY, bnd=None, steps=1)
+    g = cfg.chunk
+    n_in = [synth.make_inputs(TINY, c) for c in range(3)]
+    i_in = [synth.make_inputs(TINY, 100 + k) for k in range(2)]
+    n_out, i_out = O.interp_stream(P, cfg, n_in, i_in, n_in[0]["ref"])
+    assert len(n_out) == 3 and len(i_out) == 2
+    for a, b in zip(n_out, O.stream(P, cfg, n_in, n_in[0]["ref"])):
+        assert np.abs(a - b).max() == 0.0
+    pos = _pos(g)
+    ref_kv = O.ref_context(P, cfg, n_in[0]["ref"], cfg.ref)
+    for k in range(2):
+        last = n_out[k][pos[:, 0] == g.frames - 1]
+        first = n_out[k + 1][pos[:, 0] == 0]
+        bkv = O.context_pass(P, cfg, last, O.grid_positions(-1, 1, g.h, g.w), [[ref_kv[l]] for l in range(cfg.L)])
+        akv = O.context_pass(P, cfg, first, O.grid_positions(g.frames, 1, g.h, g.w),
+                             [[ref_kv[l], bkv[l]] for l in range(cfg.L)])
+        x = O.chunk_denoise(P, cfg, i_in[k]["x_init"], [[ref_kv[l], bkv[l], akv[l]] for l in range(cfg.L)],
+                            i_in[k]["audio"])
+        assert np.abs(x - i_out[k]).max() == 0.0
 
 
 def test_p11_context_key_permutation_invariance(tiny):
