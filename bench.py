@@ -14,6 +14,11 @@ roofline = the self-attention kernel (the dominant kernel): algorithmic flop
 bf16 dense MFMA peak.
 cpu_baseline = the f64 oracle timed on the host on a bounded sample (one DiT block of
 one denoising step at the full chunk shape, scaled to the 4-block step).
+
+--workload interp times an interpolation chunk of the same shape instead (the
+boundary from one neighbouring chunk's last frame, the anchor from the other's first
+frame, then 8 steps whose keys are [reference | boundary | anchor | chunk]); the
+reference pass runs once, outside the timed region, as it does once per request.
 """
 from __future__ import annotations
 
@@ -29,6 +34,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "DiT chunk-step latent tokens/sec and attention TFLOP/s (% bf16 MFMA peak), 1 GPU"
+METRIC_INTERP = ("DiT interpolation-chunk latent tokens/sec and attention TFLOP/s "
+                 "(% bf16 MFMA peak), 1 GPU")
 PEAK_BF16_TFLOPS = 2500.0
 ATTN_SRC = os.path.join(ROOT, "chunked_streaming_dit_amd", "csrc", "attention.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_base_chunk_traffic.json")
@@ -144,6 +151,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["base", "interp"], default="base",
+                    help="base: one N-chunk job (default); interp: one interpolation-chunk job")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 256 MiB calibration copy (for the traffic counters)")
     ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -186,10 +195,20 @@ def main() -> int:
     g_chunk = grid_of(cfg.chunk)
     g_ref = grid_of(cfg.ref)
     g_prev = grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w))
+    interp = args.workload == "interp"
+    if interp:
+        # the neighbouring N-chunks' final latents (seeded stand-ins of the chunk shape)
+        x_before = f32(synth.make_inputs(cfg, 1)["x_init"], dev)
+        x_after = f32(synth.make_inputs(cfg, 2)["x_init"], dev)
+        h.ref_kv_precompute(ref, g_ref)
 
     def step():
-        h.ref_kv_precompute(ref, g_ref)
-        h.boundary_kv_carry(bnd, g_prev)
+        if interp:
+            h.boundary_kv_carry(x_before, g_chunk)
+            h.interp_anchor_kv(x_after, g_chunk, cfg.chunk.frames)
+        else:
+            h.ref_kv_precompute(ref, g_ref)
+            h.boundary_kv_carry(bnd, g_prev)
         x.copy_(x0)
         for k in range(S):
             h.step(x, ts[k], ts[k + 1], g_chunk, audio=audio)
@@ -214,8 +233,17 @@ def main() -> int:
     value = cfg.N * S / ((t1 - t0) / args.steps)
     achieved = attn_flop / (attn_ms * 1e-3) / 1e12
     traffic = _traffic()
+    workload = ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
+                "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
+                "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = reference "
+                "K/V + boundary K/V + 8 denoising steps")
+    if interp:
+        workload = ("interpolation chunk of the base low-res shape: 7800 latent tokens, keys "
+                    "1560 reference + 1560 boundary + 1560 anchor + 7800 chunk, 50 audio tokens, "
+                    "4 blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0; one bench step = "
+                    "boundary K/V + anchor K/V + 8 denoising steps")
     line = {
-        "metric": METRIC,
+        "metric": METRIC_INTERP if interp else METRIC,
         "value": value,
         "unit": "latent tokens/s",
         "n_gpus": 1,
@@ -228,10 +256,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) latents/audio, N(0,1/fan_in) random-init weights)",
         "config": {
-            "workload": ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
-                         "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
-                         "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = reference "
-                         "K/V + boundary K/V + 8 denoising steps"),
+            "workload": workload,
             "tokens_per_step": cfg.N * S,
             "attention_tflops": achieved,
             "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
@@ -247,7 +272,7 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not interp:
         line["cpu_baseline"] = cpu_baseline(cfg, P, inp)
     print(json.dumps(line), flush=True)
     h.close()

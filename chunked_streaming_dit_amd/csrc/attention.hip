@@ -128,6 +128,47 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     else if (t < e3) { si = 2; base = (t - e2) * BKV; }
     else { si = 3; base = (t - e3) * BKV; }
   };
+  // Segment fields by runtime index (read from the kernel arguments; used only when a
+  // walker enters a segment).
+  auto seg_k = [&](int si) { return reinterpret_cast<const char*>(a.seg[si].k); };
+  auto seg_vt = [&](int si) { return reinterpret_cast<const char*>(a.seg[si].vt); };
+  auto seg_cap = [&](int si) { return a.seg[si].cap; };
+  auto seg_n = [&](int si) { return a.seg[si].n; };
+  auto seg_tiles = [&](int si) { return (a.seg[si].n + BKV - 1) / BKV; };
+  // A walker follows one stream of consecutive key tiles: segment si, tiles left in it
+  // (the current one included), and the byte offset of the current tile's first key
+  // row (K) or column (V^T).  Advancing costs a few scalar operations; the segment
+  // fields are looked up only when it enters the next (non-empty) segment.
+  struct Walk {
+    int si, left;
+    const char* kp;  // K rows of the current tile
+    const char* vp;  // V^T columns of the current tile
+    int cap;         // V^T row pitch (keys) of the segment
+  };
+  auto walk_at = [&](int t) {
+    int si, base;
+    locate(t, si, base);
+    Walk w;
+    w.si = si;
+    w.left = seg_tiles(si) - base / BKV;
+    w.kp = seg_k(si) + (size_t)base * a.ldk * SZ;
+    w.vp = seg_vt(si) + (size_t)base * SZ;
+    w.cap = seg_cap(si);
+    return w;
+  };
+  auto walk_next = [&](Walk& w) {
+    w.kp += (size_t)BKV * a.ldk * SZ;
+    w.vp += BKV * SZ;
+    if (--w.left == 0) {
+      do { ++w.si; } while (w.si < a.nseg && seg_tiles(w.si) == 0);
+      if (w.si < a.nseg) {
+        w.left = seg_tiles(w.si);
+        w.kp = seg_k(w.si);
+        w.vp = seg_vt(w.si);
+        w.cap = seg_cap(w.si);
+      }
+    }
+  };
   // Direct-to-LDS loads (global_load_lds_dwordx4): wave instruction g = wave + AW i fills
   // 1 KB of a slot = rows [RP g, RP g + RP); the lane covers row RP g + lane/(64/RP) at
   // chunk position lane % (64/RP), i.e. source chunk swz(row, position).
@@ -146,25 +187,18 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     vrow[i] = RPV * g + lane / (64 / RPV);
     vchk[i] = swz<RBV>(vrow[i], lane % (64 / RPV)) * 16;
   }
-  auto load_k = [&](int t, int slot) {
-    int si, base;
-    locate(t, si, base);
-    const char* kp = reinterpret_cast<const char*>(a.seg[si].k) + (size_t)base * a.ldk * SZ;
+  auto load_k = [&](const Walk& w, int slot) {
     char* dst = ks + slot * KTILE + wave * 1024;
 #pragma unroll
     for (int i = 0; i < NLK; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(kp + koff[i]), (void*)(dst + i * AW * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(w.kp + koff[i]), (void*)(dst + i * AW * 1024), 16, 0, 0);
   };
-  auto load_v = [&](int t, int slot) {
-    int si, base;
-    locate(t, si, base);
-    const unsigned cap = (unsigned)a.seg[si].cap;
-    const char* vp = reinterpret_cast<const char*>(a.seg[si].vt) + (size_t)base * SZ;
+  auto load_v = [&](const Walk& w, int slot) {
     char* dst = vs + slot * VTILE + wave * 1024;
 #pragma unroll
     for (int i = 0; i < NLV; ++i) {
-      const unsigned off = ((unsigned)(head * DH + vrow[i]) * cap) * SZ + vchk[i];
-      __builtin_amdgcn_global_load_lds((const void*)(vp + off), (void*)(dst + i * AW * 1024), 16, 0, 0);
+      const unsigned off = ((unsigned)(head * DH + vrow[i]) * (unsigned)w.cap) * SZ + vchk[i];
+      __builtin_amdgcn_global_load_lds((const void*)(w.vp + off), (void*)(dst + i * AW * 1024), 16, 0, 0);
     }
   };
   // S^T tile from a K slot: 2 blocks of 32 keys x 32 queries.  Lane: query l32,
@@ -207,16 +241,25 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     else if (keep >= NLK || keep >= NLV) wait_vm_lds<(NLK < NLV ? NLK : NLV)>();
     else wait_vm_lds<0>();
   };
+  // Walkers: wk at the next K tile to load, wv at the next V^T tile to load, wc at the
+  // tile being softmaxed; sl = (current tile) % NSLOT.
+  Walk wk, wv, wc;
+  int sl = tb % NSLOT;
   if (total > tb) {
-    load_k(tb, tb % NSLOT);
-    if (total > tb + 1) load_k(tb + 1, (tb + 1) % NSLOT);
-    load_v(tb, tb % NSLOT);
+    wk = walk_at(tb);
+    wv = wk;
+    wc = wk;
+    load_k(wk, sl);
+    walk_next(wk);
+    if (total > tb + 1) { load_k(wk, (sl + 1) % NSLOT); walk_next(wk); }
+    load_v(wv, sl);
+    walk_next(wv);
     int later = 0;
-    if (total > tb + 2) { load_k(tb + 2, (tb + 2) % NSLOT); later += NLK; }
-    if (total > tb + 1) { load_v(tb + 1, (tb + 1) % NSLOT); later += NLV; }
+    if (total > tb + 2) { load_k(wk, (sl + 2) % NSLOT); walk_next(wk); later += NLK; }
+    if (total > tb + 1) { load_v(wv, (sl + 1) % NSLOT); walk_next(wv); later += NLV; }
     wait_keep(later);
     lds_barrier();
-    scores(tb % NSLOT, Sc);
+    scores(sl, Sc);
   }
   // One iteration.  The softmax exponentials / P^T conversion / P V MFMAs of tile t and
   // the score MFMAs of tile t+1 form one branch-free block that the scheduler
@@ -230,20 +273,23 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     // transfers have landed (wait_keep at the end of the previous iteration, or the
     // prologue's wait); the newest ones stay in flight across this barrier.
     lds_barrier();
-    if (has3) load_k(t + 3, (t + 3) % NSLOT);
-    if (has2) load_v(t + 2, (t + 2) % NSLOT);
+    // slots: tile t and t+3 share sl, tile t+1 is sl+1, tile t+2 is sl+2 (mod NSLOT)
+    const int sl1 = sl == NSLOT - 1 ? 0 : sl + 1;
+    const int sl2 = sl1 == NSLOT - 1 ? 0 : sl1 + 1;
+    if (has3) { load_k(wk, sl); walk_next(wk); }
+    if (has2) { load_v(wv, sl2); walk_next(wv); }
 
-    int si, base;
-    locate(t, si, base);
-    const int seg_n = a.seg[si].n;
-    if (base + BKV > seg_n) {  // ragged tail of a segment: mask keys >= n
+    if (wc.left == 1) {  // last tile of its segment: mask keys >= n (ragged tail)
+      const int nk = seg_n(wc.si) - (seg_tiles(wc.si) - 1) * BKV;  // valid keys in this tile
+      if (nk < BKV) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = base + kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-          if (key >= seg_n) S[kb][r] = -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
+            if (key >= nk) S[kb][r] = -INFINITY;
+          }
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -266,8 +312,8 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float ms = m_run * a.scale;
-    const char* sv = vs + (t % NSLOT) * VTILE;
-    const char* sk = ks + ((t + 1) % NSLOT) * KTILE;
+    const char* sv = vs + sl * VTILE;
+    const char* sk = ks + sl1 * KTILE;
     // Softmax of tile t, P V of tile t and the scores of tile t+1, in NU phases.  Unit u
     // = (kb, v) covers keys [32 kb + v*2VE, +2VE) of tile t: VE exponentials per lane
     // (P^T operand elements [v*VE, v*VE+VE) of S[kb]), their row-sum contribution and
@@ -319,6 +365,8 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     }
     // this wave's loads of K tile t+2 and V tile t+1 have landed (this iteration's stay)
     wait_keep((has3 ? NLK : 0) + (has2 ? NLV : 0));
+    walk_next(wc);
+    sl = sl1;
   };
   int t = tb;
   for (; t + 1 < total; t += 2) {
