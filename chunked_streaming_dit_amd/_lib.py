@@ -60,6 +60,7 @@ _SIGS = {
     "boundary_kv_carry": (I, [P, P, DitGrid]),
     "interp_anchor_kv": (I, [P, P, DitGrid, I]),
     "dit_chunk_step": (I, [P, P, P, P, I, DitGrid, Dbl, Dbl, P]),
+    "dit_chunk_step_carry": (I, [P, P, P, P, I, DitGrid, Dbl, Dbl, P]),
     "fm_euler_step": (I, [P, P, Dbl, ctypes.c_longlong, P]),
     "dit_last_error": (ctypes.c_char_p, []),
     "dit_timing_enable": (I, [P, I]),

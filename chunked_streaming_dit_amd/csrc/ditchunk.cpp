@@ -391,8 +391,11 @@ int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_po
   return DIT_OK;
 }
 
-int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
-                   dit_grid chunk, double t, double t_next, float* v_out) {
+namespace {
+
+// One denoising step; with carry, also the boundary by reuse (see dit_chunk_step_carry).
+int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
+               dit_grid chunk, double t, double t_next, float* v_out, bool carry) {
   if (!hd) return fail(DIT_EINVAL, "handle is NULL");
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
@@ -408,6 +411,9 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
   if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
   if (M > 0 && !audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
   if (M > 0 && c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
+  const long long hw = (long long)chunk.h * chunk.w;
+  if (carry && hw > c.max_bnd)
+    return fail(DIT_ESHAPE, "boundary by reuse: frame of %lld tokens > max_bnd %d", hw, c.max_bnd);
   if (!hd->has_ref) return fail(DIT_ESTATE, "dit_chunk_step before ref_kv_precompute");
 
   const int n = (int)nn, D = c.D, F = L.F;
@@ -448,6 +454,14 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
     seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
     int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
     if (rc) return rc;
+    if (carry) {
+      // This block's attention has read its boundary slot; refill it with the last
+      // frame's K (moved from t0 + frames - 1 to t = -1) and V of this step.
+      const int first = (chunk.frames - 1) * (int)hw;
+      const float dt = (float)(-1 - (chunk.t0 + chunk.frames - 1));
+      HIPCHK(boundary_reuse(c.dtype, c.dh, c.H, hd->X(L.kc), hd->X(L.vtc), L.cap_tok, first, (int)hw, dt,
+                            (float)c.rope_theta, hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), L.cap_bnd, s));
+    }
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
     HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
@@ -489,7 +503,23 @@ int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* aud
   e.kind = EPI_EULER; e.bias = hd->W(DIT_W_FIN_B); e.out = x; e.ldo = c.c_p; e.v_out = v_out;
   e.dt = (float)(t_next - t);
   HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->W(DIT_W_FIN_W), D, n, c.c_p, D, e, s));
+  if (carry) {
+    hd->n_bnd = (int)hw;
+    hd->n_anc = 0;
+  }
   return DIT_OK;
+}
+
+}  // namespace
+
+int dit_chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
+                   dit_grid chunk, double t, double t_next, float* v_out) {
+  return chunk_step(hd, x, cond, audio, M, chunk, t, t_next, v_out, false);
+}
+
+int dit_chunk_step_carry(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
+                         dit_grid chunk, double t, double t_next, float* v_out) {
+  return chunk_step(hd, x, cond, audio, M, chunk, t, t_next, v_out, true);
 }
 
 int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_stream) {

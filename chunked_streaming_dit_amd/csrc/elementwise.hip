@@ -284,6 +284,70 @@ hipError_t modulation_t(int D, int L, double t, const void* t1w, const void* t1b
   return hipGetLastError();
 }
 
+// Boundary by reuse: K rows [first, first + n) of a chunk's K (normed, rotated at time
+// t_src) become rows [0, n) of the boundary K, their time-axis pairs turned by dt
+// (= t_dst - t_src; rotations about the same axis add, so this places them at t_dst);
+// rows [n, rows_pad) are zeroed.  One thread per (row, head, rotation pair).
+template <class T, int DH>
+__global__ __launch_bounds__(256) void bnd_reuse_k_kernel(const T* __restrict__ kc, int first, int n,
+                                                          int rows_pad, int H, float dt,
+                                                          float log2_theta, T* __restrict__ kb) {
+  constexpr int NPAIR = DH / 2;
+  const int d_t = DH - 4 * (DH / 6);  // time-axis dims (the first d_t / 2 pairs)
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)rows_pad * H * NPAIR) return;
+  const int p = (int)(i % NPAIR);
+  const int head = (int)((i / NPAIR) % H);
+  const int j = (int)(i / ((long long)NPAIR * H));
+  const int D = H * DH;
+  T* dst = kb + (size_t)j * D + head * DH + 2 * p;
+  if (j >= n) {
+    dst[0] = from_f<T>(0.f);
+    dst[1] = from_f<T>(0.f);
+    return;
+  }
+  const T* src = kc + (size_t)(first + j) * D + head * DH + 2 * p;
+  const float x0 = to_f(src[0]), x1 = to_f(src[1]);
+  if (2 * p < d_t) {
+    const float ang = dt * exp2f(-(2.0f * (float)p / (float)d_t) * log2_theta);
+    float sn, cs;
+    sincosf(ang, &sn, &cs);
+    dst[0] = from_f<T>(x0 * cs - x1 * sn);
+    dst[1] = from_f<T>(x0 * sn + x1 * cs);
+  } else {
+    dst[0] = src[0];
+    dst[1] = src[1];
+  }
+}
+
+// Stored column of key o in the V^T layout: bf16 keeps each aligned group of 16 keys
+// in MFMA operand order (key offset q at 8 ((q % 8) / 4) + 4 (q / 8) + q % 4); fp32 is
+// in natural order.
+template <class T>
+__device__ __forceinline__ int vt_col(int o) {
+  if constexpr (sizeof(T) == 2) {
+    const int q = o & 15;
+    return (o & ~15) + 8 * ((q & 7) >> 2) + 4 * (q >> 3) + (q & 3);
+  } else {
+    return o;
+  }
+}
+
+// V^T columns of keys [first, first + n) of a chunk (row pitch cap_src) become the
+// columns of keys [0, n) of the boundary V^T (pitch cap_dst); keys [n, cols_pad) are
+// zeroed.  One thread per (dim, key).
+template <class T>
+__global__ __launch_bounds__(256) void bnd_reuse_v_kernel(const T* __restrict__ vt, int cap_src, int first,
+                                                          int n, int cols_pad, int D, T* __restrict__ vb,
+                                                          int cap_dst) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)D * cols_pad) return;
+  const int j = (int)(i % cols_pad);
+  const int d = (int)(i / cols_pad);
+  vb[(size_t)d * cap_dst + vt_col<T>(j)] =
+      j < n ? vt[(size_t)d * cap_src + vt_col<T>(first + j)] : from_f<T>(0.f);
+}
+
 }  // namespace
 
 hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shift,
@@ -353,6 +417,33 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
                               fmod_out, s);
   return modulation_t<float>(D, L, t, t1w, t1b, t2w, t2b, modw, modb, fmodw, fmodb, tmp, mod_out,
                              fmod_out, s);
+}
+
+hipError_t boundary_reuse(int dtype, int dh, int H, const void* kc, const void* vtc, int cap_src, int first,
+                          int n, float dt, float theta, void* kb, void* vtb, int cap_dst, hipStream_t s) {
+  const int rows_pad = (n + 63) / 64 * 64;
+  if (n <= 0 || rows_pad > cap_dst) return hipErrorInvalidValue;
+  const int D = H * dh;
+  const float l2t = log2f(theta);
+  const long long nk = (long long)rows_pad * H * (dh / 2);
+  const long long nv = (long long)D * rows_pad;
+  dim3 gk((unsigned)((nk + 255) / 256)), gv((unsigned)((nv + 255) / 256)), b(256);
+  if (dtype == BF16 && dh == 128) {
+    bnd_reuse_k_kernel<bf16, 128><<<gk, b, 0, s>>>((const bf16*)kc, first, n, rows_pad, H, dt, l2t, (bf16*)kb);
+    bnd_reuse_v_kernel<bf16><<<gv, b, 0, s>>>((const bf16*)vtc, cap_src, first, n, rows_pad, D, (bf16*)vtb, cap_dst);
+  } else if (dtype == BF16 && dh == 64) {
+    bnd_reuse_k_kernel<bf16, 64><<<gk, b, 0, s>>>((const bf16*)kc, first, n, rows_pad, H, dt, l2t, (bf16*)kb);
+    bnd_reuse_v_kernel<bf16><<<gv, b, 0, s>>>((const bf16*)vtc, cap_src, first, n, rows_pad, D, (bf16*)vtb, cap_dst);
+  } else if (dtype == F32 && dh == 128) {
+    bnd_reuse_k_kernel<float, 128><<<gk, b, 0, s>>>((const float*)kc, first, n, rows_pad, H, dt, l2t, (float*)kb);
+    bnd_reuse_v_kernel<float><<<gv, b, 0, s>>>((const float*)vtc, cap_src, first, n, rows_pad, D, (float*)vtb, cap_dst);
+  } else if (dtype == F32 && dh == 64) {
+    bnd_reuse_k_kernel<float, 64><<<gk, b, 0, s>>>((const float*)kc, first, n, rows_pad, H, dt, l2t, (float*)kb);
+    bnd_reuse_v_kernel<float><<<gv, b, 0, s>>>((const float*)vtc, cap_src, first, n, rows_pad, D, (float*)vtb, cap_dst);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dit

@@ -95,6 +95,13 @@ hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* c
 // x[i] += dt * v[i]
 hipError_t euler(float* x, const float* v, float dt, long long n, hipStream_t s);
 
+// Boundary by reuse: keys [first, first + n) of a chunk's K [*, H*dh] and V^T
+// [H*dh, cap_src] (layouts of qknorm_rope) become keys [0, n) of a boundary segment
+// (kb [cap_dst, H*dh], vtb [H*dh, cap_dst]), K's time-axis RoPE pairs turned by dt;
+// keys [n, round_up(n, 64)) are zeroed.
+hipError_t boundary_reuse(int dtype, int dh, int H, const void* kc, const void* vtc, int cap_src, int first,
+                          int n, float dt, float theta, void* kb, void* vtb, int cap_dst, hipStream_t s);
+
 // Timestep conditioning c = SiLU(W2 SiLU(W1 phi(t) + b1) + b2) and per-block modulation
 // mod[l] = Wmod_l c + bmod_l ([6D]) and final fmod = Wf c + bf ([2D]).
 // tmp: fp32 scratch of 2*D floats.

@@ -151,14 +151,17 @@ class DitChunk:
 
     def step(self, x: torch.Tensor, t: float, t_next: float, g: C.DitGrid,
              cond: Optional[torch.Tensor] = None, audio: Optional[torch.Tensor] = None,
-             v_out: Optional[torch.Tensor] = None) -> None:
+             v_out: Optional[torch.Tensor] = None, carry_boundary: bool = False) -> None:
+        """One denoising step; carry_boundary: the chunk's last step, which also leaves its
+        last frame's K/V as the next boundary (dit_chunk_step_carry)."""
         _dev(x, "x", torch.float32)
         _dev(cond, "cond", torch.float32)
         _dev(audio, "audio", torch.float32)
         _dev(v_out, "v_out", torch.float32)
         M = 0 if audio is None else audio.shape[0]
-        C.check(C.lib().dit_chunk_step(self._h, x.data_ptr(), _ptr(cond), _ptr(audio), M, g,
-                                       float(t), float(t_next), _ptr(v_out)))
+        fn = C.lib().dit_chunk_step_carry if carry_boundary else C.lib().dit_chunk_step
+        C.check(fn(self._h, x.data_ptr(), _ptr(cond), _ptr(audio), M, g, float(t), float(t_next),
+                   _ptr(v_out)))
 
     def timing_enable(self, on: bool = True) -> None:
         C.check(C.lib().dit_timing_enable(self._h, 1 if on else 0))

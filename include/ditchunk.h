@@ -20,6 +20,8 @@
  *   interp_anchor_kv    once per interpolation chunk (see below; cleared for
  *                       ordinary chunks);
  *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
+ *   dit_chunk_step_carry  alternatively the chunk's last step, which also leaves
+ *                       that step's last-frame K/V as the next boundary;
  *   fm_euler_step       the bare Euler update, for callers with their own velocity.
  *
  * The block (readings of the pages, which give no internals): tokens are
@@ -217,6 +219,21 @@ int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_po
  * ESTATE (no reference yet). */
 int dit_chunk_step(dit_handle* h, float* x, const float* cond, const float* audio, int M,
                    dit_grid chunk, double t, double t_next, float* v_out);
+
+/* The last denoising step of a chunk, with the boundary carried by reuse: the same
+ * step as dit_chunk_step, and, block by block right after that block's
+ * self-attention, the per-block K and V that this step forms for the chunk's last
+ * frame (frame chunk.frames-1, h*w tokens) replace the boundary K/V, K turned from
+ * t = chunk.t0 + frames - 1 to t = -1 (a rotation of the RoPE time pairs; rotations
+ * about the same axis add).  The next chunk then needs no boundary_kv_carry pass.
+ * Any anchor is cleared.  This is the alternative to boundary_kv_carry's clean t = 0
+ * pass (HeyGen, "Avatar inference at scale": the boundary data of the previous segment
+ * condition the next chunk, section "The underlying model architecture"; the pages do
+ * not say how it is formed): the K/V come from the final step's input latent and
+ * timestep instead, at the cost of a K/V copy instead of a forward pass.
+ * Errors: as dit_chunk_step, and ESHAPE if h*w > max_bnd. */
+int dit_chunk_step_carry(dit_handle* h, float* x, const float* cond, const float* audio, int M,
+                         dit_grid chunk, double t, double t_next, float* v_out);
 
 /* x[i] += (float)dt * v[i] for i < n (fp32, device) on hip_stream.
  * Errors: EINVAL (null pointer with n > 0, non-finite dt, n < 0). */

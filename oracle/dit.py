@@ -37,6 +37,7 @@ __all__ = [
     "context_pass", "dit_velocity", "euler", "schedule", "chunk_denoise",
     "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone", "velocity_rows",
     "first_frame", "anchor_context", "interp_stream",
+    "bnd_reuse_context", "stream_reuse",
 ]
 
 Weights = Dict[str, np.ndarray]
@@ -350,6 +351,40 @@ def bnd_context(P: Weights, cfg, ref_kv, bnd: np.ndarray, h: int, w: int):
     return context_pass(P, cfg, bnd, pos, [[ref_kv[l]] for l in range(cfg.L)])
 
 
+def bnd_reuse_context(P: Weights, cfg, x: np.ndarray, t: float, pos: np.ndarray,
+                      ctx: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]],
+                      audio: Optional[np.ndarray], grid, cond: Optional[np.ndarray] = None):
+    """Boundary K/V by reuse [arch, loop]: the per-block K and V that a chunk's final
+    denoising step (input latent x at time t, context ctx) forms for the tokens of its
+    last frame, with K at positions (-1, y, x).
+
+    reading: the alternative to bnd_context.  The pages say the next chunk is
+    conditioned on the previous chunk's boundary frames without saying how their K/V
+    are formed; here they are not recomputed by a clean pass at t = 0 but taken from
+    the last step's own forward pass (input latent and timestep of that step), K
+    placed at the boundary's time position.  Block l's K/V are formed from that block's
+    input states, exactly as block_forward forms the keys of those rows."""
+    g = grid
+    D, H, eps = cfg.D, cfg.H, cfg.eps
+    c = conditioning(P, t)
+    h = linear(patch_input(x, cond, cfg.C_c), W(P, "pe.w"), W(P, "pe.b"))
+    hw = g.h * g.w
+    rows = slice((g.frames - 1) * hw, g.frames * hw)
+    ang_b = rope_angles(grid_positions(-1, 1, g.h, g.w), cfg.dh, cfg.rope_theta)
+    out = []
+    for l in range(cfg.L):
+        mod = block_modulation(P, l, c)
+        p = f"blk{l}."
+        u = modulate(rms_norm(h[rows], eps), mod[0], mod[1])
+        qkv = linear(u, W(P, p + "qkv.w"), W(P, p + "qkv.b"))
+        k = rope_apply(qk_norm(_heads(qkv[:, D:2 * D], H), W(P, p + "gk"), eps), ang_b)
+        v = _heads(qkv[:, 2 * D:], H)
+        out.append((k, v))
+        if l + 1 < cfg.L:  # the next block's input states (the last block's output is unused)
+            h, _, _ = block_forward(P, cfg, l, h, mod, pos, list(ctx[l]), audio)
+    return out
+
+
 def anchor_context(P: Weights, cfg, ref_kv, bnd_kv, anchor: np.ndarray, h: int, w: int,
                    t_pos: int):
     """Interpolation-anchor K/V per block [bnd]: one frame at t = t_pos, seeing the
@@ -386,6 +421,32 @@ def stream(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.nda
         x = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond)
         outs.append(x)
         prev = x
+    return outs
+
+
+def stream_reuse(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.ndarray):
+    """stream() with the boundary carried by reuse: chunk c > 0 is conditioned on the K/V
+    that chunk c-1's last denoising step formed for its last frame (bnd_reuse_context).
+    Returns the final latent of every chunk."""
+    g = cfg.chunk
+    pos = grid_positions(0, g.frames, g.h, g.w)
+    ref_kv = ref_context(P, cfg, ref, cfg.ref)
+    ts = schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    outs = []
+    carried = None
+    for inp in chunks:
+        ctx = [[ref_kv[l]] + ([carried[l]] if carried is not None else []) for l in range(cfg.L)]
+        cond = None
+        if cfg.C_c > 0:
+            cond = (upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w)
+                    if cfg.cond_up == 2 else inp["cond"])
+        audio = inp.get("audio")
+        x = np.asarray(inp["x_init"], dtype=np.float64)
+        for k in range(cfg.steps):
+            if k == cfg.steps - 1:
+                carried = bnd_reuse_context(P, cfg, x, ts[k], pos, ctx, audio, g, cond)
+            x = euler(x, dit_velocity(P, cfg, x, ts[k], pos, ctx, audio, cond), ts[k], ts[k + 1])
+        outs.append(x)
     return outs
 
 

@@ -116,6 +116,13 @@ def test_call_order_and_shape_errors():
     assert lib.boundary_kv_carry(h, FAKE, C.DitGrid(0, 1, 8, 8)) == C.DIT_ESHAPE  # 64 > max_bnd 32
     assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 2, 4, 8)) == C.DIT_EINVAL
     assert lib.boundary_kv_carry(h, None, C.DitGrid(0, 0, 0, 0)) == C.DIT_OK      # clear: no launch
+    # the boundary-carrying last step: the step's checks, and the frame must fit max_bnd
+    g32 = C.DitGrid(0, 4, 4, 8)  # 32 tokens per frame: fits max_bnd
+    assert lib.dit_chunk_step_carry(h, FAKE, None, FAKE, 16, g32, 0.5, 0.45, None) == C.DIT_ESTATE
+    assert lib.dit_chunk_step_carry(h, None, None, None, 0, g, 0.5, 0.45, None) == C.DIT_EINVAL
+    assert lib.dit_chunk_step_carry(h, FAKE, None, None, 0, C.DitGrid(0, 3, 8, 8), 0.5, 0.4, None) == C.DIT_ESHAPE
+    assert lib.dit_chunk_step_carry(h, FAKE, None, None, 0, C.DitGrid(0, 1, 8, 8), 0.5, 0.4, None) == C.DIT_ESHAPE
+    assert "max_bnd" in C.last_error()  # 64 tokens per frame > max_bnd 32
     # interpolation anchor: same checks as the boundary
     assert lib.interp_anchor_kv(h, FAKE, C.DitGrid(0, 2, 4, 8), 2) == C.DIT_ESTATE
     assert "ref_kv_precompute" in C.last_error()

@@ -156,6 +156,38 @@ def test_interp_chunk_full_shape_one_block_sampled_rows():
     assert err <= TOL["bf16"], err
 
 
+def test_boundary_by_reuse_full_shape_one_block_sampled_rows():
+    """The base-chunk shape with one block: chunk 0's only step carries its last frame's
+    K/V (1560 keys) forward; chunk 1's first-step velocity on sampled rows against the
+    oracle with that boundary."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(synth.CONFIGS[2], L=1, cid=53, steps=1, bnd=None)
+    P = synth.make_weights(cfg, threads=16)
+    c0, c1 = synth.make_inputs(cfg, 0), synth.make_inputs(cfg, 1)
+    g = cfg.chunk
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(c0["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+    x0 = f32(c0["x_init"], dev)
+    h.step(x0, cfg.t_start, cfg.t_end, grid_of(g), audio=f32(c0["audio"], dev), carry_boundary=True)
+    x1 = f32(c1["x_init"], dev)
+    v = torch.empty_like(x1)
+    h.step(x1, cfg.t_start, cfg.t_end, grid_of(g), audio=f32(c1["audio"], dev), v_out=v)
+    torch.cuda.synchronize()
+    vg = to_np(v)
+    h.close()
+    pos = O.grid_positions(0, g.frames, g.h, g.w)
+    ref_kv = O.ref_context(P, cfg, c0["ref"], cfg.ref)
+    carried = O.bnd_reuse_context(P, cfg, c0["x_init"], cfg.t_start, pos, [[ref_kv[0]]], c0["audio"], g)
+    rows = _sample_rows(cfg.N, 53)
+    vo = O.velocity_rows(P, cfg, c1["x_init"], cfg.t_start, pos, [[ref_kv[0], carried[0]]], c1["audio"], rows)
+    err = rel_err(vg[rows], vo)
+    print(f"boundary by reuse, one-block full shape, {len(rows)} sampled rows: v err {err:.2e}")
+    assert err <= TOL["bf16"], err
+
+
 def _device_weights(cfg, dev, seed):
     """Seeded N(0, 1/fan_in) weights drawn on the device (no host copy of 10+ GB)."""
     gen = torch.Generator(device=dev)

@@ -148,6 +148,35 @@ def test_mini_interp_stream(base):
             assert err <= tol, (name, k, err)
 
 
+@pytest.mark.parametrize("base", ["bf16", "f32"])
+def test_mini_stream_boundary_by_reuse(base):
+    """Three chunks, each chunk's last step carrying its last frame's K/V forward as the
+    next boundary (dit_chunk_step_carry), against oracle.stream_reuse."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(MINI_BF16 if base == "bf16" else MINI_F32, cid=209 if base == "bf16" else 210,
+                              bnd=None, n_chunks=3)
+    P = synth.make_weights(cfg)
+    chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
+    want = O.stream_reuse(P, cfg, chunks, chunks[0]["ref"])
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(chunks[0]["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+    g = cfg.chunk
+    ts = O.schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    tol = TOL[cfg.dtype]
+    for c, inp in enumerate(chunks):
+        x = f32(inp["x_init"], dev)
+        for k in range(cfg.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=f32(inp["audio"], dev),
+                   carry_boundary=k == cfg.steps - 1)
+        torch.cuda.synchronize()
+        err = rel_err(x.cpu().numpy() - inp["x_init"], want[c] - inp["x_init"])
+        print(f"chunk {c}: dx err {err:.2e}")
+        assert err <= tol, (c, err)
+
+
 def test_config2_full_size_first_step():
     """The base low-res chunk at its full shape (7800 tokens, keys 1560|1560|7800,
     4 blocks, hidden 1536, 12x128 heads, 50 audio tokens): the first denoising step."""

@@ -467,6 +467,63 @@ def test_interp_stream_schedule_and_anchor_frames(tiny):
         assert np.abs(x - i_out[k]).max() == 0.0
 
 
+# ---------------------------------------------------------------- boundary by reuse
+
+
+def test_bnd_reuse_special_case_equals_clean_boundary_pass(tiny):
+    """A one-frame chunk at t0 = 0 whose reference sits one frame earlier (t = -1), run at
+    t = 0 without audio, has the relative positions, visibility, timestep and inputs of a
+    boundary context pass (frame at -1, reference at -2): its reused K/V equal
+    bnd_context's."""
+    P, inp = tiny
+    cfg = TINY
+    g = cfg.chunk
+    frame = inp["bnd"]
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)                       # reference at t = -2
+    want = O.bnd_context(P, cfg, ref_kv, frame, g.h, g.w)                     # frame at t = -1
+    ref_m1 = O.ref_context(P, cfg, inp["ref"], Grid(-1, 1, cfg.ref.h, cfg.ref.w))
+    g1 = Grid(0, 1, g.h, g.w)
+    got = O.bnd_reuse_context(P, cfg, frame, 0.0, _pos(g1), [[ref_m1[l]] for l in range(cfg.L)], None, g1)
+    for (k1, v1), (k2, v2) in zip(got, want):
+        assert np.abs(k1 - k2).max() <= 1e-12 * np.abs(k2).max()
+        assert np.abs(v1 - v2).max() <= 1e-12 * np.abs(v2).max()
+
+
+def test_bnd_reuse_rows_and_time_shift(tiny):
+    """Multi-frame chunk: the reused K/V are the last frame's rows of the keys and values
+    each block forms in the step's own forward pass, K turned by -frames on the time axis
+    (rope_apply with the angles of a (-frames, 0, 0) offset)."""
+    P, inp = tiny
+    cfg = TINY
+    g = cfg.chunk
+    _, _, ctx = _ctx(P, cfg, inp)
+    t = 0.37
+    got = O.bnd_reuse_context(P, cfg, inp["x_init"], t, _pos(g), ctx, inp["audio"], g)
+    c = O.conditioning(P, t)
+    h = O.linear(O.patch_input(inp["x_init"], None, cfg.C_c), O.W(P, "pe.w"), O.W(P, "pe.b"))
+    hw = g.h * g.w
+    shift = O.rope_angles(np.tile([[-g.frames, 0, 0]], (hw, 1)), cfg.dh, cfg.rope_theta)
+    for l in range(cfg.L):
+        mod = O.block_modulation(P, l, c)
+        h_next, k, v = O.block_forward(P, cfg, l, h, mod, _pos(g), list(ctx[l]), inp["audio"])
+        k_last = O.rope_apply(k[(g.frames - 1) * hw:], shift)
+        assert np.abs(got[l][0] - k_last).max() <= 1e-12 * np.abs(k_last).max()
+        assert np.abs(got[l][1] - v[(g.frames - 1) * hw:]).max() == 0.0
+        h = h_next
+
+
+def test_stream_reuse_first_chunk_and_carry(tiny):
+    """stream_reuse: chunk 0 equals stream()'s; chunk 1 is conditioned on the K/V of chunk
+    0's last step (not on a clean pass), so it differs from stream()'s chunk 1."""
+    P, _ = tiny
+    cfg = dataclasses.replace(TINY, bnd=None, steps=2)
+    chunks = [synth.make_inputs(TINY, c) for c in range(2)]
+    a = O.stream_reuse(P, cfg, chunks, chunks[0]["ref"])
+    b = O.stream(P, cfg, chunks, chunks[0]["ref"])
+    assert np.abs(a[0] - b[0]).max() == 0.0
+    assert np.abs(a[1] - b[1]).max() > 1e-6 * np.abs(b[1]).max()
+
+
 def test_p11_context_key_permutation_invariance(tiny):
     P, inp = tiny
     cfg = TINY
