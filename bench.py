@@ -22,6 +22,10 @@ reference pass runs once, outside the timed region, as it does once per request.
 --workload reuse times N-chunk jobs whose boundary is carried by reuse: 8 steps, the
 last of which leaves its last frame's K/V as the next job's boundary (no boundary
 pass); the reference pass again runs once, outside the timed region.
+--workload sr / sr1 time super-resolution chunk jobs (5x60x104 = 31200 latent tokens
+conditioned on the nearest-2x upsample of a 5x30x52 latent, keys 6240 reference + 6240
+boundary + 31200 chunk, 2 blocks, no audio): the boundary pass and 4 Euler steps (sr) or
+a single step 1 -> 0 (sr1); the reference pass runs once, outside the timed region.
 """
 from __future__ import annotations
 
@@ -39,6 +43,10 @@ if ROOT not in sys.path:
 METRIC = "DiT chunk-step latent tokens/sec and attention TFLOP/s (% bf16 MFMA peak), 1 GPU"
 METRIC_INTERP = ("DiT interpolation-chunk latent tokens/sec and attention TFLOP/s "
                  "(% bf16 MFMA peak), 1 GPU")
+METRIC_SR = ("DiT super-resolution chunk latent tokens/sec and attention TFLOP/s "
+             "(% bf16 MFMA peak), 1 GPU")
+METRIC_SR1 = ("DiT single-step super-resolution chunk latent tokens/sec and attention TFLOP/s "
+              "(% bf16 MFMA peak), 1 GPU")
 METRIC_REUSE = ("DiT chunk-step latent tokens/sec, boundary carried by reuse, and attention "
                 "TFLOP/s (% bf16 MFMA peak), 1 GPU")
 PEAK_BF16_TFLOPS = 2500.0
@@ -156,7 +164,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["base", "interp", "reuse"], default="base",
+    ap.add_argument("--workload", choices=["base", "interp", "reuse", "sr", "sr1"], default="base",
                     help="base: one N-chunk job (default); interp: one interpolation-chunk job; "
                          "reuse: one N-chunk job with the boundary carried by reuse")
     ap.add_argument("--copy-probe", action="store_true",
@@ -186,7 +194,8 @@ def main() -> int:
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
 
     dev = torch.device("cuda", 0)
-    cfg = synth.CONFIGS[2]
+    sr = args.workload in ("sr", "sr1")
+    cfg = synth.CONFIGS[4 if sr else 2]
     P = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg, 0)
     W = upload_weights(P, cfg.dtype, dev)
@@ -194,15 +203,18 @@ def main() -> int:
     ref = f32(inp["ref"], dev)
     bnd = f32(inp["bnd"], dev)
     x0 = f32(inp["x_init"], dev)
-    audio = f32(inp["audio"], dev)
+    audio = f32(inp["audio"], dev) if cfg.M else None
+    cond = f32(inp["cond_lr"], dev) if sr else None
     x = torch.empty_like(x0)
-    S = cfg.steps
+    S = 1 if args.workload == "sr1" else cfg.steps
     ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S for k in range(S + 1)]
     g_chunk = grid_of(cfg.chunk)
     g_ref = grid_of(cfg.ref)
     g_prev = grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w))
     interp = args.workload == "interp"
     reuse = args.workload == "reuse"
+    if sr:
+        h.ref_kv_precompute(ref, g_ref)
     if reuse:
         h.ref_kv_precompute(ref, g_ref)
         h.boundary_kv_carry(bnd, g_prev)  # the first job's boundary; later ones are carried
@@ -216,12 +228,15 @@ def main() -> int:
         if interp:
             h.boundary_kv_carry(x_before, g_chunk)
             h.interp_anchor_kv(x_after, g_chunk, cfg.chunk.frames)
+        elif sr:
+            h.boundary_kv_carry(bnd, g_prev)
         elif not reuse:
             h.ref_kv_precompute(ref, g_ref)
             h.boundary_kv_carry(bnd, g_prev)
         x.copy_(x0)
         for k in range(S):
-            h.step(x, ts[k], ts[k + 1], g_chunk, audio=audio, carry_boundary=reuse and k == S - 1)
+            h.step(x, ts[k], ts[k + 1], g_chunk, cond=cond, audio=audio,
+                   carry_boundary=reuse and k == S - 1)
 
     for _ in range(args.warmup):
         step()
@@ -257,8 +272,21 @@ def main() -> int:
                     "1560 reference + 1560 boundary + 1560 anchor + 7800 chunk, 50 audio tokens, "
                     "4 blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0; one bench step = "
                     "boundary K/V + anchor K/V + 8 denoising steps")
+    if sr:
+        workload = ("super-resolution chunk: 5x60x104 = 31200 latent tokens conditioned on the "
+                    "nearest-2x upsample of a 5x30x52 latent (64 + 64 input channels), keys 6240 "
+                    "reference + 6240 boundary + 31200 chunk, no audio, 2 DiT blocks, hidden 1536, "
+                    f"12 heads x 128, MLP 4x, {S} Euler step{'s' if S > 1 else ''} 1 -> 0; one bench "
+                    f"step = boundary K/V + {S} denoising step{'s' if S > 1 else ''}")
+    metric = METRIC
+    if interp:
+        metric = METRIC_INTERP
+    elif reuse:
+        metric = METRIC_REUSE
+    elif sr:
+        metric = METRIC_SR1 if S == 1 else METRIC_SR
     line = {
-        "metric": METRIC_INTERP if interp else (METRIC_REUSE if reuse else METRIC),
+        "metric": metric,
         "value": value,
         "unit": "latent tokens/s",
         "n_gpus": 1,
@@ -287,7 +315,7 @@ def main() -> int:
             "traffic": traffic,
         },
     }
-    if not args.no_cpu_baseline and not interp and not reuse:
+    if not args.no_cpu_baseline and args.workload == "base":
         line["cpu_baseline"] = cpu_baseline(cfg, P, inp)
     print(json.dumps(line), flush=True)
     h.close()

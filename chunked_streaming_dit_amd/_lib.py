@@ -73,6 +73,7 @@ _SIGS = {
                            ctypes.POINTER(I), ctypes.POINTER(I), I, P, I, P, P]),
     "ditk_modulation": (I, [I, I, I, Dbl, ctypes.POINTER(P), P, P, P, P]),
     "ditk_patch_input": (I, [I, P, I, I, P, I, I, DitGrid, P, P]),
+    "ditk_patch_embed": (I, [P, I, I, P, I, I, DitGrid, P, P, P, I, P]),
 }
 EXPORTS = tuple(_SIGS)
 

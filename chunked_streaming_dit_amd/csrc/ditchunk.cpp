@@ -214,6 +214,25 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
   return DIT_OK;
 }
 
+// Patch embed into h [n, D] (fp32): the tokens' input rows [x || cond'] (cond' zero,
+// per token, or the nearest-2x upsample, by cond_mode) times W_pe, plus bias.  The
+// fused kernel assembles the rows inside its operand loads; shapes it does not take
+// (fp32 weights, odd widths) go through the assembled input matrix and a GEMM.
+int embed(dit_handle* hd, const float* x, int n, const float* cond, int cond_mode, RopeGrid g, float* h) {
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  if (patch_embed_fits(c.dtype, c.c_p, c.c_c, c.D)) {
+    HIPCHK(patch_embed(x, n, c.c_p, cond, c.c_c, cond_mode, g, hd->W(DIT_W_PE_W), hd->W(DIT_W_PE_B), h,
+                       c.D, hd->stream));
+    return DIT_OK;
+  }
+  HIPCHK(patch_input(c.dtype, x, n, c.c_p, cond, c.c_c, cond_mode, g, hd->X(L.xin), hd->stream));
+  GemmEpi e{};
+  e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = c.D;
+  HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, c.D, L.C_in, e, hd->stream));
+  return DIT_OK;
+}
+
 // One context pass (reference, boundary or interpolation anchor) at t = 0: writes K
 // (normed, rotated) and V of every block into kdst[l] / vdst[l] (capacity cap).  The
 // tokens attend to the earlier context segments and themselves: nprior 0 (reference:
@@ -231,11 +250,9 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
   HIPCHK(modulation(c.dtype, D, c.L, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
                     hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
                     hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
-  HIPCHK(patch_input(c.dtype, z, n, c.c_p, nullptr, c.c_c, 0, g, hd->X(L.xin), s));
   float* h = hd->X<float>(L.h);
+  if (const int rc = embed(hd, z, n, nullptr, 0, g, h)) return rc;
   GemmEpi e{};
-  e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = D;
-  HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, D, L.C_in, e, s));
   for (int l = 0; l < c.L; ++l) {
     const float* m = mod + (size_t)l * 6 * D;
     const bool last = l == c.L - 1;
@@ -426,14 +443,12 @@ int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, 
   HIPCHK(modulation(c.dtype, D, c.L, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
                     hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
                     hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
-  HIPCHK(patch_input(c.dtype, x, n, c.c_p, cond, c.c_c, c.c_c ? c.cond_up : 0, g, hd->X(L.xin), s));
   const bool cross = M > 0 && c.d_a > 0;
   if (cross)
     HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g, hd->X(L.ain), s));
   float* h = hd->X<float>(L.h);
+  if (const int rc = embed(hd, x, n, cond, c.c_c ? c.cond_up : 0, g, h)) return rc;
   GemmEpi e{};
-  e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = D;
-  HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, D, L.C_in, e, s));
   const char* big = hd->X<char>(L.big);
   for (int l = 0; l < c.L; ++l) {
     const float* m = mod + (size_t)l * 6 * D;

@@ -366,6 +366,138 @@ hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int
   return hipGetLastError();
 }
 
+
+// Patch embed with the input assembly fused into the A-operand loads:
+// out[n, N] (fp32) = [x || cond'] W^T + b, where cond' is zero (mode 0), cond per token
+// (mode 1), or the nearest-2x upsample of a half-resolution cond (mode 2: token (f, y, x)
+// channel 4c + 2dy + dx takes half-resolution token (f, y/2, x/2) channel 4c + 2(y%2) +
+// (x%2)).  K = c_p + c_c is small (64 or 128), so the kernel is bound by its HBM
+// traffic (x, cond, out); assembling the bf16 A tile from the fp32 sources in registers
+// saves writing and re-reading the [n, K] input matrix.  Tile 128 x 256, 8 waves (2 x 4)
+// as in gemm_lds_kernel, one 64-wide K stage at a time: the lanes convert 8 channels
+// each into a 16-byte chunk written to the swizzled LDS row; W rows arrive by
+// direct-to-LDS loads.  Rows past n repeat the last token (their outputs are not stored).
+constexpr int PE_BM = 128, PE_BN = 256;
+
+__global__ __launch_bounds__(LDS_THREADS) void patch_embed_kernel(
+    const float* __restrict__ x, int n, int c_p, const float* __restrict__ cond, int c_c, int mode,
+    RopeGrid g, const bf16* __restrict__ W, int N, GemmEpi e) {
+  typedef bf16x8 V;
+  constexpr int BM = PE_BM, BN = PE_BN;
+  constexpr int NW = LDS_WM * LDS_WN;
+  constexpr int WM = BM / LDS_WM, WN = BN / LDS_WN;
+  constexpr int MB = WM / 32, NB = WN / 32;
+  constexpr int NLW = BN / (8 * NW);        // W load instructions per wave per stage
+  constexpr int ACH = BM * 8 / LDS_THREADS;  // A chunks (8 channels) per thread per stage
+  __shared__ __attribute__((aligned(1024))) char smem[(BM + BN) * 128];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / LDS_WN, wn = wave % LDS_WN;
+  const int l32 = lane & 31, lg = lane >> 5;
+  const int K = c_p + c_c;
+  const int num_m = (n + BM - 1) / BM, num_n = N / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, num_m, num_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // A chunk i of this thread: tile row r = c / 8, channels 8 (c % 8) of the stage; the
+  // x half reads token xtok, the cond half token ctok (half-resolution in mode 2) at
+  // channel offset cofs.
+  int arow[ACH], xtok[ACH], ctok[ACH], cofs[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int c = tid + LDS_THREADS * i;
+    arow[i] = c >> 3;
+    const int tok = min(m0 + arow[i], n - 1);
+    xtok[i] = tok;
+    ctok[i] = tok;
+    cofs[i] = 0;
+    if (mode == 2) {
+      const int hw = g.h * g.w, f = tok / hw, rem = tok - f * hw;
+      const int y = rem / g.w, xx = rem - y * g.w;
+      ctok[i] = (f * (g.h / 2) + y / 2) * (g.w / 2) + xx / 2;
+      cofs[i] = 2 * (y & 1) + (xx & 1);
+    }
+  }
+  const int lsub = lane >> 3;
+  unsigned woff[NLW];
+#pragma unroll
+  for (int j = 0; j < NLW; ++j) {
+    const int r = 8 * (NW * j + wave) + lsub;
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    woff[j] = (unsigned)(min(n0 + r, N - 1) * K + chunk * 8) * 2u;
+  }
+
+  EpiCols<NB, EPI_F32> cols;
+  epi_cols_load<bf16, NB, EPI_F32>(cols, n0 + wn * WN, lg, N, e);
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int xs = (l32 >> 1) & 7;
+  const int a_base = (wm * WM + l32) * 128;
+  const int w_base = (BM + wn * WN + l32) * 128;
+  const char* Wb = reinterpret_cast<const char*>(W);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    if (k0) __syncthreads();  // the previous stage's fragments have been read
+    {
+      char* dst = smem + BM * 128 + wave * 8 * 128;
+#pragma unroll
+      for (int j = 0; j < NLW; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(Wb + (size_t)k0 * 2 + woff[j]),
+                                         (void*)(dst + j * NW * 8 * 128), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int cc = (tid + LDS_THREADS * i) & 7;
+      const int ch = k0 + 8 * cc;  // first of the 8 channels (c_p, c_c are multiples of 8)
+      f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+      if (ch < c_p) {
+        const float* p = x + (size_t)xtok[i] * c_p + ch;
+        v0 = *reinterpret_cast<const f32x4*>(p);
+        v1 = *reinterpret_cast<const f32x4*>(p + 4);
+      } else if (mode == 1) {
+        const float* p = cond + (size_t)ctok[i] * c_c + (ch - c_p);
+        v0 = *reinterpret_cast<const f32x4*>(p);
+        v1 = *reinterpret_cast<const f32x4*>(p + 4);
+      } else if (mode == 2) {
+        const float* p = cond + (size_t)ctok[i] * c_c + (ch - c_p) + cofs[i];
+        const float a = p[0], b = p[4];
+        v0 = f32x4{a, a, a, a};
+        v1 = f32x4{b, b, b, b};
+      }
+      V h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = (bf16)v0[q];
+        h[4 + q] = (bf16)v1[q];
+      }
+      const int r = arow[i];
+      st16(smem + r * 128 + ((cc ^ ((r >> 1) & 7)) << 4), __builtin_bit_cast(u32x4, h));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int coff = ((2 * s + lg) ^ xs) << 4;
+      V af[MB], wf[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) af[i] = as_vec<V>(ld16(smem + a_base + i * 32 * 128 + coff));
+#pragma unroll
+      for (int j = 0; j < NB; ++j) wf[j] = as_vec<V>(ld16(smem + w_base + j * 32 * 128 + coff));
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[j], af[i], acc[i][j]);
+    }
+  }
+  epilogue<bf16, MB, NB, EPI_F32>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, n, N, e);
+}
+
 }  // namespace
 
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
@@ -391,6 +523,27 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
     return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
   }
   return launch_t<float, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
+}
+
+bool patch_embed_fits(int dtype, int c_p, int c_c, int N) {
+  return dtype == BF16 && (c_p + c_c) % 64 == 0 && c_p % 8 == 0 && c_c % 8 == 0 && N % PE_BN == 0;
+}
+
+hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
+                       RopeGrid g, const void* W, const void* bias, float* out, int N, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (!patch_embed_fits(BF16, c_p, c_c, N) || cond_mode < 0 || cond_mode > 2 ||
+      (cond_mode && !cond) || (cond_mode == 2 && (g.h % 2 || g.w % 2 || (long long)g.frames * g.h * g.w != n)))
+    return hipErrorInvalidValue;
+  GemmEpi e{};
+  e.kind = EPI_F32;
+  e.bias = bias;
+  e.out = out;
+  e.ldo = N;
+  const int tiles = ((n + PE_BM - 1) / PE_BM) * (N / PE_BN);
+  patch_embed_kernel<<<tiles, LDS_THREADS, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g,
+                                                   reinterpret_cast<const bf16*>(W), N, e);
+  return hipGetLastError();
 }
 
 }  // namespace dit

@@ -92,6 +92,15 @@ hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const 
 hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
                        int cond_mode, RopeGrid g, void* xin, hipStream_t s);
 
+// Fused patch embed (bf16 weights): out[n, N] (fp32) = [x || cond'] W^T + b, with the
+// input row assembled as patch_input does (cond modes 0, 1, 2), without writing it out.
+// W [N, c_p + c_c], b [N] bf16.  patch_embed_fits() tells whether the shapes qualify
+// ((c_p + c_c) % 64 == 0, c_p % 8 == 0, c_c % 8 == 0, N % 256 == 0); otherwise
+// patch_embed() returns hipErrorInvalidValue.
+bool patch_embed_fits(int dtype, int c_p, int c_c, int N);
+hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
+                       RopeGrid g, const void* W, const void* bias, float* out, int N, hipStream_t s);
+
 // x[i] += dt * v[i]
 hipError_t euler(float* x, const float* v, float dt, long long n, hipStream_t s);
 

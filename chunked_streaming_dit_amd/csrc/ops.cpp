@@ -173,4 +173,17 @@ int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* con
                 "patch_input");
 }
 
+int ditk_patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
+                     dit_grid grid, const void* w, const void* b, float* out, int D, void* stream) {
+  if (!x || !w || !b || !out || (cond_mode && !cond)) return fail(DIT_EINVAL, "NULL argument");
+  if (n < 0 || c_p < 1 || c_c < 0 || D < 1 || cond_mode < 0 || cond_mode > 2) return fail(DIT_ESHAPE, "shape");
+  if (!patch_embed_fits(BF16, c_p, c_c, D))
+    return fail(DIT_ESHAPE, "patch_embed needs (c_p + c_c) %% 64 == 0, c_p and c_c %% 8 == 0, D %% 256 == 0");
+  if (cond_mode == 2 && (grid.h % 2 || grid.w % 2 || (long long)grid.frames * grid.h * grid.w != n))
+    return fail(DIT_ESHAPE, "upsample grid");
+  RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
+  return hipchk(patch_embed(x, n, c_p, cond, c_c, cond_mode, g, w, b, out, D, (hipStream_t)stream),
+                "patch_embed");
+}
+
 }  // extern "C"

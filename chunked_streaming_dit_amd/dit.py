@@ -249,3 +249,9 @@ class ops:
     def patch_input(dtype: str, x, c_p: int, cond, c_c: int, mode: int, g: C.DitGrid, xin) -> None:
         C.check(C.lib().ditk_patch_input(_dt_code(dtype), x.data_ptr(), x.shape[0], c_p, _ptr(cond), c_c,
                                          mode, g, xin.data_ptr(), _stream()))
+
+    @staticmethod
+    def patch_embed(x, c_p: int, cond, c_c: int, mode: int, g: C.DitGrid, w, b, out) -> None:
+        C.check(C.lib().ditk_patch_embed(x.data_ptr(), x.shape[0], c_p, _ptr(cond), c_c, mode, g,
+                                         w.data_ptr(), b.data_ptr(), out.data_ptr(), out.shape[1],
+                                         _stream()))

@@ -79,6 +79,20 @@ int ditk_modulation(int dtype, int D, int L, double t, const void* const* weight
 int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
                      int cond_mode, dit_grid grid, void* xin, void* hip_stream);
 
+/* Patch embed with the input rows assembled inside the GEMM's operand loads (bf16
+ * weights): out[n, D] (fp32) = [x || cond'] W^T + b, cond' as in ditk_patch_input
+ * (cond_mode 0 zeros, 1 cond [n, c_c], 2 the nearest-2x upsample of a half-resolution
+ * cond: the super-resolution stage refines the low-resolution latents, HeyGen, "Avatar
+ * inference at scale", section "The underlying model architecture"; how they enter
+ * the model is not given, and channel concatenation of the upsampled latent is this
+ * library's reading).  x [n, c_p] and cond fp32;
+ * W [D, c_p + c_c] and b [D] bf16.  Needs (c_p + c_c) % 64 == 0, c_p % 8 == 0,
+ * c_c % 8 == 0 and D % 256 == 0 (else DIT_ESHAPE); mode 2 needs an even grid with
+ * frames * h * w == n.  This is the patch embed dit_chunk_step runs for bf16. */
+int ditk_patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
+                     dit_grid grid, const void* w, const void* b, float* out, int D,
+                     void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -175,3 +175,13 @@ def test_euler_and_ops_validation():
     assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, FAKE, None) == C.DIT_EINVAL
     n[0] = 0
     assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, FAKE, None) == C.DIT_ESHAPE  # no keys
+    gp = C.DitGrid(0, 2, 4, 6)
+    assert lib.ditk_patch_embed(FAKE, 0, 64, None, 0, 0, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_OK  # empty
+    assert lib.ditk_patch_embed(FAKE, 48, 64, None, 0, 0, gp, FAKE, FAKE, FAKE, 320, None) == C.DIT_ESHAPE  # D % 256
+    assert lib.ditk_patch_embed(FAKE, 48, 60, None, 4, 0, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_ESHAPE  # c_p % 8
+    assert lib.ditk_patch_embed(FAKE, 48, 64, None, 32, 0, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_ESHAPE  # K % 64
+    assert lib.ditk_patch_embed(FAKE, 48, 64, None, 64, 2, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_EINVAL  # no cond
+    assert lib.ditk_patch_embed(FAKE, 47, 64, FAKE, 64, 2, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_ESHAPE  # grid != n
+    assert lib.ditk_patch_embed(FAKE, 30, 64, FAKE, 64, 2, C.DitGrid(0, 2, 3, 5), FAKE, FAKE, FAKE, 256,
+                                None) == C.DIT_ESHAPE  # odd grid
+    assert lib.ditk_patch_embed(FAKE, 48, 64, FAKE, 64, 3, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_ESHAPE

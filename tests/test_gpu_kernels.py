@@ -253,6 +253,40 @@ def test_patch_input_upsample(dtype):
     assert np.array_equal(to_np(xin0), O.patch_input(x, None, cc))
 
 
+@pytest.mark.parametrize("frames,h,w", [(3, 6, 10), (2, 30, 52)])
+@pytest.mark.parametrize("D", [256, 1536])
+@pytest.mark.parametrize("cc,mode", [(0, 0), (64, 0), (64, 1), (64, 2), (192, 2)])
+def test_patch_embed_fused(frames, h, w, D, cc, mode):
+    """The fused patch embed (input rows assembled in the operand loads) against the
+    oracle's patch_input + linear on the same bf16-rounded rows."""
+    dev = device()
+    cp = 64
+    n = frames * h * w
+    r = np.random.default_rng(n + D + cc + mode)
+    x = r.standard_normal((n, cp)).astype(np.float32)
+    if mode == 2:
+        cond = r.standard_normal((frames * (h // 2) * (w // 2), cc)).astype(np.float32)
+    elif mode == 1:
+        cond = r.standard_normal((n, cc)).astype(np.float32)
+    else:
+        cond = None
+    Wt = _arr(r, (D, cp + cc), "bf16", (cp + cc) ** -0.5)
+    b = _arr(r, (D,), "bf16", 0.5)
+    out = torch.full((n, D), float("nan"), device=dev, dtype=torch.float32)
+    ops.patch_embed(torch.from_numpy(x).to(dev), cp, None if cond is None else torch.from_numpy(cond).to(dev),
+                    cc, mode, grid(0, frames, h, w), _dev(Wt, "bf16", dev), _dev(b, "bf16", dev), out)
+    # the kernel rounds the input rows to bf16; the oracle takes the same rounded rows
+    xr = synth.round_bf16(x)
+    c_rows = None
+    if mode == 2:
+        c_rows = O.upsample2_tokens(synth.round_bf16(cond), frames, h, w)
+    elif mode == 1:
+        c_rows = synth.round_bf16(cond)
+    ref = O.linear(O.patch_input(xr, c_rows, cc), Wt.astype(np.float64), b.astype(np.float64))
+    torch.cuda.synchronize()
+    assert rel_err(to_np(out), ref) <= 1e-5
+
+
 @pytest.mark.parametrize("lam", [0.0, -0.7])
 def test_fm_euler_step_closed_form(lam):
     dev = device()

@@ -72,6 +72,12 @@ def test_mini_super_resolution_bf16():
     _check(MINI_SR)
 
 
+def test_mini_super_resolution_single_step_bf16():
+    """The super-resolution stage in one Euler step 1 -> 0 (x_1 = x_0 - v)."""
+    assert MINI_SR.t_start == 1.0 and MINI_SR.t_end == 0.0
+    _check(MINI_SR, steps=1)
+
+
 def test_mini_stream_bf16():
     """Chunked streaming: chunk 0 has no boundary; each later chunk's boundary is the
     previous chunk's final last frame (carried on the GPU)."""
