@@ -26,6 +26,14 @@ pass); the reference pass again runs once, outside the timed region.
 conditioned on the nearest-2x upsample of a 5x30x52 latent, keys 6240 reference + 6240
 boundary + 31200 chunk, 2 blocks, no audio): the boundary pass and 4 Euler steps (sr) or
 a single step 1 -> 0 (sr1); the reference pass runs once, outside the timed region.
+--workload large times one denoising step of the large base chunk (21x30x52 = 32760
+tokens, keys 1560 reference + 1560 boundary + 32760 chunk, 200 audio tokens, 30 blocks,
+hidden 3072, 24 heads x 128) with resident weights; --workload stream times the same
+step with the block weights streamed from pinned host memory through a 2-slot device
+ring (dit_weight_stream) and also reports, from the same process, the resident step,
+the first (cold) streamed step after the switch, and the difference.  Their weights are
+drawn on the GPU (seeded N(0, 1/fan_in), gammas 1 + 0.1 N(0, 1)) to keep the 6.7 G
+parameters' set-up short.
 """
 from __future__ import annotations
 
@@ -47,6 +55,10 @@ METRIC_SR = ("DiT super-resolution chunk latent tokens/sec and attention TFLOP/s
              "(% bf16 MFMA peak), 1 GPU")
 METRIC_SR1 = ("DiT single-step super-resolution chunk latent tokens/sec and attention TFLOP/s "
               "(% bf16 MFMA peak), 1 GPU")
+METRIC_LARGE = ("DiT large-chunk denoising step latent tokens/sec and attention TFLOP/s "
+                "(% bf16 MFMA peak), 1 GPU")
+METRIC_STREAM = ("DiT large-chunk denoising step latent tokens/sec with block weights streamed "
+                 "from pinned host memory, 1 GPU")
 METRIC_REUSE = ("DiT chunk-step latent tokens/sec, boundary carried by reuse, and attention "
                 "TFLOP/s (% bf16 MFMA peak), 1 GPU")
 PEAK_BF16_TFLOPS = 2500.0
@@ -158,13 +170,159 @@ def cpu_baseline(cfg, P, inp, budget_s: float = 12.0):
     }
 
 
+def _device_weights(cfg, dev, seed: int = 5):
+    """Random-init weights of the workload's shapes drawn on the GPU: N(0, 1/fan_in),
+    QK-norm gammas 1 + 0.1 N(0, 1), in the compute dtype."""
+    import torch
+
+    import synth
+    from chunked_streaming_dit_amd import torch_dtype
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    td = torch_dtype(cfg.dtype)
+    out = {}
+    for name, (shape, fan_in, kind) in synth.weight_catalogue(cfg).items():
+        z = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        z = z * (fan_in ** -0.5) if kind == "w" else 1.0 + 0.1 * z
+        out[name] = z.to(td)
+    return out
+
+
+def large_main(args) -> int:
+    """--workload large / stream: one denoising step of the large base chunk."""
+    import torch
+
+    import synth
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of
+
+    dev = torch.device("cuda", 0)
+    cfg = synth.CONFIGS[5]
+    W = _device_weights(cfg, dev)
+    inp = synth.make_inputs(cfg, 0)
+    h = DitChunk(chunk_config(cfg), W, dev)
+    x0 = f32(inp["x_init"], dev)
+    audio = f32(inp["audio"], dev)
+    x = torch.empty_like(x0)
+    t0, t1 = cfg.t_start, cfg.t_end
+    g_chunk = grid_of(cfg.chunk)
+    stream = args.workload == "stream"
+
+    def context():
+        h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+        h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+
+    def step():
+        x.copy_(x0)
+        h.step(x, t0, t1, g_chunk, audio=audio)
+
+    def timed(k):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for _ in range(k):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - a) * 1e3 / k
+
+    context()
+    extra = {}
+    host = None
+    if stream:
+        for _ in range(args.warmup):
+            step()
+        resident_ms = timed(args.steps)
+        host = {}
+        for name, t in W.items():
+            if name.startswith("blk"):
+                p = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+                p.copy_(t)
+                host[name] = p
+        # cold: nothing runs while the first blocks are copied
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        h.weight_stream(host, nslot=2)
+        step()
+        torch.cuda.synchronize()
+        cold_ms = (time.perf_counter() - a) * 1e3
+        extra = {"resident_ms_per_step": resident_ms, "cold_first_step_ms": cold_ms,
+                 "block_weight_bytes": h.cfg.block_weight_bytes(), "ring_slots": 2}
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    h.timing_enable(True)
+    ms = timed(args.steps)
+    n_attn, attn_ms, attn_flop = h.timing_read()
+    h.timing_enable(False)
+    if stream:
+        extra["exposed_ms_per_step"] = ms - resident_ms
+        extra["cold_exposed_ms"] = cold_ms - ms
+        # switch: streaming is enabled while a resident step still runs, so the first
+        # blocks' transfer overlaps it (the hand-over between two models' stages);
+        # exposed = pair - resident step - streamed step, median of 3
+        sw = []
+        for _ in range(3):
+            h.weight_stream(None)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            step()
+            h.weight_stream(host, nslot=2)
+            step()
+            torch.cuda.synchronize()
+            sw.append((time.perf_counter() - a) * 1e3 - resident_ms - ms)
+        extra["switch_exposed_ms"] = sorted(sw)[1]
+    if not torch.isfinite(x).all():
+        print("bench.py: non-finite output", file=sys.stderr)
+        return 1
+    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    workload = ("large base chunk: 21x30x52 = 32760 latent tokens, keys 1560 reference + 1560 "
+                "boundary + 32760 chunk, 200 audio tokens of dim 768, 30 DiT blocks, hidden 3072, "
+                "24 heads x 128, MLP 4x, one Euler step 1 -> 0.875; one bench step = one "
+                "denoising step (the context passes run before)")
+    if stream:
+        workload += ("; block weights (387.0 MB each) streamed from pinned host memory "
+                     "through a 2-slot device ring")
+    line = {
+        "metric": METRIC_STREAM if stream else METRIC_LARGE,
+        "value": cfg.N / (ms * 1e-3),
+        "unit": "latent tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) latents/audio, random-init weights drawn on the GPU)",
+        "config": dict({
+            "workload": workload,
+            "tokens_per_step": cfg.N,
+            "attention_tflops": achieved,
+            "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
+            "attention_launches": n_attn,
+            "attention_avg_launch_ms": attn_ms / max(n_attn, 1),
+        }, **extra),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+        },
+    }
+    print(json.dumps(line), flush=True)
+    h.close()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["base", "interp", "reuse", "sr", "sr1"], default="base",
+    ap.add_argument("--workload", choices=["base", "interp", "reuse", "sr", "sr1", "large", "stream"], default="base",
                     help="base: one N-chunk job (default); interp: one interpolation-chunk job; "
                          "reuse: one N-chunk job with the boundary carried by reuse")
     ap.add_argument("--copy-probe", action="store_true",
@@ -186,6 +344,9 @@ def main() -> int:
         print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
         return 2
+
+    if args.workload in ("large", "stream"):
+        return large_main(args)
 
     import torch
 

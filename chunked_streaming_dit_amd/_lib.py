@@ -56,6 +56,8 @@ _SIGS = {
     "dit_create": (I, [ctypes.POINTER(DitConfig), ctypes.POINTER(P), P, ctypes.c_size_t, P,
                        ctypes.c_size_t, P, ctypes.POINTER(P)]),
     "dit_destroy": (I, [P]),
+    "dit_block_weight_bytes": (ctypes.c_size_t, [ctypes.POINTER(DitConfig)]),
+    "dit_weight_stream": (I, [P, ctypes.POINTER(P), P, ctypes.c_size_t, I]),
     "ref_kv_precompute": (I, [P, P, DitGrid]),
     "boundary_kv_carry": (I, [P, P, DitGrid]),
     "interp_anchor_kv": (I, [P, P, DitGrid, I]),

@@ -146,10 +146,32 @@ int set_error(int code, const char* msg) {
 }
 }  // namespace dit
 
+// Per-block weight streaming (dit_weight_stream): block weights come from pinned host
+// memory through a device ring of nslot block slots.  Block uses are numbered in pass
+// order (every pass uses blocks 0..L-1 in turn); use u reads slot u % nslot, which holds
+// block u % L.  The copy for use u + nslot is issued on the copy stream once use u has
+// been enqueued, behind an event recorded after use u's last kernel, so while block l
+// runs the next nslot - 1 blocks (also those of the next pass) are in flight.
+struct Streaming {
+  bool on = false;
+  std::vector<const void*> host;  // L * DIT_W_BLOCK_COUNT host pointers
+  char* ring = nullptr;
+  int nslot = 0;
+  size_t slot_bytes = 0;
+  size_t off[DIT_W_BLOCK_COUNT] = {}, bytes[DIT_W_BLOCK_COUNT] = {};
+  hipStream_t copy = nullptr;
+  std::vector<hipEvent_t> ready, freed;  // per slot: copy landed / last reader done
+  std::vector<int> holds;                // block copied into each slot (-1: none)
+  std::vector<char> freed_rec;           // freed[slot] has been recorded
+  long long base = 0;                    // use index of block 0 of the current pass
+  long long issued = 0;                  // copies of uses [0, issued) are enqueued
+};
+
 struct dit_handle {
   dit_config cfg;
   Layout lay;
   std::vector<const void*> w;
+  Streaming st;
   char* state = nullptr;
   char* ws = nullptr;
   hipStream_t stream = nullptr;
@@ -162,7 +184,13 @@ struct dit_handle {
   double flop_acc = 0.0;
 
   const void* W(int i) const { return w[i]; }
-  const void* B(int l, int i) const { return w[DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT + i]; }
+  const void* B(int l, int i) const {
+    if (st.on) {
+      if (!st.bytes[i]) return nullptr;
+      return st.ring + (size_t)((st.base + l) % st.nslot) * st.slot_bytes + st.off[i];
+    }
+    return w[DIT_W_GLOBAL_COUNT + l * DIT_W_BLOCK_COUNT + i];
+  }
   template <class P = void> P* S(size_t off) const { return reinterpret_cast<P*>(state + off); }
   template <class P = void> P* X(size_t off) const { return reinterpret_cast<P*>(ws + off); }
 };
@@ -174,6 +202,113 @@ namespace {
     hipError_t e_ = (expr);                                                            \
     if (e_ != hipSuccess) return fail(DIT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+
+// Bytes of block weight entry i (0 for absent cross-attention entries).
+size_t block_entry_bytes(const dit_config& c, int i) {
+  const size_t D = c.D, F = (size_t)c.mlp_ratio * c.D, dh = c.dh, da = c.d_a;
+  const size_t elt = c.dtype == DIT_BF16 ? 2 : 4;
+  const bool cross = c.d_a > 0;
+  size_t n = 0;
+  switch (i) {
+    case DIT_WB_MOD_W: n = 6 * D * D; break;
+    case DIT_WB_MOD_B: n = 6 * D; break;
+    case DIT_WB_QKV_W: n = 3 * D * D; break;
+    case DIT_WB_QKV_B: n = 3 * D; break;
+    case DIT_WB_GQ: case DIT_WB_GK: n = dh; break;
+    case DIT_WB_O_W: n = D * D; break;
+    case DIT_WB_O_B: n = D; break;
+    case DIT_WB_CQ_W: case DIT_WB_CO_W: n = cross ? D * D : 0; break;
+    case DIT_WB_CQ_B: case DIT_WB_CK_B: case DIT_WB_CV_B: case DIT_WB_CO_B: n = cross ? D : 0; break;
+    case DIT_WB_CK_W: case DIT_WB_CV_W: n = D * da; break;
+    case DIT_WB_GCQ: case DIT_WB_GCK: n = cross ? dh : 0; break;
+    case DIT_WB_FC1_W: case DIT_WB_FC2_W: n = F * D; break;
+    case DIT_WB_FC1_B: n = F; break;
+    case DIT_WB_FC2_B: n = D; break;
+    default: n = 0;
+  }
+  return n * elt;
+}
+
+// Slot layout: entries in table order, each 256-byte aligned.  Returns the slot size.
+size_t block_slot_layout(const dit_config& c, size_t* off, size_t* bytes) {
+  size_t o = 0;
+  for (int i = 0; i < DIT_W_BLOCK_COUNT; ++i) {
+    bytes[i] = block_entry_bytes(c, i);
+    off[i] = o;
+    o += align256(bytes[i]);
+  }
+  return o;
+}
+
+// Enqueue the copy of block use u into its slot (nothing if the slot already holds
+// that block).
+int stream_issue(dit_handle* hd, long long u) {
+  Streaming& st = hd->st;
+  const int slot = (int)(u % st.nslot), blk = (int)(u % hd->cfg.L);
+  if (st.holds[slot] == blk) return DIT_OK;
+  if (st.freed_rec[slot]) HIPCHK(hipStreamWaitEvent(st.copy, st.freed[slot], 0));
+  char* dst = st.ring + (size_t)slot * st.slot_bytes;
+  for (int i = 0; i < DIT_W_BLOCK_COUNT; ++i) {
+    if (!st.bytes[i]) continue;
+    HIPCHK(hipMemcpyAsync(dst + st.off[i], st.host[(size_t)blk * DIT_W_BLOCK_COUNT + i], st.bytes[i],
+                          hipMemcpyHostToDevice, st.copy));
+  }
+  HIPCHK(hipEventRecord(st.ready[slot], st.copy));
+  st.holds[slot] = blk;
+  return DIT_OK;
+}
+
+int stream_issue_upto(dit_handle* hd, long long end) {
+  Streaming& st = hd->st;
+  for (; st.issued < end; ++st.issued)
+    if (int rc = stream_issue(hd, st.issued)) return rc;
+  return DIT_OK;
+}
+
+// Start of a pass: the first min(nslot, L) uses have their copies enqueued.
+int pass_begin(dit_handle* hd) {
+  Streaming& st = hd->st;
+  if (!st.on) return DIT_OK;
+  const int k = st.nslot < hd->cfg.L ? st.nslot : hd->cfg.L;
+  return stream_issue_upto(hd, st.base + k);
+}
+
+// Block l of the pass: its kernels wait for its slot's copy.
+int block_begin(dit_handle* hd, int l) {
+  Streaming& st = hd->st;
+  if (!st.on) return DIT_OK;
+  HIPCHK(hipStreamWaitEvent(hd->stream, st.ready[(st.base + l) % st.nslot], 0));
+  return DIT_OK;
+}
+
+// After block l's last kernel is enqueued: mark its slot free once those kernels have
+// run, and enqueue the copy of the use nslot later into it.
+int block_end(dit_handle* hd, int l) {
+  Streaming& st = hd->st;
+  if (!st.on) return DIT_OK;
+  const int slot = (int)((st.base + l) % st.nslot);
+  HIPCHK(hipEventRecord(st.freed[slot], hd->stream));
+  st.freed_rec[slot] = 1;
+  return stream_issue_upto(hd, st.base + l + st.nslot + 1);
+}
+
+// End of a pass.  rc != DIT_OK (a pass cut short): forget what the slots hold so the
+// next pass copies every block again, behind all work enqueued so far.
+int pass_end(dit_handle* hd, int rc) {
+  Streaming& st = hd->st;
+  if (!st.on) return rc;
+  if (rc == DIT_OK) {
+    st.base += hd->cfg.L;
+    return DIT_OK;
+  }
+  for (int k = 0; k < st.nslot; ++k) {
+    (void)hipEventRecord(st.freed[k], hd->stream);
+    st.freed_rec[k] = 1;
+    st.holds[k] = -1;
+  }
+  st.issued = st.base;
+  return rc;
+}
 
 int timed_begin(dit_handle* h, int* slot) {
   *slot = -1;
@@ -237,25 +372,26 @@ int embed(dit_handle* hd, const float* x, int n, const float* cond, int cond_mod
 // (normed, rotated) and V of every block into kdst[l] / vdst[l] (capacity cap).  The
 // tokens attend to the earlier context segments and themselves: nprior 0 (reference:
 // itself only), 1 (boundary: reference), 2 (anchor: reference and, if held, boundary).
-int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::vector<size_t>& kdst,
-                 const std::vector<size_t>& vdst, int cap, int nprior) {
+int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const std::vector<size_t>& kdst,
+                     const std::vector<size_t>& vdst, int cap, int nprior) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   const int D = c.D, F = L.F;
   hipStream_t s = hd->stream;
   float* mod = hd->X<float>(L.mod);
   float* fmod = mod + (size_t)c.L * 6 * D;
-  std::vector<const void*> mw(c.L), mb(c.L);
-  for (int l = 0; l < c.L; ++l) { mw[l] = hd->B(l, DIT_WB_MOD_W); mb[l] = hd->B(l, DIT_WB_MOD_B); }
-  HIPCHK(modulation(c.dtype, D, c.L, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
-                    hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
-                    hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
+  HIPCHK(modulation(c.dtype, D, 0, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                    hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
+                    hd->X<float>(L.tmp), mod, fmod, s));
+  const float* cvec = hd->X<float>(L.tmp) + 256 + D;
   float* h = hd->X<float>(L.h);
   if (const int rc = embed(hd, z, n, nullptr, 0, g, h)) return rc;
   GemmEpi e{};
   for (int l = 0; l < c.L; ++l) {
-    const float* m = mod + (size_t)l * 6 * D;
+    float* m = mod + (size_t)l * 6 * D;
     const bool last = l == c.L - 1;
+    if (int rc = block_begin(hd, l)) return rc;
+    HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
     e = GemmEpi{};
     e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
@@ -266,7 +402,10 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
                        1, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q),
                        hd->S(kdst[l]),
                        hd->S(vdst[l]), cap, s));
-    if (last) break;
+    if (last) {
+      if (int rc = block_end(hd, l)) return rc;
+      break;
+    }
     AttnSeg seg[3];
     int ns = 0;
     if (nprior >= 1) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
@@ -284,8 +423,16 @@ int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::v
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
     HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
+    if (int rc = block_end(hd, l)) return rc;
   }
   return DIT_OK;
+}
+
+int context_pass(dit_handle* hd, const float* z, int n, RopeGrid g, const std::vector<size_t>& kdst,
+                 const std::vector<size_t>& vdst, int cap, int nprior) {
+  int rc = pass_begin(hd);
+  if (!rc) rc = context_pass_run(hd, z, n, g, kdst, vdst, cap, nprior);
+  return pass_end(hd, rc);
 }
 
 bool grid_ok(const dit_grid& g) { return g.frames >= 1 && g.h >= 1 && g.w >= 1; }
@@ -346,7 +493,71 @@ int dit_create(const dit_config* cfg, const void* const* weights, void* state, s
 int dit_destroy(dit_handle* h) {
   if (!h) return DIT_OK;
   for (auto& e : h->ev) (void)hipEventDestroy(e);
+  if (h->st.copy) {
+    (void)hipStreamSynchronize(h->st.copy);
+    for (auto& e : h->st.ready) (void)hipEventDestroy(e);
+    for (auto& e : h->st.freed) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(h->st.copy);
+  }
   delete h;
+  return DIT_OK;
+}
+
+size_t dit_block_weight_bytes(const dit_config* cfg) {
+  if (check_config(cfg)) return 0;
+  size_t off[DIT_W_BLOCK_COUNT], bytes[DIT_W_BLOCK_COUNT];
+  return block_slot_layout(*cfg, off, bytes);
+}
+
+int dit_weight_stream(dit_handle* h, const void* const* host_blocks, void* ring, size_t ring_bytes,
+                      int nslot) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  const dit_config& c = h->cfg;
+  Streaming& st = h->st;
+  if (!host_blocks) {
+    if (ring || nslot) return fail(DIT_EINVAL, "host_blocks NULL: ring and nslot must be NULL/0");
+    if (st.copy) HIPCHK(hipStreamSynchronize(st.copy));
+    st.on = false;
+    return DIT_OK;
+  }
+  if (nslot < 1 || nslot > c.L) return fail(DIT_EINVAL, "nslot=%d out of [1, L=%d]", nslot, c.L);
+  if (!ring || ((uintptr_t)ring & 255)) return fail(DIT_EINVAL, "ring NULL or not 256-byte aligned");
+  size_t off[DIT_W_BLOCK_COUNT], bytes[DIT_W_BLOCK_COUNT];
+  const size_t slot = block_slot_layout(c, off, bytes);
+  if (ring_bytes < slot * (size_t)nslot)
+    return fail(DIT_EWORKSPACE, "ring %zu bytes < %d slots x %zu", ring_bytes, nslot, slot);
+  for (int l = 0; l < c.L; ++l)
+    for (int i = 0; i < DIT_W_BLOCK_COUNT; ++i)
+      if (bytes[i] && !host_blocks[(size_t)l * DIT_W_BLOCK_COUNT + i])
+        return fail(DIT_EINVAL, "host block %d entry %d is NULL", l, i);
+  if (!st.copy) {
+    HIPCHK(hipStreamCreateWithFlags(&st.copy, hipStreamNonBlocking));
+  } else {
+    HIPCHK(hipStreamSynchronize(st.copy));
+  }
+  for (int k = (int)st.ready.size(); k < nslot; ++k) {
+    hipEvent_t a, b;
+    HIPCHK(hipEventCreateWithFlags(&a, hipEventDisableTiming));
+    st.ready.push_back(a);
+    HIPCHK(hipEventCreateWithFlags(&b, hipEventDisableTiming));
+    st.freed.push_back(b);
+  }
+  st.host.assign(host_blocks, host_blocks + (size_t)c.L * DIT_W_BLOCK_COUNT);
+  st.ring = static_cast<char*>(ring);
+  st.nslot = nslot;
+  st.slot_bytes = slot;
+  for (int i = 0; i < DIT_W_BLOCK_COUNT; ++i) { st.off[i] = off[i]; st.bytes[i] = bytes[i]; }
+  st.holds.assign(nslot, -1);
+  st.freed_rec.assign(nslot, 0);
+  st.base = 0;
+  st.issued = 0;
+  st.on = true;
+  // Prefetch: the first blocks start moving now, alongside whatever the handle's
+  // stream is still running (e.g. passes on the resident weights).
+  if (int rc = stream_issue_upto(h, nslot)) {
+    st.on = false;
+    return rc;
+  }
   return DIT_OK;
 }
 
@@ -411,38 +622,21 @@ int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_po
 namespace {
 
 // One denoising step; with carry, also the boundary by reuse (see dit_chunk_step_carry).
-int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
-               dit_grid chunk, double t, double t_next, float* v_out, bool carry) {
-  if (!hd) return fail(DIT_EINVAL, "handle is NULL");
+// The kernels of one denoising step (arguments checked by chunk_step).
+int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, int M, dit_grid chunk,
+               double t, double t_next, float* v_out, bool carry) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
-  if (!x) return fail(DIT_EINVAL, "x is NULL");
-  if (!std::isfinite(t) || !std::isfinite(t_next)) return fail(DIT_EINVAL, "t/t_next not finite");
-  if (!grid_ok(chunk)) return fail(DIT_ESHAPE, "empty chunk grid");
-  const long long nn = grid_n(chunk);
-  if (nn > c.max_tokens) return fail(DIT_ESHAPE, "chunk tokens %lld > max_tokens %d", nn, c.max_tokens);
-  if (c.c_c > 0 && !cond) return fail(DIT_EINVAL, "cond is NULL but c_c=%d", c.c_c);
-  if (c.c_c == 0 && cond) return fail(DIT_EINVAL, "cond given but c_c=0");
-  if (c.c_c > 0 && c.cond_up == 2 && (chunk.h % 2 || chunk.w % 2))
-    return fail(DIT_ESHAPE, "cond_up=2 needs even h and w");
-  if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
-  if (M > 0 && !audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
-  if (M > 0 && c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
   const long long hw = (long long)chunk.h * chunk.w;
-  if (carry && hw > c.max_bnd)
-    return fail(DIT_ESHAPE, "boundary by reuse: frame of %lld tokens > max_bnd %d", hw, c.max_bnd);
-  if (!hd->has_ref) return fail(DIT_ESTATE, "dit_chunk_step before ref_kv_precompute");
-
-  const int n = (int)nn, D = c.D, F = L.F;
+  const int n = (int)grid_n(chunk), D = c.D, F = L.F;
   hipStream_t s = hd->stream;
   RopeGrid g{chunk.t0, chunk.frames, chunk.h, chunk.w};
   float* mod = hd->X<float>(L.mod);
   float* fmod = mod + (size_t)c.L * 6 * D;
-  std::vector<const void*> mw(c.L), mb(c.L);
-  for (int l = 0; l < c.L; ++l) { mw[l] = hd->B(l, DIT_WB_MOD_W); mb[l] = hd->B(l, DIT_WB_MOD_B); }
-  HIPCHK(modulation(c.dtype, D, c.L, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
-                    hd->W(DIT_W_T2_B), mw.data(), mb.data(), hd->W(DIT_W_FMOD_W),
-                    hd->W(DIT_W_FMOD_B), hd->X<float>(L.tmp), mod, fmod, s));
+  HIPCHK(modulation(c.dtype, D, 0, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                    hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
+                    hd->X<float>(L.tmp), mod, fmod, s));
+  const float* cvec = hd->X<float>(L.tmp) + 256 + D;
   const bool cross = M > 0 && c.d_a > 0;
   if (cross)
     HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g, hd->X(L.ain), s));
@@ -451,7 +645,9 @@ int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, 
   GemmEpi e{};
   const char* big = hd->X<char>(L.big);
   for (int l = 0; l < c.L; ++l) {
-    const float* m = mod + (size_t)l * 6 * D;
+    float* m = mod + (size_t)l * 6 * D;
+    if (int rc = block_begin(hd, l)) return rc;
+    HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
     // self-attention
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
     e = GemmEpi{};
@@ -511,6 +707,7 @@ int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, 
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
     HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
+    if (int rc = block_end(hd, l)) return rc;
   }
   // final layer + Euler
   HIPCHK(rmsnorm_mod(c.dtype, h, n, D, fmod, fmod + D, (float)c.eps, hd->X(L.u), s));
@@ -518,6 +715,34 @@ int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, 
   e.kind = EPI_EULER; e.bias = hd->W(DIT_W_FIN_B); e.out = x; e.ldo = c.c_p; e.v_out = v_out;
   e.dt = (float)(t_next - t);
   HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->W(DIT_W_FIN_W), D, n, c.c_p, D, e, s));
+  return DIT_OK;
+}
+
+int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, int M,
+               dit_grid chunk, double t, double t_next, float* v_out, bool carry) {
+  if (!hd) return fail(DIT_EINVAL, "handle is NULL");
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  if (!x) return fail(DIT_EINVAL, "x is NULL");
+  if (!std::isfinite(t) || !std::isfinite(t_next)) return fail(DIT_EINVAL, "t/t_next not finite");
+  if (!grid_ok(chunk)) return fail(DIT_ESHAPE, "empty chunk grid");
+  const long long nn = grid_n(chunk);
+  if (nn > c.max_tokens) return fail(DIT_ESHAPE, "chunk tokens %lld > max_tokens %d", nn, c.max_tokens);
+  if (c.c_c > 0 && !cond) return fail(DIT_EINVAL, "cond is NULL but c_c=%d", c.c_c);
+  if (c.c_c == 0 && cond) return fail(DIT_EINVAL, "cond given but c_c=0");
+  if (c.c_c > 0 && c.cond_up == 2 && (chunk.h % 2 || chunk.w % 2))
+    return fail(DIT_ESHAPE, "cond_up=2 needs even h and w");
+  if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
+  if (M > 0 && !audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
+  if (M > 0 && c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
+  const long long hw = (long long)chunk.h * chunk.w;
+  if (carry && hw > c.max_bnd)
+    return fail(DIT_ESHAPE, "boundary by reuse: frame of %lld tokens > max_bnd %d", hw, c.max_bnd);
+  if (!hd->has_ref) return fail(DIT_ESTATE, "dit_chunk_step before ref_kv_precompute");
+
+  int rc = pass_begin(hd);
+  if (!rc) rc = chunk_pass(hd, x, cond, audio, M, chunk, t, t_next, v_out, carry);
+  if ((rc = pass_end(hd, rc))) return rc;
   if (carry) {
     hd->n_bnd = (int)hw;
     hd->n_anc = 0;

@@ -419,6 +419,17 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
                              fmod_out, s);
 }
 
+hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
+                            hipStream_t s) {
+  if (D % 256) return hipErrorInvalidValue;
+  dim3 grid((6 * D + 3) / 4);
+  if (dtype == BF16)
+    gemv_kernel<bf16, 0><<<grid, 256, 0, s>>>((const bf16*)w, (const bf16*)b, 6 * D, D, c, out);
+  else
+    gemv_kernel<float, 0><<<grid, 256, 0, s>>>((const float*)w, (const float*)b, 6 * D, D, c, out);
+  return hipGetLastError();
+}
+
 hipError_t boundary_reuse(int dtype, int dh, int H, const void* kc, const void* vtc, int cap_src, int first,
                           int n, float dt, float theta, void* kb, void* vtb, int cap_dst, hipStream_t s) {
   const int rows_pad = (n + 63) / 64 * 64;

@@ -112,11 +112,14 @@ hipError_t boundary_reuse(int dtype, int dh, int H, const void* kc, const void* 
                           int n, float dt, float theta, void* kb, void* vtb, int cap_dst, hipStream_t s);
 
 // Timestep conditioning c = SiLU(W2 SiLU(W1 phi(t) + b1) + b2) and per-block modulation
-// mod[l] = Wmod_l c + bmod_l ([6D]) and final fmod = Wf c + bf ([2D]).
-// tmp: fp32 scratch of 2*D floats.
+// mod[l] = Wmod_l c + bmod_l ([6D]) for l < L (L may be 0) and final fmod = Wf c + bf
+// ([2D]).  tmp: fp32 scratch of 256 + 2 D floats; c is left in tmp[256 + D, 256 + 2 D).
 hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const void* t1b,
                       const void* t2w, const void* t2b, const void* const* modw,
                       const void* const* modb, const void* fmodw, const void* fmodb, float* tmp,
                       float* mod_out, float* fmod_out, hipStream_t s);
+// One block's modulation out[6D] = Wmod c + bmod (W [6D, D] dtype, c [D] fp32).
+hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
+                            hipStream_t s);
 
 }  // namespace dit

@@ -85,6 +85,14 @@ class ChunkConfig:
             raise C.DitError(C.DIT_EINVAL, C.last_error())
         return n
 
+    def block_weight_bytes(self) -> int:
+        """Bytes of one block slot of the weight-streaming ring."""
+        cs = self.c_struct()
+        n = C.lib().dit_block_weight_bytes(ctypes.byref(cs))
+        if n == 0:
+            raise C.DitError(C.DIT_EINVAL, C.last_error())
+        return n
+
     def weight_names(self):
         names = list(C.GLOBAL_ORDER)
         for l in range(self.L):
@@ -134,6 +142,36 @@ class DitChunk:
             self.close()
         except Exception:
             pass
+
+    def weight_stream(self, host_blocks: Optional[Dict[str, torch.Tensor]], nslot: int = 2) -> None:
+        """Stream the block weights from pinned host tensors (names "blk{l}.<entry>",
+        shapes and dtype of the weight table) through a device ring of nslot block slots
+        (dit_weight_stream); None switches back to the resident weights."""
+        # work already enqueued may still read the ring (or, on the library's copy
+        # stream, write it) that this call releases; a first ring needs no wait, so the
+        # prefetch of its first blocks overlaps work still running
+        if getattr(self, "_stream_keep", None) is not None or host_blocks is None:
+            torch.cuda.synchronize(self.device)
+        if host_blocks is None:
+            C.check(C.lib().dit_weight_stream(self._h, None, None, 0, 0))
+            self._stream_keep = None
+            return
+        dt = torch_dtype(self.cfg.dtype)
+        names = [f"blk{l}.{b}" for l in range(self.cfg.L) for b in C.BLOCK_ORDER]
+        ptrs = (C.P * len(names))()
+        keep = []
+        for i, nm in enumerate(names):
+            t = host_blocks.get(nm)
+            if t is None:
+                ptrs[i] = None
+                continue
+            if t.is_cuda or not t.is_pinned() or not t.is_contiguous() or t.dtype != dt:
+                raise ValueError(f"{nm} must be a contiguous pinned host tensor of {dt}")
+            keep.append(t)
+            ptrs[i] = t.data_ptr()
+        ring = torch.empty(nslot * self.cfg.block_weight_bytes(), dtype=torch.uint8, device=self.device)
+        C.check(C.lib().dit_weight_stream(self._h, ptrs, ring.data_ptr(), ring.numel(), nslot))
+        self._stream_keep = (keep, ring)
 
     def ref_kv_precompute(self, ref: torch.Tensor, g: C.DitGrid) -> None:
         _dev(ref, "ref", torch.float32)

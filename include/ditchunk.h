@@ -169,8 +169,46 @@ int dit_create(const dit_config* cfg, const void* const* weights, void* state,
                size_t state_bytes, void* workspace, size_t workspace_bytes,
                void* hip_stream, dit_handle** out);
 
-/* Destroy a handle (NULL is allowed).  Does not synchronise the stream. */
+/* Destroy a handle (NULL is allowed).  Does not synchronise the handle's stream; waits
+ * for the weight-streaming copies it has enqueued (dit_weight_stream). */
 int dit_destroy(dit_handle* h);
+
+/* Per-block weight streaming: the single-GPU part of lazily unsharding a model block by
+ * block from pinned host memory, with the transfer of the next blocks overlapped with
+ * the compute of the current one (HeyGen, "Avatar inference at scale", section "Load and
+ * offload phases within the pipeline").
+ *
+ * dit_block_weight_bytes: bytes of one block slot, i.e. the block entries of the weight
+ * table (DIT_WB_*) in table order, each starting at a 256-byte aligned offset; absent
+ * cross-attention entries (d_a == 0) take no space.  0 if the config is invalid.
+ *
+ * dit_weight_stream(h, host_blocks, ring, ring_bytes, nslot) switches the handle's
+ * block weights to streaming:
+ *   - host_blocks: host array of L * DIT_W_BLOCK_COUNT pointers (block l's entries at
+ *     l * DIT_W_BLOCK_COUNT, shapes and dtype as in the weight table) to pinned host
+ *     memory (hipHostMalloc); borrowed, contents must not change while streaming is on;
+ *   - ring: device buffer of at least nslot * dit_block_weight_bytes(cfg) bytes,
+ *     256-byte aligned, borrowed; 1 <= nslot <= L.
+ * Every pass (reference, boundary, anchor, denoising step) uses blocks 0..L-1 in turn;
+ * use u reads slot u % nslot.  The copy of the block needed nslot uses later is issued
+ * on the handle's own copy stream as soon as use u's kernels have been enqueued, and
+ * runs once they have finished; block kernels wait for their slot's copy.  So with
+ * nslot >= 2 the next blocks (also the first ones of the next pass) transfer while the
+ * current block computes; with nslot == L every block is copied once and stays.  The
+ * global weight entries stay as given to dit_create, and results equal those of the
+ * resident table bit for bit.
+ * The call itself starts copying the first nslot blocks at once, so enabling streaming
+ * while earlier passes still run (on the resident weights, or another model) overlaps
+ * the transfer with them; the ring must therefore not be read by work still enqueued.
+ * dit_weight_stream(h, NULL, NULL, 0, 0) switches back to the table of dit_create.
+ * Before freeing the ring or the host memory, synchronise the device (the copies run
+ * on the library's stream).  After a call that failed with DIT_EHIP the next pass
+ * copies every block again.
+ * Errors: EINVAL (null handle, nslot out of range, misaligned ring, a NULL host entry
+ * that is not an absent cross-attention entry), EWORKSPACE (ring too small), EHIP. */
+size_t dit_block_weight_bytes(const dit_config* cfg);
+int dit_weight_stream(dit_handle* h, const void* const* host_blocks, void* ring, size_t ring_bytes,
+                      int nslot);
 
 /* Reference K/V: run the reference latent tokens ref [grid.frames*grid.h*grid.w,
  * c_p] (fp32, device) through all blocks at t = 0, each token at position

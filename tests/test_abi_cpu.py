@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import synth
@@ -185,3 +186,38 @@ def test_euler_and_ops_validation():
     assert lib.ditk_patch_embed(FAKE, 30, 64, FAKE, 64, 2, C.DitGrid(0, 2, 3, 5), FAKE, FAKE, FAKE, 256,
                                 None) == C.DIT_ESHAPE  # odd grid
     assert lib.ditk_patch_embed(FAKE, 48, 64, FAKE, 64, 3, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_ESHAPE
+
+
+def test_block_weight_bytes_matches_the_weight_catalogue():
+    """The streaming slot holds the block entries of the weight table, 256-byte aligned."""
+    lib = C.lib()
+    for cid in range(1, 6):
+        cfg = synth.CONFIGS[cid]
+        elt = 2 if cfg.dtype == "bf16" else 4
+        cat = synth.weight_catalogue(cfg)
+        want = 0
+        for b in C.BLOCK_ORDER:
+            spec = cat.get(f"blk0.{b}")
+            nbytes = 0 if spec is None else elt * int(np.prod(spec[0]))
+            want += (nbytes + 255) // 256 * 256
+        assert lib.dit_block_weight_bytes(ctypes.byref(_cs(cid))) == want
+    assert lib.dit_block_weight_bytes(ctypes.byref(_cs(1, D=300))) == 0
+
+
+def test_weight_stream_validation():
+    lib, cs, h = _handle(2)
+    L = cs.L
+    slot = lib.dit_block_weight_bytes(ctypes.byref(cs))
+    host = (C.P * (L * 22))(*([FAKE] * (L * 22)))
+    assert lib.dit_weight_stream(None, host, FAKE, 2 * slot, 2) == C.DIT_EINVAL
+    assert lib.dit_weight_stream(h, host, FAKE, 2 * slot, 0) == C.DIT_EINVAL            # nslot < 1
+    assert lib.dit_weight_stream(h, host, FAKE, 9 * slot, L + 1) == C.DIT_EINVAL        # nslot > L
+    assert lib.dit_weight_stream(h, host, FAKE + 16, 2 * slot, 2) == C.DIT_EINVAL       # ring alignment
+    assert lib.dit_weight_stream(h, host, None, 2 * slot, 2) == C.DIT_EINVAL
+    assert lib.dit_weight_stream(h, host, FAKE, 2 * slot - 1, 2) == C.DIT_EWORKSPACE    # ring too small
+    host[22 + 2] = None                                                                  # blk1.qkv.w
+    assert lib.dit_weight_stream(h, host, FAKE, 2 * slot, 2) == C.DIT_EINVAL
+    assert "NULL" in C.last_error()
+    assert lib.dit_weight_stream(h, None, FAKE, 0, 0) == C.DIT_EINVAL                   # off, but a ring
+    assert lib.dit_weight_stream(h, None, None, 0, 0) == C.DIT_OK                        # off (already)
+    lib.dit_destroy(h)
