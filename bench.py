@@ -2,7 +2,8 @@
 
 One bench step = one whole base low-res chunk job through the C ABI: the reference
 K/V pass (ref_kv_precompute), the boundary K/V pass from the previous chunk's last
-latent frame (boundary_kv_carry), then the 8 Euler denoising steps
+latent frame (boundary_kv_carry), the chunk's audio K/V (audio_kv_precompute, once per
+chunk: the audio is the same at every step), then the 8 Euler denoising steps
 (dit_chunk_step: modulation, patch embed, 4 DiT blocks of self-attention over
 [reference | boundary | chunk] keys, audio cross-attention and adaLN MLP, final
 layer + Euler update).  Inputs are seeded synthetic tensors already resident in HBM.
@@ -193,7 +194,7 @@ def large_main(args) -> int:
     import torch
 
     import synth
-    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of
 
     dev = torch.device("cuda", 0)
@@ -214,7 +215,8 @@ def large_main(args) -> int:
 
     def step():
         x.copy_(x0)
-        h.step(x, t0, t1, g_chunk, audio=audio)
+        h.audio_kv_precompute(audio)
+        h.step(x, t0, t1, g_chunk, audio=AUDIO_HELD)
 
     def timed(k):
         torch.cuda.synchronize()
@@ -276,8 +278,8 @@ def large_main(args) -> int:
     achieved = attn_flop / (attn_ms * 1e-3) / 1e12
     workload = ("large base chunk: 21x30x52 = 32760 latent tokens, keys 1560 reference + 1560 "
                 "boundary + 32760 chunk, 200 audio tokens of dim 768, 30 DiT blocks, hidden 3072, "
-                "24 heads x 128, MLP 4x, one Euler step 1 -> 0.875; one bench step = one "
-                "denoising step (the context passes run before)")
+                "24 heads x 128, MLP 4x, one Euler step 1 -> 0.875; one bench step = audio K/V + "
+                "one denoising step (the context passes run before)")
     if stream:
         workload += ("; block weights (387.0 MB each) streamed from pinned host memory "
                      "through a 2-slot device ring")
@@ -351,7 +353,7 @@ def main() -> int:
     import torch
 
     import synth
-    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
 
     dev = torch.device("cuda", 0)
@@ -395,8 +397,10 @@ def main() -> int:
             h.ref_kv_precompute(ref, g_ref)
             h.boundary_kv_carry(bnd, g_prev)
         x.copy_(x0)
+        if audio is not None:  # the chunk's audio K/V, once per chunk
+            h.audio_kv_precompute(audio)
         for k in range(S):
-            h.step(x, ts[k], ts[k + 1], g_chunk, cond=cond, audio=audio,
+            h.step(x, ts[k], ts[k + 1], g_chunk, cond=cond, audio=AUDIO_HELD if audio is not None else None,
                    carry_boundary=reuse and k == S - 1)
 
     for _ in range(args.warmup):
@@ -422,17 +426,17 @@ def main() -> int:
     workload = ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
                 "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
                 "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = reference "
-                "K/V + boundary K/V + 8 denoising steps")
+                "K/V + boundary K/V + audio K/V + 8 denoising steps")
     if reuse:
         workload = ("base low-res chunk, boundary carried by reuse: 7800 latent tokens, keys 1560 "
                     "reference + 1560 boundary + 7800 chunk, 50 audio tokens, 4 blocks, hidden 1536, "
-                    "12 heads x 128, 8 Euler steps 1 -> 0; one bench step = 8 denoising steps, the "
+                    "12 heads x 128, 8 Euler steps 1 -> 0; one bench step = audio K/V + 8 denoising steps, the "
                     "last one leaving its last frame's K/V as the next boundary")
     if interp:
         workload = ("interpolation chunk of the base low-res shape: 7800 latent tokens, keys "
                     "1560 reference + 1560 boundary + 1560 anchor + 7800 chunk, 50 audio tokens, "
                     "4 blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0; one bench step = "
-                    "boundary K/V + anchor K/V + 8 denoising steps")
+                    "boundary K/V + anchor K/V + audio K/V + 8 denoising steps")
     if sr:
         workload = ("super-resolution chunk: 5x60x104 = 31200 latent tokens conditioned on the "
                     "nearest-2x upsample of a 5x30x52 latent (64 + 64 input channels), keys 6240 "

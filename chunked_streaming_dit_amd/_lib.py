@@ -45,6 +45,7 @@ class DitError(RuntimeError):
 
 _lib: Optional[ctypes.CDLL] = None
 
+DIT_AUDIO_HELD = -1
 P = ctypes.c_void_p
 I = ctypes.c_int
 Dbl = ctypes.c_double
@@ -56,6 +57,7 @@ _SIGS = {
     "dit_create": (I, [ctypes.POINTER(DitConfig), ctypes.POINTER(P), P, ctypes.c_size_t, P,
                        ctypes.c_size_t, P, ctypes.POINTER(P)]),
     "dit_destroy": (I, [P]),
+    "audio_kv_precompute": (I, [P, P, I]),
     "dit_block_weight_bytes": (ctypes.c_size_t, [ctypes.POINTER(DitConfig)]),
     "dit_weight_stream": (I, [P, ctypes.POINTER(P), P, ctypes.c_size_t, I]),
     "ref_kv_precompute": (I, [P, P, DitGrid]),

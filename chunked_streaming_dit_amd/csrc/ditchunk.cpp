@@ -13,8 +13,8 @@
 //     modulation(t) -> patch input -> patch embed ->
 //     per block: RMSNorm+mod -> QKV -> QK-norm+RoPE -> attention over
 //                [ref | bnd | anchor | chunk] -> out-proj (gated residual) ->
-//                [audio] RMSNorm -> q_c -> q-norm; audio K/V -> k-norm; cross
-//                attention -> out (residual) ->
+//                [audio] RMSNorm -> q_c -> q-norm; audio K/V -> k-norm (or the
+//                K/V held by audio_kv_precompute); cross attention -> out (residual) ->
 //                RMSNorm+mod -> FC1+GELU -> FC2 (gated residual)
 //     final RMSNorm+mod -> final Linear with the Euler update fused into its epilogue.
 #include <hip/hip_runtime.h>
@@ -53,7 +53,7 @@ struct Layout {
   size_t elt = 0;
   int cap_tok = 0, cap_ref = 0, cap_bnd = 0, cap_audio = 0, F = 0, C_in = 0, big_cols = 0;
   // state
-  std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc;
+  std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc, kaud, vaud;
   size_t state_total = 0;
   // workspace
   size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
@@ -108,6 +108,9 @@ Layout make_layout(const dit_config* c) {
     L.vbnd.push_back(take((size_t)L.cap_bnd * D * L.elt));
     L.kanc.push_back(take((size_t)L.cap_bnd * D * L.elt));
     L.vanc.push_back(take((size_t)L.cap_bnd * D * L.elt));
+    const size_t aud = c->d_a > 0 ? (size_t)L.cap_audio * D * L.elt : 0;
+    L.kaud.push_back(take(aud));
+    L.vaud.push_back(take(aud));
   }
   L.state_total = off;
   off = 0;
@@ -176,7 +179,7 @@ struct dit_handle {
   char* ws = nullptr;
   hipStream_t stream = nullptr;
   bool has_ref = false;
-  int n_ref = 0, n_bnd = 0, n_anc = 0;
+  int n_ref = 0, n_bnd = 0, n_anc = 0, n_aud = 0;
   // timing
   bool timing = false;
   std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created lazily
@@ -365,6 +368,25 @@ int embed(dit_handle* hd, const float* x, int n, const float* cond, int cond_mod
   GemmEpi e{};
   e.kind = EPI_F32; e.bias = hd->W(DIT_W_PE_B); e.out = h; e.ldo = c.D;
   HIPCHK(gemm(c.dtype, hd->X(L.xin), L.C_in, hd->W(DIT_W_PE_W), L.C_in, n, c.D, L.C_in, e, hd->stream));
+  return DIT_OK;
+}
+
+// Block l's audio K (k-normed) and V^T (attention layout, capacity cap_audio) from the
+// audio tokens already in the workspace (ain [M, d_a]).
+int audio_kv(dit_handle* hd, int l, int M, void* ka, void* vat) {
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  const int D = c.D;
+  hipStream_t s = hd->stream;
+  RopeGrid g0{0, 1, 1, 1};
+  GemmEpi e{};
+  e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CK_B); e.out = hd->X(L.ka_raw); e.ldo = D;
+  HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
+  e.bias = hd->B(l, DIT_WB_CV_B); e.out = hd->X(L.va_raw);
+  HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
+  HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
+                     hd->B(l, DIT_WB_GCK), 0, g0, (float)c.eps, (float)c.rope_theta, 1.0f, nullptr, ka,
+                     vat, L.cap_audio, s));
   return DIT_OK;
 }
 
@@ -600,6 +622,31 @@ int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev) {
   return DIT_OK;
 }
 
+int audio_kv_precompute(dit_handle* h, const float* audio, int M) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  const dit_config& c = h->cfg;
+  if (M == 0) {
+    if (audio) return fail(DIT_EINVAL, "audio given with M=0");
+    h->n_aud = 0;
+    return DIT_OK;
+  }
+  if (!audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
+  if (c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
+  if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [1, max_audio=%d]", M, c.max_audio);
+  h->n_aud = 0;
+  RopeGrid g0{0, 1, 1, 1};
+  HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g0, h->X(h->lay.ain), h->stream));
+  int rc = pass_begin(h);
+  for (int l = 0; l < c.L && !rc; ++l) {
+    rc = block_begin(h, l);
+    if (!rc) rc = audio_kv(h, l, M, h->S(h->lay.kaud[l]), h->S(h->lay.vaud[l]));
+    if (!rc) rc = block_end(h, l);
+  }
+  if ((rc = pass_end(h, rc))) return rc;
+  h->n_aud = M;
+  return DIT_OK;
+}
+
 int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_pos) {
   if (!h) return fail(DIT_EINVAL, "handle is NULL");
   if (next.frames == 0) {
@@ -637,8 +684,9 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
                     hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
                     hd->X<float>(L.tmp), mod, fmod, s));
   const float* cvec = hd->X<float>(L.tmp) + 256 + D;
-  const bool cross = M > 0 && c.d_a > 0;
-  if (cross)
+  const bool held = M == DIT_AUDIO_HELD;
+  const bool cross = held || (M > 0 && c.d_a > 0);
+  if (cross && !held)
     HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g, hd->X(L.ain), s));
   float* h = hd->X<float>(L.h);
   if (const int rc = embed(hd, x, n, cond, c.c_c ? c.cond_up : 0, g, h)) return rc;
@@ -685,15 +733,11 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
       HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
                          nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
                          hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
-      e = GemmEpi{};
-      e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CK_B); e.out = hd->X(L.ka_raw); e.ldo = D;
-      HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
-      e.bias = hd->B(l, DIT_WB_CV_B); e.out = hd->X(L.va_raw);
-      HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
-      HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
-                         hd->B(l, DIT_WB_GCK), 0, g, (float)c.eps, (float)c.rope_theta, 1.0f,
-                         nullptr, hd->X(L.ka), hd->X(L.vat), L.cap_audio, s));
-      AttnSeg aseg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
+      AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
+      if (!held) {
+        if (int rc2 = audio_kv(hd, l, M, hd->X(L.ka), hd->X(L.vat))) return rc2;
+        aseg = AttnSeg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
+      }
       if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS)) return rc2;
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
@@ -732,7 +776,12 @@ int chunk_step(dit_handle* hd, float* x, const float* cond, const float* audio, 
   if (c.c_c == 0 && cond) return fail(DIT_EINVAL, "cond given but c_c=0");
   if (c.c_c > 0 && c.cond_up == 2 && (chunk.h % 2 || chunk.w % 2))
     return fail(DIT_ESHAPE, "cond_up=2 needs even h and w");
-  if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
+  if (M == DIT_AUDIO_HELD) {
+    if (audio) return fail(DIT_EINVAL, "audio given with M=DIT_AUDIO_HELD");
+    if (hd->n_aud == 0) return fail(DIT_ESTATE, "M=DIT_AUDIO_HELD but no audio K/V held (audio_kv_precompute)");
+  } else if (M < 0 || M > c.max_audio) {
+    return fail(DIT_ESHAPE, "M=%d out of [0, max_audio=%d]", M, c.max_audio);
+  }
   if (M > 0 && !audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
   if (M > 0 && c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
   const long long hw = (long long)chunk.h * chunk.w;

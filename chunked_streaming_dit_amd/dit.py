@@ -100,6 +100,9 @@ class ChunkConfig:
         return names
 
 
+AUDIO_HELD = object()  # step(audio=AUDIO_HELD): use the audio K/V held by audio_kv_precompute
+
+
 class DitChunk:
     """A libditchunk handle with its state and workspace allocated as torch tensors.
 
@@ -187,16 +190,26 @@ class DitChunk:
         _dev(x_next, "x_next", torch.float32)
         C.check(C.lib().interp_anchor_kv(self._h, _ptr(x_next), g, int(t_pos)))
 
+    def audio_kv_precompute(self, audio: Optional[torch.Tensor]) -> None:
+        """Hold the chunk's audio K/V of every block (audio_kv_precompute); steps given
+        audio=AUDIO_HELD reuse them.  None clears them."""
+        _dev(audio, "audio", torch.float32)
+        C.check(C.lib().audio_kv_precompute(self._h, _ptr(audio), 0 if audio is None else audio.shape[0]))
+
     def step(self, x: torch.Tensor, t: float, t_next: float, g: C.DitGrid,
-             cond: Optional[torch.Tensor] = None, audio: Optional[torch.Tensor] = None,
+             cond: Optional[torch.Tensor] = None, audio=None,
              v_out: Optional[torch.Tensor] = None, carry_boundary: bool = False) -> None:
-        """One denoising step; carry_boundary: the chunk's last step, which also leaves its
-        last frame's K/V as the next boundary (dit_chunk_step_carry)."""
+        """One denoising step; audio: features [M, d_a], None, or AUDIO_HELD (the K/V held
+        by audio_kv_precompute); carry_boundary: the chunk's last step, which also leaves
+        its last frame's K/V as the next boundary (dit_chunk_step_carry)."""
         _dev(x, "x", torch.float32)
         _dev(cond, "cond", torch.float32)
-        _dev(audio, "audio", torch.float32)
         _dev(v_out, "v_out", torch.float32)
-        M = 0 if audio is None else audio.shape[0]
+        if audio is AUDIO_HELD:
+            M, audio = C.DIT_AUDIO_HELD, None
+        else:
+            _dev(audio, "audio", torch.float32)
+            M = 0 if audio is None else audio.shape[0]
         fn = C.lib().dit_chunk_step_carry if carry_boundary else C.lib().dit_chunk_step
         C.check(fn(self._h, x.data_ptr(), _ptr(cond), _ptr(audio), M, g, float(t), float(t_next),
                    _ptr(v_out)))

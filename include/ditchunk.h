@@ -19,6 +19,8 @@
  *   boundary_kv_carry   once per chunk (a zero-frame grid clears it for chunk 0);
  *   interp_anchor_kv    once per interpolation chunk (see below; cleared for
  *                       ordinary chunks);
+ *   audio_kv_precompute once per chunk: the audio K/V of every block, which the
+ *                       chunk's steps then reuse;
  *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
  *   dit_chunk_step_carry  alternatively the chunk's last step, which also leaves
  *                       that step's last-frame K/V as the next boundary;
@@ -152,8 +154,9 @@ enum {
 int dit_weight_count(const dit_config* cfg);
 
 /* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
- * max_bnd boundary tokens and of max_bnd interpolation-anchor tokens (each rounded
- * up to 64 tokens).  0 if the config is invalid (see dit_last_error). */
+ * max_bnd boundary tokens, of max_bnd interpolation-anchor tokens and (d_a > 0) of
+ * max_audio audio tokens (each rounded up to 64 tokens).  0 if the config is invalid
+ * (see dit_last_error). */
 size_t dit_state_bytes(const dit_config* cfg);
 
 /* Bytes of per-call transients (activations of max(max_tokens, max_ref, max_bnd)
@@ -244,17 +247,29 @@ int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev);
  * ESTATE (no reference yet). */
 int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_pos);
 
+/* Audio K/V, once per chunk: the chunk's audio features are the same at every
+ * denoising step, so their cross-attention keys and values (per block: the K and V
+ * Linears of audio [M, d_a] (fp32, device), K per-head normed) are computed once and
+ * held in the state.  dit_chunk_step with audio NULL and M == DIT_AUDIO_HELD then
+ * attends to them.  M == 0 (audio NULL) clears them.  The step's output is the same,
+ * bit for bit, as when the audio is passed to every step.
+ * Errors: EINVAL (null audio with M > 0, d_a == 0), ESHAPE (M > max_audio). */
+enum { DIT_AUDIO_HELD = -1 };
+int audio_kv_precompute(dit_handle* h, const float* audio, int M);
+
 /* One denoising step of the chunk: v = DiT(x, t) and x += (t_next - t) v,
  * with dt computed in double on the host and applied in fp32.
  *   x     [N, c_p] fp32, device, updated in place; N = frames*h*w of chunk;
  *         token (f, y, x) at position (chunk.t0 + f, y, x).
  *   cond  fp32 conditioning (c_c > 0): [N, c_c] if cond_up == 1, else
  *         [frames*(h/2)*(w/2), c_c]; must be NULL when c_c == 0.
- *   audio [M, d_a] fp32 audio features (M == 0 or d_a == 0: no cross-attention).
+ *   audio [M, d_a] fp32 audio features (M == 0 or d_a == 0: no cross-attention);
+ *         or audio NULL with M == DIT_AUDIO_HELD: the audio K/V held by
+ *         audio_kv_precompute.
  *   v_out optional [N, c_p] fp32 copy of the velocity (NULL: not written).
  * Errors: EINVAL (null x, non-finite t/t_next, cond/audio mismatch), ESHAPE
  * (N > max_tokens, M > max_audio, odd h or w with cond_up == 2),
- * ESTATE (no reference yet). */
+ * ESTATE (no reference yet; DIT_AUDIO_HELD with no audio held). */
 int dit_chunk_step(dit_handle* h, float* x, const float* cond, const float* audio, int M,
                    dit_grid chunk, double t, double t_next, float* v_out);
 

@@ -52,10 +52,12 @@ def test_sizes_and_weight_count():
         cfg = synth.CONFIGS[cid]
         assert lib.dit_weight_count(ctypes.byref(cs)) == 10 + 22 * cfg.L
         sb = lib.dit_state_bytes(ctypes.byref(cs))
-        # per block K and V of the reference, the boundary and the interpolation anchor
+        # per block K and V of the reference, the boundary, the interpolation anchor and
+        # (with audio weights) the held audio
+        aud = (max(cfg.M, 1) + 63) // 64 * 64 if cfg.d_a > 0 else 0
         kv = cfg.L * 2 * cfg.D * (2 if cfg.dtype == "bf16" else 4) * (
-            (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64))
-        assert kv <= sb <= kv + 6 * cfg.L * 256
+            (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64) + aud)
+        assert kv <= sb <= kv + 8 * cfg.L * 256
         assert lib.dit_workspace_bytes(ctypes.byref(cs)) > 0
 
 
@@ -220,4 +222,21 @@ def test_weight_stream_validation():
     assert "NULL" in C.last_error()
     assert lib.dit_weight_stream(h, None, FAKE, 0, 0) == C.DIT_EINVAL                   # off, but a ring
     assert lib.dit_weight_stream(h, None, None, 0, 0) == C.DIT_OK                        # off (already)
+    lib.dit_destroy(h)
+
+
+def test_audio_kv_precompute_validation():
+    lib, cs, h = _handle(2)
+    assert lib.audio_kv_precompute(None, FAKE, 10) == C.DIT_EINVAL
+    assert lib.audio_kv_precompute(h, None, 10) == C.DIT_EINVAL
+    assert lib.audio_kv_precompute(h, FAKE, 0) == C.DIT_EINVAL                     # audio with M = 0
+    assert lib.audio_kv_precompute(h, FAKE, cs.max_audio + 1) == C.DIT_ESHAPE
+    assert lib.audio_kv_precompute(h, FAKE, -3) == C.DIT_ESHAPE
+    assert lib.audio_kv_precompute(h, None, 0) == C.DIT_OK                         # clear
+    g = C.DitGrid(0, 1, 4, 4)
+    # held audio requested with nothing held, or together with an audio pointer
+    assert lib.dit_chunk_step(h, FAKE, None, FAKE, C.DIT_AUDIO_HELD, g, 1.0, 0.9, None) == C.DIT_EINVAL
+    lib.dit_destroy(h)
+    lib, cs, h = _handle(4)  # no audio weights (d_a = 0)
+    assert lib.audio_kv_precompute(h, FAKE, 4) == C.DIT_EINVAL
     lib.dit_destroy(h)

@@ -78,6 +78,38 @@ def test_mini_super_resolution_single_step_bf16():
     _check(MINI_SR, steps=1)
 
 
+@pytest.mark.parametrize("base", [MINI_BF16, MINI_F32])
+def test_held_audio_kv_bitwise_equals_per_step_audio(base):
+    """audio_kv_precompute once per chunk, then every step with DIT_AUDIO_HELD: the same
+    x and v, bit for bit, as passing the audio to every step (which the parity tests
+    above check against the oracle)."""
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    P = synth.make_weights(base)
+    inp = synth.make_inputs(base, 0)
+    W = upload_weights(P, base.dtype, dev)
+    x_ref, v_ref, h = run_standalone_gpu(base, P, inp, dev, weights=W)
+    audio = f32(inp["audio"], dev)
+    for rep in range(2):
+        h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(base.ref))
+        b = base.bnd
+        h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, b.h, b.w)))
+        h.audio_kv_precompute(audio)
+        x = f32(inp["x_init"], dev)
+        v = torch.empty_like(x)
+        ts = [base.t_start + (base.t_end - base.t_start) * k / base.steps for k in range(base.steps + 1)]
+        for k in range(base.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(base.chunk), audio=AUDIO_HELD, v_out=v)
+            torch.cuda.synchronize()
+            assert np.array_equal(v.cpu().numpy(), v_ref[k]), (rep, k)
+        assert np.array_equal(x.cpu().numpy(), x_ref), rep
+    h.audio_kv_precompute(None)
+    with pytest.raises(Exception):
+        h.step(x, 1.0, 0.5, grid_of(base.chunk), audio=AUDIO_HELD)
+    h.close()
+
+
 def test_mini_stream_bf16():
     """Chunked streaming: chunk 0 has no boundary; each later chunk's boundary is the
     previous chunk's final last frame (carried on the GPU)."""
