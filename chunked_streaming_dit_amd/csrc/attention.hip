@@ -12,6 +12,11 @@
 // LDS round trip); the key order they are held in is matched by the stored order of V^T
 // (see kernels.h).  Softmax statistics and accumulation are fp32; the softmax is taken
 // in base 2 with log2(e)/sqrt(dh) folded into q (given pre-scaled, or applied here).
+// When q and k are QK-normed (per-head RMSNorm times gamma), every logit is bounded by
+// |q||k| <= q_scale dh max|gq| max|gk|; if that bound is small the weights 2^s cannot
+// overflow and the softmax needs no running max at all: the common factor of numerator
+// and denominator cancels, so the row max, its cross-lane exchange, the rescale test
+// and the shift all drop out of the loop.
 #include <math.h>
 
 #include "common.h"
@@ -31,6 +36,11 @@ struct AttnArgs {
   int nsplit;   // key-range splits per (head, q-tile); > 1 writes partials
   float* opart; // [nsplit, nq, H*DH] normalised partial outputs (nsplit > 1)
   float* ml;    // [nsplit, nq, H, 2] (running max * scale, row sum) per partial
+  // QK-norm gammas of q and k (or NULL) and the logit bound coefficient: every exp2-domain
+  // logit is at most bcoef * max|gq| * max|gk| in magnitude (see attention()).
+  const void* gq;
+  const void* gk;
+  float bcoef;
   AttnSeg seg[ATTN_MAX_SEGS];
 };
 
@@ -38,6 +48,10 @@ constexpr int AW = 8;          // waves per workgroup (32 queries each)
 constexpr int BQ = 32 * AW;    // queries per workgroup
 constexpr int NSLOT = 3;       // ring depth of the K and of the V^T tile rings
 constexpr float RESCALE_LOG2 = 8.0f;
+// Logit bound (exp2 domain) up to which the softmax is taken without a running max:
+// 2^60 per weight, summed over at most 2^24 keys, stays far inside the fp32 range.
+constexpr float NOMAX_BOUND = 60.0f;
+
 
 // Row-sum accumulation from the P^T operand vector.
 __device__ __forceinline__ float row_sum_add(bf16x8 p, float acc) {
@@ -110,6 +124,20 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
       if (qvalid) r = ld16(qp + s * 32 + lg * 16);
       qf[s] = as_vec<V>(r);
     }
+  }
+
+  // Offset-free softmax when the QK-norm bound allows it (uniform over the launch).
+  int nomax = 0;
+  if (a.gq) {
+    const T* gq = reinterpret_cast<const T*>(a.gq);
+    const T* gk = reinterpret_cast<const T*>(a.gk);
+    float mq = 0.f, mk = 0.f;
+    for (int i = lane; i < DH; i += 64) {
+      mq = fmaxf(mq, fabsf(to_f(gq[i])));
+      mk = fmaxf(mk, fabsf(to_f(gk[i])));
+    }
+    nomax = a.bcoef * wave_max(mq) * wave_max(mk) <= NOMAX_BOUND;
+    nomax = __builtin_amdgcn_readfirstlane(nomax);
   }
 
   // Tiles of all segments in order: tile t lies in segment si at key offset base.
@@ -291,27 +319,29 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
           }
       }
     }
-    float mx = -INFINITY;
+    if (!nomax) {  // uniform branch: the running max and its lazy rescale
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescale: keep the running max unless a score exceeds it by more than
-    // RESCALE_LOG2 in the exp2 domain (then p stays <= 2^RESCALE_LOG2, which fp32
-    // sums and bf16 operands hold exactly as well as p <= 1).  The decision is
-    // wave-uniform; lanes l and l^32 hold the same query and the same max.
-    if (__any(mx > m_run + a.thr)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale);
-      l_run *= alpha;
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescale: keep the running max unless a score exceeds it by more than
+      // RESCALE_LOG2 in the exp2 domain (then p stays <= 2^RESCALE_LOG2, which fp32
+      // sums and bf16 operands hold exactly as well as p <= 1).  The decision is
+      // wave-uniform; lanes l and l^32 hold the same query and the same max.
+      if (__any(mx > m_run + a.thr)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * a.scale);
+        l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[d][r] *= alpha;
-      m_run = m_new;
+          for (int r = 0; r < 16; ++r) O[d][r] *= alpha;
+        m_run = m_new;
+      }
     }
-    const float ms = m_run * a.scale;
+    const float ms = nomax ? 0.f : m_run * a.scale;
     const char* sv = vs + sl * VTILE;
     const char* sk = ks + sl1 * KTILE;
     // Softmax of tile t, P V of tile t and the scores of tile t+1, in NU phases.  Unit u
@@ -405,7 +435,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     }
   if (lg == 0) {
     float* mp = a.ml + (((size_t)split * a.nq + qrow) * a.H + head) * 2;
-    mp[0] = l_tot > 0.f ? m_run * a.scale : -INFINITY;
+    mp[0] = l_tot > 0.f ? (nomax ? 0.f : m_run * a.scale) : -INFINITY;
     mp[1] = l_tot;
   }
 }
@@ -460,7 +490,7 @@ int attention_splits(int nq, int H, int total_keys_tiles, int partial_rows, int 
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
                      int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
-                     hipStream_t s, int kind) {
+                     hipStream_t s, int kind, const AttnNorm* norm) {
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
   if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
@@ -478,6 +508,11 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.nsplit = sp.nsplit;
   a.opart = sp.opart;
   a.ml = sp.ml;
+  // q = q_fold (gq . q^) and k = gk . k^ with |q^|^2, |k^|^2 <= dh (RMS-normed rows), so
+  // |q . k| <= q_fold dh max|gq| max|gk|; the factor covers the bf16 rounding of q and k.
+  a.gq = (norm && q_prescaled && norm->gq && norm->gk) ? norm->gq : nullptr;
+  a.gk = a.gq ? norm->gk : nullptr;
+  a.bcoef = a.gq ? (float)(norm->q_fold * dh * 1.02) : 0.f;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
   dim3 grid(((nq + BQ - 1) / BQ) * H * sp.nsplit), block(64 * AW);
   const bool cross = kind == ATTN_CROSS;

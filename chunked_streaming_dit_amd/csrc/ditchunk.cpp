@@ -332,17 +332,21 @@ int timed_end(dit_handle* h, int slot, double flop) {
   return DIT_OK;
 }
 
-// Self-attention launch: picks the key-range split, times the main kernel when timing is
-// on (the flop count is the method's 4 n_q n_kv D), then merges partials if split.
-int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed, int kind) {
+// Attention launch: picks the key-range split, times the main kernel when timing is on
+// (the flop count is the method's 4 n_q n_kv D), then merges partials if split.  q and
+// k are QK-normed with block l's gammas (self: gq/gk, cross: gcq/gck), q pre-scaled.
+int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed, int kind, int l) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   AttnSplit sp{1, hd->X<float>(L.opart), hd->X<float>(L.ml)};
   sp.nsplit = attention_splits(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
   int slot = -1, rc;
   if (timed && (rc = timed_begin(hd, &slot))) return rc;
+  const bool cross = kind == ATTN_CROSS;
+  const AttnNorm norm{hd->B(l, cross ? DIT_WB_GCQ : DIT_WB_GQ), hd->B(l, cross ? DIT_WB_GCK : DIT_WB_GK),
+                      (double)attention_q_scale(c.dh)};
   HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
-                   true, hd->stream, kind));
+                   true, hd->stream, kind, &norm));
   if (timed) {
     double nkv = 0;
     for (int i = 0; i < ns; ++i) nkv += seg[i].n;
@@ -433,7 +437,7 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     if (nprior >= 1) seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
     if (nprior >= 2 && hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->S(kdst[l]), hd->S(vdst[l]), n, cap};
-    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
+    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF, l);
     if (rc) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
@@ -711,7 +715,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     if (hd->n_bnd > 0) seg[ns++] = AttnSeg{hd->S(L.kbnd[l]), hd->S(L.vbnd[l]), hd->n_bnd, L.cap_bnd};
     if (hd->n_anc > 0) seg[ns++] = AttnSeg{hd->S(L.kanc[l]), hd->S(L.vanc[l]), hd->n_anc, L.cap_bnd};
     seg[ns++] = AttnSeg{hd->X(L.kc), hd->X(L.vtc), n, L.cap_tok};
-    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF);
+    int rc = run_attention(hd, n, seg, ns, true, ATTN_SELF, l);
     if (rc) return rc;
     if (carry) {
       // This block's attention has read its boundary slot; refill it with the last
@@ -738,7 +742,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
         if (int rc2 = audio_kv(hd, l, M, hd->X(L.ka), hd->X(L.vat))) return rc2;
         aseg = AttnSeg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
       }
-      if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS)) return rc2;
+      if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
       HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));

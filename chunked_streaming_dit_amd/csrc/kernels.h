@@ -55,10 +55,19 @@ struct AttnSplit {
 // q_prescaled: q holds q * log2(e)/sqrt(dh) (as written by qknorm_rope with that
 // q_scale), the form the kernels consume; otherwise the kernel scales q itself (for
 // bf16 with dh = 128 that rounds the scaled q to bf16 a second time).
+// norm (optional): q and k are QK-normed rows, q = q_fold * gq . q^, k = gk . k^ with
+// q^, k^ RMS-normalised (gq, gk: dtype [dh]).  With q pre-scaled, the kernel then bounds
+// the logits by q_fold dh max|gq| max|gk| and, when that bound is small, takes the
+// softmax without a running max (same result up to rounding).
+struct AttnNorm {
+  const void* gq;
+  const void* gk;
+  double q_fold;
+};
 enum { ATTN_SELF = 0, ATTN_CROSS = 1 };
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
                      int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
-                     hipStream_t s, int kind = ATTN_SELF);
+                     hipStream_t s, int kind = ATTN_SELF, const AttnNorm* norm = nullptr);
 // log2(e) / sqrt(dh): the q scale of the exp2-domain logits.
 inline float attention_q_scale(int dh) { return (float)(1.4426950408889634 / __builtin_sqrt((double)dh)); }
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,

@@ -114,8 +114,11 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, int q_prescaled, void* o, void* stream) {
+                   int nsplit, float* partial, int q_prescaled, const void* gq, const void* gk,
+                   double q_fold, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
+  if ((gq != nullptr) != (gk != nullptr)) return fail(DIT_EINVAL, "gq and gk must both be given or both NULL");
+  if (gq && !(q_fold > 0 && std::isfinite(q_fold))) return fail(DIT_EINVAL, "q_fold must be finite and > 0");
   if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
   if (!q || !o || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
   if (dtype == DIT_F32 && dh != 64) return fail(DIT_EINVAL, "fp32 attention supports dh=64 only");
@@ -134,8 +137,9 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   const int D = H * dh;
   AttnSplit sp{nsplit, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
+  const AttnNorm norm{gq, gk, q_fold};
   int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, q_prescaled != 0,
-                            (hipStream_t)stream),
+                            (hipStream_t)stream, ATTN_SELF, gq ? &norm : nullptr),
                   "attention");
   if (rc) return rc;
   return hipchk(attention_combine(dtype, dh, H, nq, sp, o, D, (hipStream_t)stream), "attention_combine");

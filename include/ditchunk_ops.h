@@ -62,10 +62,17 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
  * q_prescaled != 0: q holds q * log2(e)/sqrt(dh) (ditk_qknorm_rope with that q_scale;
  * the softmax is then taken in base 2 on q k^T directly).  q_prescaled == 0: plain q,
  * scaled inside the kernel (for bf16 with dh = 128 this rounds the scaled q to bf16
- * once more, i.e. slightly less accurate than the pre-scaled form). */
+ * once more, i.e. slightly less accurate than the pre-scaled form).
+ * gq, gk (dtype [dh], both or neither): q and k are QK-normed rows, q = q_fold gq . q^
+ * and k = gk . k^ with q^, k^ RMS-normalised (ditk_qknorm_rope with q_scale q_fold and
+ * 1).  With q pre-scaled, every exp2-domain logit is then at most q_fold dh max|gq|
+ * max|gk| in magnitude; when that is small the kernel computes the softmax weights as
+ * 2^s without a running max (the common factor cancels; same result up to rounding).
+ * The caller guarantees the normalisation: for other q, k pass NULL. */
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, int q_prescaled, void* o, void* hip_stream);
+                   int nsplit, float* partial, int q_prescaled, const void* gq, const void* gk,
+                   double q_fold, void* o, void* hip_stream);
 
 /* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
  * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,

@@ -149,18 +149,36 @@ def test_qknorm_rope(dtype, dh, rope, q_scale):
     assert np.all(pad == 0)
 
 
-def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False):
+def _normed(r, n, H, dh, g, fold, dtype):
+    """Rows of H heads that are RMS-normalised per head, times gamma g [dh] and fold."""
+    x = r.standard_normal((n, H, dh))
+    x = x / np.sqrt((x * x).mean(axis=2, keepdims=True) + 1e-6)
+    a = (fold * g[None, None, :] * x).reshape(n, H * dh).astype(np.float32)
+    return synth.round_bf16(a) if dtype == "bf16" else a
+
+
+def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False, gamma=None):
     """prescaled: the kernel gets q as the exp2-domain logit scale (q * log2(e)/sqrt(dh)); the
-    oracle then takes q / that factor in fp64, so both see the same logits exactly."""
+    oracle then takes q / that factor in fp64, so both see the same logits exactly.
+    gamma = (mean, spread): q and k are QK-normed rows with gammas mean + spread N(0, 1),
+    passed to the kernel, which may then drop the running max."""
     dev = device()
     r = np.random.default_rng(seed)
     D = H * dh
-    q = _arr(r, (nq, D), dtype, 2.0)
+    gq = gk = None
+    if gamma is not None:
+        gq = _arr(r, (dh,), dtype) * gamma[1] + gamma[0]
+        gk = _arr(r, (dh,), dtype) * gamma[1] + gamma[0]
+        gq = synth.round_bf16(gq) if dtype == "bf16" else gq
+        gk = synth.round_bf16(gk) if dtype == "bf16" else gk
+        q = _normed(r, nq, H, dh, gq.astype(np.float64), Q_SCALE[dh], dtype)
+    else:
+        q = _arr(r, (nq, D), dtype, 2.0)
     segs, ks, vs = [], [], []
     keep = []
     for n in seg_ns:
         cap = max(64, (n + 63) // 64 * 64)
-        k = _arr(r, (n, D), dtype, 2.0)
+        k = _normed(r, n, H, dh, gk.astype(np.float64), 1.0, dtype) if gamma is not None else _arr(r, (n, D), dtype, 2.0)
         v = _arr(r, (n, D), dtype)
         kp = np.zeros((cap, D), dtype=np.float32)
         kp[:n] = k
@@ -171,7 +189,11 @@ def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False):
         vs.append(v)
     o = torch.empty((nq, D), device=dev, dtype=torch_dtype(dtype))
     part = torch.empty(nsplit * nq * (D + 2 * H), device=dev) if nsplit > 1 else None
-    ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled)
+    if gamma is not None:
+        ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled,
+                      gq=_dev(gq, dtype, dev), gk=_dev(gk, dtype, dev), q_fold=Q_SCALE[dh])
+    else:
+        ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled)
     K = np.concatenate(ks).astype(np.float64).reshape(-1, H, dh)
     V = np.concatenate(vs).astype(np.float64).reshape(-1, H, dh)
     q64 = q.astype(np.float64) / (Q_SCALE[dh] if prescaled else 1.0)
@@ -203,6 +225,21 @@ def test_attention(dtype, dh, nq, seg_ns, prescaled):
 def test_attention_key_split(dtype, dh, nsplit, nq, seg_ns):
     """Key tiles split over workgroups and merged; includes splits with no tiles."""
     err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + nsplit, nsplit, prescaled=True)
+    assert err <= TOL[dtype] / 4, err
+
+
+@pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("gamma", [(1.0, 0.1), (0.5, 0.2), (1.75, 0.02), (4.0, 0.5)])
+@pytest.mark.parametrize("nsplit", [1, 2])
+@pytest.mark.parametrize("nq,seg_ns", [(150, [70, 33, 129]), (257, [1, 1, 1]), (90, [70, 33, 65, 129])])
+def test_attention_qk_normed(dtype, dh, gamma, nsplit, nq, seg_ns):
+    """QK-normed q and k with their gammas (mean, spread).  The logit bound q_fold dh
+    max|gq| max|gk| (x 1.02) is about 28, 20 and 55 for the first three (dh = 128), so
+    they take the softmax without a running max, the last close to the 60 limit (weights
+    up to 2^55); gammas near 4 (bound about 500) keep the running max.  All match the
+    exact softmax."""
+    err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + dh + nsplit, nsplit, prescaled=True,
+                     gamma=gamma)
     assert err <= TOL[dtype] / 4, err
 
 
