@@ -515,6 +515,11 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
         const long long cost = (tiles + 255) / 256 * (long long)bm;
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = bm; }
       }
+      // Too few tiles to occupy the chip (short context passes): smaller tiles.
+      if (((M + best - 1) / best) * (N / 256) < 160) {
+        if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
+        return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
+      }
       if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s);
       if (best == 192) return launch_lds<192, 256>(A, lda, W, ldw, M, N, K, e, s);
       return launch_lds<128, 256>(A, lda, W, ldw, M, N, K, e, s);
