@@ -54,6 +54,54 @@ __global__ __launch_bounds__(256) void rmsnorm_mod_kernel(const float* __restric
   }
 }
 
+// Fixed width D = 256 IT, two rows per wave: both rows' loads are in flight together and
+// the modulation vectors are read once per two rows.
+template <class T, int IT>
+__global__ __launch_bounds__(256) void rmsnorm_mod2_kernel(const float* __restrict__ h, int n,
+                                                           const float* __restrict__ shift,
+                                                           const float* __restrict__ scale,
+                                                           float eps, T* __restrict__ out) {
+  constexpr int D = 256 * IT;
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+  if (row0 >= n) return;
+  const bool two = row0 + 1 < n;
+  f32x4 v[2][IT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float* hr = h + (size_t)(two ? row0 + r : row0) * D + lane * 4;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) v[r][i] = *reinterpret_cast<const f32x4*>(hr + i * 256);
+  }
+  float rs[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i)
+      ss += v[r][i][0] * v[r][i][0] + v[r][i][1] * v[r][i][1] + v[r][i][2] * v[r][i][2] + v[r][i][3] * v[r][i][3];
+    ss = wave_sum(ss);
+    rs[r] = 1.0f / sqrtf(ss / (float)D + eps);
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int c = i * 256 + lane * 4;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sh = sc;
+    if (scale) {
+      sc = *reinterpret_cast<const f32x4*>(scale + c);
+      sh = *reinterpret_cast<const f32x4*>(shift + c);
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if (r == 1 && !two) break;
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = fmaf(v[r][i][q] * rs[r], 1.0f + sc[q], sh[q]);
+      store4<T>(out + (size_t)(row0 + r) * D + c, o);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- QK-norm + RoPE + repack
 // Grid: (round_up(n, 64) / 64, H).  A workgroup owns 64 tokens x one head.  A lane moves
 // one 16-byte vector (VE elements, VE/2 rotation pairs) of a head row, so a row of dh
@@ -354,6 +402,14 @@ hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shi
                        const float* scale, float eps, void* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (D % 256 || D > 4096) return hipErrorInvalidValue;
+  if (D == 1536 || D == 3072) {
+    dim3 g2((n + 7) / 8);
+#define RMS2(T, IT) rmsnorm_mod2_kernel<T, IT><<<g2, 256, 0, s>>>(h, n, shift, scale, eps, (T*)out)
+    if (dtype == BF16) { if (D == 1536) RMS2(bf16, 6); else RMS2(bf16, 12); }
+    else { if (D == 1536) RMS2(float, 6); else RMS2(float, 12); }
+#undef RMS2
+    return hipGetLastError();
+  }
   dim3 grid((n + 3) / 4);
   if (dtype == BF16)
     rmsnorm_mod_kernel<bf16><<<grid, 256, 0, s>>>(h, n, D, shift, scale, eps, (bf16*)out);
