@@ -338,6 +338,10 @@ int timed_end(dit_handle* h, int slot, double flop) {
 int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed, int kind, int l) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
+  if (kind == ATTN_CROSS && short_attention_fits(c.dtype, c.dh, ns, seg)) {
+    HIPCHK(short_attention(c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, seg[0], true, hd->stream));
+    return DIT_OK;
+  }
   AttnSplit sp{1, hd->X<float>(L.opart), hd->X<float>(L.ml)};
   sp.nsplit = attention_splits(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
   int slot = -1, rc;

@@ -72,6 +72,11 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
 inline float attention_q_scale(int dh) { return (float)(1.4426950408889634 / __builtin_sqrt((double)dh)); }
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
                              hipStream_t s);
+// One short key segment (1..64 keys, bf16, dh = 128): the exact softmax over one tile,
+// o[nq, ldo] per head, in a kernel whose whole grid is resident at once.
+bool short_attention_fits(int dtype, int dh, int nseg, const AttnSeg* segs);
+hipError_t short_attention(int dh, int H, const void* q, int ldq, void* o, int ldo, int nq, const AttnSeg& seg,
+                           bool q_prescaled, hipStream_t s);
 // Splits minimising the estimated time for nq queries, H heads, key_tiles 64-key tiles,
 // partial storage of partial_rows rows and `slots` concurrent workgroups.
 int attention_splits(int nq, int H, int key_tiles, int partial_rows, int slots);

@@ -136,6 +136,9 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
   if (nsplit < 1 || nsplit > 8) return fail(DIT_EINVAL, "nsplit=%d out of [1, 8]", nsplit);
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   const int D = H * dh;
+  if (nsplit == 1 && short_attention_fits(dtype, dh, nseg, seg))
+    return hipchk(short_attention(dh, H, q, D, o, D, nq, seg[0], q_prescaled != 0, (hipStream_t)stream),
+                  "short_attention");
   AttnSplit sp{nsplit, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
   const AttnNorm norm{gq, gk, q_fold};
   int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, q_prescaled != 0,

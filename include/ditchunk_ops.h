@@ -68,7 +68,9 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
  * 1).  With q pre-scaled, every exp2-domain logit is then at most q_fold dh max|gq|
  * max|gk| in magnitude; when that is small the kernel computes the softmax weights as
  * 2^s without a running max (the common factor cancels; same result up to rounding).
- * The caller guarantees the normalisation: for other q, k pass NULL. */
+ * The caller guarantees the normalisation: for other q, k pass NULL.
+ * One segment of 1..64 keys with bf16, dh = 128 and nsplit = 1 (the audio
+ * cross-attention's shape) runs a single-tile kernel with the exact softmax. */
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
                    int nsplit, float* partial, int q_prescaled, const void* gq, const void* gk,

@@ -243,6 +243,16 @@ def test_attention_qk_normed(dtype, dh, gamma, nsplit, nq, seg_ns):
     assert err <= TOL[dtype] / 4, err
 
 
+@pytest.mark.parametrize("nq,n", [(1, 1), (300, 50), (129, 64), (7800, 50), (2000, 37)])
+@pytest.mark.parametrize("prescaled", [True, False])
+def test_attention_short_segment_bf16(nq, n, prescaled):
+    """One segment of at most 64 keys (the audio cross-attention's shape): the
+    single-tile kernel, 12 heads of 128."""
+    err = _attn_case("bf16", 128, 12, nq, [n], nq + n + 11, prescaled=prescaled)
+    tol = TOL["bf16"] / 4 if prescaled else TOL["bf16"] / 2
+    assert err <= tol, err
+
+
 def test_attention_real_head_shape_bf16():
     """One head group at the base-chunk shape: 12 heads of 128, keys 1560 | 1560 | 1000."""
     err = _attn_case("bf16", 128, 12, 1000, [1560, 1560, 1000], 5, prescaled=True)
