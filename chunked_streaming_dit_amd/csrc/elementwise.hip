@@ -284,22 +284,29 @@ __global__ void timestep_features_kernel(double t, float* __restrict__ phi) {
   phi[128 + i] = (float)sin(s * w);
 }
 
-// y[r] = act(W[r, :] . x + b[r]) for r < R; one wave per output row.
+// y[r] = act(W[r, :] . x + b[r]) for r < R; one wave per output row.  A lane reads 16
+// bytes of the row per step (8 bf16 or 4 fp32); K is a multiple of 256, and the steps
+// are unrolled so that a row's loads are in flight together.
 template <class T, int ACT>
 __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
                                                    const T* __restrict__ b, int R, int K,
                                                    const float* __restrict__ x,
                                                    float* __restrict__ y) {
+  typedef typename Vec<T>::type V;
+  constexpr int VE = Vec<T>::n;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   const T* wr = W + (size_t)r * K;
   float acc = 0.f;
-  for (int k = lane * 4; k < K; k += 256) {
-    float w4[4];
-    load4<T>(wr + k, w4);
-    f32x4 x4 = *reinterpret_cast<const f32x4*>(x + k);
-    acc += w4[0] * x4[0] + w4[1] * x4[1] + w4[2] * x4[2] + w4[3] * x4[3];
+#pragma unroll 4
+  for (int k = lane * VE; k < K; k += 64 * VE) {
+    const V w = as_vec<V>(ld16(wr + k));
+#pragma unroll
+    for (int j = 0; j < VE; j += 4) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(x + k + j);
+      acc += to_f(w[j]) * x4[0] + to_f(w[j + 1]) * x4[1] + to_f(w[j + 2]) * x4[2] + to_f(w[j + 3]) * x4[3];
+    }
   }
   acc = wave_sum(acc);
   if (lane == 0) {
