@@ -232,7 +232,7 @@ int boundary_kv_carry(dit_handle* h, const float* x_prev, dit_grid prev);
 /* Interpolation anchor K/V (HeyGen, "Avatar inference at scale", section "Boundary
  * continuity and chunk consistency": ordinary N-chunks make the timeline, and an
  * interpolation chunk between N_k and N_k+1, generated after both, smooths the
- * transition using the last frame of N_k and an early frame of N_k+1 as anchors;
+ * transition anchored on the final frame of N_k and one of the first frames of N_k+1;
  * the order is N0, N1, I0, N2, I1, ...).  Reading: both anchors are context
  * segments.  The boundary (boundary_kv_carry on N_k's final latent) is the first;
  * this call makes the second from frame 0 (h*w tokens) of N_k+1's final latent

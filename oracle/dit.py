@@ -334,7 +334,7 @@ def last_frame(x: np.ndarray, frames: int, h: int, w: int) -> np.ndarray:
 def first_frame(x: np.ndarray, frames: int, h: int, w: int) -> np.ndarray:
     """Tokens of the first latent frame of a chunk (the later interpolation anchor) [bnd].
 
-    reading: "an early frame" of the later N-chunk is its frame 0."""
+    reading: of the later N-chunk's first frames, the anchor is its frame 0."""
     n = h * w
     return np.asarray(x, dtype=np.float64)[:n]
 
