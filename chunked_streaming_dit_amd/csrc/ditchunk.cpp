@@ -398,6 +398,38 @@ int audio_kv(dit_handle* hd, int l, int M, void* ka, void* vat) {
   return DIT_OK;
 }
 
+// QKV of block l over n tokens (u in the workspace): q (QK-normed, pre-scaled, rotated)
+// -> q_out (NULL: not needed), k (QK-normed, rotated) -> k_out [cap rows], V^T -> vt_out
+// [D, cap].  When the launch allows it the QK-norm and RoPE run in the GEMM's epilogue
+// and only V goes through the repacking kernel.
+int qkv_project(dit_handle* hd, int l, int n, RopeGrid g, void* q_out, void* k_out, void* vt_out, int cap) {
+  const dit_config& c = hd->cfg;
+  const Layout& L = hd->lay;
+  const int D = c.D;
+  hipStream_t s = hd->stream;
+  const char* big = hd->X<char>(L.big);
+  GemmEpi e{};
+  e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
+  if (gemm_qknorm_fits(c.dtype, n, 3 * D, c.dh)) {
+    e.kind = EPI_QKNORM;
+    e.gq = hd->B(l, DIT_WB_GQ); e.gk = hd->B(l, DIT_WB_GK);
+    e.q_out = q_out; e.k_out = k_out;
+    e.D = D; e.kpad = round64(n); e.rope = 1;
+    e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.log2_theta = (float)std::log2(c.rope_theta);
+    e.g = g;
+    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
+    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, nullptr, nullptr, big + (size_t)2 * D * L.elt, 3 * D, nullptr,
+                       nullptr, 0, g, (float)c.eps, (float)c.rope_theta, 1.0f, nullptr, nullptr, vt_out, cap, s));
+    return DIT_OK;
+  }
+  e.kind = EPI_BIAS;
+  HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
+  HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, q_out ? big : nullptr, big + (size_t)D * L.elt,
+                     big + (size_t)2 * D * L.elt, 3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g,
+                     (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh), q_out, k_out, vt_out, cap, s));
+  return DIT_OK;
+}
+
 // One context pass (reference, boundary or interpolation anchor) at t = 0: writes K
 // (normed, rotated) and V of every block into kdst[l] / vdst[l] (capacity cap).  The
 // tokens attend to the earlier context segments and themselves: nprior 0 (reference:
@@ -423,15 +455,8 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     if (int rc = block_begin(hd, l)) return rc;
     HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
-    e = GemmEpi{};
-    e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
-    const char* big = hd->X<char>(L.big);
-    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, last ? nullptr : big, big + (size_t)D * L.elt,
-                       big + (size_t)2 * D * L.elt, 3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK),
-                       1, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q),
-                       hd->S(kdst[l]),
-                       hd->S(vdst[l]), cap, s));
+    if (int rc = qkv_project(hd, l, n, g, last ? nullptr : hd->X(L.q), hd->S(kdst[l]), hd->S(vdst[l]), cap))
+      return rc;
     if (last) {
       if (int rc = block_end(hd, l)) return rc;
       break;
@@ -706,13 +731,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
     // self-attention
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
-    e = GemmEpi{};
-    e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_QKV_B); e.out = hd->X(L.big); e.ldo = 3 * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
-    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, big + (size_t)D * L.elt, big + (size_t)2 * D * L.elt,
-                       3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g, (float)c.eps,
-                       (float)c.rope_theta, attention_q_scale(c.dh), hd->X(L.q), hd->X(L.kc),
-                       hd->X(L.vtc), L.cap_tok, s));
+    if (int rc = qkv_project(hd, l, n, g, hd->X(L.q), hd->X(L.kc), hd->X(L.vtc), L.cap_tok)) return rc;
     AttnSeg seg[ATTN_MAX_SEGS];
     int ns = 0;
     seg[ns++] = AttnSeg{hd->S(L.kref[l]), hd->S(L.vref[l]), hd->n_ref, L.cap_ref};
@@ -736,11 +755,18 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     if (cross) {
       HIPCHK(rmsnorm_mod(c.dtype, h, n, D, nullptr, nullptr, (float)c.eps, hd->X(L.u), s));
       e = GemmEpi{};
-      e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
-      HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
-      HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
-                         nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
-                         hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
+      e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
+      if (gemm_qknorm_fits(c.dtype, n, D, c.dh)) {  // q-norm in the GEMM epilogue (no RoPE)
+        e.kind = EPI_QKNORM; e.gq = hd->B(l, DIT_WB_GCQ); e.q_out = hd->X(L.q); e.D = D;
+        e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
+        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+      } else {
+        e.kind = EPI_BIAS;
+        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+        HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
+                           nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
+                           hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
+      }
       AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
       if (!held) {
         if (int rc2 = audio_kv(hd, l, M, hd->X(L.ka), hd->X(L.vat))) return rc2;

@@ -111,6 +111,131 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const EpiC
   }
 }
 
+// EPI_QKNORM epilogue of gemm_lds_kernel (bf16, heads of 128 columns).  The tile's 256
+// columns lie in one part of [q | k | v].  v columns are stored as computed (C + b).
+// For q and k, a head's 128 columns are split over two waves (wn even / odd), so each
+// row's sum of squares is completed through LDS (free once the K loop has ended); then
+// each value is normalised, scaled by its gamma (and q_scale for q), pairs (2i, 2i+1)
+// are rotated by the 3D RoPE of the row's token (axis t for the first d_t/2 pairs, then
+// y, then x; pair j of an axis with d_a dims turns at theta^(-2j/d_a)), and the head is
+// written in bf16.  k rows in [M, kpad) are written as zeros.  The rotation uses the
+// hardware sine and cosine (v_sin_f32 / v_cos_f32, argument in turns) on the angle
+// reduced to half a turn; their error is far below the bf16 rounding that follows.
+template <int MB, int NB>
+__device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], const EpiCols<NB, EPI_QKNORM>& cols,
+                                                char* smem, int wm, int wn, int mw, int nw, int l32, int lg,
+                                                int M, const GemmEpi& e) {
+  constexpr int DH = 128;
+  static_assert(NB == 2, "one wave covers half a head (64 columns)");
+  const int part = nw / e.D;
+  if (part == 2) {
+    epilogue<bf16, MB, NB, EPI_BIAS>(acc, reinterpret_cast<const EpiCols<NB, EPI_BIAS>&>(cols), mw, nw, l32, lg,
+                                     M, 3 * e.D, e);
+    return;
+  }
+  const bool isq = part == 0;
+  const int col0 = nw - part * e.D;  // column of the wave's first value within its part
+  const int half = (col0 % DH) / 64;
+  float v[MB][NB][4][4], rs[MB];
+  float* red = reinterpret_cast<float*>(smem);  // [2 wm][4 wn][MB * 32] row partial sums
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[i][j][q][r] = acc[i][j][4 * q + r] + cols.b[j][q][r];
+          ss += v[i][j][q][r] * v[i][j][q][r];
+        }
+    ss += __shfl_xor(ss, 32);
+    rs[i] = ss;
+    if (lg == 0) red[(wm * 4 + wn) * MB * 32 + i * 32 + l32] = ss;
+  }
+  __syncthreads();
+  void* outp = isq ? e.q_out : e.k_out;
+  if (!outp) return;  // q not needed (last block of a context pass)
+  bf16* out = reinterpret_cast<bf16*>(outp);
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const float tot = rs[i] + red[(wm * 4 + (wn ^ 1)) * MB * 32 + i * 32 + l32];
+    rs[i] = 1.0f / sqrtf(tot / (float)DH + e.eps);
+  }
+  // gamma (x q_scale for q) and rotation frequency of the lane's columns
+  const bf16* gam = reinterpret_cast<const bf16*>(isq ? e.gq : e.gk);
+  const float gs = isq ? e.q_scale : 1.0f;
+  constexpr int D_HW = 2 * (DH / 6), D_T = DH - 2 * D_HW;
+  float gm[NB][4][4], inv_freq[NB][4][2];
+  int axis[NB][4][2];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = half * 64 + j * 32 + 8 * q + 4 * lg;  // column within the head
+      load4<bf16>(gam + c, gm[j][q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gm[j][q][r] *= gs;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pair = c / 2 + h2;
+        int jj, da;
+        if (pair < D_T / 2) { axis[j][q][h2] = 0; jj = pair; da = D_T; }
+        else if (pair < D_T / 2 + D_HW / 2) { axis[j][q][h2] = 1; jj = pair - D_T / 2; da = D_HW; }
+        else { axis[j][q][h2] = 2; jj = pair - D_T / 2 - D_HW / 2; da = D_HW; }
+        // turns (revolutions) per position step
+        inv_freq[j][q][h2] = exp2f(-(2.0f * (float)jj / (float)da) * e.log2_theta) * 0.15915494309189535f;
+      }
+    }
+  const int hw = e.g.h * e.g.w;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = mw + i * 32 + l32;
+    bf16* orow = out + (size_t)m * e.D + col0;
+    if (m >= M) {
+      if (!isq && m < e.kpad) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) store4<bf16>(orow + j * 32 + 8 * q + 4 * lg, z);
+      }
+      continue;
+    }
+    float pt = 0.f, py = 0.f, px = 0.f;
+    if (e.rope) {
+      const int f = m / hw, rem = m - f * hw;
+      const int y = rem / e.g.w;
+      pt = (float)(e.g.t0 + f);
+      py = (float)y;
+      px = (float)(rem - y * e.g.w);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float o[4];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float y0 = v[i][j][q][2 * h2] * rs[i] * gm[j][q][2 * h2];
+          const float y1 = v[i][j][q][2 * h2 + 1] * rs[i] * gm[j][q][2 * h2 + 1];
+          float sn = 0.f, cs = 1.f;
+          if (e.rope) {  // hardware sin / cos of the angle reduced to [-1/2, 1/2] turn
+            const int ax = axis[j][q][h2];
+            const float turns = (ax == 0 ? pt : (ax == 1 ? py : px)) * inv_freq[j][q][h2];
+            const float fr = turns - rintf(turns);
+            sn = __builtin_amdgcn_sinf(fr);
+            cs = __builtin_amdgcn_cosf(fr);
+          }
+          o[2 * h2] = y0 * cs - y1 * sn;
+          o[2 * h2 + 1] = y0 * sn + y1 * cs;
+        }
+        store4<bf16>(orow + j * 32 + 8 * q + 4 * lg, o);
+      }
+  }
+}
+
 // Tile order: XCD-contiguous ranges of a grouped order in which GM consecutive
 // m-tiles share each W column block.
 __device__ __forceinline__ void tile_of(int b, int num_m, int num_n, int& tm, int& tn) {
@@ -345,7 +470,10 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
+  if constexpr (EPI == EPI_QKNORM)
+    epilogue_qknorm<MB, NB>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg, M, e);
+  else
+    epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }
 
 template <int BM, int BN>
@@ -361,6 +489,7 @@ hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int
     case EPI_RESID: gemm_lds_kernel<BM, BN, EPI_RESID><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_F32: gemm_lds_kernel<BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_EULER: gemm_lds_kernel<BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_QKNORM: gemm_lds_kernel<BM, BN, EPI_QKNORM><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -500,9 +629,15 @@ __global__ __launch_bounds__(LDS_THREADS) void patch_embed_kernel(
 
 }  // namespace
 
+bool gemm_qknorm_fits(int dtype, int M, int N, int dh) {
+  return dtype == BF16 && dh == 128 && M >= 256 && N % 256 == 0;
+}
+
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                 const GemmEpi& e, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (e.kind == EPI_QKNORM && (!gemm_qknorm_fits(dtype, M, N, 128) || e.D % 256 || (N != e.D && N != 3 * e.D)))
+    return hipErrorInvalidValue;
   if (dtype == BF16) {
     if (M >= 256 && N >= 256 && N % 256 == 0) {
       // Pick the tile height that minimises (waves of 256 workgroups) x tile area,
@@ -516,7 +651,7 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = bm; }
       }
       // Too few tiles to occupy the chip (short context passes): smaller tiles.
-      if (((M + best - 1) / best) * (N / 256) < 160) {
+      if (e.kind != EPI_QKNORM && ((M + best - 1) / best) * (N / 256) < 160) {
         if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
         return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
       }

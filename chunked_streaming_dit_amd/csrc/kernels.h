@@ -7,6 +7,11 @@ namespace dit {
 
 enum Dtype { F32 = 0, BF16 = 1 };
 
+// Token grid of a RoPE'd sequence: token i = (f, y, x) row-major, at position (t0 + f, y, x).
+struct RopeGrid {
+  int t0, frames, h, w;
+};
+
 // ---------------------------------------------------------------- GEMM (MFMA)
 // C = A W^T (+ bias), A [M, K] (lda), W [N, K] (ldw), fp32 accumulation, then:
 enum EpiKind {
@@ -15,6 +20,10 @@ enum EpiKind {
   EPI_RESID = 2,  // h[M, N]   (fp32)  += gate (.) (C + b)      (gate NULL: 1)
   EPI_F32 = 3,    // out[M, N] (fp32)   = C + b
   EPI_EULER = 4,  // v = C + b; x[M, N] (fp32) += dt v; v_out (fp32, optional) = v
+  EPI_QKNORM = 5, // y = C + b over N = [q | k | v] blocks of D columns (k, v optional):
+                  //   q heads: QK-RMSNorm x gq x q_scale (+ 3D RoPE) -> q_out [M, D];
+                  //   k heads: QK-RMSNorm x gk (+ RoPE) -> k_out [kpad, D], rows M..kpad zero;
+                  //   v columns: y -> out [M, ldo] (columns 2D..3D of the C matrix).
 };
 struct GemmEpi {
   int kind;
@@ -24,7 +33,17 @@ struct GemmEpi {
   const float* gate;  // EPI_RESID
   float* v_out;       // EPI_EULER
   float dt;           // EPI_EULER
+  // EPI_QKNORM (bf16, dh = 128): gammas [dh]; q_out may be NULL (q not needed)
+  const void* gq;
+  const void* gk;
+  void* q_out;
+  void* k_out;
+  int D, kpad, rope;
+  float q_scale, eps, log2_theta;
+  RopeGrid g;
 };
+// Whether gemm() can fuse EPI_QKNORM for this launch (else: EPI_BIAS + qknorm_rope).
+bool gemm_qknorm_fits(int dtype, int M, int N, int dh);
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
                 const GemmEpi& e, hipStream_t s);
 
@@ -93,9 +112,6 @@ hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shi
 //   q_out [n, D] (times q_scale), k_out [cap, D], vt_out [D, cap] (attention layout above).
 //   Rows/columns in [n, round_up(n, 64)) of k_out/vt_out are zeroed.
 //   rope: positions from the grid (t0 + f, y, x); rope == 0: no rotation.
-struct RopeGrid {
-  int t0, frames, h, w;
-};
 hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,
                        const void* v_in, int ld_in, const void* gq, const void* gk, int rope,
                        RopeGrid g, float eps, float theta, float q_scale, void* q_out,
