@@ -400,8 +400,8 @@ int audio_kv(dit_handle* hd, int l, int M, void* ka, void* vat) {
 
 // QKV of block l over n tokens (u in the workspace): q (QK-normed, pre-scaled, rotated)
 // -> q_out (NULL: not needed), k (QK-normed, rotated) -> k_out [cap rows], V^T -> vt_out
-// [D, cap].  When the launch allows it the QK-norm and RoPE run in the GEMM's epilogue
-// and only V goes through the repacking kernel.
+// [D, cap].  When the launch allows it the QK-norm, the RoPE and the V^T repack all run
+// in the GEMM's epilogue.
 int qkv_project(dit_handle* hd, int l, int n, RopeGrid g, void* q_out, void* k_out, void* vt_out, int cap) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
@@ -413,13 +413,11 @@ int qkv_project(dit_handle* hd, int l, int n, RopeGrid g, void* q_out, void* k_o
   if (gemm_qknorm_fits(c.dtype, n, 3 * D, c.dh)) {
     e.kind = EPI_QKNORM;
     e.gq = hd->B(l, DIT_WB_GQ); e.gk = hd->B(l, DIT_WB_GK);
-    e.q_out = q_out; e.k_out = k_out;
+    e.q_out = q_out; e.k_out = k_out; e.vt_out = vt_out; e.vcap = cap;
     e.D = D; e.kpad = round64(n); e.rope = 1;
     e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.log2_theta = (float)std::log2(c.rope_theta);
     e.g = g;
     HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
-    HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, nullptr, nullptr, big + (size_t)2 * D * L.elt, 3 * D, nullptr,
-                       nullptr, 0, g, (float)c.eps, (float)c.rope_theta, 1.0f, nullptr, nullptr, vt_out, cap, s));
     return DIT_OK;
   }
   e.kind = EPI_BIAS;

@@ -121,16 +121,54 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const EpiC
 // written in bf16.  k rows in [M, kpad) are written as zeros.  The rotation uses the
 // hardware sine and cosine (v_sin_f32 / v_cos_f32, argument in turns) on the angle
 // reduced to half a turn; their error is far below the bf16 rounding that follows.
-template <int MB, int NB>
+template <int BM, int MB, int NB>
 __device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], const EpiCols<NB, EPI_QKNORM>& cols,
                                                 char* smem, int wm, int wn, int mw, int nw, int l32, int lg,
                                                 int M, const GemmEpi& e) {
   constexpr int DH = 128;
   static_assert(NB == 2, "one wave covers half a head (64 columns)");
   const int part = nw / e.D;
-  if (part == 2) {
+  if (part == 2 && !e.vt_out) {
     epilogue<bf16, MB, NB, EPI_BIAS>(acc, reinterpret_cast<const EpiCols<NB, EPI_BIAS>&>(cols), mw, nw, l32, lg,
                                      M, 3 * e.D, e);
+    return;
+  }
+  if (part == 2) {
+    // V^T: the tile (BM tokens x 256 columns) goes transposed through LDS, then each
+    // thread writes one column's 16-token group in the attention layout (token offset
+    // o of the group at position 8((o%8)/4) + 4(o/8) + o%4); tokens in [M, kpad) as 0.
+    constexpr int P = BM;  // LDS row pitch (tokens) of a column: 256 x BM x 2 bytes fit the ring
+    bf16* st = reinterpret_cast<bf16*>(smem);
+    const int tid = threadIdx.x;
+    const int c0 = nw - (nw / 256) * 256;  // wave's first column within the tile
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            st[(c0 + j * 32 + 8 * q + 4 * lg + r) * P + (mw % BM) + i * 32 + l32] =
+                (bf16)(acc[i][j][4 * q + r] + cols.b[j][q][r]);
+    __syncthreads();
+    const int m0 = mw - mw % BM, ncol0 = nw - c0 - 2 * e.D;  // tile's first token / V column
+    constexpr int G = BM / 16;
+    bf16* vt = reinterpret_cast<bf16*>(e.vt_out);
+    for (int it = tid; it < 256 * G; it += (int)blockDim.x) {
+      const int col = it / G, grp = it - col * G;
+      const int tok0 = m0 + grp * 16;
+      if (tok0 >= e.kpad) continue;
+      typedef bf16 b16 __attribute__((ext_vector_type(16)));
+      b16 o;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int src = u;  // token offset
+        const int pos = 8 * ((src % 8) / 4) + 4 * (src / 8) + src % 4;
+        o[pos] = tok0 + src < M ? st[col * P + grp * 16 + src] : (bf16)0.f;
+      }
+      *reinterpret_cast<b16*>(vt + (size_t)(ncol0 + col) * e.vcap + tok0) = o;
+    }
     return;
   }
   const bool isq = part == 0;
@@ -471,7 +509,7 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     __syncthreads();
   }
   if constexpr (EPI == EPI_QKNORM)
-    epilogue_qknorm<MB, NB>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg, M, e);
+    epilogue_qknorm<BM, MB, NB>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg, M, e);
   else
     epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }

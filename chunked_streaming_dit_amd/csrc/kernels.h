@@ -23,7 +23,8 @@ enum EpiKind {
   EPI_QKNORM = 5, // y = C + b over N = [q | k | v] blocks of D columns (k, v optional):
                   //   q heads: QK-RMSNorm x gq x q_scale (+ 3D RoPE) -> q_out [M, D];
                   //   k heads: QK-RMSNorm x gk (+ RoPE) -> k_out [kpad, D], rows M..kpad zero;
-                  //   v columns: y -> out [M, ldo] (columns 2D..3D of the C matrix).
+                  //   v columns: V^T -> vt_out [D, vcap] in the attention layout (columns
+                  //   M..kpad zero), or, with vt_out NULL, y -> out [M, ldo] (columns 2D..3D).
 };
 struct GemmEpi {
   int kind;
@@ -38,7 +39,8 @@ struct GemmEpi {
   const void* gk;
   void* q_out;
   void* k_out;
-  int D, kpad, rope;
+  void* vt_out;
+  int D, kpad, rope, vcap;
   float q_scale, eps, log2_theta;
   RopeGrid g;
 };
