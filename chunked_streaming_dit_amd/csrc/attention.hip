@@ -19,6 +19,12 @@
 // and the shift all drop out of the loop.
 #include <math.h>
 
+#include <algorithm>
+#include <array>
+#include <map>
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -33,7 +39,8 @@ struct AttnArgs {
   int nseg;
   float scale;  // log2(e) / sqrt(dh), or 1 when q comes pre-scaled
   float thr;    // RESCALE_LOG2 / scale: lazy-rescale threshold in raw score units
-  int nsplit;   // key-range splits per (head, q-tile); > 1 writes partials
+  int nsplit;   // key-range splits per (head, q-tile) from q-tile qt0 on; > 1 writes partials
+  int qt0;      // q-tiles [0, qt0) take the whole key range and write o directly
   float* opart; // [nsplit, nq, H*DH] normalised partial outputs (nsplit > 1)
   float* ml;    // [nsplit, nq, H, 2] (running max * scale, row sum) per partial
   // QK-norm gammas of q and k (or NULL) and the logit bound coefficient: every exp2-domain
@@ -46,6 +53,7 @@ struct AttnArgs {
 
 constexpr int AW = 8;          // waves per workgroup (32 queries each)
 constexpr int BQ = 32 * AW;    // queries per workgroup
+static_assert(BQ == ATTN_QTILE, "q-tile of the split plan");
 constexpr int NSLOT = 3;       // ring depth of the K and of the V^T tile rings
 constexpr float RESCALE_LOG2 = 8.0f;
 // Logit bound (exp2 domain) up to which the softmax is taken without a running max:
@@ -103,14 +111,31 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, lg = lane >> 5;
-  // 1-D grid over (head, q-tile), head-major, remapped so that each XCD works through
-  // a contiguous range: the q-tiles of a head share that head's K/V in one L2.
-  // With nsplit > 1 the work item also names a contiguous part of the key tiles.
+  // 1-D grid of two parts.  The first qt0 * H workgroups take q-tiles [0, qt0) over the
+  // whole key range; the rest take q-tiles [qt0, nqt), each (head, q-tile) split into
+  // nsplit contiguous parts of the key tiles.  The whole-range items come first, so they
+  // are dispatched first and the shorter split items fill the last wave.  Within each
+  // part the order is head-major and remapped so that each XCD works through a
+  // contiguous range: the q-tiles of a head share that head's K/V in one L2.
   const int nqt = (a.nq + BQ - 1) / BQ;
-  const int wi = xcd_remap(blockIdx.x, nqt * a.H * a.nsplit);
-  const int hs = wi / nqt;                      // head * nsplit + split
-  const int head = hs / a.nsplit, split = hs - head * a.nsplit;
-  const int qrow = (wi - hs * nqt) * BQ + wave * 32 + l32;
+  const int n1 = a.qt0 * a.H;
+  int head, split, nsp, qt;
+  if ((int)blockIdx.x < n1) {
+    const int wi = xcd_remap(blockIdx.x, n1);
+    head = wi / a.qt0;
+    qt = wi - head * a.qt0;
+    split = 0;
+    nsp = 1;
+  } else {
+    const int nqs = nqt - a.qt0;
+    const int wi = xcd_remap(blockIdx.x - n1, nqs * a.H * a.nsplit);
+    const int hs = wi / nqs;  // head * nsplit + split
+    head = hs / a.nsplit;
+    split = hs - head * a.nsplit;
+    nsp = a.nsplit;
+    qt = a.qt0 + (wi - hs * nqs);
+  }
+  const int qrow = qt * BQ + wave * 32 + l32;
   const bool qvalid = qrow < a.nq;
 
   // Q fragments (second MFMA operand): query qrow, dh = s*2VE + lg*VE + [0, VE).
@@ -148,8 +173,8 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   static_assert(ATTN_MAX_SEGS == 4, "segment walk below");
   const int e1 = c[0], e2 = e1 + c[1], e3 = e2 + c[2];
   const int ntiles = e3 + c[3];
-  const int tb = (int)((long long)ntiles * split / a.nsplit);
-  const int total = (int)((long long)ntiles * (split + 1) / a.nsplit);  // tiles [tb, total)
+  const int tb = (int)((long long)ntiles * split / nsp);
+  const int total = (int)((long long)ntiles * (split + 1) / nsp);  // tiles [tb, total)
   auto locate = [&](int t, int& si, int& base) {
     if (t < e1) { si = 0; base = t * BKV; }
     else if (t < e2) { si = 1; base = (t - e1) * BKV; }
@@ -409,7 +434,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (a.nsplit == 1) {
+  if (nsp == 1) {
     T* op = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * DH;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
@@ -440,17 +465,18 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge key-range partials: o = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - max m).
-// One thread per (query, head, 4 consecutive dh).
+// Merge key-range partials of queries [r0, nq): o = sum_s w_s o_s / sum_s w_s,
+// w_s = l_s 2^(m_s - max m).  One thread per (query, head, 4 consecutive dh).
 template <class T, int DH>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ opart,
                                                            const float* __restrict__ ml, int nsplit,
-                                                           int nq, int H, T* __restrict__ o, int ldo) {
+                                                           int r0, int nq, int H, T* __restrict__ o,
+                                                           int ldo) {
   const int D = H * DH;
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)nq * D / 4) return;
-  const int qrow = (int)(i / (D / 4));
-  const int c = (int)(i - (long long)qrow * (D / 4)) * 4;
+  if (i >= (long long)(nq - r0) * D / 4) return;
+  const int qrow = r0 + (int)(i / (D / 4));
+  const int c = (int)(i - (long long)(qrow - r0) * (D / 4)) * 4;
   const int head = c / DH;
   float mmax = -INFINITY;
   for (int sp = 0; sp < nsplit; ++sp) mmax = fmaxf(mmax, ml[(((size_t)sp * nq + qrow) * H + head) * 2]);
@@ -590,19 +616,68 @@ __global__ __launch_bounds__(64 * XW, 3) void xattn_kernel(XArgs a) {
 
 }  // namespace
 
-// Key-range splits for a launch: the smallest estimated time, counting waves of
-// `slots` concurrent workgroups and a small fixed cost for the merge pass.  Splitting
-// needs at least 2 tiles per split and partial storage for nsplit * nq rows.
-int attention_splits(int nq, int H, int total_keys_tiles, int partial_rows, int slots) {
-  const int nqt = (nq + BQ - 1) / BQ;
-  int best = 1;
-  double best_cost = 1e30;
-  for (int ns = 1; ns <= 4; ++ns) {
-    if (ns > 1 && (total_keys_tiles < 2 * ns || (long long)ns * nq > partial_rows)) break;
-    const long long items = (long long)nqt * H * ns;
-    const double cost = (double)((items + slots - 1) / slots) / ns + (ns > 1 ? 0.05 : 0.0);
-    if (cost < best_cost - 1e-9) { best_cost = cost; best = ns; }
+// Key-range split plan of a launch.  Workgroups are modelled as dispatched in grid
+// order, round-robin over the 8 XCDs, each XCD list-scheduling its share on slots/8
+// concurrent slots; a workgroup of k key tiles takes k + ATTN_WG_FIXED tile-times.  For
+// every split count (1..4) and first split q-tile qt0 the plan takes the modelled
+// makespan plus the merge pass (ATTN_MERGE_COST tile-times per split part of a
+// (head, q-tile), spread over the chip) and keeps the cheapest; at equal cost, fewer
+// parts and fewer split q-tiles.  Splitting needs at least 2 tiles per part and partial
+// storage for nsplit * nq rows.  Plans are memoised per shape.
+constexpr double ATTN_WG_FIXED = 2.0;
+constexpr double ATTN_MERGE_COST = 0.02;
+
+static double attention_makespan(int nqt, int H, int key_tiles, int ns, int qt0, int slots) {
+  constexpr int NXCD = 8;
+  const int per = slots / NXCD > 0 ? slots / NXCD : 1;
+  const long long n1 = (long long)qt0 * H;
+  const long long n = n1 + (long long)(nqt - qt0) * H * ns;
+  const double c1 = key_tiles + ATTN_WG_FIXED, c2 = (double)key_tiles / ns + ATTN_WG_FIXED;
+  double worst = 0.0;
+  std::vector<double> busy(per);
+  for (int x = 0; x < NXCD && x < n; ++x) {
+    std::fill(busy.begin(), busy.end(), 0.0);
+    for (long long b = x; b < n; b += NXCD) {
+      // earliest free slot of this XCD takes block b
+      size_t k = std::min_element(busy.begin(), busy.end()) - busy.begin();
+      busy[k] += b < n1 ? c1 : c2;
+    }
+    worst = std::max(worst, *std::max_element(busy.begin(), busy.end()));
   }
+  return worst;
+}
+
+AttnSplit attention_plan(int nq, int H, int key_tiles, int partial_rows, int slots) {
+  AttnSplit best{1, 0, nullptr, nullptr};
+  if (nq <= 0 || H <= 0 || key_tiles <= 0) return best;
+  static std::mutex mu;
+  static std::map<std::array<int, 5>, std::pair<int, int>> memo;
+  const std::array<int, 5> key{nq, H, key_tiles, partial_rows, slots};
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) {
+      best.nsplit = it->second.first;
+      best.qt0 = it->second.second;
+      return best;
+    }
+  }
+  const int nqt = (nq + BQ - 1) / BQ;
+  double best_cost = attention_makespan(nqt, H, key_tiles, 1, 0, slots);
+  for (int ns = 2; ns <= 4; ++ns) {
+    if (key_tiles < 2 * ns || (long long)ns * nq > partial_rows) break;
+    for (int qt0 = nqt - 1; qt0 >= 0; --qt0) {
+      const double cost = attention_makespan(nqt, H, key_tiles, ns, qt0, slots) +
+                          ATTN_MERGE_COST * ns * (double)(nqt - qt0) * H;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best.nsplit = ns;
+        best.qt0 = qt0;
+      }
+    }
+  }
+  std::lock_guard<std::mutex> g(mu);
+  memo.emplace(key, std::make_pair(best.nsplit, best.qt0));
   return best;
 }
 
@@ -612,6 +687,8 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
   if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
+  const int nqt = (nq + BQ - 1) / BQ;
+  const int qt0 = sp.nsplit > 1 ? std::min(std::max(sp.qt0, 0), nqt) : 0;
   AttnArgs a;
   a.q = q;
   a.o = o;
@@ -624,6 +701,7 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.scale = q_prescaled ? 1.0f : attention_q_scale(dh);
   a.thr = RESCALE_LOG2 / a.scale;
   a.nsplit = sp.nsplit;
+  a.qt0 = qt0;
   a.opart = sp.opart;
   a.ml = sp.ml;
   // q = q_fold (gq . q^) and k = gk . k^ with |q^|^2, |k^|^2 <= dh (RMS-normed rows), so
@@ -632,7 +710,7 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.gk = a.gq ? norm->gk : nullptr;
   a.bcoef = a.gq ? (float)(norm->q_fold * dh * 1.02) : 0.f;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
-  dim3 grid(((nq + BQ - 1) / BQ) * H * sp.nsplit), block(64 * AW);
+  dim3 grid(qt0 * H + (nqt - qt0) * H * sp.nsplit), block(64 * AW);
   const bool cross = kind == ATTN_CROSS;
   if (dtype == BF16 && dh == 128) {
     if (cross) attn_kernel<bf16, 128, 1><<<grid, block, 0, s>>>(a);
@@ -677,14 +755,16 @@ hipError_t short_attention(int dh, int H, const void* q, int ldq, void* o, int l
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
                              hipStream_t s) {
   if (nq <= 0 || sp.nsplit <= 1) return hipSuccess;
-  const long long n4 = (long long)nq * H * dh / 4;
+  const int r0 = std::min(std::max(sp.qt0, 0) * BQ, nq);  // rows before r0 were not split
+  if (r0 >= nq) return hipSuccess;
+  const long long n4 = (long long)(nq - r0) * H * dh / 4;
   dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
   if (dtype == BF16 && dh == 128)
-    attn_combine_kernel<bf16, 128><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (bf16*)o, ldo);
+    attn_combine_kernel<bf16, 128><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (bf16*)o, ldo);
   else if (dtype == BF16 && dh == 64)
-    attn_combine_kernel<bf16, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (bf16*)o, ldo);
+    attn_combine_kernel<bf16, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (bf16*)o, ldo);
   else if (dtype == F32 && dh == 64)
-    attn_combine_kernel<float, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, nq, H, (float*)o, ldo);
+    attn_combine_kernel<float, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (float*)o, ldo);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -342,8 +342,9 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
     HIPCHK(short_attention(c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, seg[0], true, hd->stream));
     return DIT_OK;
   }
-  AttnSplit sp{1, hd->X<float>(L.opart), hd->X<float>(L.ml)};
-  sp.nsplit = attention_splits(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
+  AttnSplit sp = attention_plan(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
+  sp.opart = hd->X<float>(L.opart);
+  sp.ml = hd->X<float>(L.ml);
   int slot = -1, rc;
   if (timed && (rc = timed_begin(hd, &slot))) return rc;
   const bool cross = kind == ATTN_CROSS;

@@ -67,11 +67,17 @@ enum { ATTN_MAX_SEGS = 4 };  // reference | boundary | anchor | chunk
 // opart [nsplit, nq, H*dh] and (running max of the exp2-domain logits, row sum) pairs
 // ml [nsplit, nq, H, 2]
 // (fp32), which attention_combine() merges into o.
+// Key-range split of an attention launch: the q-tiles (ATTN_QTILE queries) from qt0 on
+// are each split into nsplit contiguous parts of the key tiles, computed by separate
+// workgroups into opart/ml and merged by attention_combine; q-tiles before qt0 take the
+// whole key range and write o directly.  nsplit == 1: no split (qt0 ignored).
 struct AttnSplit {
   int nsplit;
+  int qt0;
   float* opart;
   float* ml;
 };
+constexpr int ATTN_QTILE = 256;
 // o[nq, ldo] = softmax(q k^T / sqrt(dh)) v over the concatenated segments, per head.
 // q_prescaled: q holds q * log2(e)/sqrt(dh) (as written by qknorm_rope with that
 // q_scale), the form the kernels consume; otherwise the kernel scales q itself (for
@@ -98,9 +104,10 @@ hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& 
 bool short_attention_fits(int dtype, int dh, int nseg, const AttnSeg* segs);
 hipError_t short_attention(int dh, int H, const void* q, int ldq, void* o, int ldo, int nq, const AttnSeg& seg,
                            bool q_prescaled, hipStream_t s);
-// Splits minimising the estimated time for nq queries, H heads, key_tiles 64-key tiles,
-// partial storage of partial_rows rows and `slots` concurrent workgroups.
-int attention_splits(int nq, int H, int key_tiles, int partial_rows, int slots);
+// Split plan (nsplit, qt0; no buffers) minimising the modelled time for nq queries, H
+// heads, key_tiles 64-key tiles, partial storage of partial_rows rows and `slots`
+// concurrent workgroups.
+AttnSplit attention_plan(int nq, int H, int key_tiles, int partial_rows, int slots);
 int attention_key_tiles(const AttnSeg* segs, int nseg);
 int device_cus();
 

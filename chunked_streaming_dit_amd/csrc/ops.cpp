@@ -114,8 +114,8 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, int q_prescaled, const void* gq, const void* gk,
-                   double q_fold, void* o, void* stream) {
+                   int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
+                   const void* gk, double q_fold, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if ((gq != nullptr) != (gk != nullptr)) return fail(DIT_EINVAL, "gq and gk must both be given or both NULL");
   if (gq && !(q_fold > 0 && std::isfinite(q_fold))) return fail(DIT_EINVAL, "q_fold must be finite and > 0");
@@ -134,12 +134,16 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
   }
   if (total < 1) return fail(DIT_ESHAPE, "no keys");
   if (nsplit < 1 || nsplit > 8) return fail(DIT_EINVAL, "nsplit=%d out of [1, 8]", nsplit);
+  if (unsplit_rows < 0 || (unsplit_rows % ATTN_QTILE && unsplit_rows < nq))
+    return fail(DIT_EINVAL, "unsplit_rows=%d: must be >= 0 and a multiple of %d or >= nq=%d", unsplit_rows,
+                ATTN_QTILE, nq);
+  if (unsplit_rows >= nq) nsplit = 1;  // nothing left to split
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   const int D = H * dh;
   if (nsplit == 1 && short_attention_fits(dtype, dh, nseg, seg))
     return hipchk(short_attention(dh, H, q, D, o, D, nq, seg[0], q_prescaled != 0, (hipStream_t)stream),
                   "short_attention");
-  AttnSplit sp{nsplit, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
+  AttnSplit sp{nsplit, unsplit_rows / ATTN_QTILE, partial, partial ? partial + (size_t)nsplit * nq * D : nullptr};
   const AttnNorm norm{gq, gk, q_fold};
   int rc = hipchk(attention(dtype, dh, H, q, D, o, D, nq, D, seg, nseg, sp, q_prescaled != 0,
                             (hipStream_t)stream, ATTN_SELF, gq ? &norm : nullptr),

@@ -278,16 +278,18 @@ class ops:
     def attention(dtype: str, dh: int, H: int, q, segs: Sequence[Tuple[torch.Tensor, torch.Tensor, int, int]],
                   o, nsplit: int = 1, partial: Optional[torch.Tensor] = None,
                   q_prescaled: bool = False, gq: Optional[torch.Tensor] = None,
-                  gk: Optional[torch.Tensor] = None, q_fold: float = 0.0) -> None:
+                  gk: Optional[torch.Tensor] = None, q_fold: float = 0.0, unsplit_rows: int = 0) -> None:
         """gq, gk: QK-norm gammas of normed q (times q_fold) and k: lets the kernel bound
-        the logits and drop the running max (ditk_attention)."""
+        the logits and drop the running max.  unsplit_rows: leading queries (a multiple of
+        256, or >= nq) that take the whole key range unsplit (ditk_attention)."""
         ns = len(segs)
         kp = (C.P * ns)(*[s[0].data_ptr() for s in segs])
         vp = (C.P * ns)(*[s[1].data_ptr() for s in segs])
         nn = (ctypes.c_int * ns)(*[s[2] for s in segs])
         cp = (ctypes.c_int * ns)(*[s[3] for s in segs])
         C.check(C.lib().ditk_attention(_dt_code(dtype), dh, H, q.data_ptr(), q.shape[0], ns, kp, vp, nn,
-                                       cp, nsplit, _ptr(partial), 1 if q_prescaled else 0, _ptr(gq),
+                                       cp, nsplit, _ptr(partial), int(unsplit_rows),
+                                       1 if q_prescaled else 0, _ptr(gq),
                                        _ptr(gk), float(q_fold), o.data_ptr(), _stream()))
 
     @staticmethod

@@ -58,7 +58,11 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
  * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
  * nsplit (1..8) splits the key tiles into contiguous parts computed by separate
  * workgroups and merged afterwards; nsplit > 1 needs partial: fp32 scratch of
- * nsplit * nq * (H*dh + 2*H) floats (NULL allowed for nsplit == 1).
+ * nsplit * nq * (H*dh + 2*H) floats (NULL allowed when nothing is split).
+ * unsplit_rows: queries [0, unsplit_rows) are not split (each 256-query tile takes the
+ * whole key range in one workgroup); the split applies from there on.  It must be a
+ * multiple of 256 or >= nq (then nothing is split); 0 splits every query (DIT_EINVAL
+ * otherwise).
  * q_prescaled != 0: q holds q * log2(e)/sqrt(dh) (ditk_qknorm_rope with that q_scale;
  * the softmax is then taken in base 2 on q k^T directly).  q_prescaled == 0: plain q,
  * scaled inside the kernel (for bf16 with dh = 128 this rounds the scaled q to bf16
@@ -73,8 +77,8 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
  * cross-attention's shape) runs a single-tile kernel with the exact softmax. */
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, int q_prescaled, const void* gq, const void* gk,
-                   double q_fold, void* o, void* hip_stream);
+                   int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
+                   const void* gk, double q_fold, void* o, void* hip_stream);
 
 /* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
  * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,

@@ -171,13 +171,21 @@ def test_euler_and_ops_validation():
     k = (C.P * 1)(FAKE)
     n = (ctypes.c_int * 1)(70)
     cap = (ctypes.c_int * 1)(64)
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, None, None, 0.0, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_ESHAPE
     n[0] = 40
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
-    assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    # unsplit_rows: negative, or neither a multiple of the 256-query tile nor >= nq
+    assert lib.ditk_attention(1, 128, 2, FAKE, 300, 1, k, k, n, cap, 2, FAKE, -1, 0, None, None, 0.0, FAKE,
+                              None) == C.DIT_EINVAL
+    assert lib.ditk_attention(1, 128, 2, FAKE, 300, 1, k, k, n, cap, 2, FAKE, 100, 0, None, None, 0.0, FAKE,
+                              None) == C.DIT_EINVAL
+    # rows 256..299 are still split, so the partial buffer is required
+    assert lib.ditk_attention(1, 128, 2, FAKE, 300, 1, k, k, n, cap, 2, None, 256, 0, None, None, 0.0, FAKE,
+                              None) == C.DIT_EINVAL
     n[0] = 0
-    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, None, None, 0.0, FAKE, None) == C.DIT_ESHAPE  # no keys
+    assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_ESHAPE  # no keys
     gp = C.DitGrid(0, 2, 4, 6)
     assert lib.ditk_patch_embed(FAKE, 0, 64, None, 0, 0, gp, FAKE, FAKE, FAKE, 256, None) == C.DIT_OK  # empty
     assert lib.ditk_patch_embed(FAKE, 48, 64, None, 0, 0, gp, FAKE, FAKE, FAKE, 320, None) == C.DIT_ESHAPE  # D % 256

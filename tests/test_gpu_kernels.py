@@ -157,7 +157,7 @@ def _normed(r, n, H, dh, g, fold, dtype):
     return synth.round_bf16(a) if dtype == "bf16" else a
 
 
-def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False, gamma=None):
+def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False, gamma=None, unsplit_rows=0):
     """prescaled: the kernel gets q as the exp2-domain logit scale (q * log2(e)/sqrt(dh)); the
     oracle then takes q / that factor in fp64, so both see the same logits exactly.
     gamma = (mean, spread): q and k are QK-normed rows with gammas mean + spread N(0, 1),
@@ -191,9 +191,11 @@ def _attn_case(dtype, dh, H, nq, seg_ns, seed, nsplit=1, prescaled=False, gamma=
     part = torch.empty(nsplit * nq * (D + 2 * H), device=dev) if nsplit > 1 else None
     if gamma is not None:
         ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled,
-                      gq=_dev(gq, dtype, dev), gk=_dev(gk, dtype, dev), q_fold=Q_SCALE[dh])
+                      gq=_dev(gq, dtype, dev), gk=_dev(gk, dtype, dev), q_fold=Q_SCALE[dh],
+                      unsplit_rows=unsplit_rows)
     else:
-        ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled)
+        ops.attention(dtype, dh, H, _dev(q, dtype, dev), segs, o, nsplit, part, q_prescaled=prescaled,
+                      unsplit_rows=unsplit_rows)
     K = np.concatenate(ks).astype(np.float64).reshape(-1, H, dh)
     V = np.concatenate(vs).astype(np.float64).reshape(-1, H, dh)
     q64 = q.astype(np.float64) / (Q_SCALE[dh] if prescaled else 1.0)
@@ -225,6 +227,20 @@ def test_attention(dtype, dh, nq, seg_ns, prescaled):
 def test_attention_key_split(dtype, dh, nsplit, nq, seg_ns):
     """Key tiles split over workgroups and merged; includes splits with no tiles."""
     err = _attn_case(dtype, dh, 2, nq, seg_ns, nq + sum(seg_ns) + nsplit, nsplit, prescaled=True)
+    assert err <= TOL[dtype] / 4, err
+
+
+@pytest.mark.parametrize("dtype,dh", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("nsplit", [2, 3])
+@pytest.mark.parametrize("nq,unsplit,seg_ns", [(300, 256, [70, 33, 129]), (600, 256, [64, 0, 200]),
+                                               (600, 512, [130, 1, 1000]), (513, 512, [70, 33, 65, 129]),
+                                               (600, 768, [200])])
+def test_attention_partial_split(dtype, dh, nsplit, nq, unsplit, seg_ns):
+    """Only the queries from unsplit_rows on are split (the leading 256-query tiles take
+    the whole key range and write the output directly); the merge covers only the split
+    rows, including a split part of a single query and unsplit_rows past nq."""
+    err = _attn_case(dtype, dh, 3, nq, seg_ns, nq + sum(seg_ns) + nsplit + unsplit, nsplit, prescaled=True,
+                     unsplit_rows=unsplit)
     assert err <= TOL[dtype] / 4, err
 
 
