@@ -46,6 +46,7 @@ class DitError(RuntimeError):
 _lib: Optional[ctypes.CDLL] = None
 
 DIT_AUDIO_HELD = -1
+DIT_MOD_TABLE_MAX = 16
 P = ctypes.c_void_p
 I = ctypes.c_int
 Dbl = ctypes.c_double
@@ -58,6 +59,7 @@ _SIGS = {
                        ctypes.c_size_t, P, ctypes.POINTER(P)]),
     "dit_destroy": (I, [P]),
     "audio_kv_precompute": (I, [P, P, I]),
+    "dit_modulation_table": (I, [P, ctypes.POINTER(Dbl), I]),
     "dit_block_weight_bytes": (ctypes.c_size_t, [ctypes.POINTER(DitConfig)]),
     "dit_weight_stream": (I, [P, ctypes.POINTER(P), P, ctypes.c_size_t, I]),
     "ref_kv_precompute": (I, [P, P, DitGrid]),

@@ -54,6 +54,8 @@ struct Layout {
   int cap_tok = 0, cap_ref = 0, cap_bnd = 0, cap_audio = 0, F = 0, C_in = 0, big_cols = 0;
   // state
   std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc, kaud, vaud;
+  size_t modtab = 0;  // DIT_MOD_TABLE_MAX entries of mod_entry floats
+  size_t mod_entry = 0;
   size_t state_total = 0;
   // workspace
   size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
@@ -112,6 +114,8 @@ Layout make_layout(const dit_config* c) {
     L.kaud.push_back(take(aud));
     L.vaud.push_back(take(aud));
   }
+  L.mod_entry = ((size_t)c->L * 6 + 2) * D;
+  L.modtab = take(DIT_MOD_TABLE_MAX * L.mod_entry * 4);
   L.state_total = off;
   off = 0;
   const size_t T = L.cap_tok;
@@ -180,6 +184,7 @@ struct dit_handle {
   hipStream_t stream = nullptr;
   bool has_ref = false;
   int n_ref = 0, n_bnd = 0, n_anc = 0, n_aud = 0;
+  std::vector<double> mod_t;  // timesteps of the modulation table entries
   // timing
   bool timing = false;
   std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created lazily
@@ -205,6 +210,14 @@ namespace {
     hipError_t e_ = (expr);                                                            \
     if (e_ != hipSuccess) return fail(DIT_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
+
+// The modulation table entry held for timestep t (dit_modulation_table), or NULL: then
+// the pass computes its modulation itself.  Entry layout: [L, 6, D] then [2, D].
+const float* mod_table_entry(const dit_handle* hd, double t) {
+  for (size_t j = 0; j < hd->mod_t.size(); ++j)
+    if (hd->mod_t[j] == t) return hd->S<float>(hd->lay.modtab) + j * hd->lay.mod_entry;
+  return nullptr;
+}
 
 // Bytes of block weight entry i (0 for absent cross-attention entries).
 size_t block_entry_bytes(const dit_config& c, int i) {
@@ -440,19 +453,22 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
   const int D = c.D, F = L.F;
   hipStream_t s = hd->stream;
   float* mod = hd->X<float>(L.mod);
-  float* fmod = mod + (size_t)c.L * 6 * D;
-  HIPCHK(modulation(c.dtype, D, 0, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
-                    hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
-                    hd->X<float>(L.tmp), mod, fmod, s));
+  const float* tab = mod_table_entry(hd, 0.0);
+  if (!tab)
+    HIPCHK(modulation(c.dtype, D, 0, 0.0, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                      hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
+                      hd->X<float>(L.tmp), mod, mod + (size_t)c.L * 6 * D, s));
   const float* cvec = hd->X<float>(L.tmp) + 256 + D;
   float* h = hd->X<float>(L.h);
   if (const int rc = embed(hd, z, n, nullptr, 0, g, h)) return rc;
   GemmEpi e{};
   for (int l = 0; l < c.L; ++l) {
-    float* m = mod + (size_t)l * 6 * D;
+    const float* m = (tab ? tab : mod) + (size_t)l * 6 * D;
     const bool last = l == c.L - 1;
     if (int rc = block_begin(hd, l)) return rc;
-    HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
+    if (!tab)
+      HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec,
+                              mod + (size_t)l * 6 * D, s));
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
     if (int rc = qkv_project(hd, l, n, g, last ? nullptr : hd->X(L.q), hd->S(kdst[l]), hd->S(vdst[l]), cap))
       return rc;
@@ -679,6 +695,44 @@ int audio_kv_precompute(dit_handle* h, const float* audio, int M) {
   return DIT_OK;
 }
 
+int dit_modulation_table(dit_handle* h, const double* t, int nt) {
+  if (!h) return fail(DIT_EINVAL, "handle is NULL");
+  if (nt < 0 || nt > DIT_MOD_TABLE_MAX) return fail(DIT_EINVAL, "nt=%d out of [0, %d]", nt, DIT_MOD_TABLE_MAX);
+  if (nt > 0 && !t) return fail(DIT_EINVAL, "t is NULL with nt=%d", nt);
+  for (int j = 0; j < nt; ++j)
+    if (!std::isfinite(t[j])) return fail(DIT_EINVAL, "t[%d] is not finite", j);
+  static_assert(DIT_MOD_TABLE_MAX <= MOD_BATCH, "one batched launch per weight matrix");
+  h->mod_t.clear();
+  if (nt == 0) return DIT_OK;
+  const dit_config& c = h->cfg;
+  const Layout& L = h->lay;
+  const int D = c.D;
+  hipStream_t s = h->stream;
+  // scratch: the attention partials, unused between passes; the conditioning c[j] after
+  // the feature and hidden rows of timestep_cond_batch
+  if ((size_t)MOD_BATCH * (256 + 2 * D) > (size_t)L.part_rows * D)
+    return fail(DIT_EWORKSPACE, "modulation scratch exceeds the partial buffer");
+  float* tmp = h->X<float>(L.opart);
+  float* cv = tmp + (size_t)MOD_BATCH * (256 + D);
+  float* tab = h->S<float>(L.modtab);
+  const int E = (int)L.mod_entry;
+  HIPCHK(timestep_cond_batch(c.dtype, D, t, nt, h->W(DIT_W_T1_W), h->W(DIT_W_T1_B), h->W(DIT_W_T2_W),
+                             h->W(DIT_W_T2_B), tmp, cv, s));
+  HIPCHK(gemv_batch(c.dtype, 2 * D, D, h->W(DIT_W_FMOD_W), h->W(DIT_W_FMOD_B), cv, D, nt,
+                    tab + (size_t)c.L * 6 * D, E, s));
+  int rc = pass_begin(h);
+  for (int l = 0; l < c.L && !rc; ++l) {
+    rc = block_begin(h, l);
+    if (!rc && gemv_batch(c.dtype, 6 * D, D, h->B(l, DIT_WB_MOD_W), h->B(l, DIT_WB_MOD_B), cv, D, nt,
+                          tab + (size_t)l * 6 * D, E, s) != hipSuccess)
+      rc = fail(DIT_EHIP, "gemv_batch: %s", hipGetErrorString(hipGetLastError()));
+    if (!rc) rc = block_end(h, l);
+  }
+  if ((rc = pass_end(h, rc))) return rc;
+  h->mod_t.assign(t, t + nt);
+  return DIT_OK;
+}
+
 int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_pos) {
   if (!h) return fail(DIT_EINVAL, "handle is NULL");
   if (next.frames == 0) {
@@ -711,10 +765,12 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
   hipStream_t s = hd->stream;
   RopeGrid g{chunk.t0, chunk.frames, chunk.h, chunk.w};
   float* mod = hd->X<float>(L.mod);
-  float* fmod = mod + (size_t)c.L * 6 * D;
-  HIPCHK(modulation(c.dtype, D, 0, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
-                    hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
-                    hd->X<float>(L.tmp), mod, fmod, s));
+  const float* tab = mod_table_entry(hd, t);
+  const float* fmod = (tab ? tab : mod) + (size_t)c.L * 6 * D;
+  if (!tab)
+    HIPCHK(modulation(c.dtype, D, 0, t, hd->W(DIT_W_T1_W), hd->W(DIT_W_T1_B), hd->W(DIT_W_T2_W),
+                      hd->W(DIT_W_T2_B), nullptr, nullptr, hd->W(DIT_W_FMOD_W), hd->W(DIT_W_FMOD_B),
+                      hd->X<float>(L.tmp), mod, mod + (size_t)c.L * 6 * D, s));
   const float* cvec = hd->X<float>(L.tmp) + 256 + D;
   const bool held = M == DIT_AUDIO_HELD;
   const bool cross = held || (M > 0 && c.d_a > 0);
@@ -725,9 +781,11 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
   GemmEpi e{};
   const char* big = hd->X<char>(L.big);
   for (int l = 0; l < c.L; ++l) {
-    float* m = mod + (size_t)l * 6 * D;
+    const float* m = (tab ? tab : mod) + (size_t)l * 6 * D;
     if (int rc = block_begin(hd, l)) return rc;
-    HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec, m, s));
+    if (!tab)
+      HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec,
+                              mod + (size_t)l * 6 * D, s));
     // self-attention
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
     if (int rc = qkv_project(hd, l, n, g, hd->X(L.q), hd->X(L.kc), hd->X(L.vtc), L.cap_tok)) return rc;

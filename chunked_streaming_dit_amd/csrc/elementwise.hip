@@ -276,44 +276,77 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 
 // ---------------------------------------------------------------- timestep conditioning
 // phi(t) = [cos(s w_i) || sin(s w_i)], s = 1000 t, w_i = 10000^(-i/128), in double.
-__global__ void timestep_features_kernel(double t, float* __restrict__ phi) {
+__device__ __forceinline__ void timestep_features_at(double t, float* __restrict__ phi) {
   const int i = threadIdx.x;  // 128 threads
   const double s = 1000.0 * t;
   const double w = pow(10000.0, -(double)i / 128.0);
   phi[i] = (float)cos(s * w);
   phi[128 + i] = (float)sin(s * w);
 }
+__global__ void timestep_features_kernel(double t, float* __restrict__ phi) { timestep_features_at(t, phi); }
+// Features of up to MOD_BATCH timesteps, one workgroup each: phi[j] = features of t[j].
+struct TimeBatch {
+  double t[MOD_BATCH];
+};
+__global__ void timestep_features_batch_kernel(TimeBatch tb, float* __restrict__ phi) {
+  timestep_features_at(tb.t[blockIdx.x], phi + (size_t)blockIdx.x * 256);
+}
 
-// y[r] = act(W[r, :] . x + b[r]) for r < R; one wave per output row.  A lane reads 16
-// bytes of the row per step (8 bf16 or 4 fp32); K is a multiple of 256, and the steps
-// are unrolled so that a row's loads are in flight together.
-template <class T, int ACT>
+// y_j[r] = act(W[r, :] . x_j + b[r]) for r < R and nt <= NT vectors x_j (x_j at
+// x + j ldx, y_j at y + j ldy); one wave per output row, so every weight row is read
+// once for all nt vectors.  A lane reads 16 bytes of the row per step (8 bf16 or 4
+// fp32); K is a multiple of 256, and the steps are unrolled so that a row's loads are
+// in flight together.
+template <class T, int ACT, int NT>
 __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
                                                    const T* __restrict__ b, int R, int K,
-                                                   const float* __restrict__ x,
-                                                   float* __restrict__ y) {
+                                                   const float* __restrict__ x, int ldx, int nt,
+                                                   float* __restrict__ y, int ldy) {
   typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
   const T* wr = W + (size_t)r * K;
-  float acc = 0.f;
+  float acc[NT];
+#pragma unroll
+  for (int v = 0; v < NT; ++v) acc[v] = 0.f;
 #pragma unroll 4
   for (int k = lane * VE; k < K; k += 64 * VE) {
     const V w = as_vec<V>(ld16(wr + k));
 #pragma unroll
-    for (int j = 0; j < VE; j += 4) {
-      const f32x4 x4 = *reinterpret_cast<const f32x4*>(x + k + j);
-      acc += to_f(w[j]) * x4[0] + to_f(w[j + 1]) * x4[1] + to_f(w[j + 2]) * x4[2] + to_f(w[j + 3]) * x4[3];
+    for (int v = 0; v < NT; ++v) {
+      if (v < nt) {
+        const float* xv = x + (size_t)v * ldx;
+#pragma unroll
+        for (int j = 0; j < VE; j += 4) {
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(xv + k + j);
+          acc[v] += to_f(w[j]) * x4[0] + to_f(w[j + 1]) * x4[1] + to_f(w[j + 2]) * x4[2] + to_f(w[j + 3]) * x4[3];
+        }
+      }
     }
   }
-  acc = wave_sum(acc);
-  if (lane == 0) {
-    float v = acc + to_f(b[r]);
-    if (ACT) v = silu(v);
-    y[r] = v;
+#pragma unroll
+  for (int v = 0; v < NT; ++v) {
+    if (v < nt) {
+      const float a = wave_sum(acc[v]);
+      if (lane == 0) {
+        float o = a + to_f(b[r]);
+        if (ACT) o = silu(o);
+        y[(size_t)v * ldy + r] = o;
+      }
+    }
   }
+}
+
+template <class T, int NT>
+void gemv_launch(const void* w, const void* b, int R, int K, const float* x, int ldx, int nt, float* y, int ldy,
+                 int act, hipStream_t s) {
+  dim3 grid((R + 3) / 4);
+  if (act)
+    gemv_kernel<T, 1, NT><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
+  else
+    gemv_kernel<T, 0, NT><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
 }
 
 template <class T>
@@ -326,11 +359,7 @@ hipError_t modulation_t(int D, int L, double t, const void* t1w, const void* t1b
   float* c = tmp + 256 + D;    // [D]
   timestep_features_kernel<<<1, 128, 0, s>>>(t, phi);
   auto G = [&](const void* w, const void* b, int R, int K, const float* x, float* y, int act) {
-    dim3 grid((R + 3) / 4);
-    if (act)
-      gemv_kernel<T, 1><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, y);
-    else
-      gemv_kernel<T, 0><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, y);
+    gemv_launch<T, 1>(w, b, R, K, x, K, 1, y, R, act, s);
   };
   G(t1w, t1b, D, 256, phi, e1, 1);
   G(t2w, t2b, D, D, e1, c, 1);
@@ -485,11 +514,38 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
 hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
                             hipStream_t s) {
   if (D % 256) return hipErrorInvalidValue;
-  dim3 grid((6 * D + 3) / 4);
   if (dtype == BF16)
-    gemv_kernel<bf16, 0><<<grid, 256, 0, s>>>((const bf16*)w, (const bf16*)b, 6 * D, D, c, out);
+    gemv_launch<bf16, 1>(w, b, 6 * D, D, c, D, 1, out, 6 * D, 0, s);
   else
-    gemv_kernel<float, 0><<<grid, 256, 0, s>>>((const float*)w, (const float*)b, 6 * D, D, c, out);
+    gemv_launch<float, 1>(w, b, 6 * D, D, c, D, 1, out, 6 * D, 0, s);
+  return hipGetLastError();
+}
+
+hipError_t timestep_cond_batch(int dtype, int D, const double* t, int nt, const void* t1w, const void* t1b,
+                               const void* t2w, const void* t2b, float* tmp, float* c, hipStream_t s) {
+  if (nt < 1 || nt > MOD_BATCH || D % 256) return hipErrorInvalidValue;
+  TimeBatch tb{};
+  for (int j = 0; j < nt; ++j) tb.t[j] = t[j];
+  float* phi = tmp;                          // [nt, 256]
+  float* e1 = tmp + (size_t)MOD_BATCH * 256;  // [nt, D]
+  timestep_features_batch_kernel<<<nt, 128, 0, s>>>(tb, phi);
+  if (dtype == BF16) {
+    gemv_launch<bf16, MOD_BATCH>(t1w, t1b, D, 256, phi, 256, nt, e1, D, 1, s);
+    gemv_launch<bf16, MOD_BATCH>(t2w, t2b, D, D, e1, D, nt, c, D, 1, s);
+  } else {
+    gemv_launch<float, MOD_BATCH>(t1w, t1b, D, 256, phi, 256, nt, e1, D, 1, s);
+    gemv_launch<float, MOD_BATCH>(t2w, t2b, D, D, e1, D, nt, c, D, 1, s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t gemv_batch(int dtype, int R, int K, const void* w, const void* b, const float* x, int ldx, int nt,
+                      float* y, int ldy, hipStream_t s) {
+  if (nt < 1 || nt > MOD_BATCH || K % 256) return hipErrorInvalidValue;
+  if (dtype == BF16)
+    gemv_launch<bf16, MOD_BATCH>(w, b, R, K, x, ldx, nt, y, ldy, 0, s);
+  else
+    gemv_launch<float, MOD_BATCH>(w, b, R, K, x, ldx, nt, y, ldy, 0, s);
   return hipGetLastError();
 }
 

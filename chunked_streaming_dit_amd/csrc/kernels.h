@@ -160,5 +160,15 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
 // One block's modulation out[6D] = Wmod c + bmod (W [6D, D] dtype, c [D] fp32).
 hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
                             hipStream_t s);
+// The same products for up to MOD_BATCH timesteps at once, each weight row read once
+// for all of them; per timestep the arithmetic (and so the result, bit for bit) is that
+// of modulation / block_modulation.
+constexpr int MOD_BATCH = 16;
+// c[j] ([D], rows D apart) for t[j], j < nt.  tmp: fp32 scratch of MOD_BATCH (256 + D).
+hipError_t timestep_cond_batch(int dtype, int D, const double* t, int nt, const void* t1w, const void* t1b,
+                               const void* t2w, const void* t2b, float* tmp, float* c, hipStream_t s);
+// y[j][r] = W[r, :] . x[j] + b[r] for r < R, j < nt (x[j] at x + j ldx, y[j] at y + j ldy).
+hipError_t gemv_batch(int dtype, int R, int K, const void* w, const void* b, const float* x, int ldx, int nt,
+                      float* y, int ldy, hipStream_t s);
 
 }  // namespace dit

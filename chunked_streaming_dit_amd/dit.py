@@ -196,6 +196,14 @@ class DitChunk:
         _dev(audio, "audio", torch.float32)
         C.check(C.lib().audio_kv_precompute(self._h, _ptr(audio), 0 if audio is None else audio.shape[0]))
 
+    def modulation_table(self, ts: Optional[Sequence[float]]) -> None:
+        """Hold the adaLN vectors of the timesteps ts (at most DIT_MOD_TABLE_MAX; a
+        request's schedule plus 0.0 for the context passes): passes at one of these exact
+        timesteps reuse them (dit_modulation_table).  None or [] clears the table."""
+        ts = [] if ts is None else [float(t) for t in ts]
+        arr = (ctypes.c_double * max(len(ts), 1))(*ts)
+        C.check(C.lib().dit_modulation_table(self._h, arr, len(ts)))
+
     def step(self, x: torch.Tensor, t: float, t_next: float, g: C.DitGrid,
              cond: Optional[torch.Tensor] = None, audio=None,
              v_out: Optional[torch.Tensor] = None, carry_boundary: bool = False) -> None:

@@ -21,6 +21,8 @@
  *                       ordinary chunks);
  *   audio_kv_precompute once per chunk: the audio K/V of every block, which the
  *                       chunk's steps then reuse;
+ *   dit_modulation_table  once per request: the adaLN vectors of every timestep of
+ *                       the schedule (and t = 0), which the passes then reuse;
  *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
  *   dit_chunk_step_carry  alternatively the chunk's last step, which also leaves
  *                       that step's last-frame K/V as the next boundary;
@@ -155,8 +157,9 @@ int dit_weight_count(const dit_config* cfg);
 
 /* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
  * max_bnd boundary tokens, of max_bnd interpolation-anchor tokens and (d_a > 0) of
- * max_audio audio tokens (each rounded up to 64 tokens).  0 if the config is invalid
- * (see dit_last_error). */
+ * max_audio audio tokens (each rounded up to 64 tokens), and the modulation table
+ * (DIT_MOD_TABLE_MAX entries of (6 L + 2) D floats).  0 if the config is invalid (see
+ * dit_last_error). */
 size_t dit_state_bytes(const dit_config* cfg);
 
 /* Bytes of per-call transients (activations of max(max_tokens, max_ref, max_bnd)
@@ -256,6 +259,21 @@ int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_po
  * Errors: EINVAL (null audio with M > 0, d_a == 0), ESHAPE (M > max_audio). */
 enum { DIT_AUDIO_HELD = -1 };
 int audio_kv_precompute(dit_handle* h, const float* audio, int M);
+
+/* The modulation table of a schedule.  The adaLN vectors (per block shift, scale and
+ * gate of the attention and MLP sublayers, and the final layer's shift and scale) depend
+ * only on the timestep and the weights (HeyGen, "Avatar inference at scale", section
+ * "The underlying model architecture" names the DiT; its conditioning is this library's
+ * reading), so the table is computed once for the timesteps t[0..nt) of a request's
+ * schedule (host array; t = 0 serves the context passes) and held in the state: each
+ * weight row is read once for all nt timesteps instead of once per step.  Every later
+ * pass whose timestep equals some t[j] exactly uses entry j; other timesteps are
+ * computed per pass as before.  The results are the same, bit for bit.  nt == 0 clears
+ * the table.  Errors: EINVAL (nt outside [0, DIT_MOD_TABLE_MAX], t NULL with nt > 0, a
+ * non-finite t); on an error the table is unchanged, except that a HIP failure leaves
+ * it cleared. */
+enum { DIT_MOD_TABLE_MAX = 16 };
+int dit_modulation_table(dit_handle* h, const double* t, int nt);
 
 /* One denoising step of the chunk: v = DiT(x, t) and x += (t_next - t) v,
  * with dt computed in double on the host and applied in fp32.

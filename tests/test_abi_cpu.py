@@ -57,7 +57,9 @@ def test_sizes_and_weight_count():
         aud = (max(cfg.M, 1) + 63) // 64 * 64 if cfg.d_a > 0 else 0
         kv = cfg.L * 2 * cfg.D * (2 if cfg.dtype == "bf16" else 4) * (
             (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64) + aud)
-        assert kv <= sb <= kv + 8 * cfg.L * 256
+        # plus the modulation table: DIT_MOD_TABLE_MAX entries of (6 L + 2) D fp32
+        kv += 16 * (6 * cfg.L + 2) * cfg.D * 4
+        assert kv <= sb <= kv + (8 * cfg.L + 1) * 256
         assert lib.dit_workspace_bytes(ctypes.byref(cs)) > 0
 
 
@@ -134,6 +136,16 @@ def test_call_order_and_shape_errors():
     assert lib.interp_anchor_kv(h, FAKE, C.DitGrid(0, 1, 0, 8), 2) == C.DIT_ESHAPE
     assert lib.interp_anchor_kv(h, None, C.DitGrid(0, 0, 0, 0), 2) == C.DIT_OK     # clear: no launch
     assert lib.interp_anchor_kv(None, FAKE, C.DitGrid(0, 1, 4, 8), 2) == C.DIT_EINVAL
+    # modulation table: checked before any launch; nt = 0 clears without a launch
+    ts = (ctypes.c_double * 17)(*[1.0 - k / 16 for k in range(17)])
+    assert lib.dit_modulation_table(h, ts, 17) == C.DIT_EINVAL  # > DIT_MOD_TABLE_MAX
+    assert lib.dit_modulation_table(h, ts, -1) == C.DIT_EINVAL
+    assert lib.dit_modulation_table(h, None, 2) == C.DIT_EINVAL
+    ts[1] = float("inf")
+    assert lib.dit_modulation_table(h, ts, 2) == C.DIT_EINVAL
+    assert "not finite" in C.last_error()
+    assert lib.dit_modulation_table(h, None, 0) == C.DIT_OK
+    assert lib.dit_modulation_table(None, ts, 1) == C.DIT_EINVAL
     assert lib.dit_destroy(h) == C.DIT_OK
     assert lib.dit_destroy(None) == C.DIT_OK
 

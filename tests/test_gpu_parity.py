@@ -78,6 +78,34 @@ def test_mini_super_resolution_single_step_bf16():
     _check(MINI_SR, steps=1)
 
 
+def _schedule(cfg):
+    # the same doubles as run_standalone_gpu's step times
+    return [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
+
+
+@pytest.mark.parametrize("base", [MINI_BF16, MINI_F32])
+def test_modulation_table_bitwise_equals_per_pass(base):
+    """dit_modulation_table for the schedule (and t = 0 for the context passes): every
+    pass then takes its adaLN vectors from the table, with the same x and v, bit for bit,
+    as computing them in each pass (which the parity tests above check against the
+    oracle).  Also a partial table (some passes computed, some from the table), a table
+    holding other timesteps only, and the cleared table."""
+    from chunked_streaming_dit_amd.workload import upload_weights
+    dev = device()
+    P = synth.make_weights(base)
+    inp = synth.make_inputs(base, 0)
+    W = upload_weights(P, base.dtype, dev)
+    x_ref, v_ref, h = run_standalone_gpu(base, P, inp, dev, weights=W)
+    ts = _schedule(base)
+    for table in (ts[:-1] + [0.0], ts[1:2], [0.0, 0.123, 0.7], None, [0.0] + ts[::-1]):
+        h.modulation_table(table)
+        x, vs, _ = run_standalone_gpu(base, P, inp, dev, handle=h)
+        assert np.array_equal(x, x_ref), table
+        for k, (a, b) in enumerate(zip(vs, v_ref)):
+            assert np.array_equal(a, b), (table, k)
+    h.close()
+
+
 @pytest.mark.parametrize("base", [MINI_BF16, MINI_F32])
 def test_held_audio_kv_bitwise_equals_per_step_audio(base):
     """audio_kv_precompute once per chunk, then every step with DIT_AUDIO_HELD: the same

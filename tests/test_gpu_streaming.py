@@ -63,6 +63,24 @@ def test_streamed_equals_resident_bitwise(mini, nslot):
     h.close()
 
 
+def test_streamed_modulation_table(mini):
+    """The modulation table computed while the block weights stream through the ring
+    (it is one more pass over the blocks): the same results as the resident run."""
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config
+    dev, P, inp, W, x_res, v_res = mini
+    ts = [MINI.t_start + (MINI.t_end - MINI.t_start) * k / MINI.steps for k in range(MINI.steps + 1)]
+    h = DitChunk(chunk_config(MINI), W, dev)
+    h.weight_stream(_pinned_blocks(P, MINI), nslot=2)
+    for rep in range(2):
+        h.modulation_table(ts[:-1] + [0.0])
+        x, vs, _ = run_standalone_gpu(MINI, P, inp, dev, handle=h)
+        assert np.array_equal(x, x_res), rep
+        for a, b in zip(vs, v_res):
+            assert np.array_equal(a, b), rep
+    h.close()
+
+
 def test_stream_switching_and_oracle(mini):
     """Streaming on, off, on again with another ring depth: every run equals the
     resident one; the streamed run also matches the oracle."""
