@@ -26,15 +26,24 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def run_standalone_gpu(cfg, P, inp, dev, steps=None, record_v=True, weights=None, handle=None):
+def schedule(cfg, steps=None):
+    """The chunk's step times t_0..t_S (the doubles run_standalone_gpu uses)."""
+    S_ = cfg.steps if steps is None else steps
+    return [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S_ for k in range(S_ + 1)]
+
+
+def run_standalone_gpu(cfg, P, inp, dev, steps=None, record_v=True, weights=None, handle=None, table=None):
     """One self-contained chunk on the GPU through the C ABI: reference K/V, the
-    boundary frame's K/V (if any), then the chunk's Euler steps.
+    boundary frame's K/V (if any), then the chunk's Euler steps.  table: timesteps
+    given to dit_modulation_table first (None: the handle's table is left as it is).
     Returns (x_final numpy, [v per step] numpy, handle)."""
     import synth as S
     from chunked_streaming_dit_amd import DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
     W = weights if weights is not None else upload_weights(P, cfg.dtype, dev)
     h = handle if handle is not None else DitChunk(chunk_config(cfg), W, dev)
+    if table is not None:
+        h.modulation_table(table)
     h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
     if cfg.bnd is not None:
         b = cfg.bnd
@@ -47,7 +56,7 @@ def run_standalone_gpu(cfg, P, inp, dev, steps=None, record_v=True, weights=None
         cond = f32(inp["cond_lr"] if cfg.cond_up == 2 else inp["cond"], dev)
     audio = f32(inp["audio"], dev) if cfg.M > 0 else None
     S_ = cfg.steps if steps is None else steps
-    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S_ for k in range(S_ + 1)]
+    ts = schedule(cfg, steps)
     vs = []
     v = torch.empty_like(x) if record_v else None
     for k in range(S_):

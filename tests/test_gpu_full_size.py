@@ -102,14 +102,17 @@ def _sample_rows(n, seed):
     return np.unique(np.concatenate([np.arange(64), tail, r.choice(n, 128, replace=False)]))
 
 
-@pytest.mark.parametrize("base", [4, 5])
-def test_full_shape_one_block_sampled_rows(base):
-    """One block at the full launch shape; the oracle evaluates sampled query rows."""
+@pytest.mark.parametrize("table", [False, True], ids=["per_pass", "table"])
+@pytest.mark.parametrize("base", [2, 4, 5])
+def test_full_shape_one_block_sampled_rows(base, table):
+    """One block at the full launch shape; the oracle evaluates sampled query rows.
+    table: with the modulation table for the step and t = 0 (the bench's path)."""
     dev = device()
     cfg = dataclasses.replace(synth.CONFIGS[base], L=1, cid=40 + base, steps=1)
     P = synth.make_weights(cfg, threads=16)
     inp = synth.make_inputs(cfg, 0)
-    _, vg, h = run_standalone_gpu(cfg, P, inp, dev, steps=1)
+    _, vg, h = run_standalone_gpu(cfg, P, inp, dev, steps=1,
+                                  table=[cfg.t_start, 0.0] if table else None)
     h.close()
     g = cfg.chunk
     ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
@@ -119,7 +122,7 @@ def test_full_shape_one_block_sampled_rows(base):
     vo = O.velocity_rows(P, cfg, inp["x_init"], cfg.t_start, O.grid_positions(0, g.frames, g.h, g.w),
                          [[ref_kv[0], bkv[0]]], inp.get("audio"), rows, cond)
     err = rel_err(vg[0][rows], vo)
-    print(f"config {base} one-block full shape, {len(rows)} sampled rows: v err {err:.2e}")
+    print(f"config {base} one-block full shape, table {table}, {len(rows)} sampled rows: v err {err:.2e}")
     assert err <= TOL["bf16"], err
 
 

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import synth
 from synth import Grid
-from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu
+from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu, schedule
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +29,12 @@ MINI_SR = synth.config(4, cid=205, L=2, D=256, H=2, dh=128,
                        steps=2)
 
 
-def _check(cfg, steps=None):
+def _check(cfg, steps=None, table=None):
+    """GPU chunk vs the oracle; table: timesteps of a modulation table set first."""
     dev = device()
     P = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg, 0)
-    xg, vg, _ = run_standalone_gpu(cfg, P, inp, dev, steps=steps)
+    xg, vg, _ = run_standalone_gpu(cfg, P, inp, dev, steps=steps, table=table)
     S = cfg.steps if steps is None else steps
     g = cfg.chunk
     ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
@@ -48,8 +49,9 @@ def _check(cfg, steps=None):
     tol = TOL[cfg.dtype]
     errs = [rel_err(a, b) for a, b in zip(vg, vo)]
     dx = rel_err(xg - inp["x_init"], xo - inp["x_init"])
-    print(f"{cfg.name} cid={cfg.cid}: v errs {['%.2e' % e for e in errs]}, dx err {dx:.2e}")
+    print(f"{cfg.name} cid={cfg.cid} table={table}: v errs {['%.2e' % e for e in errs]}, dx err {dx:.2e}")
     assert max(errs) <= tol and dx <= tol, (errs, dx)
+    return xg, vg
 
 
 def test_config1_tiny_fp32():
@@ -78,28 +80,31 @@ def test_mini_super_resolution_single_step_bf16():
     _check(MINI_SR, steps=1)
 
 
-def _schedule(cfg):
-    # the same doubles as run_standalone_gpu's step times
-    return [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
+@pytest.mark.parametrize("cfg", [synth.CONFIGS[1], MINI_F32, MINI_F32_DH64, MINI_BF16, MINI_SR],
+                         ids=["config1", "mini_f32", "mini_f32_dh64", "mini_bf16", "mini_sr"])
+def test_modulation_table_parity(cfg):
+    """dit_modulation_table for the schedule and t = 0 (every pass takes its adaLN
+    vectors from the table), and a partial table (the context passes and the second step
+    from the table, the other steps computed per pass): the chunk matches the oracle."""
+    ts = schedule(cfg)
+    _check(cfg, table=ts[:-1] + [0.0])
+    _check(cfg, table=[0.0] + ts[1:2])
 
 
 @pytest.mark.parametrize("base", [MINI_BF16, MINI_F32])
 def test_modulation_table_bitwise_equals_per_pass(base):
-    """dit_modulation_table for the schedule (and t = 0 for the context passes): every
-    pass then takes its adaLN vectors from the table, with the same x and v, bit for bit,
-    as computing them in each pass (which the parity tests above check against the
-    oracle).  Also a partial table (some passes computed, some from the table), a table
-    holding other timesteps only, and the cleared table."""
+    """The table's vectors are computed with the per-pass arithmetic: the same x and v,
+    bit for bit, with the table for the schedule, a partial table, a table holding other
+    timesteps only, the cleared table and the schedule in another order."""
     from chunked_streaming_dit_amd.workload import upload_weights
     dev = device()
     P = synth.make_weights(base)
     inp = synth.make_inputs(base, 0)
     W = upload_weights(P, base.dtype, dev)
     x_ref, v_ref, h = run_standalone_gpu(base, P, inp, dev, weights=W)
-    ts = _schedule(base)
-    for table in (ts[:-1] + [0.0], ts[1:2], [0.0, 0.123, 0.7], None, [0.0] + ts[::-1]):
-        h.modulation_table(table)
-        x, vs, _ = run_standalone_gpu(base, P, inp, dev, handle=h)
+    ts = schedule(base)
+    for table in (ts[:-1] + [0.0], ts[1:2], [0.0, 0.123, 0.7], [], [0.0] + ts[::-1]):
+        x, vs, _ = run_standalone_gpu(base, P, inp, dev, handle=h, table=table)
         assert np.array_equal(x, x_ref), table
         for k, (a, b) in enumerate(zip(vs, v_ref)):
             assert np.array_equal(a, b), (table, k)

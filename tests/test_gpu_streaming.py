@@ -14,7 +14,7 @@ import oracle as O
 import synth
 from synth import Grid
 from chunked_streaming_dit_amd import torch_dtype
-from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu
+from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu, schedule
 
 pytestmark = pytest.mark.gpu
 
@@ -65,16 +65,18 @@ def test_streamed_equals_resident_bitwise(mini, nslot):
 
 def test_streamed_modulation_table(mini):
     """The modulation table computed while the block weights stream through the ring
-    (it is one more pass over the blocks): the same results as the resident run."""
+    (it is one more pass over the blocks): the same results, bit for bit, as the
+    resident run with the table."""
     from chunked_streaming_dit_amd import DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config
-    dev, P, inp, W, x_res, v_res = mini
-    ts = [MINI.t_start + (MINI.t_end - MINI.t_start) * k / MINI.steps for k in range(MINI.steps + 1)]
+    dev, P, inp, W, _, _ = mini
+    table = schedule(MINI)[:-1] + [0.0]
+    x_res, v_res, hr = run_standalone_gpu(MINI, P, inp, dev, weights=W, table=table)
+    hr.close()
     h = DitChunk(chunk_config(MINI), W, dev)
     h.weight_stream(_pinned_blocks(P, MINI), nslot=2)
     for rep in range(2):
-        h.modulation_table(ts[:-1] + [0.0])
-        x, vs, _ = run_standalone_gpu(MINI, P, inp, dev, handle=h)
+        x, vs, _ = run_standalone_gpu(MINI, P, inp, dev, handle=h, table=table)
         assert np.array_equal(x, x_res), rep
         for a, b in zip(vs, v_res):
             assert np.array_equal(a, b), rep
