@@ -54,6 +54,7 @@ struct Layout {
   int cap_tok = 0, cap_ref = 0, cap_bnd = 0, cap_audio = 0, F = 0, C_in = 0, big_cols = 0;
   // state
   std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc, kaud, vaud;
+  size_t aud_in = 0;  // held audio features [cap_audio, d_a] (dtype), d_a > 0
   size_t modtab = 0;  // DIT_MOD_TABLE_MAX entries of mod_entry floats
   size_t mod_entry = 0;
   size_t state_total = 0;
@@ -114,6 +115,7 @@ Layout make_layout(const dit_config* c) {
     L.kaud.push_back(take(aud));
     L.vaud.push_back(take(aud));
   }
+  L.aud_in = take(c->d_a > 0 ? (size_t)L.cap_audio * c->d_a * L.elt : 0);
   L.mod_entry = ((size_t)c->L * 6 + 2) * D;
   L.modtab = take(DIT_MOD_TABLE_MAX * L.mod_entry * 4);
   L.state_total = off;
@@ -184,6 +186,10 @@ struct dit_handle {
   hipStream_t stream = nullptr;
   bool has_ref = false;
   int n_ref = 0, n_bnd = 0, n_anc = 0, n_aud = 0;
+  // Held audio K/V of block l still to compute (set by audio_kv_precompute while block
+  // weights stream: each block's K/V is then computed when the next pass brings that
+  // block's weights into the ring, instead of in a pass of its own).
+  std::vector<char> aud_pend;
   std::vector<double> mod_t;  // timesteps of the modulation table entries
   // timing
   bool timing = false;
@@ -289,11 +295,18 @@ int pass_begin(dit_handle* hd) {
   return stream_issue_upto(hd, st.base + k);
 }
 
-// Block l of the pass: its kernels wait for its slot's copy.
+int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat);
+
+// Block l of the pass: its kernels wait for its slot's copy.  A held audio K/V of block
+// l still pending is computed first (its weights are now in place).
 int block_begin(dit_handle* hd, int l) {
   Streaming& st = hd->st;
-  if (!st.on) return DIT_OK;
-  HIPCHK(hipStreamWaitEvent(hd->stream, st.ready[(st.base + l) % st.nslot], 0));
+  if (st.on) HIPCHK(hipStreamWaitEvent(hd->stream, st.ready[(st.base + l) % st.nslot], 0));
+  if (!hd->aud_pend.empty() && hd->aud_pend[l]) {
+    const Layout& L = hd->lay;
+    if (int rc = audio_kv(hd, l, hd->n_aud, hd->S(L.aud_in), hd->S(L.kaud[l]), hd->S(L.vaud[l]))) return rc;
+    hd->aud_pend[l] = 0;
+  }
   return DIT_OK;
 }
 
@@ -394,8 +407,8 @@ int embed(dit_handle* hd, const float* x, int n, const float* cond, int cond_mod
 }
 
 // Block l's audio K (k-normed) and V^T (attention layout, capacity cap_audio) from the
-// audio tokens already in the workspace (ain [M, d_a]).
-int audio_kv(dit_handle* hd, int l, int M, void* ka, void* vat) {
+// audio tokens ain [M, d_a] (dtype).
+int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   const int D = c.D;
@@ -403,9 +416,9 @@ int audio_kv(dit_handle* hd, int l, int M, void* ka, void* vat) {
   RopeGrid g0{0, 1, 1, 1};
   GemmEpi e{};
   e.kind = EPI_BIAS; e.bias = hd->B(l, DIT_WB_CK_B); e.out = hd->X(L.ka_raw); e.ldo = D;
-  HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
+  HIPCHK(gemm(c.dtype, ain, c.d_a, hd->B(l, DIT_WB_CK_W), c.d_a, M, D, c.d_a, e, s));
   e.bias = hd->B(l, DIT_WB_CV_B); e.out = hd->X(L.va_raw);
-  HIPCHK(gemm(c.dtype, hd->X(L.ain), c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
+  HIPCHK(gemm(c.dtype, ain, c.d_a, hd->B(l, DIT_WB_CV_W), c.d_a, M, D, c.d_a, e, s));
   HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
                      hd->B(l, DIT_WB_GCK), 0, g0, (float)c.eps, (float)c.rope_theta, 1.0f, nullptr, ka,
                      vat, L.cap_audio, s));
@@ -676,18 +689,27 @@ int audio_kv_precompute(dit_handle* h, const float* audio, int M) {
   if (M == 0) {
     if (audio) return fail(DIT_EINVAL, "audio given with M=0");
     h->n_aud = 0;
+    h->aud_pend.clear();
     return DIT_OK;
   }
   if (!audio) return fail(DIT_EINVAL, "audio is NULL with M=%d", M);
   if (c.d_a == 0) return fail(DIT_EINVAL, "audio given but d_a=0");
   if (M < 0 || M > c.max_audio) return fail(DIT_ESHAPE, "M=%d out of [1, max_audio=%d]", M, c.max_audio);
   h->n_aud = 0;
+  h->aud_pend.clear();
   RopeGrid g0{0, 1, 1, 1};
-  HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g0, h->X(h->lay.ain), h->stream));
+  HIPCHK(patch_input(c.dtype, audio, M, c.d_a, nullptr, 0, 0, g0, h->S(h->lay.aud_in), h->stream));
+  if (h->st.on) {
+    // Streamed weights: a pass of its own would copy every block slot for two small
+    // Linears; instead each block's K/V is computed at the next pass's block_begin.
+    h->aud_pend.assign(c.L, 1);
+    h->n_aud = M;
+    return DIT_OK;
+  }
   int rc = pass_begin(h);
   for (int l = 0; l < c.L && !rc; ++l) {
     rc = block_begin(h, l);
-    if (!rc) rc = audio_kv(h, l, M, h->S(h->lay.kaud[l]), h->S(h->lay.vaud[l]));
+    if (!rc) rc = audio_kv(h, l, M, h->S(h->lay.aud_in), h->S(h->lay.kaud[l]), h->S(h->lay.vaud[l]));
     if (!rc) rc = block_end(h, l);
   }
   if ((rc = pass_end(h, rc))) return rc;
@@ -826,7 +848,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
       }
       AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
       if (!held) {
-        if (int rc2 = audio_kv(hd, l, M, hd->X(L.ka), hd->X(L.vat))) return rc2;
+        if (int rc2 = audio_kv(hd, l, M, hd->X(L.ain), hd->X(L.ka), hd->X(L.vat))) return rc2;
         aseg = AttnSeg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
       }
       if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;

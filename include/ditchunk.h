@@ -157,7 +157,8 @@ int dit_weight_count(const dit_config* cfg);
 
 /* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
  * max_bnd boundary tokens, of max_bnd interpolation-anchor tokens and (d_a > 0) of
- * max_audio audio tokens (each rounded up to 64 tokens), and the modulation table
+ * max_audio audio tokens (each rounded up to 64 tokens); (d_a > 0) the held audio
+ * features [max_audio rounded up to 64, d_a]; and the modulation table
  * (DIT_MOD_TABLE_MAX entries of (6 L + 2) D floats).  0 if the config is invalid (see
  * dit_last_error). */
 size_t dit_state_bytes(const dit_config* cfg);
@@ -255,7 +256,10 @@ int interp_anchor_kv(dit_handle* h, const float* x_next, dit_grid next, int t_po
  * Linears of audio [M, d_a] (fp32, device), K per-head normed) are computed once and
  * held in the state.  dit_chunk_step with audio NULL and M == DIT_AUDIO_HELD then
  * attends to them.  M == 0 (audio NULL) clears them.  The step's output is the same,
- * bit for bit, as when the audio is passed to every step.
+ * bit for bit, as when the audio is passed to every step.  While block weights stream
+ * (dit_weight_stream) the features are held and each block's K/V is computed when the
+ * next pass (any pass: step, context or modulation table) brings that block's weights
+ * into the ring, so the audio adds no pass over the weights of its own.
  * Errors: EINVAL (null audio with M > 0, d_a == 0), ESHAPE (M > max_audio). */
 enum { DIT_AUDIO_HELD = -1 };
 int audio_kv_precompute(dit_handle* h, const float* audio, int M);

@@ -55,8 +55,10 @@ def test_sizes_and_weight_count():
         # per block K and V of the reference, the boundary, the interpolation anchor and
         # (with audio weights) the held audio
         aud = (max(cfg.M, 1) + 63) // 64 * 64 if cfg.d_a > 0 else 0
-        kv = cfg.L * 2 * cfg.D * (2 if cfg.dtype == "bf16" else 4) * (
+        elt = 2 if cfg.dtype == "bf16" else 4
+        kv = cfg.L * 2 * cfg.D * elt * (
             (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64) + aud)
+        kv += aud * cfg.d_a * elt  # the held audio features
         # plus the modulation table: DIT_MOD_TABLE_MAX entries of (6 L + 2) D fp32
         kv += 16 * (6 * cfg.L + 2) * cfg.D * 4
         assert kv <= sb <= kv + (8 * cfg.L + 1) * 256

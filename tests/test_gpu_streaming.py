@@ -103,3 +103,34 @@ def test_stream_switching_and_oracle(mini):
     errs = [rel_err(a, b) for a, b in zip(v_res, vo)]
     dx = rel_err(x_res - inp["x_init"], xo - inp["x_init"])
     assert max(errs) <= TOL[MINI.dtype] and dx <= TOL[MINI.dtype], (errs, dx)
+
+
+@pytest.mark.parametrize("audio_first", [True, False], ids=["before_context", "after_context"])
+def test_streamed_held_audio(mini, audio_first):
+    """Held audio with streamed weights: audio_kv_precompute only holds the features,
+    and each block's audio K/V is computed when the next pass (a context pass, or the
+    first step) brings the block's weights into the ring.  The chunk equals, bit for bit,
+    the resident run with the audio given to every step."""
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of
+    dev, P, inp, W, x_res, v_res = mini
+    h = DitChunk(chunk_config(MINI), W, dev)
+    h.weight_stream(_pinned_blocks(P, MINI), nslot=2)
+    audio = f32(inp["audio"], dev)
+    ts = schedule(MINI)
+    for rep in range(2):
+        if audio_first:
+            h.audio_kv_precompute(audio)
+        h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(MINI.ref))
+        b = MINI.bnd
+        h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, b.h, b.w)))
+        if not audio_first:
+            h.audio_kv_precompute(audio)
+        x = f32(inp["x_init"], dev)
+        v = torch.empty_like(x)
+        for k in range(MINI.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(MINI.chunk), audio=AUDIO_HELD, v_out=v)
+            torch.cuda.synchronize()
+            assert np.array_equal(v.cpu().numpy(), v_res[k]), (rep, k)
+        assert np.array_equal(x.cpu().numpy(), x_res), rep
+    h.close()
