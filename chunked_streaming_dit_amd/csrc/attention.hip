@@ -20,10 +20,6 @@
 #include <math.h>
 
 #include <algorithm>
-#include <array>
-#include <map>
-#include <mutex>
-#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -615,71 +611,6 @@ __global__ __launch_bounds__(64 * XW, 3) void xattn_kernel(XArgs a) {
 }
 
 }  // namespace
-
-// Key-range split plan of a launch.  Workgroups are modelled as dispatched in grid
-// order, round-robin over the 8 XCDs, each XCD list-scheduling its share on slots/8
-// concurrent slots; a workgroup of k key tiles takes k + ATTN_WG_FIXED tile-times.  For
-// every split count (1..4) and first split q-tile qt0 the plan takes the modelled
-// makespan plus the merge pass (ATTN_MERGE_COST tile-times per split part of a
-// (head, q-tile), spread over the chip) and keeps the cheapest; at equal cost, fewer
-// parts and fewer split q-tiles.  Splitting needs at least 2 tiles per part and partial
-// storage for nsplit * nq rows.  Plans are memoised per shape.
-constexpr double ATTN_WG_FIXED = 2.0;
-constexpr double ATTN_MERGE_COST = 0.02;
-
-static double attention_makespan(int nqt, int H, int key_tiles, int ns, int qt0, int slots) {
-  constexpr int NXCD = 8;
-  const int per = slots / NXCD > 0 ? slots / NXCD : 1;
-  const long long n1 = (long long)qt0 * H;
-  const long long n = n1 + (long long)(nqt - qt0) * H * ns;
-  const double c1 = key_tiles + ATTN_WG_FIXED, c2 = (double)key_tiles / ns + ATTN_WG_FIXED;
-  double worst = 0.0;
-  std::vector<double> busy(per);
-  for (int x = 0; x < NXCD && x < n; ++x) {
-    std::fill(busy.begin(), busy.end(), 0.0);
-    for (long long b = x; b < n; b += NXCD) {
-      // earliest free slot of this XCD takes block b
-      size_t k = std::min_element(busy.begin(), busy.end()) - busy.begin();
-      busy[k] += b < n1 ? c1 : c2;
-    }
-    worst = std::max(worst, *std::max_element(busy.begin(), busy.end()));
-  }
-  return worst;
-}
-
-AttnSplit attention_plan(int nq, int H, int key_tiles, int partial_rows, int slots) {
-  AttnSplit best{1, 0, nullptr, nullptr};
-  if (nq <= 0 || H <= 0 || key_tiles <= 0) return best;
-  static std::mutex mu;
-  static std::map<std::array<int, 5>, std::pair<int, int>> memo;
-  const std::array<int, 5> key{nq, H, key_tiles, partial_rows, slots};
-  {
-    std::lock_guard<std::mutex> g(mu);
-    auto it = memo.find(key);
-    if (it != memo.end()) {
-      best.nsplit = it->second.first;
-      best.qt0 = it->second.second;
-      return best;
-    }
-  }
-  const int nqt = (nq + BQ - 1) / BQ;
-  double best_cost = attention_makespan(nqt, H, key_tiles, 1, 0, slots);
-  for (int ns = 2; ns <= 4; ++ns) {
-    if (key_tiles < 2 * ns || (long long)ns * nq > partial_rows) break;
-    for (int qt0 = nqt - 1; qt0 >= 0; --qt0) {
-      const double cost = attention_makespan(nqt, H, key_tiles, ns, qt0, slots) +
-                          ATTN_MERGE_COST * ns * (double)(nqt - qt0) * H;
-      if (cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best.nsplit = ns;
-        best.qt0 = qt0;
-      }
-    }
-  }
-  std::lock_guard<std::mutex> g(mu);
-  memo.emplace(key, std::make_pair(best.nsplit, best.qt0));
-  return best;
-}
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
                      int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
