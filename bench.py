@@ -199,7 +199,7 @@ def large_main(args) -> int:
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of
 
     dev = torch.device("cuda", 0)
-    cfg = synth.CONFIGS[5]
+    cfg = synth.LARGE_CHUNK
     W = _device_weights(cfg, dev)
     inp = synth.make_inputs(cfg, 0)
     h = DitChunk(chunk_config(cfg), W, dev)
@@ -344,7 +344,7 @@ def main() -> int:
         print(json.dumps(d))
         return 0
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
               "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
         return 2
 
@@ -359,7 +359,7 @@ def main() -> int:
 
     dev = torch.device("cuda", 0)
     sr = args.workload in ("sr", "sr1")
-    cfg = synth.CONFIGS[4 if sr else 2]
+    cfg = synth.SUPER_RES if sr else synth.BASE_CHUNK
     P = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg, 0)
     W = upload_weights(P, cfg.dtype, dev)

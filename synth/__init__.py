@@ -122,6 +122,14 @@ CONFIGS: Dict[int, Config] = {
 }
 
 
+# The workloads by name (the integer keys above seed their tensors).
+TINY_FP32 = CONFIGS[1]
+BASE_CHUNK = CONFIGS[2]
+STREAM_6_CHUNKS = CONFIGS[3]
+SUPER_RES = CONFIGS[4]
+LARGE_CHUNK = CONFIGS[5]
+
+
 def config(base: int, **overrides) -> Config:
     """Return workload ``base``, optionally with fields replaced (small test variants;
     give a variant its own ``cid`` so that its seeds differ)."""

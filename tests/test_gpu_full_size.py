@@ -49,7 +49,7 @@ def _run_chunk(h, cfg, x, audio, prev, v0=None):
 def test_config3_stream_full_size():
     from chunked_streaming_dit_amd.workload import f32, grid_of
     dev = device()
-    cfg = synth.CONFIGS[3]
+    cfg = synth.STREAM_6_CHUNKS
     g = cfg.chunk
     P = synth.make_weights(cfg)
     chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
@@ -133,7 +133,7 @@ def test_interp_chunk_full_shape_one_block_sampled_rows():
     from chunked_streaming_dit_amd import DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
     dev = device()
-    cfg = dataclasses.replace(synth.CONFIGS[2], L=1, cid=52, steps=1)
+    cfg = dataclasses.replace(synth.BASE_CHUNK, L=1, cid=52, steps=1)
     P = synth.make_weights(cfg, threads=16)
     inp = synth.make_inputs(cfg, 0)
     anchor = synth.make_inputs(cfg, 1)["bnd"]  # frame 0 of the "next" chunk
@@ -166,7 +166,7 @@ def test_boundary_by_reuse_full_shape_one_block_sampled_rows():
     from chunked_streaming_dit_amd import DitChunk
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
     dev = device()
-    cfg = dataclasses.replace(synth.CONFIGS[2], L=1, cid=53, steps=1, bnd=None)
+    cfg = dataclasses.replace(synth.BASE_CHUNK, L=1, cid=53, steps=1, bnd=None)
     P = synth.make_weights(cfg, threads=16)
     c0, c1 = synth.make_inputs(cfg, 0), synth.make_inputs(cfg, 1)
     g = cfg.chunk

@@ -55,7 +55,7 @@ def _check(cfg, steps=None, table=None):
 
 
 def test_config1_tiny_fp32():
-    _check(synth.CONFIGS[1])
+    _check(synth.TINY_FP32)
 
 
 def test_mini_fp32_multi_tile():
@@ -80,7 +80,7 @@ def test_mini_super_resolution_single_step_bf16():
     _check(MINI_SR, steps=1)
 
 
-@pytest.mark.parametrize("cfg", [synth.CONFIGS[1], MINI_F32, MINI_F32_DH64, MINI_BF16, MINI_SR],
+@pytest.mark.parametrize("cfg", [synth.TINY_FP32, MINI_F32, MINI_F32_DH64, MINI_BF16, MINI_SR],
                          ids=["config1", "mini_f32", "mini_f32_dh64", "mini_bf16", "mini_sr"])
 def test_modulation_table_parity(cfg):
     """dit_modulation_table for the schedule and t = 0 (every pass takes its adaLN
@@ -251,4 +251,4 @@ def test_mini_stream_boundary_by_reuse(base):
 def test_config2_full_size_first_step():
     """The base low-res chunk at its full shape (7800 tokens, keys 1560|1560|7800,
     4 blocks, hidden 1536, 12x128 heads, 50 audio tokens): the first denoising step."""
-    _check(synth.CONFIGS[2], steps=1)
+    _check(synth.BASE_CHUNK, steps=1)
