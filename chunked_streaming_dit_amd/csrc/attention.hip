@@ -21,7 +21,7 @@
 
 #include <algorithm>
 
-#include "common.h"
+#include "attn_common.h"
 #include "kernels.h"
 
 namespace dit {
@@ -56,31 +56,6 @@ constexpr float RESCALE_LOG2 = 8.0f;
 // 2^60 per weight, summed over at most 2^24 keys, stays far inside the fp32 range.
 constexpr float NOMAX_BOUND = 60.0f;
 
-
-// Row-sum accumulation from the P^T operand vector.
-__device__ __forceinline__ float row_sum_add(bf16x8 p, float acc) {
-  typedef bf16 b2 __attribute__((ext_vector_type(2)));
-  const b2 one = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    b2 q = {p[2 * i], p[2 * i + 1]};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(q, one, acc, false);
-  }
-  return acc;
-}
-__device__ __forceinline__ float row_sum_add(f32x4 p, float acc) {
-  return acc + p[0] + p[1] + p[2] + p[3];
-}
-constexpr int BKV = 64;  // keys per tile
-
-
-// 16-byte chunk position of chunk c of row r in an unpadded LDS tile whose rows are RB
-// bytes: consecutive rows reading the same chunk spread over all 64 banks.
-template <int RB>
-__device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (RB >= 256) return c ^ (r & 15);
-  else return c ^ ((r >> 1) & 7);
-}
 
 // KIND only names the launch site in profiles (0: self-attention over the segmented
 // keys, 1: audio cross-attention); the code is the same.
@@ -492,124 +467,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   store4<T>(o + (size_t)qrow * ldo + c, acc);
 }
 
-// Attention over one short key segment (at most one 64-key tile, e.g. the audio tokens
-// of the cross-attention), bf16 with dh = 128.  A workgroup is 4 waves x 32 queries of
-// one head; it stages the head's K and V^T tile in LDS once (swizzled as in attn_kernel)
-// and each wave computes S^T = K Q^T, the exact softmax over the tile and O^T = V^T P^T.
-// With 32 KB of LDS and no pipeline state, several workgroups fit per CU, so the whole
-// grid is resident at once: the kernel streams Q in and O out.
-constexpr int XW = 4;           // waves per workgroup
-constexpr int XBQ = 32 * XW;    // queries per workgroup
-
-struct XArgs {
-  const void* q;
-  void* o;
-  const void* k;
-  const void* vt;
-  int ldq, ldo, nq, n, cap, H;
-  float scale;
-};
-
-__global__ __launch_bounds__(64 * XW, 3) void xattn_kernel(XArgs a) {
-  typedef bf16x8 V;
-  typedef bf16 T;
-  constexpr int DH = 128, VE = 8, SZ = 2, QV = DH / 16, DB = DH / 32;
-  constexpr int RBK = DH * SZ, RBV = BKV * SZ;
-  __shared__ __attribute__((aligned(1024))) char smem[BKV * RBK + DH * RBV];
-  char* const sk = smem;
-  char* const sv = smem + BKV * RBK;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, lg = lane >> 5;
-  const int nqt = (a.nq + XBQ - 1) / XBQ;
-  const int head = blockIdx.x / nqt, qt = blockIdx.x - head * nqt;
-  const int qrow = qt * XBQ + wave * 32 + l32;
-  const bool qvalid = qrow < a.nq;
-  const int D = a.H * DH;
-
-  // K tile: 64 rows x 16 chunks; V^T tile: 128 rows x 8 chunks (1024 chunks each);
-  // chunk c of row r goes to position swz(r, c).  Rows / columns past n are zero in
-  // the source (padded to cap).
-  {
-    const char* kg = reinterpret_cast<const char*>(a.k) + (size_t)head * DH * SZ;
-    const char* vg = reinterpret_cast<const char*>(a.vt) + (size_t)head * DH * a.cap * SZ;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int rk = c >> 4, ck = c & 15;
-      st16(sk + rk * RBK + swz<RBK>(rk, ck) * 16, ld16(kg + (size_t)rk * D * SZ + ck * 16));
-      const int rv = c >> 3, cv = c & 7;
-      st16(sv + rv * RBV + swz<RBV>(rv, cv) * 16, ld16(vg + (size_t)rv * a.cap * SZ + cv * 16));
-    }
-  }
-  V qf[QV];
-  {
-    const char* qp = reinterpret_cast<const char*>(a.q) + ((size_t)(qvalid ? qrow : 0) * a.ldq + head * DH) * SZ;
-#pragma unroll
-    for (int s = 0; s < QV; ++s) {
-      u32x4 r = {0u, 0u, 0u, 0u};
-      if (qvalid) r = ld16(qp + s * 32 + lg * 16);
-      qf[s] = as_vec<V>(r);
-    }
-  }
-  __syncthreads();
-
-  f32x16 S[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < QV; ++st) {
-      const V kf = as_vec<V>(ld16(sk + (kb * 32 + l32) * RBK + swz<RBK>(l32, 2 * st + lg) * 16));
-      S[kb] = mfma32(kf, qf[st], S[kb]);
-    }
-  }
-  // exact softmax over the tile: keys past n get zero weight
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-      if (key >= a.n) S[kb][r] = -INFINITY;
-      mx = fmaxf(mx, S[kb][r]);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float ms = mx * a.scale;
-  f32x16 O[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) O[d][r] = 0.f;
-  float l = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      V pf;
-#pragma unroll
-      for (int j = 0; j < VE; ++j) pf[j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(S[kb][v * VE + j], a.scale, -ms)));
-      l = row_sum_add(pf, l);
-      const int pos = swz<RBV>(l32, (kb * 32 + v * 16 + lg * 8) * SZ / 16);
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-        O[d] = mfma32(as_vec<V>(ld16(sv + (d * 32 + l32) * RBV + pos * 16)), pf, O[d]);
-    }
-  const float lt = l + __shfl_xor(l, 32);
-  if (!qvalid) return;
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  T* op = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * DH;
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float v[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = O[d][4 * q + r] * inv;
-      store4<T>(op + d * 32 + 8 * q + 4 * lg, v);
-    }
-}
-
 }  // namespace
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
@@ -655,31 +512,6 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   } else {
     return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-bool short_attention_fits(int dtype, int dh, int nseg, const AttnSeg* segs) {
-  return dtype == BF16 && dh == 128 && nseg == 1 && segs[0].n >= 1 && segs[0].n <= BKV && segs[0].cap >= BKV;
-}
-
-hipError_t short_attention(int dh, int H, const void* q, int ldq, void* o, int ldo, int nq, const AttnSeg& seg,
-                           bool q_prescaled, hipStream_t s) {
-  if (nq <= 0) return hipSuccess;
-  if (dh != 128 || seg.n < 1 || seg.n > BKV || seg.cap < BKV) return hipErrorInvalidValue;
-  XArgs a;
-  a.q = q;
-  a.o = o;
-  a.k = seg.k;
-  a.vt = seg.vt;
-  a.ldq = ldq;
-  a.ldo = ldo;
-  a.nq = nq;
-  a.n = seg.n;
-  a.cap = seg.cap;
-  a.H = H;
-  a.scale = q_prescaled ? 1.0f : attention_q_scale(dh);
-  const int nqt = (nq + XBQ - 1) / XBQ;
-  xattn_kernel<<<nqt * H, 64 * XW, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -55,10 +55,16 @@ struct Layout {
   // state
   std::vector<size_t> kref, vref, kbnd, vbnd, kanc, vanc, kaud, vaud;
   size_t aud_in = 0;  // held audio features [cap_audio, d_a] (dtype), d_a > 0
+  // Audio cross-attention folded into its output Linear (bf16, dh 128, at most 64 audio
+  // tokens): per block U^T = W_co [V_a restricted to each head]^T, [D, H*64] (dtype), so
+  // that the cross out-projection is P [n, H*64] U^T (see short_attention_probs).
+  bool fold = false;
+  std::vector<size_t> uta;  // held audio: per block U^T
   size_t modtab = 0;  // DIT_MOD_TABLE_MAX entries of mod_entry floats
   size_t mod_entry = 0;
   size_t state_total = 0;
   // workspace
+  size_t wbd = 0, uta_ws = 0;  // fold: head-block-diagonal V_a [H*64, D]; U^T of per-step audio
   size_t xin = 0, h = 0, u = 0, big = 0, q = 0, kc = 0, vtc = 0, o = 0, ain = 0, ka_raw = 0,
          va_raw = 0, ka = 0, vat = 0, mod = 0, tmp = 0, opart = 0, ml = 0;
   int part_rows = 0;  // rows of key-range attention partials (split count x queries)
@@ -116,6 +122,9 @@ Layout make_layout(const dit_config* c) {
     L.vaud.push_back(take(aud));
   }
   L.aud_in = take(c->d_a > 0 ? (size_t)L.cap_audio * c->d_a * L.elt : 0);
+  L.fold = c->dtype == DIT_BF16 && c->dh == 128 && c->d_a > 0 && L.cap_audio == 64;
+  const size_t ubytes = L.fold ? D * (size_t)c->H * 64 * L.elt : 0;
+  for (int l = 0; l < c->L; ++l) L.uta.push_back(take(ubytes));
   L.mod_entry = ((size_t)c->L * 6 + 2) * D;
   L.modtab = take(DIT_MOD_TABLE_MAX * L.mod_entry * 4);
   L.state_total = off;
@@ -140,6 +149,8 @@ Layout make_layout(const dit_config* c) {
   L.part_rows = 2 * L.cap_tok;
   L.opart = take((size_t)L.part_rows * D * 4);
   L.ml = take((size_t)L.part_rows * c->H * 2 * 4);
+  L.wbd = take(L.fold ? (size_t)c->H * 64 * D * L.elt : 0);
+  L.uta_ws = take(L.fold ? D * (size_t)c->H * 64 * L.elt : 0);
   L.ws_total = off;
   return L;
 }
@@ -295,7 +306,7 @@ int pass_begin(dit_handle* hd) {
   return stream_issue_upto(hd, st.base + k);
 }
 
-int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat);
+int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat, void* uta);
 
 // Block l of the pass: its kernels wait for its slot's copy.  A held audio K/V of block
 // l still pending is computed first (its weights are now in place).
@@ -304,7 +315,9 @@ int block_begin(dit_handle* hd, int l) {
   if (st.on) HIPCHK(hipStreamWaitEvent(hd->stream, st.ready[(st.base + l) % st.nslot], 0));
   if (!hd->aud_pend.empty() && hd->aud_pend[l]) {
     const Layout& L = hd->lay;
-    if (int rc = audio_kv(hd, l, hd->n_aud, hd->S(L.aud_in), hd->S(L.kaud[l]), hd->S(L.vaud[l]))) return rc;
+    if (int rc = audio_kv(hd, l, hd->n_aud, hd->S(L.aud_in), hd->S(L.kaud[l]), hd->S(L.vaud[l]),
+                          L.fold ? hd->S(L.uta[l]) : nullptr))
+      return rc;
     hd->aud_pend[l] = 0;
   }
   return DIT_OK;
@@ -407,8 +420,9 @@ int embed(dit_handle* hd, const float* x, int n, const float* cond, int cond_mod
 }
 
 // Block l's audio K (k-normed) and V^T (attention layout, capacity cap_audio) from the
-// audio tokens ain [M, d_a] (dtype).
-int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat) {
+// audio tokens ain [M, d_a] (dtype); with uta (the folded cross-attention) also
+// U^T = W_co V_bd^T [D, H*64], V_bd the head-block-diagonal copy of V [M, D].
+int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat, void* uta) {
   const dit_config& c = hd->cfg;
   const Layout& L = hd->lay;
   const int D = c.D;
@@ -422,6 +436,13 @@ int audio_kv(dit_handle* hd, int l, int M, const void* ain, void* ka, void* vat)
   HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, M, nullptr, hd->X(L.ka_raw), hd->X(L.va_raw), D, nullptr,
                      hd->B(l, DIT_WB_GCK), 0, g0, (float)c.eps, (float)c.rope_theta, 1.0f, nullptr, ka,
                      vat, L.cap_audio, s));
+  if (uta) {
+    const int HK = c.H * 64;
+    HIPCHK(head_blockdiag(c.dtype, hd->X(L.va_raw), M, D, c.dh, hd->X(L.wbd), s));
+    GemmEpi eu{};
+    eu.kind = EPI_BIAS; eu.bias = nullptr; eu.out = uta; eu.ldo = HK;
+    HIPCHK(gemm(c.dtype, hd->B(l, DIT_WB_CO_W), D, hd->X(L.wbd), D, D, HK, D, eu, s));
+  }
   return DIT_OK;
 }
 
@@ -709,7 +730,9 @@ int audio_kv_precompute(dit_handle* h, const float* audio, int M) {
   int rc = pass_begin(h);
   for (int l = 0; l < c.L && !rc; ++l) {
     rc = block_begin(h, l);
-    if (!rc) rc = audio_kv(h, l, M, h->S(h->lay.aud_in), h->S(h->lay.kaud[l]), h->S(h->lay.vaud[l]));
+    if (!rc)
+      rc = audio_kv(h, l, M, h->S(h->lay.aud_in), h->S(h->lay.kaud[l]), h->S(h->lay.vaud[l]),
+                    h->lay.fold ? h->S(h->lay.uta[l]) : nullptr);
     if (!rc) rc = block_end(h, l);
   }
   if ((rc = pass_end(h, rc))) return rc;
@@ -847,14 +870,23 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
                            hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
       }
       AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
+      void* uta = L.fold ? hd->S(L.uta[l]) : nullptr;
       if (!held) {
-        if (int rc2 = audio_kv(hd, l, M, hd->X(L.ain), hd->X(L.ka), hd->X(L.vat))) return rc2;
+        uta = L.fold ? hd->X(L.uta_ws) : nullptr;
+        if (int rc2 = audio_kv(hd, l, M, hd->X(L.ain), hd->X(L.ka), hd->X(L.vat), uta)) return rc2;
         aseg = AttnSeg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
       }
-      if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
-      HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));
+      if (uta) {
+        // folded: P [n, H*64] from the short softmax, then h += P U^T + b_co
+        const int HK = c.H * 64;
+        HIPCHK(short_attention_probs(c.dh, c.H, hd->X(L.q), D, hd->X(L.o), HK, n, aseg, true, s));
+        HIPCHK(gemm(c.dtype, hd->X(L.o), HK, uta, HK, n, D, HK, e, s));
+      } else {
+        if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;
+        HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));
+      }
     }
     // MLP
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));

@@ -531,6 +531,32 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
                              fmod_out, s);
 }
 
+// One thread per 16-byte chunk of the output (8 bf16 or 4 fp32).
+template <class T>
+__global__ __launch_bounds__(256) void head_blockdiag_kernel(const T* __restrict__ v, int M, int D, int dh,
+                                                             T* __restrict__ out) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  const int H = D / dh, cpr = D / VE;  // 16-byte chunks per row
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)H * 64 * cpr) return;
+  const int row = (int)(i / cpr), c = (int)(i - (long long)row * cpr) * VE;
+  const int h = row / 64, k = row - h * 64;
+  u32x4 val = {0u, 0u, 0u, 0u};
+  if (k < M && c / dh == h) val = ld16(v + (size_t)k * D + c);
+  st16(out + (size_t)row * D + c, val);
+}
+
+hipError_t head_blockdiag(int dtype, const void* v, int M, int D, int dh, void* out, hipStream_t s) {
+  if (M < 0 || M > 64 || D % 8 || dh % 8 || D % dh) return hipErrorInvalidValue;
+  const long long n = (long long)(D / dh) * 64 * (D / (dtype == BF16 ? 8 : 4));
+  dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (dtype == BF16)
+    head_blockdiag_kernel<bf16><<<grid, block, 0, s>>>((const bf16*)v, M, D, dh, (bf16*)out);
+  else
+    head_blockdiag_kernel<float><<<grid, block, 0, s>>>((const float*)v, M, D, dh, (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
                             hipStream_t s) {
   if (D % 256) return hipErrorInvalidValue;

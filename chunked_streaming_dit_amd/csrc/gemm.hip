@@ -37,7 +37,7 @@ __device__ __forceinline__ void epi_cols_load(EpiCols<NB, EPI>& c, int nw, int l
       const int n = nw + j * 32 + 8 * q + 4 * lg;
 #pragma unroll
       for (int r = 0; r < 4; ++r) c.b[j][q][r] = 0.f;
-      if (n < N) load4<T>(bias + n, c.b[j][q]);
+      if (n < N && bias) load4<T>(bias + n, c.b[j][q]);
     }
 }
 

@@ -28,7 +28,7 @@ enum EpiKind {
 };
 struct GemmEpi {
   int kind;
-  const void* bias;   // [N] dtype
+  const void* bias;   // [N] dtype, or NULL (no bias)
   void* out;          // EPI_BIAS/EPI_GELU/EPI_F32 output, EPI_RESID h, EPI_EULER x
   int ldo;
   const float* gate;  // EPI_RESID
@@ -104,6 +104,12 @@ hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& 
 bool short_attention_fits(int dtype, int dh, int nseg, const AttnSeg* segs);
 hipError_t short_attention(int dh, int H, const void* q, int ldq, void* o, int ldo, int nq, const AttnSeg& seg,
                            bool q_prescaled, hipStream_t s);
+// The same softmax, writing the normalised probabilities p [nq, ldp >= H*64] (bf16; head
+// h's 64 key columns from h*64, keys >= n as 0) instead of O; seg.vt is not read.  With
+// U_h = V_h W_o[:, h]^T per head, sum_h P_h U_h is the attention output times the output
+// Linear W_o: for a short segment that product has H*64 terms per output against D.
+hipError_t short_attention_probs(int dh, int H, const void* q, int ldq, void* p, int ldp, int nq,
+                                 const AttnSeg& seg, bool q_prescaled, hipStream_t s);
 // Split plan (nsplit, qt0; no buffers) minimising the modelled time for nq queries, H
 // heads, key_tiles 64-key tiles, partial storage of partial_rows rows and `slots`
 // concurrent workgroups.
@@ -157,6 +163,10 @@ hipError_t modulation(int dtype, int D, int L, double t, const void* t1w, const 
                       const void* t2w, const void* t2b, const void* const* modw,
                       const void* const* modb, const void* fmodw, const void* fmodb, float* tmp,
                       float* mod_out, float* fmod_out, hipStream_t s);
+// Head-block-diagonal copy of v [M, D] (dtype, heads of dh columns): out [H*64, D] with
+// row h*64 + k = v row k restricted to head h's columns (other columns 0), rows k >= M 0.
+// Requires M <= 64 and D % 8 == 0.
+hipError_t head_blockdiag(int dtype, const void* v, int M, int D, int dh, void* out, hipStream_t s);
 // One block's modulation out[6D] = Wmod c + bmod (W [6D, D] dtype, c [D] fp32).
 hipError_t block_modulation(int dtype, int D, const void* w, const void* b, const float* c, float* out,
                             hipStream_t s);

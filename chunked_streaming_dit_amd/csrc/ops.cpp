@@ -112,6 +112,17 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
                 "qknorm_rope");
 }
 
+int ditk_attention_probs(int H, const void* q, int nq, const void* k, int n, int cap, int q_prescaled,
+                         void* p, void* stream) {
+  if (!q || !k || !p) return fail(DIT_EINVAL, "NULL argument");
+  if (H < 1 || nq < 0) return fail(DIT_ESHAPE, "H=%d nq=%d", H, nq);
+  if (n < 1 || n > 64 || cap < 64 || cap % 64) return fail(DIT_ESHAPE, "n=%d cap=%d: needs 1 <= n <= 64 <= cap", n, cap);
+  const AttnSeg seg{k, nullptr, n, cap};
+  return hipchk(short_attention_probs(128, H, q, H * 128, p, H * 64, nq, seg, q_prescaled != 0,
+                                      (hipStream_t)stream),
+                "short_attention_probs");
+}
+
 int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
                    int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,

@@ -301,6 +301,12 @@ class ops:
                                        _ptr(gk), float(q_fold), o.data_ptr(), _stream()))
 
     @staticmethod
+    def attention_probs(H: int, q, k, n: int, p, q_prescaled: bool = False) -> None:
+        """Softmax probabilities of one short key segment, p [nq, H*64] (ditk_attention_probs)."""
+        C.check(C.lib().ditk_attention_probs(H, q.data_ptr(), q.shape[0], k.data_ptr(), n, k.shape[0],
+                                             1 if q_prescaled else 0, p.data_ptr(), _stream()))
+
+    @staticmethod
     def modulation(dtype: str, cfg: ChunkConfig, weights: Dict[str, torch.Tensor], t: float,
                    mod_out, fmod_out, tmp) -> None:
         names = cfg.weight_names()

@@ -158,7 +158,9 @@ int dit_weight_count(const dit_config* cfg);
 /* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
  * max_bnd boundary tokens, of max_bnd interpolation-anchor tokens and (d_a > 0) of
  * max_audio audio tokens (each rounded up to 64 tokens); (d_a > 0) the held audio
- * features [max_audio rounded up to 64, d_a]; and the modulation table
+ * features [max_audio rounded up to 64, d_a]; for bf16 with dh = 128 and max_audio <= 64
+ * per block the audio values folded into the cross-attention's output Linear
+ * (D x H*64, see ditk_attention_probs); and the modulation table
  * (DIT_MOD_TABLE_MAX entries of (6 L + 2) D floats).  0 if the config is invalid (see
  * dit_last_error). */
 size_t dit_state_bytes(const dit_config* cfg);

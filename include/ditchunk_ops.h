@@ -80,6 +80,20 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
                    const void* gk, double q_fold, void* o, void* hip_stream);
 
+/* The softmax probabilities of one short key segment (bf16, dh = 128, 1..64 keys; the
+ * audio cross-attention's shape): p [nq, H*64] (bf16), head h's 64 key columns from
+ * h*64, p[i, h*64 + j] = softmax_j(q_i k_j / sqrt(dh)) for j < n and 0 for n <= j < 64.
+ * q [nq, H*128] (q_prescaled as in ditk_attention), k [cap, H*128] in the layout of
+ * ditk_qknorm_rope (rows >= n zero).  With U_h = V_h W_o[:, head h]^T this gives the
+ * attention output already multiplied by the output Linear W_o as sum_h P_h U_h, a
+ * product of H*64 terms per output instead of D (HeyGen, "Avatar inference at scale",
+ * section "The underlying model architecture": the audio conditioning; folding the
+ * output Linear into the values is this library's reading).
+ * Errors: EINVAL (NULL pointer), ESHAPE (n outside 1..64, cap < 64 or not a multiple
+ * of 64, H < 1, nq < 0). */
+int ditk_attention_probs(int H, const void* q, int nq, const void* k, int n, int cap, int q_prescaled,
+                         void* p, void* hip_stream);
+
 /* Timestep conditioning and adaLN modulation for timestep t, from the weight table of
  * ditchunk.h: mod_out [L, 6, D] (fp32: shift_msa, scale_msa, gate_msa, shift_mlp,
  * scale_mlp, gate_mlp), fmod_out [2, D] (fp32: shift, scale).  tmp: fp32 scratch of

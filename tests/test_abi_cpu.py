@@ -59,6 +59,8 @@ def test_sizes_and_weight_count():
         kv = cfg.L * 2 * cfg.D * elt * (
             (cfg.N_ref + 63) // 64 * 64 + 2 * ((cfg.chunk.h * cfg.chunk.w + 63) // 64 * 64) + aud)
         kv += aud * cfg.d_a * elt  # the held audio features
+        if cfg.dtype == "bf16" and cfg.dh == 128 and 0 < cfg.M <= 64 and cfg.d_a > 0:
+            kv += cfg.L * cfg.D * cfg.H * 64 * elt  # the folded cross-attention values
         # plus the modulation table: DIT_MOD_TABLE_MAX entries of (6 L + 2) D fp32
         kv += 16 * (6 * cfg.L + 2) * cfg.D * 4
         assert kv <= sb <= kv + (8 * cfg.L + 1) * 256
@@ -190,6 +192,10 @@ def test_euler_and_ops_validation():
     assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
     assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
     assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 65, 128, 1, FAKE, None) == C.DIT_ESHAPE  # n > 64
+    assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 0, 64, 1, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 50, 32, 1, FAKE, None) == C.DIT_ESHAPE  # cap < 64
+    assert lib.ditk_attention_probs(2, None, 10, FAKE, 50, 64, 1, FAKE, None) == C.DIT_EINVAL
     # unsplit_rows: negative, or neither a multiple of the 256-query tile nor >= nq
     assert lib.ditk_attention(1, 128, 2, FAKE, 300, 1, k, k, n, cap, 2, FAKE, -1, 0, None, None, 0.0, FAKE,
                               None) == C.DIT_EINVAL

@@ -267,6 +267,41 @@ def test_attention_short_segment_bf16(nq, n, prescaled):
     assert err <= tol, err
 
 
+@pytest.mark.parametrize("nq,n,H", [(1, 1, 1), (300, 50, 12), (129, 64, 2), (7800, 50, 12), (77, 7, 3)])
+def test_attention_probs_short_segment(nq, n, H):
+    """The probabilities of the short-segment softmax (the folded audio cross-attention):
+    p[i, h*64 + j] = softmax_j(q_i . k_j / sqrt(128)) per head against the f64 softmax,
+    with the padding columns j >= n exactly 0, and sum_h P_h (V_h W_o,h^T) equal to the
+    attention output times W_o (the fold's identity) in f64."""
+    dev = device()
+    r = np.random.default_rng(nq + 7 * n + H)
+    D = H * 128
+    q = _arr(r, (nq, D), "bf16", 2.0)
+    k = _arr(r, (n, D), "bf16", 2.0)
+    kp = np.zeros((64, D), np.float32)
+    kp[:n] = k
+    qd = _dev(synth.round_bf16((q * Q_SCALE[128]).astype(np.float32)), "bf16", dev)
+    p = torch.full((nq, H * 64), 7.0, device=dev, dtype=torch.bfloat16)
+    ops.attention_probs(H, qd, _dev(kp, "bf16", dev), n, p, q_prescaled=True)
+    torch.cuda.synchronize()
+    pg = p.float().cpu().numpy().reshape(nq, H, 64)
+    q64 = synth.round_bf16((q * Q_SCALE[128]).astype(np.float32)).astype(np.float64) / Q_SCALE[128]
+    s = np.einsum("ihd,jhd->ihj", q64.reshape(nq, H, 128), k.astype(np.float64).reshape(n, H, 128)) / math.sqrt(128)
+    s -= s.max(axis=2, keepdims=True)
+    po = np.exp(s)
+    po /= po.sum(axis=2, keepdims=True)
+    assert np.all(pg[:, :, n:] == 0.0)
+    err = rel_err(pg[:, :, :n], po)
+    assert err <= TOL["bf16"] / 4, err
+    # the fold: sum_h P_h (V_h W_h^T) == (P V) W^T, checked in f64 on the GPU's P
+    v = r.standard_normal((n, H, 128))
+    W = r.standard_normal((64, D)) / math.sqrt(D)  # an output Linear with 64 outputs
+    pv = np.einsum("ihj,jhd->ihd", pg[:, :, :n].astype(np.float64), v).reshape(nq, D)
+    U = np.einsum("jhd,ohd->hjo", v, W.reshape(64, H, 128))  # [H, n, out]
+    fold = np.einsum("ihj,hjo->io", pg[:, :, :n].astype(np.float64), U)
+    assert np.allclose(fold, pv @ W.T, rtol=1e-10, atol=1e-10)
+
+
 def test_attention_real_head_shape_bf16():
     """One head group at the base-chunk shape: 12 heads of 128, keys 1560 | 1560 | 1000."""
     err = _attn_case("bf16", 128, 12, 1000, [1560, 1560, 1000], 5, prescaled=True)
