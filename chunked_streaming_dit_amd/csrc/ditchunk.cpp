@@ -899,6 +899,11 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     if (int rc = block_end(hd, l)) return rc;
   }
   // final layer + Euler
+  if (final_layer_fits(c.dtype, D, c.c_p)) {
+    HIPCHK(final_layer(h, n, D, fmod, fmod + D, (float)c.eps, hd->W(DIT_W_FIN_W), hd->W(DIT_W_FIN_B),
+                       (float)(t_next - t), x, v_out, s));
+    return DIT_OK;
+  }
   HIPCHK(rmsnorm_mod(c.dtype, h, n, D, fmod, fmod + D, (float)c.eps, hd->X(L.u), s));
   e = GemmEpi{};
   e.kind = EPI_EULER; e.bias = hd->W(DIT_W_FIN_B); e.out = x; e.ldo = c.c_p; e.v_out = v_out;

@@ -665,6 +665,102 @@ __global__ __launch_bounds__(LDS_THREADS) void patch_embed_kernel(
   epilogue<bf16, MB, NB, EPI_F32>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, n, N, e);
 }
 
+// Final layer with its pre-norm and the Euler update in one pass: for 32 tokens per
+// workgroup, u = RMSNorm(h) (1 + scale) + shift is formed in registers from the fp32
+// rows of h and kept in LDS as bf16 (the operand the unfused GEMM would read), then
+// v = u W^T + b (N = 64 outputs) with the K range split over the 4 waves and the
+// partial products summed through LDS; x += dt v and v_out = v.  h is read once and u
+// never leaves the CU, against a norm pass writing u and a 122-workgroup GEMM reading it.
+constexpr int FL_BM = 32, FL_N = 64, FL_THREADS = 256;
+
+template <int IT>
+__global__ __launch_bounds__(FL_THREADS) void final_layer_kernel(const float* __restrict__ h, int n,
+                                                               const float* __restrict__ shift,
+                                                               const float* __restrict__ scale, float eps,
+                                                               const bf16* __restrict__ W,
+                                                               const bf16* __restrict__ b, float dt,
+                                                               float* __restrict__ x, float* __restrict__ v_out) {
+  typedef bf16x8 V;
+  constexpr int D = 256 * IT;
+  constexpr int PITCH = D * 2 + 16;  // bytes per u row: 16-byte pad spreads a fragment read over the banks
+  __shared__ __attribute__((aligned(16))) char su[FL_BM * PITCH];
+  __shared__ float red[4][2][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, lg = lane >> 5;
+  const int row0 = blockIdx.x * FL_BM;
+
+  // u rows: wave w forms rows 8w .. 8w + 7 of the tile (rows past n repeat row n - 1)
+  f32x4 sc[IT], sh[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    sc[i] = *reinterpret_cast<const f32x4*>(scale + i * 256 + lane * 4);
+    sh[i] = *reinterpret_cast<const f32x4*>(shift + i * 256 + lane * 4);
+  }
+  for (int rr = 0; rr < FL_BM / 4; ++rr) {
+    const int r = wave * (FL_BM / 4) + rr;
+    const float* hr = h + (size_t)min(row0 + r, n - 1) * D + lane * 4;
+    f32x4 v[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) v[i] = *reinterpret_cast<const f32x4*>(hr + i * 256);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = fmaf(v[i][q] * rs, 1.0f + sc[i][q], sh[i][q]);
+      store4<bf16>(reinterpret_cast<bf16*>(su + r * PITCH) + i * 256 + lane * 4, o);
+    }
+  }
+  __syncthreads();
+
+  // v^T partial over this wave's quarter of K: first MFMA operand W rows (outputs),
+  // second u rows, so the lane holds token row0 + l32 and 16 outputs per 32-block
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) acc[j][t] = 0.f;
+  constexpr int KW = D / 4;
+  const int k_begin = wave * KW;
+#pragma unroll 4
+  for (int k0 = k_begin; k0 < k_begin + KW; k0 += 16) {
+    const V af = as_vec<V>(ld16(su + l32 * PITCH + (k0 + lg * 8) * 2));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const V wf = as_vec<V>(ld16(W + (size_t)(j * 32 + l32) * D + k0 + lg * 8));
+      acc[j] = mfma32(wf, af, acc[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) red[wave][j][t][lane] = acc[j][t];
+  __syncthreads();
+
+  // wave w completes registers 4w .. 4w + 3 of both blocks: outputs j*32 + 8w + 4lg + {0..3}
+  const int m = row0 + l32;
+  if (m >= n) return;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = j * 32 + 8 * wave + 4 * lg;
+    float bb[4], v[4], xo[4];
+    load4<bf16>(b + c, bb);
+    load4<float>(x + (size_t)m * FL_N + c, xo);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = 4 * wave + q;
+      v[q] = red[0][j][t][lane] + red[1][j][t][lane] + red[2][j][t][lane] + red[3][j][t][lane] + bb[q];
+      xo[q] = fmaf(dt, v[q], xo[q]);
+    }
+    store4<float>(x + (size_t)m * FL_N + c, xo);
+    if (v_out) store4<float>(v_out + (size_t)m * FL_N + c, v);
+  }
+}
+
 }  // namespace
 
 bool gemm_qknorm_fits(int dtype, int M, int N, int dh) {
@@ -721,6 +817,26 @@ hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_
   const int tiles = ((n + PE_BM - 1) / PE_BM) * (N / PE_BN);
   patch_embed_kernel<<<tiles, LDS_THREADS, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g,
                                                    reinterpret_cast<const bf16*>(W), N, e);
+  return hipGetLastError();
+}
+
+bool final_layer_fits(int dtype, int D, int c_p) {
+  return dtype == BF16 && c_p == FL_N && (D == 1536 || D == 1024 || D == 512 || D == 256);
+}
+
+hipError_t final_layer(const float* h, int n, int D, const float* shift, const float* scale, float eps,
+                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + FL_BM - 1) / FL_BM), block(FL_THREADS);
+  const bf16* w = reinterpret_cast<const bf16*>(W);
+  const bf16* bb = reinterpret_cast<const bf16*>(b);
+  switch (D) {
+    case 256: final_layer_kernel<1><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
+    case 512: final_layer_kernel<2><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
+    case 1024: final_layer_kernel<4><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
+    case 1536: final_layer_kernel<6><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

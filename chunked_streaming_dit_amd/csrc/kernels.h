@@ -143,6 +143,13 @@ hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* c
 // ((c_p + c_c) % 64 == 0, c_p % 8 == 0, c_c % 8 == 0, N % 256 == 0); otherwise
 // patch_embed() returns hipErrorInvalidValue.
 bool patch_embed_fits(int dtype, int c_p, int c_c, int N);
+// Final layer with its pre-norm and the Euler step: v = (RMSNorm(h) (1 + scale) + shift)
+// W^T + b with u rounded to bf16 as the GEMM operand, x += dt v, v_out (optional) = v.
+// h [n, D] fp32, shift/scale [D] fp32, W [64, D] and b [64] bf16, x and v_out [n, 64]
+// fp32.  final_layer_fits: the shapes it takes (bf16, c_p = 64, D in 256/512/1024/1536).
+bool final_layer_fits(int dtype, int D, int c_p);
+hipError_t final_layer(const float* h, int n, int D, const float* shift, const float* scale, float eps,
+                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s);
 hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
                        RopeGrid g, const void* W, const void* bias, float* out, int N, hipStream_t s);
 
