@@ -72,7 +72,7 @@ _SIGS = {
     "dit_timing_enable": (I, [P, I]),
     "dit_timing_read": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(Dbl), ctypes.POINTER(Dbl)]),
     "ditk_linear": (I, [I, P, P, P, I, I, I, I, P, P]),
-    "ditk_linear_residual": (I, [I, P, P, P, P, I, I, I, P, P]),
+    "ditk_linear_residual": (I, [I, P, P, P, P, I, I, I, P, P, ctypes.c_longlong, P]),
     "ditk_rmsnorm_modulate": (I, [I, P, I, I, P, P, Dbl, P, P]),
     "ditk_qknorm_rope": (I, [I, I, I, I, P, P, P, I, P, P, I, DitGrid, Dbl, Dbl, Dbl, P, P, P, I, P]),
     "ditk_attention": (I, [I, I, I, P, I, I, ctypes.POINTER(P), ctypes.POINTER(P),

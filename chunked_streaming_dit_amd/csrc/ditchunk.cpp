@@ -519,6 +519,7 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     if (rc) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
+    e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
     HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));
     e = GemmEpi{};
@@ -526,6 +527,7 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
+    e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
     HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
     if (int rc = block_end(hd, l)) return rc;
   }
@@ -852,6 +854,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     }
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
+    e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
     HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
     // audio cross-attention
     if (cross) {
@@ -878,6 +881,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
       }
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
+      e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
       if (uta) {
         // folded: P [n, H*64] from the short softmax, then h += P U^T + b_co
         const int HK = c.H * 64;
@@ -895,6 +899,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
+    e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
     HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
     if (int rc = block_end(hd, l)) return rc;
   }

@@ -12,6 +12,8 @@
 //     operand is W rows and second operand A rows, so each lane ends up holding 4
 //     consecutive output columns of one output row: the epilogue reads bias, gate and
 //     the fp32 residual as 16-byte vectors.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -423,8 +425,11 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
   const int wm = wave / LDS_WN, wn = wave % LDS_WN;
   const int l32 = lane & 31, lg = lane >> 5;
   const int num_m = (M + BM - 1) / BM, num_n = (N + BN - 1) / BN;
+  // EPI_PARTIAL: workgroup b takes K part b / tiles of tile b % tiles
+  const int tiles = num_m * num_n;
+  const int part = EPI == EPI_PARTIAL ? (int)blockIdx.x / tiles : 0;
   int tm, tn;
-  tile_of(blockIdx.x, num_m, num_n, tm, tn);
+  tile_of((int)blockIdx.x - part * tiles, num_m, num_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Loader: instruction j of this wave fills tile rows 8 (NW j + wave) + [0, 8); the
@@ -453,8 +458,16 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     }
   };
 
+  // EPI_PARTIAL stores the raw product of its K part as an fp32 tile of ws
+  GemmEpi ep = e;
+  if constexpr (EPI == EPI_PARTIAL) {
+    ep.kind = EPI_F32;
+    ep.bias = nullptr;
+    ep.out = e.ws + (size_t)part * M * N;
+    ep.ldo = N;
+  }
   EpiCols<NB, EPI> cols;
-  epi_cols_load<bf16, NB, EPI>(cols, n0 + wn * WN, lg, N, e);
+  epi_cols_load<bf16, NB, EPI>(cols, n0 + wn * WN, lg, N, ep);
   f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
@@ -469,13 +482,16 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
   const int a_base = (wm * WM + l32) * 128;
   const int w_base = (BM + wn * WN + l32) * 128;
 
+  // 64-wide K steps [it0, it1): all of them, or this workgroup's part of them
   const int nk = K / 64;
-  issue(0, 0);
+  const int it0 = EPI == EPI_PARTIAL ? (int)((long long)nk * part / e.ksplit) : 0;
+  const int it1 = EPI == EPI_PARTIAL ? (int)((long long)nk * (part + 1) / e.ksplit) : nk;
+  issue(0, it0 * 64);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < nk; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < nk) issue(buf ^ 1, (it + 1) * 64);
+  for (int it = it0; it < it1; ++it) {
+    const int buf = (it - it0) & 1;
+    if (it + 1 < it1) issue(buf ^ 1, (it + 1) * 64);
     const char* st = smem + buf * STAGE;
     // Fragments of sub-step s+1 are requested before sub-step s multiplies and the
     // scheduler is asked to interleave them one per MFMA, so LDS latency hides under
@@ -510,8 +526,35 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
   }
   if constexpr (EPI == EPI_QKNORM)
     epilogue_qknorm<BM, MB, NB>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg, M, e);
+  else if constexpr (EPI == EPI_PARTIAL)
+    epilogue<bf16, MB, NB, EPI_F32>(acc, reinterpret_cast<const EpiCols<NB, EPI_F32>&>(cols), m0 + wm * WM,
+                                    n0 + wn * WN, l32, lg, M, N, ep);
   else
     epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
+}
+
+// Split K: h[m, n] += gate[n] (sum_p ws[p, m, n] + b[n]) (gate NULL: 1), one thread per
+// 4 consecutive columns.
+template <class T>
+__global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restrict__ ws, int parts, int M, int N,
+                                                           const T* __restrict__ bias,
+                                                           const float* __restrict__ gate,
+                                                           float* __restrict__ h, int ldh) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)M * N / 4) return;
+  const int m = (int)(i / (N / 4)), n = (int)(i - (long long)m * (N / 4)) * 4;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, v[4], b[4] = {0.f, 0.f, 0.f, 0.f}, g[4] = {1.f, 1.f, 1.f, 1.f}, hv[4];
+  for (int p = 0; p < parts; ++p) {
+    load4<float>(ws + ((size_t)p * M + m) * N + n, v);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += v[r];
+  }
+  if (bias) load4<T>(bias + n, b);
+  if (gate) load4<float>(gate + n, g);
+  load4<float>(h + (size_t)m * ldh + n, hv);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hv[r] += g[r] * (acc[r] + b[r]);
+  store4<float>(h + (size_t)m * ldh + n, hv);
 }
 
 template <int BM, int BN>
@@ -528,8 +571,27 @@ hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int
     case EPI_F32: gemm_lds_kernel<BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_EULER: gemm_lds_kernel<BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_QKNORM: gemm_lds_kernel<BM, BN, EPI_QKNORM><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_PARTIAL:
+      grid.x = tiles * e.ksplit;
+      gemm_lds_kernel<BM, BN, EPI_PARTIAL><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e);
+      break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// EPI_RESID with the K range split into parts (see GemmEpi::ws): partial products of
+// 128 x 256 tiles into ws, then the residual epilogue over their sum.
+hipError_t gemm_resid_splitk(const void* A, int lda, const void* W, int ldw, int M, int N, int K, int parts,
+                             const GemmEpi& e, hipStream_t s) {
+  GemmEpi ep = e;
+  ep.kind = EPI_PARTIAL;
+  ep.ksplit = parts;
+  hipError_t err = launch_lds<128, 256>(A, lda, W, ldw, M, N, K, ep, s);
+  if (err != hipSuccess) return err;
+  const long long n4 = (long long)M * N / 4;
+  splitk_resid_kernel<bf16><<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(
+      e.ws, parts, M, N, reinterpret_cast<const bf16*>(e.bias), e.gate, reinterpret_cast<float*>(e.out), e.ldo);
   return hipGetLastError();
 }
 
@@ -784,7 +846,16 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
         const long long cost = (tiles + 255) / 256 * (long long)bm;
         if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = bm; }
       }
-      // Too few tiles to occupy the chip (short context passes): smaller tiles.
+      // Too few tiles to occupy the chip (short context passes): a residual GEMM with a
+      // long K (>= 4096) and a workspace splits its K range over 128 x 256 tiles, as many
+      // parts (2-4) as fit one wave of workgroups; other launches take smaller tiles.
+      // (With K = 1536 the merge pass costs more than the split saves.)
+      const long long t128 = (long long)((M + 127) / 128) * (N / 256);
+      if (e.kind == EPI_RESID && e.ws && t128 < 160 && K >= 4096 && K % 64 == 0) {
+        int parts = (int)std::min<long long>(4, 256 / t128);
+        while (parts > 1 && (long long)parts * M * N > e.ws_floats) --parts;
+        if (parts > 1) return gemm_resid_splitk(A, lda, W, ldw, M, N, K, parts, e, s);
+      }
       if (e.kind != EPI_QKNORM && ((M + best - 1) / best) * (N / 256) < 160) {
         if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
         return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);

@@ -25,6 +25,7 @@ enum EpiKind {
                   //   k heads: QK-RMSNorm x gk (+ RoPE) -> k_out [kpad, D], rows M..kpad zero;
                   //   v columns: V^T -> vt_out [D, vcap] in the attention layout (columns
                   //   M..kpad zero), or, with vt_out NULL, y -> out [M, ldo] (columns 2D..3D).
+  EPI_PARTIAL = 6,  // internal (split K): the raw product of one K part -> ws (fp32)
 };
 struct GemmEpi {
   int kind;
@@ -43,6 +44,12 @@ struct GemmEpi {
   int D, kpad, rope, vcap;
   float q_scale, eps, log2_theta;
   RopeGrid g;
+  // Optional fp32 workspace for EPI_RESID launches too small to fill the chip with large
+  // tiles: the K range is then split over workgroups, their products summed by a second
+  // kernel that applies the residual epilogue (needs splits x M x N floats).
+  float* ws;
+  long long ws_floats;
+  int ksplit;  // internal: number of K parts of an EPI_PARTIAL launch
 };
 // Whether gemm() can fuse EPI_QKNORM for this launch (else: EPI_BIAS + qknorm_rope).
 bool gemm_qknorm_fits(int dtype, int M, int N, int dh);

@@ -66,16 +66,21 @@ int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, i
 }
 
 int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b, const float* gate,
-                         int M, int N, int K, float* h, void* stream) {
+                         int M, int N, int K, float* h, float* workspace, long long workspace_floats,
+                         void* stream) {
   int rc = gemm_args(dtype, A, W, b, M, N, K);
   if (rc) return rc;
   if (!h) return fail(DIT_EINVAL, "h is NULL");
+  if (workspace_floats < 0 || (workspace_floats > 0 && !workspace))
+    return fail(DIT_EINVAL, "workspace NULL with workspace_floats=%lld", workspace_floats);
   GemmEpi e{};
   e.kind = EPI_RESID;
   e.bias = b;
   e.out = h;
   e.ldo = N;
   e.gate = gate;
+  e.ws = workspace_floats > 0 ? workspace : nullptr;
+  e.ws_floats = workspace_floats;
   return hipchk(gemm(dtype, A, K, W, K, M, N, K, e, (hipStream_t)stream), "gemm");
 }
 

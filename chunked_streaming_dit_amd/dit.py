@@ -256,14 +256,17 @@ class ops:
                                     act, out.data_ptr(), _stream()))
 
     @staticmethod
-    def linear_residual(A, W, b, gate, h, dtype: str) -> None:
+    def linear_residual(A, W, b, gate, h, dtype: str, workspace: Optional[torch.Tensor] = None) -> None:
+        """workspace: optional fp32 tensor for the split-K launch (ditk_linear_residual)."""
         M, K = A.shape
         N = W.shape[0]
         for t, n in ((A, "A"), (W, "W"), (b, "b"), (h, "h")):
             _dev(t, n)
         _dev(gate, "gate", torch.float32)
+        _dev(workspace, "workspace", torch.float32)
         C.check(C.lib().ditk_linear_residual(_dt_code(dtype), A.data_ptr(), W.data_ptr(), b.data_ptr(),
-                                             _ptr(gate), M, N, K, h.data_ptr(), _stream()))
+                                             _ptr(gate), M, N, K, h.data_ptr(), _ptr(workspace),
+                                             0 if workspace is None else workspace.numel(), _stream()))
 
     @staticmethod
     def rmsnorm_modulate(h, shift, scale, eps, out, dtype: str) -> None:

@@ -28,9 +28,15 @@ int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, i
                 int act, void* out, void* hip_stream);
 
 /* h[M, N] (fp32) += gate[N] (.) (A W^T + b); gate fp32, NULL means 1.  The gated
- * residual of the adaLN DiT block (out-proj, cross out-proj, FC2). */
+ * residual of the adaLN DiT block (out-proj, cross out-proj, FC2).  workspace (fp32
+ * device memory of workspace_floats floats, or NULL with 0): when given, a bf16 launch
+ * whose large-tile grid would leave most of the chip idle (the context passes' MLP-out
+ * Linear, K >= 4096) splits its K range into 2-4 parts computed by separate
+ * workgroups and sums them in a second pass (needs parts x M x N floats; with less
+ * workspace it is not split). */
 int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b, const float* gate,
-                         int M, int N, int K, float* h, void* hip_stream);
+                         int M, int N, int K, float* h, float* workspace, long long workspace_floats,
+                         void* hip_stream);
 
 /* out[n, D] (dtype) = RMSNorm(h) (.) (1 + scale) + shift, h fp32 [n, D], shift/scale fp32
  * [D] (both NULL: plain RMSNorm).  D a multiple of 256, <= 4096. */

@@ -192,6 +192,8 @@ def test_euler_and_ops_validation():
     assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 2, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
     assert lib.ditk_attention(1, 128, 2, FAKE, 10, 1, k, k, n, cap, 9, FAKE, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
     assert lib.ditk_attention(0, 128, 2, FAKE, 10, 1, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, FAKE, None) == C.DIT_EINVAL
+    assert lib.ditk_linear_residual(1, FAKE, FAKE, FAKE, None, 64, 256, 64, FAKE, None, 5, None) == C.DIT_EINVAL
+    assert lib.ditk_linear_residual(1, FAKE, FAKE, FAKE, None, 64, 256, 64, FAKE, FAKE, -1, None) == C.DIT_EINVAL
     assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 65, 128, 1, FAKE, None) == C.DIT_ESHAPE  # n > 64
     assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 0, 64, 1, FAKE, None) == C.DIT_ESHAPE
     assert lib.ditk_attention_probs(2, FAKE, 10, FAKE, 50, 32, 1, FAKE, None) == C.DIT_ESHAPE  # cap < 64

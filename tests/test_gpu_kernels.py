@@ -46,18 +46,24 @@ def test_linear(dtype, M, N, K, act):
     assert rel_err(to_np(out), ref) <= TOL[dtype] / 4
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(130, 192, 128), (1000, 1536, 1536), (600, 512, 2048)])
+@pytest.mark.parametrize("dtype,M,N,K,ws", [
+    ("f32", 130, 192, 128, 0), ("bf16", 130, 192, 128, 0), ("f32", 1000, 1536, 1536, 0),
+    ("bf16", 1000, 1536, 1536, 0), ("f32", 600, 512, 2048, 0), ("bf16", 600, 512, 2048, 0),
+    # split K: the context passes' MLP-out shape (3 parts), a ragged M (4 parts), and a
+    # workspace too small for more than 2 parts
+    ("bf16", 1560, 1536, 6144, 3), ("bf16", 777, 512, 4096, 4), ("bf16", 1560, 1536, 6144, 2)])
 @pytest.mark.parametrize("gated", [False, True])
-def test_linear_residual(dtype, M, N, K, gated):
+def test_linear_residual(dtype, M, N, K, ws, gated):
+    """ws: workspace of ws x M x N floats (the split-K launch; 0: none)."""
     dev = device()
     r = np.random.default_rng(M + N + K)
     A, W, b = _arr(r, (M, K), dtype), _arr(r, (N, K), dtype, K ** -0.5), _arr(r, (N,), dtype, 0.5)
     h0 = r.standard_normal((M, N)).astype(np.float32)
     gate = r.standard_normal(N).astype(np.float32) if gated else None
     h = torch.from_numpy(h0).to(dev)
+    work = torch.full((ws * M * N,), float("nan"), device=dev) if ws else None
     ops.linear_residual(_dev(A, dtype, dev), _dev(W, dtype, dev), _dev(b, dtype, dev),
-                        None if gate is None else torch.from_numpy(gate).to(dev), h, dtype)
+                        None if gate is None else torch.from_numpy(gate).to(dev), h, dtype, workspace=work)
     y = O.linear(A.astype(np.float64), W.astype(np.float64), b.astype(np.float64))
     ref = h0 + (y if gate is None else gate * y)
     torch.cuda.synchronize()
