@@ -859,19 +859,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     // audio cross-attention
     if (cross) {
       HIPCHK(rmsnorm_mod(c.dtype, h, n, D, nullptr, nullptr, (float)c.eps, hd->X(L.u), s));
-      e = GemmEpi{};
-      e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
-      if (gemm_qknorm_fits(c.dtype, n, D, c.dh)) {  // q-norm in the GEMM epilogue (no RoPE)
-        e.kind = EPI_QKNORM; e.gq = hd->B(l, DIT_WB_GCQ); e.q_out = hd->X(L.q); e.D = D;
-        e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
-        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
-      } else {
-        e.kind = EPI_BIAS;
-        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
-        HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
-                           nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
-                           hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
-      }
+      // the audio keys and values: held, or from this step's audio
       AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
       void* uta = L.fold ? hd->S(L.uta[l]) : nullptr;
       if (!held) {
@@ -879,18 +867,40 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
         if (int rc2 = audio_kv(hd, l, M, hd->X(L.ain), hd->X(L.ka), hd->X(L.vat), uta)) return rc2;
         aseg = AttnSeg{hd->X(L.ka), hd->X(L.vat), M, L.cap_audio};
       }
+      const int HK = c.H * 64;
+      e = GemmEpi{};
+      e.bias = hd->B(l, DIT_WB_CQ_B); e.out = hd->X(L.big); e.ldo = D;
+      if (uta && gemm_qknorm_fits(c.dtype, n, D, c.dh)) {
+        // folded, and the softmax in the cross-q GEMM's epilogue: P [n, H*64] directly
+        e.kind = EPI_QKNORM_X; e.gq = hd->B(l, DIT_WB_GCQ); e.D = D;
+        e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
+        e.xk = aseg.k; e.xn = aseg.n; e.p_out = hd->X(L.o); e.ldp = HK;
+        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+      } else {
+        if (gemm_qknorm_fits(c.dtype, n, D, c.dh)) {  // q-norm in the GEMM epilogue (no RoPE)
+          e.kind = EPI_QKNORM; e.gq = hd->B(l, DIT_WB_GCQ); e.q_out = hd->X(L.q); e.D = D;
+          e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
+          HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+        } else {
+          e.kind = EPI_BIAS;
+          HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+          HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
+                             nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
+                             hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
+        }
+        if (uta) {  // folded: P [n, H*64] from the short softmax
+          HIPCHK(short_attention_probs(c.dh, c.H, hd->X(L.q), D, hd->X(L.o), HK, n, aseg, true, s));
+        } else {
+          if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;
+        }
+      }
       e = GemmEpi{};
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
       e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
-      if (uta) {
-        // folded: P [n, H*64] from the short softmax, then h += P U^T + b_co
-        const int HK = c.H * 64;
-        HIPCHK(short_attention_probs(c.dh, c.H, hd->X(L.q), D, hd->X(L.o), HK, n, aseg, true, s));
+      if (uta)  // h += P U^T + b_co
         HIPCHK(gemm(c.dtype, hd->X(L.o), HK, uta, HK, n, D, HK, e, s));
-      } else {
-        if (int rc2 = run_attention(hd, n, &aseg, 1, false, ATTN_CROSS, l)) return rc2;
+      else
         HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));
-      }
     }
     // MLP
     HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));

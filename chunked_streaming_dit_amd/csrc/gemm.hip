@@ -14,7 +14,7 @@
 //     the fp32 residual as 16-byte vectors.
 #include <algorithm>
 
-#include "common.h"
+#include "attn_common.h"
 #include "kernels.h"
 
 namespace dit {
@@ -22,6 +22,8 @@ namespace dit {
 namespace {
 
 constexpr int ROWB = 128 + 16;  // LDS bytes per staged row (128 data + 16 pad)
+// Wave layout of gemm_lds_kernel (and patch_embed_kernel): 2 x 4 waves.
+constexpr int LDS_WM = 2, LDS_WN = 4, LDS_THREADS = 64 * LDS_WM * LDS_WN;
 
 // Bias of a wave's NB x 32 columns, loaded into registers before the K loop so that its
 // latency hides under it: lane columns n = nw + 32 j + 8 q + 4 lg + {0..3} in [j][q][0..3].
@@ -123,19 +125,38 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const EpiC
 // written in bf16.  k rows in [M, kpad) are written as zeros.  The rotation uses the
 // hardware sine and cosine (v_sin_f32 / v_cos_f32, argument in turns) on the angle
 // reduced to half a turn; their error is far below the bf16 rounding that follows.
-template <int BM, int MB, int NB>
-__device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], const EpiCols<NB, EPI_QKNORM>& cols,
+// EPI_QKNORM_X layout of the ring after the K loop: the row sums of squares at 0, the
+// normalised q tile (bf16, rows of XQ_PITCH bytes: 16-byte pad) from XQ_OFF, the tile's
+// two heads' key tiles after it.
+constexpr int XQ_OFF = 4096, XQ_PITCH = 512 + 16;
+template <int BM>
+constexpr int xattn_smem() { return XQ_OFF + BM * XQ_PITCH + 2 * XK_TILE; }
+
+template <int BM, int MB, int NB, bool XATT, class Cols>
+__device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], const Cols& cols,
                                                 char* smem, int wm, int wn, int mw, int nw, int l32, int lg,
                                                 int M, const GemmEpi& e) {
   constexpr int DH = 128;
   static_assert(NB == 2, "one wave covers half a head (64 columns)");
   const int part = nw / e.D;
-  if (part == 2 && !e.vt_out) {
+  if constexpr (XATT) {
+    // the tile's two heads' key tiles (rows past xn are zero in the source)
+    const int head0 = (nw - nw % 256) / DH, D = e.D;
+    char* sk = smem + XQ_OFF + BM * XQ_PITCH;
+#pragma unroll
+    for (int i = 0; i < 2 * BKV * 16 / LDS_THREADS; ++i) {
+      const int c = threadIdx.x + LDS_THREADS * i;
+      const int hh = c / (BKV * 16), cc = c - hh * BKV * 16, rk = cc >> 4, ck = cc & 15;
+      const char* src = reinterpret_cast<const char*>(e.xk) + ((size_t)rk * D + (head0 + hh) * DH) * 2 + ck * 16;
+      st16(sk + hh * XK_TILE + rk * XK_RB + swz<XK_RB>(rk, ck) * 16, ld16(src));
+    }
+  }
+  if (!XATT && part == 2 && !e.vt_out) {
     epilogue<bf16, MB, NB, EPI_BIAS>(acc, reinterpret_cast<const EpiCols<NB, EPI_BIAS>&>(cols), mw, nw, l32, lg,
                                      M, 3 * e.D, e);
     return;
   }
-  if (part == 2) {
+  if (!XATT && part == 2) {
     // V^T: the tile (BM tokens x 256 columns) goes transposed through LDS, then each
     // thread writes one column's 16-token group in the attention layout (token offset
     // o of the group at position 8((o%8)/4) + 4(o/8) + o%4); tokens in [M, kpad) as 0.
@@ -196,7 +217,7 @@ __device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], con
   }
   __syncthreads();
   void* outp = isq ? e.q_out : e.k_out;
-  if (!outp) return;  // q not needed (last block of a context pass)
+  if (!XATT && !outp) return;  // q not needed (last block of a context pass)
   bf16* out = reinterpret_cast<bf16*>(outp);
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -232,7 +253,8 @@ __device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], con
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
     const int m = mw + i * 32 + l32;
-    bf16* orow = out + (size_t)m * e.D + col0;
+    bf16* orow = XATT ? reinterpret_cast<bf16*>(smem + XQ_OFF + (m % BM) * XQ_PITCH) + (nw % 256)
+                      : out + (size_t)m * e.D + col0;
     if (m >= M) {
       if (!isq && m < e.kpad) {
         const float z[4] = {0.f, 0.f, 0.f, 0.f};
@@ -273,6 +295,35 @@ __device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], con
         }
         store4<bf16>(orow + j * 32 + 8 * q + 4 * lg, o);
       }
+  }
+  if constexpr (XATT) {
+    // the short softmax of every (head, 32-row block) of the tile from the LDS copies
+    __syncthreads();
+    const int head0 = (nw - nw % 256) / DH, m0 = mw - mw % BM;
+    const char* sk = smem + XQ_OFF + BM * XQ_PITCH;
+    const int wave = threadIdx.x >> 6;
+    for (int u = wave; u < 2 * (BM / 32); u += LDS_THREADS / 64) {
+      const int hh = u / (BM / 32), rb = u - hh * (BM / 32);
+      const char* qrow = smem + XQ_OFF + (rb * 32 + l32) * XQ_PITCH + hh * DH * 2;
+      bf16x8 qf[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) qf[st] = __builtin_bit_cast(bf16x8, ld16(qrow + st * 32 + lg * 16));
+      f32x16 S[2];
+      short_scores(sk + hh * XK_TILE, qf, e.xn, l32, lg, S);
+      short_probs(S, 1.0f);
+      const int m = m0 + rb * 32 + l32;
+      if (m >= M) continue;
+      bf16* pp = reinterpret_cast<bf16*>(e.p_out) + (size_t)m * e.ldp + (head0 + hh) * BKV;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = S[kb][4 * q + r];
+          store4<bf16>(pp + kb * 32 + 8 * q + 4 * lg, v);
+        }
+    }
   }
 }
 
@@ -405,7 +456,6 @@ hipError_t launch_t(const void* A, int lda, const void* W, int ldw, int M, int N
 // multiplied; one barrier per 64-wide K step.  Rows past M or N re-read the last valid
 // row (their outputs are never stored).  While one wave of a SIMD waits on LDS the
 // other issues MFMAs.
-constexpr int LDS_WM = 2, LDS_WN = 4, LDS_THREADS = 64 * LDS_WM * LDS_WN;
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __restrict__ A, int lda,
@@ -419,7 +469,8 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
   constexpr int STAGE = ROWS * 128;
   constexpr int NLD = ROWS / (8 * NW);  // load instructions per wave per stage (8 rows each)
   static_assert(WM % 32 == 0 && WN % 32 == 0 && ROWS % (8 * NW) == 0 && BM % (8 * NW) == 0, "tile");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int SMEM = EPI == EPI_QKNORM_X && xattn_smem<BM>() > 2 * STAGE ? xattn_smem<BM>() : 2 * STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / LDS_WN, wn = wave % LDS_WN;
@@ -524,8 +575,9 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  if constexpr (EPI == EPI_QKNORM)
-    epilogue_qknorm<BM, MB, NB>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg, M, e);
+  if constexpr (EPI == EPI_QKNORM || EPI == EPI_QKNORM_X)
+    epilogue_qknorm<BM, MB, NB, EPI == EPI_QKNORM_X>(acc, cols, smem, wm, wn, m0 + wm * WM, n0 + wn * WN, l32, lg,
+                                                     M, e);
   else if constexpr (EPI == EPI_PARTIAL)
     epilogue<bf16, MB, NB, EPI_F32>(acc, reinterpret_cast<const EpiCols<NB, EPI_F32>&>(cols), m0 + wm * WM,
                                     n0 + wn * WN, l32, lg, M, N, ep);
@@ -571,6 +623,13 @@ hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int
     case EPI_F32: gemm_lds_kernel<BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_EULER: gemm_lds_kernel<BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
     case EPI_QKNORM: gemm_lds_kernel<BM, BN, EPI_QKNORM><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_QKNORM_X:
+      if constexpr (BM <= 192) {
+        gemm_lds_kernel<BM, BN, EPI_QKNORM_X><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e);
+        break;
+      } else {
+        return hipErrorInvalidValue;
+      }
     case EPI_PARTIAL:
       grid.x = tiles * e.ksplit;
       gemm_lds_kernel<BM, BN, EPI_PARTIAL><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e);
@@ -834,6 +893,9 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
   if (M <= 0 || N <= 0) return hipSuccess;
   if (e.kind == EPI_QKNORM && (!gemm_qknorm_fits(dtype, M, N, 128) || e.D % 256 || (N != e.D && N != 3 * e.D)))
     return hipErrorInvalidValue;
+  if (e.kind == EPI_QKNORM_X && (!gemm_qknorm_fits(dtype, M, N, 128) || e.D % 256 || N != e.D || e.rope || !e.xk ||
+                                 !e.p_out || e.xn < 1 || e.xn > 64 || e.ldp < e.D / 2))
+    return hipErrorInvalidValue;
   if (dtype == BF16) {
     if (M >= 256 && N >= 256 && N % 256 == 0) {
       // Pick the tile height that minimises (waves of 256 workgroups) x tile area,
@@ -856,10 +918,11 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
         while (parts > 1 && (long long)parts * M * N > e.ws_floats) --parts;
         if (parts > 1) return gemm_resid_splitk(A, lda, W, ldw, M, N, K, parts, e, s);
       }
-      if (e.kind != EPI_QKNORM && ((M + best - 1) / best) * (N / 256) < 160) {
+      if (e.kind != EPI_QKNORM && e.kind != EPI_QKNORM_X && ((M + best - 1) / best) * (N / 256) < 160) {
         if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
         return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
       }
+      if (best == 256 && e.kind == EPI_QKNORM_X) best = 192;  // its LDS holds a 192-row q tile at most
       if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s);
       if (best == 192) return launch_lds<192, 256>(A, lda, W, ldw, M, N, K, e, s);
       return launch_lds<128, 256>(A, lda, W, ldw, M, N, K, e, s);

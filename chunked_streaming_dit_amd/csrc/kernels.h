@@ -26,6 +26,11 @@ enum EpiKind {
                   //   v columns: V^T -> vt_out [D, vcap] in the attention layout (columns
                   //   M..kpad zero), or, with vt_out NULL, y -> out [M, ldo] (columns 2D..3D).
   EPI_PARTIAL = 6,  // internal (split K): the raw product of one K part -> ws (fp32)
+  EPI_QKNORM_X = 7, // EPI_QKNORM for q only (N = D, no RoPE), followed in the epilogue by
+                    //   the short-segment softmax of each head's q against the keys xk
+                    //   ([>= 64, D], xn of them, 1..64): the normalised probabilities ->
+                    //   p_out [M, ldp >= H*64] as short_attention_probs writes them; q
+                    //   itself is not stored.
 };
 struct GemmEpi {
   int kind;
@@ -50,6 +55,11 @@ struct GemmEpi {
   float* ws;
   long long ws_floats;
   int ksplit;  // internal: number of K parts of an EPI_PARTIAL launch
+  // EPI_QKNORM_X: the keys (attention layout, rows >= xn zero), their count, and P
+  const void* xk;
+  int xn;
+  void* p_out;
+  int ldp;
 };
 // Whether gemm() can fuse EPI_QKNORM for this launch (else: EPI_BIAS + qknorm_rope).
 bool gemm_qknorm_fits(int dtype, int M, int N, int dh);

@@ -74,40 +74,10 @@ __global__ __launch_bounds__(64 * XW, 3) void xattn_kernel(XArgs a) {
   __syncthreads();
 
   f32x16 S[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S[kb][r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < QV; ++st) {
-      const V kf = as_vec<V>(ld16(sk + (kb * 32 + l32) * RBK + swz<RBK>(l32, 2 * st + lg) * 16));
-      S[kb] = mfma32(kf, qf[st], S[kb]);
-    }
-  }
-  // exact softmax over the tile: keys past n get zero weight
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb * 32 + 8 * (r >> 2) + 4 * lg + (r & 3);
-      if (key >= a.n) S[kb][r] = -INFINITY;
-      mx = fmaxf(mx, S[kb][r]);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float ms = mx * a.scale;
+  short_scores(sk, qf, a.n, l32, lg, S);
   if constexpr (POUT) {
-    float l = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S[kb][r] = __builtin_amdgcn_exp2f(fmaf(S[kb][r], a.scale, -ms));
-        l += S[kb][r];
-      }
-    const float lt = l + __shfl_xor(l, 32);
+    short_probs(S, a.scale);
     if (!qvalid) return;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     T* pp = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * BKV;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -115,11 +85,19 @@ __global__ __launch_bounds__(64 * XW, 3) void xattn_kernel(XArgs a) {
       for (int q = 0; q < 4; ++q) {
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = S[kb][4 * q + r] * inv;
+        for (int r = 0; r < 4; ++r) v[r] = S[kb][4 * q + r];
         store4<T>(pp + kb * 32 + 8 * q + 4 * lg, v);  // keys kb*32 + 8q + 4lg + r
       }
     return;
   }
+  // exact softmax over the tile (keys past n have score -inf, so zero weight)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float ms = mx * a.scale;
   f32x16 O[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d)
