@@ -293,12 +293,13 @@ __global__ void timestep_features_batch_kernel(TimeBatch tb, float* __restrict__
 }
 
 // y_j[r] = act(W[r, :] . x_j + b[r]) for r < R and nt <= NT vectors x_j (x_j at
-// x + j ldx, y_j at y + j ldy).  One wave per output row, so every weight row is read
-// once for all nt vectors.  A lane reads 16 bytes of the row per step (8 bf16 or 4
-// fp32); K is a multiple of 256, and the steps are unrolled so that their loads are in
-// flight together.  Per (row, vector) the products are accumulated by explicit
-// operations in the same order for every NT, so the results do not depend on it.
-template <class T, int ACT, int NT>
+// x + j ldx, y_j at y + j ldy).  One wave per RW consecutive output rows, so every
+// weight row is read once for all nt vectors.  A lane reads 16 bytes of a row per step
+// (8 bf16 or 4 fp32); K is a multiple of 256, and the steps are unrolled so that their
+// loads are in flight together.  Per (row, vector) the products are accumulated by
+// explicit operations in the same order for every NT and RW, so the results do not
+// depend on them.
+template <class T, int ACT, int NT, int RW>
 __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
                                                    const T* __restrict__ b, int R, int K,
                                                    const float* __restrict__ x, int ldx, int nt,
@@ -306,15 +307,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
   typedef typename Vec<T>::type V;
   constexpr int VE = Vec<T>::n;
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const T* wr = W + (size_t)r * K;
-  float acc[NT];
+  const int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * RW;
+  if (r0 >= R) return;
+  float acc[RW][NT];
 #pragma unroll
-  for (int v = 0; v < NT; ++v) acc[v] = 0.f;
-#pragma unroll 4
+  for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+    for (int v = 0; v < NT; ++v) acc[rr][v] = 0.f;
+#pragma unroll(RW == 1 ? 4 : 2)
   for (int k = lane * VE; k < K; k += 64 * VE) {
-    const V w = as_vec<V>(ld16(wr + k));
+    V w[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) w[rr] = as_vec<V>(ld16(W + (size_t)min(r0 + rr, R - 1) * K + k));
 #pragma unroll
     for (int v = 0; v < NT; ++v) {
       if (v < nt) {
@@ -323,39 +327,46 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T* __restrict__ W,
 #pragma unroll
         for (int j = 0; j < VE; j += 4) {
           const f32x4 x4 = *reinterpret_cast<const f32x4*>(x + (size_t)v * ldx + k + j);
-          float p = to_f(w[j]) * x4[0];
-          p = fmaf(to_f(w[j + 1]), x4[1], p);
-          p = fmaf(to_f(w[j + 2]), x4[2], p);
-          p = fmaf(to_f(w[j + 3]), x4[3], p);
-          acc[v] += p;
+#pragma unroll
+          for (int rr = 0; rr < RW; ++rr) {
+            float p = to_f(w[rr][j]) * x4[0];
+            p = fmaf(to_f(w[rr][j + 1]), x4[1], p);
+            p = fmaf(to_f(w[rr][j + 2]), x4[2], p);
+            p = fmaf(to_f(w[rr][j + 3]), x4[3], p);
+            acc[rr][v] += p;
+          }
         }
       }
     }
   }
 #pragma unroll
-  for (int v = 0; v < NT; ++v) {
-    if (v < nt) {
-      const float a = wave_sum(acc[v]);
-      if (lane == 0) {
-        float o = a + to_f(b[r]);
-        if (ACT) o = silu(o);
-        y[(size_t)v * ldy + r] = o;
+  for (int rr = 0; rr < RW; ++rr) {
+    const int r = r0 + rr;
+#pragma unroll
+    for (int v = 0; v < NT; ++v) {
+      if (v < nt && r < R) {
+        const float a = wave_sum(acc[rr][v]);
+        if (lane == 0) {
+          float o = a + to_f(b[r]);
+          if (ACT) o = silu(o);
+          y[(size_t)v * ldy + r] = o;
+        }
       }
     }
   }
 }
 
-// One row per wave.  (Several rows per wave, sharing each lane's vector fragments,
-// measured slower for the batched form: their registers left too few waves to hide the
-// load latency.)
+// One row per wave for a single vector; two rows per wave for a batch (each vector
+// fragment then serves both rows; the weight chunks are the only per-row registers).
 template <class T, int NT>
 void gemv_launch(const void* w, const void* b, int R, int K, const float* x, int ldx, int nt, float* y, int ldy,
                  int act, hipStream_t s) {
-  dim3 grid((R + 3) / 4);
+  constexpr int RW = NT == 1 ? 1 : 2;
+  dim3 grid((R + 4 * RW - 1) / (4 * RW));
   if (act)
-    gemv_kernel<T, 1, NT><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
+    gemv_kernel<T, 1, NT, RW><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
   else
-    gemv_kernel<T, 0, NT><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
+    gemv_kernel<T, 0, NT, RW><<<grid, 256, 0, s>>>((const T*)w, (const T*)b, R, K, x, ldx, nt, y, ldy);
 }
 
 template <class T>
