@@ -4,6 +4,9 @@
   step of chunk 0 (no boundary) and of chunk 1 (boundary K/V carried from the GPU's
   chunk-0 latent); a resumed handle reproduces a chunk bit for bit; device memory
   does not grow with the number of chunks.
+- The base chunk job exactly as the benchmark launches it (4 blocks, modulation table,
+  held audio K/V, 8 steps): the first step's velocity on all 7800 tokens against the
+  oracle, and the job repeated bit for bit.
 - Super-resolution and large base chunks: the launch shapes of the full workloads
   (tokens, keys, hidden size, heads, audio) with one block, the oracle evaluated on
   sampled query rows (first, last and ragged-tail tiles plus random rows); and the
@@ -94,6 +97,45 @@ def test_config3_stream_full_size():
     e1 = rel_err(to_np(v_first[1]), vo1)
     print(f"stream: chunk0 v err {e0:.2e}, chunk1 v err {e1:.2e}")
     assert e0 <= TOL["bf16"] and e1 <= TOL["bf16"], (e0, e1)
+
+
+def test_bench_launch_configuration_first_step():
+    """The base chunk job exactly as bench.py runs it (4 blocks, modulation table for the
+    schedule and t = 0, reference and boundary passes, held audio K/V, 8 Euler steps):
+    the first step's velocity on every token against the oracle, and the whole job's
+    result repeatable bit for bit."""
+    from chunked_streaming_dit_amd import AUDIO_HELD
+    from chunked_streaming_dit_amd.workload import f32, grid_of
+    dev = device()
+    cfg = synth.BASE_CHUNK
+    g = cfg.chunk
+    P = synth.make_weights(cfg, threads=16)
+    inp = synth.make_inputs(cfg, 0)
+    h = _handle(cfg, P, dev)
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
+    ref, bnd, audio = f32(inp["ref"], dev), f32(inp["bnd"], dev), f32(inp["audio"], dev)
+    v0 = torch.empty((cfg.N, cfg.C_p), device=dev)
+    xs = []
+    for rep in range(2):
+        h.modulation_table(ts[:-1] + [0.0])
+        h.ref_kv_precompute(ref, grid_of(cfg.ref))
+        h.boundary_kv_carry(bnd, grid_of(Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+        h.audio_kv_precompute(audio)
+        x = f32(inp["x_init"], dev)
+        for k in range(cfg.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=AUDIO_HELD, v_out=v0 if k == 0 and rep == 0 else None)
+        torch.cuda.synchronize()
+        xs.append(to_np(x))
+    h.close()
+    assert np.array_equal(xs[0], xs[1])
+    assert np.isfinite(xs[0]).all()
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    bkv = O.bnd_context(P, cfg, ref_kv, inp["bnd"], cfg.bnd.h, cfg.bnd.w)
+    vo = O.dit_velocity(P, cfg, inp["x_init"], ts[0], O.grid_positions(0, g.frames, g.h, g.w),
+                        [[ref_kv[l], bkv[l]] for l in range(cfg.L)], inp["audio"])
+    err = rel_err(to_np(v0), vo)
+    print(f"bench launch configuration: first-step v err {err:.2e} over {cfg.N} tokens")
+    assert err <= TOL["bf16"], err
 
 
 def _sample_rows(n, seed):
