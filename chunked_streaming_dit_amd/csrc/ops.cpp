@@ -38,7 +38,7 @@ bool dtype_ok(int d) { return d == DIT_F32 || d == DIT_BF16; }
 
 int gemm_args(int dtype, const void* A, const void* W, const void* b, int M, int N, int K) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
-  if (!A || !W || !b) return fail(DIT_EINVAL, "A, W and b must be non-NULL");
+  if ((M > 0 && !A) || !W || !b) return fail(DIT_EINVAL, "A, W and b must be non-NULL");
   if (M < 0 || N < 1 || K < 1) return fail(DIT_ESHAPE, "M=%d N=%d K=%d", M, N, K);
   if (K % 64) return fail(DIT_ESHAPE, "K=%d must be a multiple of 64", K);
   if (N % 4) return fail(DIT_ESHAPE, "N=%d must be a multiple of 4", N);
@@ -53,12 +53,13 @@ int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, i
                 int act, void* out, void* stream) {
   int rc = gemm_args(dtype, A, W, b, M, N, K);
   if (rc) return rc;
-  if (!out) return fail(DIT_EINVAL, "out is NULL");
+  if (M > 0 && !out) return fail(DIT_EINVAL, "out is NULL");
   GemmEpi e{};
   if (act == DITK_ACT_NONE) e.kind = EPI_BIAS;
   else if (act == DITK_ACT_GELU) e.kind = EPI_GELU;
   else if (act == DITK_OUT_F32) e.kind = EPI_F32;
   else return fail(DIT_EINVAL, "act %d", act);
+  if (M == 0) return DIT_OK;
   e.bias = b;
   e.out = out;
   e.ldo = N;
@@ -70,9 +71,10 @@ int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b,
                          void* stream) {
   int rc = gemm_args(dtype, A, W, b, M, N, K);
   if (rc) return rc;
-  if (!h) return fail(DIT_EINVAL, "h is NULL");
+  if (M > 0 && !h) return fail(DIT_EINVAL, "h is NULL");
   if (workspace_floats < 0 || (workspace_floats > 0 && !workspace))
     return fail(DIT_EINVAL, "workspace NULL with workspace_floats=%lld", workspace_floats);
+  if (M == 0) return DIT_OK;
   GemmEpi e{};
   e.kind = EPI_RESID;
   e.bias = b;
@@ -87,10 +89,11 @@ int ditk_linear_residual(int dtype, const void* A, const void* W, const void* b,
 int ditk_rmsnorm_modulate(int dtype, const float* h, int n, int D, const float* shift,
                           const float* scale, double eps, void* out, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
-  if (!h || !out) return fail(DIT_EINVAL, "h/out NULL");
+  if (n > 0 && (!h || !out)) return fail(DIT_EINVAL, "h/out NULL");
   if (!shift != !scale) return fail(DIT_EINVAL, "shift and scale must both be given or both NULL");
   if (n < 0 || D < 256 || D % 256 || D > 4096) return fail(DIT_ESHAPE, "n=%d D=%d", n, D);
   if (!(eps > 0) || !std::isfinite(eps)) return fail(DIT_EINVAL, "eps");
+  if (n == 0) return DIT_OK;
   return hipchk(rmsnorm_mod(dtype, h, n, D, shift, scale, (float)eps, out, (hipStream_t)stream),
                 "rmsnorm_mod");
 }
@@ -110,6 +113,7 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
     return fail(DIT_ESHAPE, "grid does not cover n tokens");
   if (!(eps > 0) || !(theta > 1)) return fail(DIT_EINVAL, "eps/theta");
   if (!(q_scale > 0) || !std::isfinite(q_scale)) return fail(DIT_EINVAL, "q_scale");
+  if (n == 0) return DIT_OK;
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
   return hipchk(qknorm_rope(dtype, dh, H, n, q_in, k_in, v_in, ld_in, gq, gk, rope, g, (float)eps,
                             (float)theta, (float)q_scale, q_out, k_out, vt_out, cap,
@@ -119,9 +123,10 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 int ditk_attention_probs(int H, const void* q, int nq, const void* k, int n, int cap, int q_prescaled,
                          void* p, void* stream) {
-  if (!q || !k || !p) return fail(DIT_EINVAL, "NULL argument");
+  if ((nq > 0 && (!q || !p)) || !k) return fail(DIT_EINVAL, "NULL argument");
   if (H < 1 || nq < 0) return fail(DIT_ESHAPE, "H=%d nq=%d", H, nq);
   if (n < 1 || n > 64 || cap < 64 || cap % 64) return fail(DIT_ESHAPE, "n=%d cap=%d: needs 1 <= n <= 64 <= cap", n, cap);
+  if (nq == 0) return DIT_OK;
   const AttnSeg seg{k, nullptr, n, cap};
   return hipchk(short_attention_probs(128, H, q, H * 128, p, H * 64, nq, seg, q_prescaled != 0,
                                       (hipStream_t)stream),
@@ -136,7 +141,7 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
   if ((gq != nullptr) != (gk != nullptr)) return fail(DIT_EINVAL, "gq and gk must both be given or both NULL");
   if (gq && !(q_fold > 0 && std::isfinite(q_fold))) return fail(DIT_EINVAL, "q_fold must be finite and > 0");
   if (dh != 64 && dh != 128) return fail(DIT_EINVAL, "dh %d", dh);
-  if (!q || !o || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
+  if ((nq > 0 && (!q || !o)) || !k || !vt || !n || !cap) return fail(DIT_EINVAL, "NULL argument");
   if (dtype == DIT_F32 && dh != 64) return fail(DIT_EINVAL, "fp32 attention supports dh=64 only");
   if (H < 1 || nq < 0 || nseg < 1 || nseg > ATTN_MAX_SEGS) return fail(DIT_ESHAPE, "H/nq/nseg");
   AttnSeg seg[ATTN_MAX_SEGS];
@@ -155,6 +160,7 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                 ATTN_QTILE, nq);
   if (unsplit_rows >= nq) nsplit = 1;  // nothing left to split
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
+  if (nq == 0) return DIT_OK;
   const int D = H * dh;
   if (nsplit == 1 && short_attention_fits(dtype, dh, nseg, seg))
     return hipchk(short_attention(dh, H, q, D, o, D, nq, seg[0], q_prescaled != 0, (hipStream_t)stream),
@@ -190,11 +196,12 @@ int ditk_modulation(int dtype, int D, int L, double t, const void* const* w, flo
 int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* cond, int c_c,
                      int cond_mode, dit_grid grid, void* xin, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
-  if (!x || !xin || (cond_mode && !cond)) return fail(DIT_EINVAL, "NULL argument");
+  if (n > 0 && (!x || !xin || (cond_mode && !cond))) return fail(DIT_EINVAL, "NULL argument");
   if (n < 0 || c_p < 1 || c_c < 0 || cond_mode < 0 || cond_mode > 2) return fail(DIT_ESHAPE, "shape");
   if (cond_mode == 2 && (grid.h % 2 || grid.w % 2 || c_c % 4 ||
                          (long long)grid.frames * grid.h * grid.w != n))
     return fail(DIT_ESHAPE, "upsample grid");
+  if (n == 0) return DIT_OK;
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
   return hipchk(patch_input(dtype, x, n, c_p, cond, c_c, cond_mode, g, xin, (hipStream_t)stream),
                 "patch_input");
@@ -202,12 +209,13 @@ int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* con
 
 int ditk_patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
                      dit_grid grid, const void* w, const void* b, float* out, int D, void* stream) {
-  if (!x || !w || !b || !out || (cond_mode && !cond)) return fail(DIT_EINVAL, "NULL argument");
+  if ((n > 0 && (!x || !out || (cond_mode && !cond))) || !w || !b) return fail(DIT_EINVAL, "NULL argument");
   if (n < 0 || c_p < 1 || c_c < 0 || D < 1 || cond_mode < 0 || cond_mode > 2) return fail(DIT_ESHAPE, "shape");
   if (!patch_embed_fits(BF16, c_p, c_c, D))
     return fail(DIT_ESHAPE, "patch_embed needs (c_p + c_c) %% 64 == 0, c_p and c_c %% 8 == 0, D %% 256 == 0");
   if (cond_mode == 2 && (grid.h % 2 || grid.w % 2 || (long long)grid.frames * grid.h * grid.w != n))
     return fail(DIT_ESHAPE, "upsample grid");
+  if (n == 0) return DIT_OK;
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
   return hipchk(patch_embed(x, n, c_p, cond, c_c, cond_mode, g, w, b, out, D, (hipStream_t)stream),
                 "patch_embed");

@@ -6,7 +6,10 @@
  *   - device pointers, dtype DIT_F32 or DIT_BF16 for "dtype" buffers, fp32 where stated;
  *   - asynchronous on the given hipStream_t (NULL: default stream);
  *   - arguments are validated on the host before any launch; failures return a
- *     negative DIT_E* code and set dit_last_error().
+ *     negative DIT_E* code and set dit_last_error();
+ *   - a call with zero rows (M, n or nq == 0) is validated like any other, then
+ *     returns 0 without a launch; its row buffers (A, h, out, q, o, p, x, xin, cond)
+ *     may then be NULL.  Weights, keys and the other arguments are still checked.
  * Linear weights are [out, in] row-major with a bias [out].
  */
 #ifndef DITCHUNK_OPS_H

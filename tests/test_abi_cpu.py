@@ -270,3 +270,32 @@ def test_audio_kv_precompute_validation():
     lib, cs, h = _handle(4)  # no audio weights (d_a = 0)
     assert lib.audio_kv_precompute(h, FAKE, 4) == C.DIT_EINVAL
     lib.dit_destroy(h)
+
+
+def test_zero_rows_launch_nothing():
+    """A call with zero rows is validated, then returns 0 without a launch; its row
+    buffers may be NULL (what an empty tensor hands over), the weights may not."""
+    lib = C.lib()
+    assert lib.ditk_linear(1, None, FAKE, FAKE, 0, 64, 128, 0, None, None) == C.DIT_OK
+    assert lib.ditk_linear(1, None, None, FAKE, 0, 64, 128, 0, None, None) == C.DIT_EINVAL  # W
+    assert lib.ditk_linear(1, None, FAKE, FAKE, 0, 64, 100, 0, None, None) == C.DIT_ESHAPE  # K % 64
+    assert lib.ditk_linear(1, None, FAKE, FAKE, 0, 64, 128, 9, None, None) == C.DIT_EINVAL  # act
+    assert lib.ditk_linear_residual(1, None, FAKE, FAKE, None, 0, 256, 64, None, None, 0, None) == C.DIT_OK
+    assert lib.ditk_rmsnorm_modulate(1, None, 0, 256, None, None, 1e-6, None, None) == C.DIT_OK
+    assert lib.ditk_rmsnorm_modulate(1, None, 0, 300, None, None, 1e-6, None, None) == C.DIT_ESHAPE
+    g = C.DitGrid(0, 1, 2, 2)
+    assert lib.ditk_qknorm_rope(1, 128, 2, 0, None, FAKE, None, 256, None, FAKE, 1, g, 1e-6, 1e4,
+                                1.0, None, FAKE, None, 64, None) == C.DIT_OK
+    assert lib.ditk_attention_probs(2, None, 0, FAKE, 50, 64, 1, None, None) == C.DIT_OK
+    assert lib.ditk_attention_probs(2, None, 0, None, 50, 64, 1, None, None) == C.DIT_EINVAL  # keys
+    k = (C.P * 2)(FAKE, FAKE)
+    n = (ctypes.c_int * 2)(40, 130)
+    cap = (ctypes.c_int * 2)(64, 192)
+    assert lib.ditk_attention(1, 128, 2, None, 0, 2, k, k, n, cap, 2, None, 0, 0, None, None, 0.0, None,
+                              None) == C.DIT_OK
+    n[1] = 200  # > cap: still rejected with zero queries
+    assert lib.ditk_attention(1, 128, 2, None, 0, 2, k, k, n, cap, 1, None, 0, 0, None, None, 0.0, None,
+                              None) == C.DIT_ESHAPE
+    assert lib.ditk_patch_input(1, None, 0, 64, None, 0, 0, g, None, None) == C.DIT_OK
+    assert lib.ditk_patch_embed(None, 0, 64, None, 0, 0, g, FAKE, FAKE, None, 256, None) == C.DIT_OK
+    assert lib.fm_euler_step(None, None, 0.1, 0, None) == C.DIT_OK

@@ -411,3 +411,29 @@ def test_fm_euler_step_closed_form(lam):
         want = gg * x0 + c * (gg - 1) / lam
     torch.cuda.synchronize()
     assert np.abs(to_np(x) - want).max() <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_rows(dtype):
+    """Every kernel entry point with zero rows (empty tensors, NULL data pointers) is a
+    no-op: no error, and buffers shared with a non-empty call are left as they were."""
+    dev = device()
+    td = torch_dtype(dtype)
+    D, H = 256, 4 if dtype == "f32" else 2
+    dh = D // H
+    W = torch.ones((D, D), device=dev, dtype=td)
+    b = torch.ones(D, device=dev, dtype=td)
+    e = lambda *shape, dt=td: torch.empty(shape, device=dev, dtype=dt)
+    ops.linear(e(0, D), W, b, 0, e(0, D), dtype)
+    ops.linear_residual(e(0, D), W, b, None, e(0, D, dt=torch.float32), dtype)
+    ops.rmsnorm_modulate(e(0, D, dt=torch.float32), None, None, 1e-6, e(0, D), dtype)
+    k = torch.full((64, D), 3.0, device=dev, dtype=td)
+    vt = torch.full((D, 64), 5.0, device=dev, dtype=td)
+    ops.attention(dtype, dh, H, e(0, D), [(k, vt, 40, 64)], e(0, D))
+    if dtype == "bf16":
+        ops.attention_probs(2, e(0, 256), k, 40, e(0, 128))
+    x = torch.full((10, 64), 2.0, device=dev)
+    fm_euler_step(x[:0], x[:0], 0.5)
+    torch.cuda.synchronize()
+    assert bool((k == 3.0).all()) and bool((vt == 5.0).all()) and bool((x == 2.0).all())
+    assert bool((W == 1.0).all()) and bool((b == 1.0).all())
