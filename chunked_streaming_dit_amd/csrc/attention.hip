@@ -17,6 +17,7 @@
 // overflow and the softmax needs no running max at all: the common factor of numerator
 // and denominator cancels, so the row max, its cross-lane exchange, the rescale test
 // and the shift all drop out of the loop.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include <algorithm>
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
 
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
                      int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
-                     hipStream_t s, int kind, const AttnNorm* norm) {
+                     hipStream_t s, int kind, const AttnNorm* norm, const hipEvent_t* ev) {
   if (nq <= 0) return hipSuccess;
   if (nseg < 1 || nseg > ATTN_MAX_SEGS) return hipErrorInvalidValue;
   if (sp.nsplit < 1 || (sp.nsplit > 1 && (!sp.opart || !sp.ml))) return hipErrorInvalidValue;
@@ -498,21 +499,22 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
   a.gk = a.gq ? norm->gk : nullptr;
   a.bcoef = a.gq ? (float)(norm->q_fold * dh * 1.02) : 0.f;
   for (int i = 0; i < ATTN_MAX_SEGS; ++i) a.seg[i] = i < nseg ? segs[i] : AttnSeg{nullptr, nullptr, 0, 64};
-  dim3 grid(qt0 * H + (nqt - qt0) * H * sp.nsplit), block(64 * AW);
+  const dim3 grid(qt0 * H + (nqt - qt0) * H * sp.nsplit), block(64 * AW);
   const bool cross = kind == ATTN_CROSS;
-  if (dtype == BF16 && dh == 128) {
-    if (cross) attn_kernel<bf16, 128, 1><<<grid, block, 0, s>>>(a);
-    else attn_kernel<bf16, 128, 0><<<grid, block, 0, s>>>(a);
-  } else if (dtype == BF16 && dh == 64) {
-    if (cross) attn_kernel<bf16, 64, 1><<<grid, block, 0, s>>>(a);
-    else attn_kernel<bf16, 64, 0><<<grid, block, 0, s>>>(a);
-  } else if (dtype == F32 && dh == 64) {
-    if (cross) attn_kernel<float, 64, 1><<<grid, block, 0, s>>>(a);
-    else attn_kernel<float, 64, 0><<<grid, block, 0, s>>>(a);
-  } else {
+  const void* fn;
+  if (dtype == BF16 && dh == 128)
+    fn = cross ? (const void*)attn_kernel<bf16, 128, 1> : (const void*)attn_kernel<bf16, 128, 0>;
+  else if (dtype == BF16 && dh == 64)
+    fn = cross ? (const void*)attn_kernel<bf16, 64, 1> : (const void*)attn_kernel<bf16, 64, 0>;
+  else if (dtype == F32 && dh == 64)
+    fn = cross ? (const void*)attn_kernel<float, 64, 1> : (const void*)attn_kernel<float, 64, 0>;
+  else
     return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  // With events, the dispatch itself stamps the kernel's start and end into them: no
+  // separate marker packets (and their waits) between this launch and its neighbours.
+  void* args[1] = {&a};
+  if (ev) return hipExtLaunchKernel(fn, grid, block, args, 0, s, ev[0], ev[1], 0);
+  return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,

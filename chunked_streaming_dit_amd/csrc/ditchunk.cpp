@@ -357,18 +357,18 @@ int timed_begin(dit_handle* h, int* slot) {
   if (!h->timing) return DIT_OK;
   if (h->ev.empty()) {
     h->ev.resize(2 * MAX_EVENT_PAIRS);
-    for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
+    // Timing-only events: no system-scope fence when they complete (it would write
+    // back and invalidate the caches around the timed launch).  Elapsed times are read
+    // after hipEventSynchronize, which needs no memory ordering with the timed work.
+    for (auto& e : h->ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   }
   if (h->ev_used >= MAX_EVENT_PAIRS) return DIT_OK;
   *slot = h->ev_used++;
-  HIPCHK(hipEventRecord(h->ev[2 * *slot], h->stream));
   return DIT_OK;
 }
-int timed_end(dit_handle* h, int slot, double flop) {
-  if (slot < 0) return DIT_OK;
-  HIPCHK(hipEventRecord(h->ev[2 * slot + 1], h->stream));
-  h->flop_acc += flop;
-  return DIT_OK;
+// The pair of slot (>= 0) is stamped by the timed launch itself (see run_attention).
+void timed_end(dit_handle* h, int slot, double flop) {
+  if (slot >= 0) h->flop_acc += flop;
 }
 
 // Attention launch: picks the key-range split, times the main kernel when timing is on
@@ -385,16 +385,18 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
   sp.opart = hd->X<float>(L.opart);
   sp.ml = hd->X<float>(L.ml);
   int slot = -1, rc;
-  if (timed && (rc = timed_begin(hd, &slot))) return rc;
+  if (timed && n > 0 && (rc = timed_begin(hd, &slot))) return rc;
   const bool cross = kind == ATTN_CROSS;
   const AttnNorm norm{hd->B(l, cross ? DIT_WB_GCQ : DIT_WB_GQ), hd->B(l, cross ? DIT_WB_GCK : DIT_WB_GK),
                       (double)attention_q_scale(c.dh)};
-  HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
-                   true, hd->stream, kind, &norm));
+  const hipError_t err = attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
+                                   true, hd->stream, kind, &norm, slot >= 0 ? &hd->ev[2 * slot] : nullptr);
+  if (err != hipSuccess && slot >= 0) --hd->ev_used;  // its events were never stamped
+  HIPCHK(err);
   if (timed) {
     double nkv = 0;
     for (int i = 0; i < ns; ++i) nkv += seg[i].n;
-    if ((rc = timed_end(hd, slot, 4.0 * n * nkv * c.D))) return rc;
+    timed_end(hd, slot, 4.0 * n * nkv * c.D);
   }
   HIPCHK(attention_combine(c.dtype, c.dh, c.H, n, sp, hd->X(L.o), c.D, hd->stream));
   return DIT_OK;

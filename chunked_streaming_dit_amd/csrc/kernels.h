@@ -103,6 +103,8 @@ constexpr int ATTN_QTILE = 256;
 // q^, k^ RMS-normalised (gq, gk: dtype [dh]).  With q pre-scaled, the kernel then bounds
 // the logits by q_fold dh max|gq| max|gk| and, when that bound is small, takes the
 // softmax without a running max (same result up to rounding).
+// ev (optional): a start/stop pair of timing events that the main kernel's dispatch
+// stamps (hipExtLaunchKernel); the merge of split partials is not included.
 struct AttnNorm {
   const void* gq;
   const void* gk;
@@ -111,7 +113,8 @@ struct AttnNorm {
 enum { ATTN_SELF = 0, ATTN_CROSS = 1 };
 hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, int ldo, int nq,
                      int ldk, const AttnSeg* segs, int nseg, const AttnSplit& sp, bool q_prescaled,
-                     hipStream_t s, int kind = ATTN_SELF, const AttnNorm* norm = nullptr);
+                     hipStream_t s, int kind = ATTN_SELF, const AttnNorm* norm = nullptr,
+                     const hipEvent_t* ev = nullptr);
 // log2(e) / sqrt(dh): the q scale of the exp2-domain logits.
 inline float attention_q_scale(int dh) { return (float)(1.4426950408889634 / __builtin_sqrt((double)dh)); }
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,

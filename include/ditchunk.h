@@ -319,10 +319,11 @@ int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_st
 /* Message of the last failure on this thread ("" if none). */
 const char* dit_last_error(void);
 
-/* Kernel timing on the handle's stream.  While enabled, each attention launch of
- * dit_chunk_step, ref_kv_precompute, boundary_kv_carry and interp_anchor_kv is
- * bracketed by a pair
- * of HIP events (created lazily, at most 4096 pairs per window).
+/* Kernel timing on the handle's stream.  While enabled, the self-attention kernel of
+ * each attention launch of dit_chunk_step, ref_kv_precompute, boundary_kv_carry and
+ * interp_anchor_kv is timed by a pair of HIP events that its dispatch stamps with the
+ * kernel's start and end (hipExtLaunchKernel: no marker packets between launches;
+ * events created lazily, at most 4096 pairs per window).
  * dit_timing_read synchronises those events and returns the count and the summed
  * milliseconds of the window, then opens a new window.
  * kind: DIT_TIME_ATTN (self-attention launches). */

@@ -252,3 +252,32 @@ def test_config2_full_size_first_step():
     """The base low-res chunk at its full shape (7800 tokens, keys 1560|1560|7800,
     4 blocks, hidden 1536, 12x128 heads, 50 audio tokens): the first denoising step."""
     _check(synth.BASE_CHUNK, steps=1)
+
+
+def test_attention_timing_counts_every_launch():
+    """dit_timing: with timing on, every self-attention launch of a chunk (the context
+    passes run blocks 0..L-2, the steps all L blocks) is counted with its 4 n_q n_kv D
+    flop and a positive duration, and the chunk's x and v are bit for bit those of an
+    untimed run (the timed launch is the same kernel)."""
+    from chunked_streaming_dit_amd.workload import upload_weights
+    cfg = MINI_BF16
+    dev = device()
+    P = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, 0)
+    W = upload_weights(P, cfg.dtype, dev)
+    x_ref, v_ref, h = run_standalone_gpu(cfg, P, inp, dev, weights=W)
+    h.timing_enable(True)
+    x, vs, _ = run_standalone_gpu(cfg, P, inp, dev, handle=h)
+    count, ms, flop = h.timing_read()
+    n_ref, n_bnd, N = cfg.ref.n, cfg.bnd.n, cfg.chunk.n
+    D, L = cfg.D, cfg.L
+    assert count == 2 * (L - 1) + cfg.steps * L
+    want = 4.0 * D * ((L - 1) * (n_ref * n_ref + n_bnd * (n_ref + n_bnd)) + cfg.steps * L * N * (n_ref + n_bnd + N))
+    assert flop == want
+    assert ms > 0 and ms / count < 100.0
+    assert h.timing_read()[0] == 0  # the read opened a new window
+    h.timing_enable(False)
+    h.close()
+    assert np.array_equal(x, x_ref)
+    for a, b in zip(vs, v_ref):
+        assert np.array_equal(a, b)
