@@ -163,13 +163,22 @@ def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
     return e / np.sum(e, axis=axis, keepdims=True)
 
 
+QUERY_GROUP = 2048  # query rows per score matrix (bounds memory at full-size workloads)
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
-    """Per head softmax(q k^T / sqrt(dh)) v.  q [n, H, dh], k/v [m, H, dh] -> [n, H, dh]."""
+    """Per head softmax(q k^T / sqrt(dh)) v.  q [n, H, dh], k/v [m, H, dh] -> [n, H, dh].
+
+    Every query row is its own softmax over all m keys, so the rows are taken
+    QUERY_GROUP at a time: the arithmetic of each row is the same, only the size of
+    the score matrix held at once changes."""
     n, H, dh = q.shape
     out = np.empty((n, H, dh), dtype=np.float64)
     for hh in range(H):
-        s = (q[:, hh, :] @ k[:, hh, :].T) / np.sqrt(dh)
-        out[:, hh, :] = softmax(s, axis=1) @ v[:, hh, :]
+        for r0 in range(0, n, QUERY_GROUP):
+            r1 = min(n, r0 + QUERY_GROUP)
+            s = (q[r0:r1, hh, :] @ k[:, hh, :].T) / np.sqrt(dh)
+            out[r0:r1, hh, :] = softmax(s, axis=1) @ v[:, hh, :]
     return out
 
 
@@ -400,13 +409,15 @@ def anchor_context(P: Weights, cfg, ref_kv, bnd_kv, anchor: np.ndarray, h: int, 
     return context_pass(P, cfg, anchor, pos, prior)
 
 
-def stream(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.ndarray):
+def stream(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.ndarray,
+           record: bool = False):
     """Chunked generation [arch, loop, mem]: reference K/V once, then per chunk the
     boundary K/V from the previous chunk's last frame (none for chunk 0), then the
-    multi-step pass.  Returns the final latent of every chunk."""
+    multi-step pass.  Returns the final latent of every chunk (with record, also the
+    list of every chunk's per-step velocities)."""
     g = cfg.chunk
     ref_kv = ref_context(P, cfg, ref, cfg.ref)
-    outs = []
+    outs, vels = [], []
     prev = None
     for inp in chunks:
         if prev is None:
@@ -418,10 +429,11 @@ def stream(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.nda
         if cfg.C_c > 0:
             cond = (upsample2_tokens(inp["cond_lr"], g.frames, g.h, g.w)
                     if cfg.cond_up == 2 else inp["cond"])
-        x = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond)
+        x, vs = chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio"), cond, record=True)
         outs.append(x)
+        vels.append(vs)
         prev = x
-    return outs
+    return (outs, vels) if record else outs
 
 
 def stream_reuse(P: Weights, cfg, chunks: Sequence[Dict[str, np.ndarray]], ref: np.ndarray):

@@ -14,6 +14,7 @@ N(0, 1/fan_in) weights and N(0, 1) latents and audio features.
 """
 from __future__ import annotations
 
+import collections.abc
 import dataclasses
 import zlib
 from concurrent.futures import ThreadPoolExecutor
@@ -24,7 +25,7 @@ import numpy as np
 __all__ = [
     "Grid", "Config", "CONFIGS", "config", "round_bf16", "to_bf16_bits",
     "weight_catalogue", "make_weights", "make_inputs", "GLOBAL_NAMES",
-    "BLOCK_NAMES",
+    "BLOCK_NAMES", "Bf16Weights", "from_bf16_bits",
 ]
 
 # --------------------------------------------------------------------------------------
@@ -245,13 +246,43 @@ def _one_weight(cfg: Config, name: str, spec) -> np.ndarray:
     return _finish(z, cfg.dtype).reshape(shape)
 
 
-def make_weights(cfg: Config, threads: int = 8) -> Dict[str, np.ndarray]:
-    """All parameters of workload ``cfg`` as float32 arrays (bf16-exact for bf16 workloads)."""
+def from_bf16_bits(b: np.ndarray) -> np.ndarray:
+    """float32 values of bf16 bit patterns (uint16)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+class Bf16Weights(collections.abc.Mapping):
+    """A bf16 workload's parameters held as bf16 bit patterns (half the memory of float32:
+    10.5 GB instead of 21 GB for the large chunk); indexing returns the float32 values,
+    the same values make_weights returns."""
+
+    def __init__(self, bits: Dict[str, np.ndarray]):
+        self.bits = bits
+
+    def __getitem__(self, name: str) -> np.ndarray:
+        return from_bf16_bits(self.bits[name])
+
+    def __iter__(self):
+        return iter(self.bits)
+
+    def __len__(self) -> int:
+        return len(self.bits)
+
+
+def make_weights(cfg: Config, threads: int = 8, compact: bool = False):
+    """All parameters of workload ``cfg`` as float32 arrays (bf16-exact for bf16 workloads).
+
+    compact (bf16 workloads only): a Bf16Weights mapping that stores the bit patterns."""
     cat = weight_catalogue(cfg)
     names = list(cat)
+    if compact and cfg.dtype != "bf16":
+        raise ValueError("compact weights need a bf16 workload")
+    one = (lambda nm: to_bf16_bits(_one_weight(cfg, nm, cat[nm]))) if compact else \
+        (lambda nm: _one_weight(cfg, nm, cat[nm]))
     with ThreadPoolExecutor(max(1, threads)) as ex:
-        arrs = list(ex.map(lambda nm: _one_weight(cfg, nm, cat[nm]), names))
-    return dict(zip(names, arrs))
+        arrs = list(ex.map(one, names))
+    d = dict(zip(names, arrs))
+    return Bf16Weights(d) if compact else d
 
 
 def _tokens(cfg: Config, name: str, chunk: int, shape, dtype: str) -> np.ndarray:

@@ -512,6 +512,72 @@ def test_bnd_reuse_rows_and_time_shift(tiny):
         h = h_next
 
 
+def test_stream_reuse_carries_last_step_input(tiny):
+    """stream_reuse, composed by hand: chunk c is chunk_denoise with the context
+    [reference, bnd_reuse_context(x_{S-1}, t_{S-1})], where x_{S-1} is chunk c-1's input
+    to its LAST denoising step (S-1 Euler steps from its x_init) and t_{S-1} that step's
+    time.  A carry from any other step (e.g. the first: x_init at t_0) fails."""
+    P, _ = tiny
+    cfg = dataclasses.replace(TINY, bnd=None, steps=3)
+    chunks = [synth.make_inputs(TINY, c) for c in range(3)]
+    got = O.stream_reuse(P, cfg, chunks, chunks[0]["ref"])
+    g = cfg.chunk
+    pos = _pos(g)
+    ts = O.schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    ref_kv = O.ref_context(P, cfg, chunks[0]["ref"], cfg.ref)
+    carried = None
+    for c, inp in enumerate(chunks):
+        ctx = [[ref_kv[l]] + ([carried[l]] if carried is not None else []) for l in range(cfg.L)]
+        want = O.chunk_denoise(P, cfg, inp["x_init"], ctx, inp["audio"])
+        assert np.abs(got[c] - want).max() <= 1e-12 * np.abs(want).max(), c
+        x = inp["x_init"].astype(np.float64)
+        for k in range(cfg.steps - 1):
+            x = x + (ts[k + 1] - ts[k]) * O.dit_velocity(P, cfg, x, ts[k], pos, ctx, inp["audio"])
+        carried = O.bnd_reuse_context(P, cfg, x, ts[-2], pos, ctx, inp["audio"], g)
+        if c == 0:
+            # the carry of the first step's input differs: chunk 1 would change
+            first = O.bnd_reuse_context(P, cfg, inp["x_init"], ts[0], pos, ctx, inp["audio"], g)
+            other = O.chunk_denoise(P, cfg, chunks[1]["x_init"], [[ref_kv[l], first[l]] for l in range(cfg.L)],
+                                    chunks[1]["audio"])
+            assert np.abs(other - got[1]).max() > 1e-6 * np.abs(got[1]).max()
+
+
+def test_qk_norm_per_head_and_gamma_after_normalisation():
+    """qk_norm on its own: each head of each row is RMS-normalised over dh, then
+    multiplied elementwise by gamma (shared by the heads).
+      - scaling one head's input leaves every output unchanged up to eps (a per-head
+        normalisation: no other head moves at all);
+      - with gamma = g for every entry, mean(y^2) over a head = g^2 ms / (ms + eps);
+      - non-uniform gamma against the per-element formula written out with scalar
+        loops; a gamma applied before the normalisation (rms_norm(x * gamma)) fails it."""
+    r = _rng(31)
+    n, H, dh, eps = 3, 4, 6, 1e-6
+    x = r.standard_normal((n, H, dh)) * 2.0
+    gamma = 1.0 + 0.5 * r.standard_normal(dh)
+    y = O.qk_norm(x, gamma, eps)
+    x2 = x.copy()
+    x2[:, 1, :] *= 7.0
+    y2 = O.qk_norm(x2, gamma, eps)
+    assert np.abs(np.delete(y2, 1, axis=1) - np.delete(y, 1, axis=1)).max() == 0.0
+    assert np.abs(y2[:, 1] - y[:, 1]).max() <= 1e-6 * np.abs(y).max()
+    g = 1.7
+    yg = O.qk_norm(x, np.full(dh, g), eps)
+    ms = np.mean(x * x, axis=-1)
+    assert np.abs(np.mean(yg * yg, axis=-1) - g * g * ms / (ms + eps)).max() <= 1e-13
+    want = np.empty_like(x)
+    for i in range(n):
+        for hh in range(H):
+            ss = 0.0
+            for d in range(dh):
+                ss += x[i, hh, d] * x[i, hh, d]
+            rinv = 1.0 / (ss / dh + eps) ** 0.5
+            for d in range(dh):
+                want[i, hh, d] = x[i, hh, d] * rinv * gamma[d]
+    assert np.abs(y - want).max() <= 1e-14 * np.abs(want).max()
+    slip = O.rms_norm(x * gamma, eps)
+    assert np.abs(slip - want).max() > 1e-3
+
+
 def test_stream_reuse_first_chunk_and_carry(tiny):
     """stream_reuse: chunk 0 equals stream()'s; chunk 1 is conditioned on the K/V of chunk
     0's last step (not on a clean pass), so it differs from stream()'s chunk 1."""
