@@ -1,41 +1,52 @@
 """Benchmark of the chunked streaming DiT step on one MI355X.
 
-One bench step = one whole base low-res chunk job through the C ABI: the adaLN
-modulation table of the job's timesteps (dit_modulation_table), the reference
-K/V pass (ref_kv_precompute), the boundary K/V pass from the previous chunk's last
-latent frame (boundary_kv_carry), the chunk's audio K/V (audio_kv_precompute, once per
-chunk: the audio is the same at every step), then the 8 Euler denoising steps
-(dit_chunk_step: patch embed, 4 DiT blocks of self-attention over
-[reference | boundary | chunk] keys, audio cross-attention and adaLN MLP, final
-layer + Euler update).  Inputs are seeded synthetic tensors already resident in HBM.
+Default workload (the headline): one full denoising step of the large base chunk, the
+largest workload that fits one GPU: 21x30x52 = 32760 latent tokens attending to keys
+[1560 reference | 1560 boundary | 32760 chunk], 200 audio tokens, 30 DiT blocks, hidden
+3072, 24 heads x 128, MLP 4x, resident bf16 weights.  One bench step = the chunk's audio
+K/V (audio_kv_precompute) + one dit_chunk_step (patch embed, 30 blocks of
+self-attention, audio cross-attention and adaLN MLP, final layer + Euler update 1 ->
+0.875); the reference and boundary passes run once before, as they do once per request
+and chunk.  Inputs are resident in HBM when the timed region starts.
 
-value = latent tokens x denoising steps / second (7800 x 8 per bench step; the
-context passes are included in the time).
-roofline = the self-attention kernel (the dominant kernel): algorithmic flop
-4 * N_q * N_kv * D per launch over its HIP-event-timed duration, against the
-bf16 dense MFMA peak.
-cpu_baseline = the f64 oracle timed on the host on a bounded sample (one DiT block of
-one denoising step at the full chunk shape, scaled to the 4-block step).
+value = latent tokens per second of the timed steps (32760 per bench step).
+roofline = the self-attention kernel (the dominant kernel: 58% of the step): algorithmic
+flop 4 N_q N_kv D per launch over its dispatch-stamped HIP-event duration (from the main
+kernel's start to the end of the merge of its key-range parts), against the bf16 dense
+MFMA peak; traffic = the measured HBM bytes per launch (rocprofv3 FETCH_SIZE and
+WRITE_SIZE, scaled by a 256 MiB copy) of profiles/attention_<workload>_traffic.json,
+null when that file was taken on another attention source.
+After the timed region one more bench step runs with the block GEMMs and the
+elementwise kernels timed the same way: GEMM TFLOP/s (2 M N K per launch) and
+elementwise GB/s (bytes the RMSNorm passes and the final layer must move).  Then the
+board's measured ceilings (the library's dense bf16 MFMA loop with changing operands
+and its 1 GiB copy) are taken, and every figure is also given as a fraction of them.
+cpu_baseline = the f64 oracle timed on the host on a bounded sample (large chunk: one
+DiT block with the K/V of all tokens and the queries of 1 and of 2048 sampled rows,
+extrapolated linearly in the rows to the whole block and times 30 blocks; base chunk:
+one whole DiT block of one step, times 4).
 
---workload interp times an interpolation chunk of the same shape instead (the
-boundary from one neighbouring chunk's last frame, the anchor from the other's first
-frame, then 8 steps whose keys are [reference | boundary | anchor | chunk]); the
-reference pass runs once, outside the timed region, as it does once per request.
---workload reuse times N-chunk jobs whose boundary is carried by reuse: 8 steps, the
-last of which leaves its last frame's K/V as the next job's boundary (no boundary
-pass); the reference pass again runs once, outside the timed region.
---workload sr / sr1 time super-resolution chunk jobs (5x60x104 = 31200 latent tokens
-conditioned on the nearest-2x upsample of a 5x30x52 latent, keys 6240 reference + 6240
-boundary + 31200 chunk, 2 blocks, no audio): the boundary pass and 4 Euler steps (sr) or
-a single step 1 -> 0 (sr1); the reference pass runs once, outside the timed region.
---workload large times one denoising step of the large base chunk (21x30x52 = 32760
-tokens, keys 1560 reference + 1560 boundary + 32760 chunk, 200 audio tokens, 30 blocks,
-hidden 3072, 24 heads x 128) with resident weights; --workload stream times the same
-step with the block weights streamed from pinned host memory through a 2-slot device
-ring (dit_weight_stream) and also reports, from the same process, the resident step,
-the first (cold) streamed step after the switch, and the difference.  Their weights are
-drawn on the GPU (seeded N(0, 1/fan_in), gammas 1 + 0.1 N(0, 1)) to keep the 6.7 G
-parameters' set-up short.
+Other workloads (--workload):
+  base     one base low-res chunk job: modulation table, reference K/V, boundary K/V,
+           audio K/V, 8 Euler steps 1 -> 0 (7800 tokens, keys 1560 + 1560 + 7800, 4
+           blocks, hidden 1536, 12 heads); value = 7800 x 8 latent tokens per job / time
+  stream6  the streaming sequence: 6 consecutive base chunks, each chunk's boundary
+           from the previous chunk's final latent (the first chunk has none); one bench
+           step = one whole session (modulation table and reference K/V once, then per
+           chunk boundary K/V, audio K/V and 8 steps); value = generated latent tokens/s
+           at the steady-state per-chunk latency (median over chunks 1-5); chunk 0's
+           latency is reported as the time to the first chunk
+  interp   an interpolation chunk of the base shape (boundary and anchor passes, keys
+           [reference | boundary | anchor | chunk])
+  reuse    base chunk jobs whose boundary is carried by reuse (no boundary pass)
+  sr, sr1  super-resolution chunk jobs (31200 tokens, 2 blocks, no audio): boundary
+           pass + 4 Euler steps (sr) or one step 1 -> 0 (sr1)
+  wstream  the large-chunk step with the block weights streamed from pinned host memory
+           through a 2-slot device ring (dit_weight_stream), with the resident step, the
+           first (cold) streamed step and the stage hand-over measured in the same process
+The large-chunk weights are drawn on the GPU (seeded N(0, 1/fan_in), gammas
+1 + 0.1 N(0, 1)) to keep the 6.7 G parameters' set-up short; the other workloads use the
+seeded host catalogue of synth.
 """
 from __future__ import annotations
 
@@ -51,33 +62,48 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "DiT chunk-step latent tokens/sec and attention TFLOP/s (% bf16 MFMA peak), 1 GPU"
+METRIC_STREAM6 = ("DiT streaming sequence generated latent tokens/sec (steady-state chunk latency) and "
+                  "attention TFLOP/s (% bf16 MFMA peak), 1 GPU")
 METRIC_INTERP = ("DiT interpolation-chunk latent tokens/sec and attention TFLOP/s "
                  "(% bf16 MFMA peak), 1 GPU")
 METRIC_SR = ("DiT super-resolution chunk latent tokens/sec and attention TFLOP/s "
              "(% bf16 MFMA peak), 1 GPU")
 METRIC_SR1 = ("DiT single-step super-resolution chunk latent tokens/sec and attention TFLOP/s "
               "(% bf16 MFMA peak), 1 GPU")
-METRIC_LARGE = ("DiT large-chunk denoising step latent tokens/sec and attention TFLOP/s "
-                "(% bf16 MFMA peak), 1 GPU")
-METRIC_STREAM = ("DiT large-chunk denoising step latent tokens/sec with block weights streamed "
-                 "from pinned host memory, 1 GPU")
+METRIC_WSTREAM = ("DiT large-chunk denoising step latent tokens/sec with block weights streamed "
+                  "from pinned host memory, 1 GPU")
 METRIC_REUSE = ("DiT chunk-step latent tokens/sec, boundary carried by reuse, and attention "
                 "TFLOP/s (% bf16 MFMA peak), 1 GPU")
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
 ATTN_SRC = os.path.join(ROOT, "chunked_streaming_dit_amd", "csrc", "attention.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_base_chunk_traffic.json")
+TRAFFIC_FILES = {
+    "large": os.path.join(ROOT, "profiles", "attention_large_chunk_traffic.json"),
+    "base": os.path.join(ROOT, "profiles", "attention_base_chunk_traffic.json"),
+}
+DIT_TIME_ATTN, DIT_TIME_GEMM, DIT_TIME_ELEM = 0, 1, 2
+
+WORKLOAD_LARGE = ("large base chunk: 21x30x52 = 32760 latent tokens, keys 1560 reference + 1560 "
+                  "boundary + 32760 chunk, 200 audio tokens of dim 768, 30 DiT blocks, hidden 3072, "
+                  "24 heads x 128, MLP 4x, one Euler step 1 -> 0.875; one bench step = audio K/V + "
+                  "one denoising step (the reference and boundary passes run before)")
+WORKLOAD_BASE = ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
+                 "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
+                 "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = modulation "
+                 "table + reference K/V + boundary K/V + audio K/V + 8 denoising steps")
 
 
 def _src_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def _traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or
-    None if it is missing or was taken on a different attention source."""
+def _traffic(workload: str):
+    """HBM bytes per self-attention launch from the committed rocprofv3 counter summary of
+    the workload, or None if it is missing or was taken on a different attention source."""
+    path = TRAFFIC_FILES.get(workload)
     try:
-        d = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
+        d = json.load(open(path))
+    except (OSError, ValueError, TypeError):
         return None
     if d.get("attention_src_sha256_16") != _src_hash(ATTN_SRC):
         return None
@@ -88,15 +114,58 @@ COPY_PROBE_BYTES = 256 << 20
 
 
 def copy_probe(reps: int = 3) -> None:
-    """A plain device copy of COPY_PROBE_BYTES, the known-size kernel that calibrates
-    the FETCH_SIZE / WRITE_SIZE counters."""
+    """The library's plain copy kernel (ditk_probe_copy) over COPY_PROBE_BYTES: the
+    known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
+
+    from chunked_streaming_dit_amd import _lib as C
     dev = torch.device("cuda", 0)
     a = torch.empty(COPY_PROBE_BYTES // 4, device=dev)
     b = torch.empty_like(a)
     for _ in range(reps):
-        b.copy_(a)
+        C.check(C.lib().ditk_probe_copy(a.data_ptr(), b.data_ptr(), COPY_PROBE_BYTES,
+                                        torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
+
+
+def ceilings() -> dict:
+    """Measured ceilings on this board, in the same process: the library's dense bf16
+    MFMA loop (operands with changing bits, no memory traffic; about 0.2 s) and its plain
+    copy of 1 GiB (HBM bandwidth, 2 x bytes moved), each timed with HIP events."""
+    import ctypes
+
+    import torch
+
+    from chunked_streaming_dit_amd import _lib as C
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    data = torch.randn(2048, generator=g, device=dev).to(torch.bfloat16)
+    sink = torch.empty(C.DITK_PROBE_SINK_FLOATS, device=dev)
+    flop = ctypes.c_double()
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b)
+
+    C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 20000, sink.data_ptr(), sink.numel(), ctypes.byref(flop), st))
+    ms = timed(lambda: C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 400000, sink.data_ptr(), sink.numel(),
+                                                        ctypes.byref(flop), st)))
+    mfma = flop.value / (ms * 1e-3) / 1e12
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    copy = lambda: C.check(C.lib().ditk_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, st))  # noqa: E731
+    copy()
+    ms = timed(lambda: [copy() for _ in range(10)]) / 10
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    del src, dst
+    return {"mfma_bf16_ceiling_tflops": mfma, "hbm_copy_ceiling_gbs": gbs}
 
 
 def _counter_means(path: str, counter: str, match) -> tuple:
@@ -138,13 +207,30 @@ def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv) -> dict
     }
 
 
-def cpu_baseline(cfg, P, inp, budget_s: float = 12.0):
-    """Time the oracle on one DiT block of one denoising step at the full chunk shape
-    (repeated up to L times while under the budget) and scale to the L-block step."""
+# ---------------------------------------------------------------------------- CPU baseline
+
+
+def _cpu_info() -> tuple:
+    """(BLAS threads in use, CPU model name)."""
+    from threadpoolctl import threadpool_info
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return threads, model
+
+
+def cpu_baseline_block(cfg, P, inp, budget_s: float = 12.0):
+    """The oracle on one DiT block of one denoising step at the full chunk shape (repeated
+    up to L times while under the budget), scaled to the L-block step."""
     import dataclasses
 
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     import oracle as O
 
@@ -159,17 +245,62 @@ def cpu_baseline(cfg, P, inp, budget_s: float = 12.0):
         O.dit_velocity(P, one, inp["x_init"], 1.0, pos, ctx, inp["audio"])
         times.append(time.perf_counter() - t0)
     t_block = float(np.median(times))
-    t_step = t_block * cfg.L
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads, model = _cpu_info()
     return {
-        "value": cfg.N / t_step,
+        "value": cfg.N / (t_block * cfg.L),
         "unit": "latent tokens/s",
         "cores": threads,
+        "cpu": model,
         "kind": "oracle",
         "sample": (f"{len(times)} x one DiT block of one denoising step at the full chunk shape "
                    f"({cfg.N} tokens, {cfg.N_ref}+{cfg.N_bnd}+{cfg.N} keys, audio {cfg.M}), "
                    f"median {t_block:.2f} s x {cfg.L} blocks; context passes excluded"),
     }
+
+
+def cpu_baseline_rows(cfg, inp, rows=(1, 2048)):
+    """The oracle on one DiT block of the workload (its block 0 weights from the seeded
+    catalogue) with the keys and values of every token and the queries of sampled rows,
+    timed for one row (almost only the keys and values of all tokens) and for many rows;
+    the block's time is extrapolated linearly in the rows to all N rows, times L blocks."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    one = dataclasses.replace(cfg, L=1)
+    P = synth.make_weights(one, threads=16, compact=True)
+    ref_kv = O.ref_context(P, one, inp["ref"], one.ref)
+    bkv = O.bnd_context(P, one, ref_kv, inp["bnd"], one.bnd.h, one.bnd.w)
+    ctx = [[ref_kv[0], bkv[0]]]
+    g = cfg.chunk
+    pos = O.grid_positions(0, g.frames, g.h, g.w)
+    ts = []
+    for r in rows:
+        sel = np.linspace(0, cfg.N - 1, r).astype(np.int64)
+        t0 = time.perf_counter()
+        O.velocity_rows(P, one, inp["x_init"], cfg.t_start, pos, ctx, inp["audio"], sel)
+        ts.append(time.perf_counter() - t0)
+    t_row = max(ts[1] - ts[0], 0.0) / (rows[1] - rows[0])
+    t_block = ts[0] + t_row * (cfg.N - rows[0])
+    threads, model = _cpu_info()
+    return {
+        "value": cfg.N / (t_block * cfg.L),
+        "unit": "latent tokens/s",
+        "cores": threads,
+        "cpu": model,
+        "kind": "oracle",
+        "sample": (f"one DiT block of the large chunk ({cfg.N} tokens, keys {cfg.N_ref}+{cfg.N_bnd}+{cfg.N}, "
+                   f"audio {cfg.M}): K/V of every token with the queries of {rows[0]} row in {ts[0]:.1f} s "
+                   f"and of {rows[1]} sampled rows in {ts[1]:.1f} s; block extrapolated linearly in the "
+                   f"rows to {t_block:.0f} s ({t_row * 1e3:.2f} ms per row), x {cfg.L} blocks; "
+                   f"context passes excluded"),
+    }
+
+
+# ---------------------------------------------------------------------------- shared
 
 
 def _device_weights(cfg, dev, seed: int = 5):
@@ -190,8 +321,76 @@ def _device_weights(cfg, dev, seed: int = 5):
     return out
 
 
+def _attn_fields(h):
+    """(attention TFLOP/s, config fields) from the handle's self-attention timing window."""
+    n, ms, flop = h.timing_read(DIT_TIME_ATTN)
+    tf = flop / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+    return tf, {"attention_tflops": tf, "attention_frac_bf16_peak": tf / PEAK_BF16_TFLOPS,
+                "attention_launches": n, "attention_avg_launch_ms": ms / max(n, 1)}
+
+
+def _breakdown(h, one_step) -> dict:
+    """One more bench step with the block GEMMs and the elementwise kernels timed by
+    dispatch-stamped events (outside the timed region)."""
+    import torch
+    h.timing_enable((1 << DIT_TIME_GEMM) | (1 << DIT_TIME_ELEM))
+    one_step()
+    torch.cuda.synchronize()
+    ng, msg, fg = h.timing_read(DIT_TIME_GEMM)
+    ne, mse, be = h.timing_read(DIT_TIME_ELEM)
+    h.timing_enable(False)
+    gtf = fg / (msg * 1e-3) / 1e12 if msg > 0 else 0.0
+    egb = be / (mse * 1e-3) / 1e9 if mse > 0 else 0.0
+    return {"gemm_tflops": gtf, "gemm_frac_bf16_peak": gtf / PEAK_BF16_TFLOPS, "gemm_launches": ng,
+            "gemm_ms_per_step": msg, "elementwise_gbs": egb, "elementwise_frac_hbm": egb / PEAK_HBM_GBS,
+            "elementwise_launches": ne, "elementwise_ms_per_step": mse}
+
+
+def _with_ceilings(extra: dict) -> dict:
+    """The measured ceilings and each figure's fraction of them."""
+    c = ceilings()
+    extra.update(c)
+    m, h = c["mfma_bf16_ceiling_tflops"], c["hbm_copy_ceiling_gbs"]
+    if "attention_tflops" in extra:
+        extra["attention_frac_mfma_ceiling"] = extra["attention_tflops"] / m
+    if "gemm_tflops" in extra:
+        extra["gemm_frac_mfma_ceiling"] = extra["gemm_tflops"] / m
+    if "elementwise_gbs" in extra:
+        extra["elementwise_frac_copy_ceiling"] = extra["elementwise_gbs"] / h
+    return extra
+
+
+def _line(metric, value, args, ms, workload, extra, achieved, traffic, data=None):
+    return {
+        "metric": metric,
+        "value": value,
+        "unit": "latent tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": data or "synthetic (seeded N(0,1) latents/audio, N(0,1/fan_in) random-init weights)",
+        "config": dict({"workload": workload}, **extra),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+    }
+
+
+# ---------------------------------------------------------------------------- workloads
+
+
 def large_main(args) -> int:
-    """--workload large / stream: one denoising step of the large base chunk."""
+    """large (default) / wstream: one denoising step of the large base chunk."""
     import torch
 
     import synth
@@ -208,7 +407,7 @@ def large_main(args) -> int:
     x = torch.empty_like(x0)
     t0, t1 = cfg.t_start, cfg.t_end
     g_chunk = grid_of(cfg.chunk)
-    stream = args.workload == "stream"
+    wstream = args.workload == "wstream"
 
     def context():
         h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
@@ -228,9 +427,9 @@ def large_main(args) -> int:
         return (time.perf_counter() - a) * 1e3 / k
 
     context()
-    extra = {}
+    extra = {"tokens_per_step": cfg.N}
     host = None
-    if stream:
+    if wstream:
         for _ in range(args.warmup):
             step()
         resident_ms = timed(args.steps)
@@ -247,16 +446,17 @@ def large_main(args) -> int:
         step()
         torch.cuda.synchronize()
         cold_ms = (time.perf_counter() - a) * 1e3
-        extra = {"resident_ms_per_step": resident_ms, "cold_first_step_ms": cold_ms,
-                 "block_weight_bytes": h.cfg.block_weight_bytes(), "ring_slots": 2}
+        extra.update({"resident_ms_per_step": resident_ms, "cold_first_step_ms": cold_ms,
+                      "block_weight_bytes": h.cfg.block_weight_bytes(), "ring_slots": 2})
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    h.timing_enable(True)
+    h.timing_enable(1 << DIT_TIME_ATTN)
     ms = timed(args.steps)
-    n_attn, attn_ms, attn_flop = h.timing_read()
+    achieved, af = _attn_fields(h)
     h.timing_enable(False)
-    if stream:
+    extra.update(af)
+    if wstream:
         extra["exposed_ms_per_step"] = ms - resident_ms
         extra["cold_exposed_ms"] = cold_ms - ms
         # switch: streaming is enabled while a resident step still runs, so the first
@@ -273,84 +473,101 @@ def large_main(args) -> int:
             torch.cuda.synchronize()
             sw.append((time.perf_counter() - a) * 1e3 - resident_ms - ms)
         extra["switch_exposed_ms"] = sorted(sw)[1]
+    else:
+        extra.update(_breakdown(h, step))
+        _with_ceilings(extra)
     if not torch.isfinite(x).all():
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
-    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
-    workload = ("large base chunk: 21x30x52 = 32760 latent tokens, keys 1560 reference + 1560 "
-                "boundary + 32760 chunk, 200 audio tokens of dim 768, 30 DiT blocks, hidden 3072, "
-                "24 heads x 128, MLP 4x, one Euler step 1 -> 0.875; one bench step = audio K/V + "
-                "one denoising step (the context passes run before)")
-    if stream:
+    workload = WORKLOAD_LARGE
+    if wstream:
         workload += ("; block weights (387.0 MB each) streamed from pinned host memory "
                      "through a 2-slot device ring")
-    line = {
-        "metric": METRIC_STREAM if stream else METRIC_LARGE,
-        "value": cfg.N / (ms * 1e-3),
-        "unit": "latent tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) latents/audio, random-init weights drawn on the GPU)",
-        "config": dict({
-            "workload": workload,
-            "tokens_per_step": cfg.N,
-            "attention_tflops": achieved,
-            "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
-            "attention_launches": n_attn,
-            "attention_avg_launch_ms": attn_ms / max(n_attn, 1),
-        }, **extra),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": None,
-        },
-    }
+    line = _line(METRIC_WSTREAM if wstream else METRIC, cfg.N / (ms * 1e-3), args, ms, workload, extra,
+                 achieved, None if wstream else _traffic("large"),
+                 data="synthetic (seeded N(0,1) latents/audio, random-init weights drawn on the GPU)")
+    # Teardown before the baseline and the exit: the handle first (streaming off, device
+    # synchronised), then the ring and the pinned host blocks.
+    h.close()
+    host = None
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline and not wstream:
+        line["cpu_baseline"] = cpu_baseline_rows(cfg, inp)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def stream6_main(args) -> int:
+    """stream6: whole 6-chunk streaming sessions of the base chunk shape."""
+    import numpy as np
+    import torch
+
+    import synth
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+
+    dev = torch.device("cuda", 0)
+    cfg = synth.STREAM_6_CHUNKS
+    P = synth.make_weights(cfg)
+    chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
+    h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+    ref = f32(chunks[0]["ref"], dev)
+    x0 = [f32(c["x_init"], dev) for c in chunks]
+    aud = [f32(c["audio"], dev) for c in chunks]
+    xs = [torch.empty_like(a) for a in x0]
+    S = cfg.steps
+    ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S for k in range(S + 1)]
+    g_chunk, g_ref, g_none = grid_of(cfg.chunk), grid_of(cfg.ref), grid_of(synth.Grid(0, 0, 0, 0))
+
+    def session():
+        """One request: per-chunk latencies (ms), chunk 0 including the request's set-up."""
+        lat = []
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        h.modulation_table(ts[:-1] + [0.0])
+        h.ref_kv_precompute(ref, g_ref)
+        for c in range(cfg.n_chunks):
+            h.boundary_kv_carry(xs[c - 1] if c else None, g_chunk if c else g_none)
+            xs[c].copy_(x0[c])
+            h.audio_kv_precompute(aud[c])
+            for k in range(S):
+                h.step(xs[c], ts[k], ts[k + 1], g_chunk, audio=AUDIO_HELD)
+            torch.cuda.synchronize()
+            b = time.perf_counter()
+            lat.append((b - a) * 1e3)
+            a = b
+        return lat
+
+    for _ in range(args.warmup):
+        session()
+    h.timing_enable(1 << DIT_TIME_ATTN)
+    lats = [session() for _ in range(args.steps)]
+    achieved, af = _attn_fields(h)
+    h.timing_enable(False)
+    steady = float(np.median([l for s in lats for l in s[1:]]))
+    first = float(np.median([s[0] for s in lats]))
+    ms = float(np.mean([sum(s) for s in lats]))
+    if not all(torch.isfinite(x).all() for x in xs):
+        print("bench.py: non-finite output", file=sys.stderr)
+        return 1
+    extra = {"chunks": cfg.n_chunks, "tokens_per_chunk": cfg.N, "steady_chunk_ms": steady,
+             "first_chunk_ms": first,
+             "chunk_ms_median_by_index": [float(np.median([s[c] for s in lats])) for c in range(cfg.n_chunks)]}
+    extra.update(af)
+    workload = ("streaming sequence: 6 consecutive base low-res chunks (7800 latent tokens each, keys "
+                "1560 reference + 1560 boundary (none for chunk 0) + 7800 chunk, 50 audio tokens, 4 DiT "
+                "blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0 per chunk), each boundary the "
+                "last latent frame of the previous chunk's final latent; one bench step = one session "
+                "(modulation table + reference K/V once, then per chunk boundary K/V + audio K/V + 8 "
+                "steps); value = 7800 / steady-state chunk latency (median over chunks 1-5)")
+    print(json.dumps(_line(METRIC_STREAM6, cfg.N / (steady * 1e-3), args, ms, workload, extra, achieved, None)),
+          flush=True)
     h.close()
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["base", "interp", "reuse", "sr", "sr1", "large", "stream"], default="base",
-                    help="base: one N-chunk job (default); interp: one interpolation-chunk job; "
-                         "reuse: one N-chunk job with the boundary carried by reuse")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run the 256 MiB calibration copy (for the traffic counters)")
-    ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="write the attention traffic file from rocprofv3 counter CSVs")
-    args = ap.parse_args()
-    if args.copy_probe:
-        copy_probe()
-        return 0
-    if args.reduce_traffic:
-        d = reduce_traffic(*args.reduce_traffic)
-        with open(TRAFFIC_FILE, "w") as fh:
-            json.dump(d, fh, indent=1)
-            fh.write("\n")
-        print(json.dumps(d))
-        return 0
-    if args.gpus != 1:
-        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
-              "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
-        return 2
-
-    if args.workload in ("large", "stream"):
-        return large_main(args)
-
+def chunk_main(args) -> int:
+    """base / interp / reuse / sr / sr1: chunk jobs of the base or super-resolution shape."""
     import torch
 
     import synth
@@ -377,16 +594,14 @@ def main() -> int:
     g_prev = grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w))
     interp = args.workload == "interp"
     reuse = args.workload == "reuse"
-    if sr:
-        h.ref_kv_precompute(ref, g_ref)
+    if sr or reuse or interp:
+        h.ref_kv_precompute(ref, g_ref)  # once per request, outside the timed region
     if reuse:
-        h.ref_kv_precompute(ref, g_ref)
         h.boundary_kv_carry(bnd, g_prev)  # the first job's boundary; later ones are carried
     if interp:
         # the neighbouring N-chunks' final latents (seeded stand-ins of the chunk shape)
         x_before = f32(synth.make_inputs(cfg, 1)["x_init"], dev)
         x_after = f32(synth.make_inputs(cfg, 2)["x_init"], dev)
-        h.ref_kv_precompute(ref, g_ref)
 
     table = ts[:-1] + [0.0]  # the schedule's timesteps and t = 0 of the context passes
 
@@ -410,32 +625,29 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    h.timing_enable(True)
+    h.timing_enable(1 << DIT_TIME_ATTN)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    n_attn, attn_ms, attn_flop = h.timing_read()
+    achieved, af = _attn_fields(h)
     h.timing_enable(False)
     if not torch.isfinite(x).all():
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
-
+    extra = {"tokens_per_step": cfg.N * S}
+    extra.update(af)
+    extra.update(_breakdown(h, step))
+    _with_ceilings(extra)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = cfg.N * S / ((t1 - t0) / args.steps)
-    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
-    traffic = _traffic()
-    workload = ("base low-res chunk: 5x30x52 = 7800 latent tokens, 1560 reference + 1560 "
-                "boundary tokens, 50 audio tokens of dim 768, 4 DiT blocks, hidden 1536, "
-                "12 heads x 128, MLP 4x, 8 Euler steps 1 -> 0; one bench step = modulation "
-                "table + reference K/V + boundary K/V + audio K/V + 8 denoising steps")
+    workload = WORKLOAD_BASE
     if reuse:
         workload = ("base low-res chunk, boundary carried by reuse: 7800 latent tokens, keys 1560 "
                     "reference + 1560 boundary + 7800 chunk, 50 audio tokens, 4 blocks, hidden 1536, "
-                    "12 heads x 128, 8 Euler steps 1 -> 0; one bench step = modulation table + audio K/V + 8 denoising steps, the "
-                    "last one leaving its last frame's K/V as the next boundary")
+                    "12 heads x 128, 8 Euler steps 1 -> 0; one bench step = modulation table + audio K/V + "
+                    "8 denoising steps, the last one leaving its last frame's K/V as the next boundary")
     if interp:
         workload = ("interpolation chunk of the base low-res shape: 7800 latent tokens, keys "
                     "1560 reference + 1560 boundary + 1560 anchor + 7800 chunk, 50 audio tokens, "
@@ -447,48 +659,53 @@ def main() -> int:
                     "reference + 6240 boundary + 31200 chunk, no audio, 2 DiT blocks, hidden 1536, "
                     f"12 heads x 128, MLP 4x, {S} Euler step{'s' if S > 1 else ''} 1 -> 0; one bench "
                     f"step = modulation table + boundary K/V + {S} denoising step{'s' if S > 1 else ''}")
-    metric = METRIC
-    if interp:
-        metric = METRIC_INTERP
-    elif reuse:
-        metric = METRIC_REUSE
-    elif sr:
-        metric = METRIC_SR1 if S == 1 else METRIC_SR
-    line = {
-        "metric": metric,
-        "value": value,
-        "unit": "latent tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) latents/audio, N(0,1/fan_in) random-init weights)",
-        "config": {
-            "workload": workload,
-            "tokens_per_step": cfg.N * S,
-            "attention_tflops": achieved,
-            "attention_frac_bf16_peak": achieved / PEAK_BF16_TFLOPS,
-            "attention_launches": n_attn,
-            "attention_avg_launch_ms": attn_ms / max(n_attn, 1),
-        },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
-        },
-    }
-    if not args.no_cpu_baseline and args.workload == "base":
-        line["cpu_baseline"] = cpu_baseline(cfg, P, inp)
-    print(json.dumps(line), flush=True)
+    metric = {"interp": METRIC_INTERP, "reuse": METRIC_REUSE, "sr": METRIC_SR, "sr1": METRIC_SR1}.get(
+        args.workload, METRIC)
+    line = _line(metric, cfg.N * S / ((t1 - t0) / args.steps), args, ms_per_step, workload, extra, achieved,
+                 _traffic(args.workload))
     h.close()
+    if not args.no_cpu_baseline and args.workload == "base":
+        line["cpu_baseline"] = cpu_baseline_block(cfg, P, inp)
+    print(json.dumps(line), flush=True)
     return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="large",
+                    choices=["large", "base", "stream6", "interp", "reuse", "sr", "sr1", "wstream"],
+                    help="large: one large-chunk denoising step (default, the headline); base: one base "
+                         "chunk job; stream6: whole 6-chunk streaming sessions; see the module docstring")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the 256 MiB calibration copy (for the traffic counters)")
+    ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the workload's attention traffic file from rocprofv3 counter CSVs")
+    args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe()
+        return 0
+    if args.reduce_traffic:
+        if args.workload not in TRAFFIC_FILES:
+            raise SystemExit(f"bench.py: no traffic file for workload {args.workload}")
+        d = reduce_traffic(*args.reduce_traffic)
+        with open(TRAFFIC_FILES[args.workload], "w") as fh:
+            json.dump(d, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(d))
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); "
+              "the multi-GPU sharding is a design, not a measured path", file=sys.stderr)
+        return 2
+    if args.workload in ("large", "wstream"):
+        return large_main(args)
+    if args.workload == "stream6":
+        return stream6_main(args)
+    return chunk_main(args)
 
 
 if __name__ == "__main__":

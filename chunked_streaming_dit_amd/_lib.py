@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libditchunk.so")
 DIT_OK, DIT_EINVAL, DIT_ESHAPE, DIT_ESTATE, DIT_EWORKSPACE, DIT_EHIP = 0, -1, -2, -3, -4, -5
 DIT_F32, DIT_BF16 = 0, 1
 DITK_ACT_NONE, DITK_ACT_GELU, DITK_OUT_F32 = 0, 1, 2
-DIT_TIME_ATTN = 0
+DIT_TIME_ATTN, DIT_TIME_GEMM, DIT_TIME_ELEM = 0, 1, 2
 
 # Weight table order of ditchunk.h (DIT_W_* then DIT_WB_* per block).
 GLOBAL_ORDER = ("pe.w", "pe.b", "t1.w", "t1.b", "t2.w", "t2.b", "fmod.w", "fmod.b", "fin.w", "fin.b")
@@ -47,6 +47,7 @@ _lib: Optional[ctypes.CDLL] = None
 
 DIT_AUDIO_HELD = -1
 DIT_MOD_TABLE_MAX = 16
+DITK_PROBE_SINK_FLOATS = 512 * 256
 P = ctypes.c_void_p
 I = ctypes.c_int
 Dbl = ctypes.c_double
@@ -81,6 +82,8 @@ _SIGS = {
     "ditk_modulation": (I, [I, I, I, Dbl, ctypes.POINTER(P), P, P, P, P]),
     "ditk_patch_input": (I, [I, P, I, I, P, I, I, DitGrid, P, P]),
     "ditk_patch_embed": (I, [P, I, I, P, I, I, DitGrid, P, P, P, I, P]),
+    "ditk_probe_mfma": (I, [P, I, P, ctypes.c_longlong, ctypes.POINTER(Dbl), P]),
+    "ditk_probe_copy": (I, [P, P, ctypes.c_longlong, P]),
 }
 EXPORTS = tuple(_SIGS)
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libditchunk.so")
-SOURCES = ["gemm.hip", "attention.hip", "xattn.hip", "attention_plan.cpp", "elementwise.hip", "ditchunk.cpp", "ops.cpp"]
+SOURCES = ["gemm.hip", "attention.hip", "xattn.hip", "attention_plan.cpp", "elementwise.hip", "probe.hip", "ditchunk.cpp", "ops.cpp"]
 ARCH = os.environ.get("DITCHUNK_ARCH", "gfx950")
 
 

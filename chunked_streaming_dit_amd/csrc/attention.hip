@@ -512,26 +512,33 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
     return hipErrorInvalidValue;
   // With events, the dispatch itself stamps the kernel's start and end into them: no
   // separate marker packets (and their waits) between this launch and its neighbours.
+  // When q-tiles are split the merge (attention_combine) stamps the end instead.
   void* args[1] = {&a};
-  if (ev) return hipExtLaunchKernel(fn, grid, block, args, 0, s, ev[0], ev[1], 0);
+  if (ev) return hipExtLaunchKernel(fn, grid, block, args, 0, s, ev[0], attention_splits(nq, sp) ? nullptr : ev[1], 0);
   return hipLaunchKernel(fn, grid, block, args, 0, s);
 }
 
+bool attention_splits(int nq, const AttnSplit& sp) {
+  return nq > 0 && sp.nsplit > 1 && std::min(std::max(sp.qt0, 0) * BQ, nq) < nq;
+}
+
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
-                             hipStream_t s) {
-  if (nq <= 0 || sp.nsplit <= 1) return hipSuccess;
+                             hipStream_t s, hipEvent_t stop) {
+  if (!attention_splits(nq, sp)) return hipSuccess;
   const int r0 = std::min(std::max(sp.qt0, 0) * BQ, nq);  // rows before r0 were not split
-  if (r0 >= nq) return hipSuccess;
   const long long n4 = (long long)(nq - r0) * H * dh / 4;
-  dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+  const dim3 grid((unsigned)((n4 + 255) / 256)), block(256);
+  const hipEvent_t ev[2] = {nullptr, stop};
   if (dtype == BF16 && dh == 128)
-    attn_combine_kernel<bf16, 128><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (bf16*)o, ldo);
-  else if (dtype == BF16 && dh == 64)
-    attn_combine_kernel<bf16, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (bf16*)o, ldo);
-  else if (dtype == F32 && dh == 64)
-    attn_combine_kernel<float, 64><<<grid, block, 0, s>>>(sp.opart, sp.ml, sp.nsplit, r0, nq, H, (float*)o, ldo);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+    return launch_k(attn_combine_kernel<bf16, 128>, grid, block, s, ev, (const float*)sp.opart, (const float*)sp.ml,
+                    sp.nsplit, r0, nq, H, (bf16*)o, ldo);
+  if (dtype == BF16 && dh == 64)
+    return launch_k(attn_combine_kernel<bf16, 64>, grid, block, s, ev, (const float*)sp.opart, (const float*)sp.ml,
+                    sp.nsplit, r0, nq, H, (bf16*)o, ldo);
+  if (dtype == F32 && dh == 64)
+    return launch_k(attn_combine_kernel<float, 64>, grid, block, s, ev, (const float*)sp.opart, (const float*)sp.ml,
+                    sp.nsplit, r0, nq, H, (float*)o, ldo);
+  return hipErrorInvalidValue;
 }
 
 int attention_key_tiles(const AttnSeg* segs, int nseg) {

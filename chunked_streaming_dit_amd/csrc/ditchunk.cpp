@@ -89,6 +89,22 @@ int check_config(const dit_config* c) {
     return fail(DIT_EINVAL, "capacities must be max_tokens>=1, max_ref>=1, max_bnd>=0, max_audio>=0");
   if (c->max_tokens > (1 << 24) || c->max_ref > (1 << 24) || c->max_bnd > (1 << 24) || c->max_audio > 65536)
     return fail(DIT_EINVAL, "capacity too large");
+  {
+    // 32-bit operand offsets of the GEMM and attention kernels (GEMM_MAX_ELEMS,
+    // VT_MAX_BYTES): the widest activation matrix is [token capacity, max(3D, mlp D)],
+    // the largest V^T buffer [D, token capacity].
+    long long cap = c->max_tokens;
+    if (c->max_ref > cap) cap = c->max_ref;
+    if (c->max_bnd > cap) cap = c->max_bnd;
+    cap = (cap + 63) / 64 * 64;
+    const long long elt = c->dtype == DIT_BF16 ? 2 : 4;
+    const long long widest = 3LL * c->D > (long long)c->mlp_ratio * c->D ? 3LL * c->D : (long long)c->mlp_ratio * c->D;
+    if (cap * widest >= GEMM_MAX_ELEMS || cap * c->D * elt >= VT_MAX_BYTES)
+      return fail(DIT_EINVAL,
+                  "token capacity %lld too large for D=%d, mlp_ratio=%d: activations [%lld, %lld] must stay under "
+                  "2^31 elements and V^T [%d, %lld] under 2^31 bytes",
+                  cap, c->D, c->mlp_ratio, cap, widest, c->D, cap);
+  }
   if (!(c->eps > 0) || !std::isfinite(c->eps)) return fail(DIT_EINVAL, "eps must be finite and > 0");
   if (!(c->rope_theta > 1) || !std::isfinite(c->rope_theta)) return fail(DIT_EINVAL, "rope_theta must be finite and > 1");
   return DIT_OK;
@@ -202,11 +218,13 @@ struct dit_handle {
   // block's weights into the ring, instead of in a pass of its own).
   std::vector<char> aud_pend;
   std::vector<double> mod_t;  // timesteps of the modulation table entries
-  // timing
-  bool timing = false;
-  std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created lazily
-  int ev_used = 0;
-  double flop_acc = 0.0;
+  // timing (dit_timing_enable): per kind, event pairs stamped by the timed dispatches
+  struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // 2 * MAX_EVENT_PAIRS, created by dit_timing_enable
+    int used = 0;                // pairs stamped in this window
+    double work = 0.0;           // their algorithmic flop (attention, GEMM) or bytes
+  } tm[DIT_TIME_KINDS];
 
   const void* W(int i) const { return w[i]; }
   const void* B(int l, int i) const {
@@ -352,23 +370,37 @@ int pass_end(dit_handle* hd, int rc) {
   return rc;
 }
 
-int timed_begin(dit_handle* h, int* slot) {
-  *slot = -1;
-  if (!h->timing) return DIT_OK;
-  if (h->ev.empty()) {
-    h->ev.resize(2 * MAX_EVENT_PAIRS);
-    // Timing-only events: no system-scope fence when they complete (it would write
-    // back and invalidate the caches around the timed launch).  Elapsed times are read
-    // after hipEventSynchronize, which needs no memory ordering with the timed work.
-    for (auto& e : h->ev) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
-  }
-  if (h->ev_used >= MAX_EVENT_PAIRS) return DIT_OK;
-  *slot = h->ev_used++;
+// The start/stop event pair for the next launch of timing kind k, or NULL when that kind
+// is not being timed (or the window is full).  The pair counts once timed_done has
+// charged its work, i.e. only for a launch that was enqueued.
+const hipEvent_t* timed_ev(dit_handle* h, int k) {
+  dit_handle::Timing& t = h->tm[k];
+  if (!t.on || t.used >= MAX_EVENT_PAIRS) return nullptr;
+  return &t.ev[2 * (size_t)t.used];
+}
+void timed_done(dit_handle* h, int k, const hipEvent_t* ev, double work) {
+  if (!ev) return;
+  ++h->tm[k].used;
+  h->tm[k].work += work;
+}
+
+// A GEMM of the block passes, timed as kind DIT_TIME_GEMM (flop 2 M N K).
+int block_gemm(dit_handle* hd, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
+               const GemmEpi& e) {
+  const hipEvent_t* ev = M > 0 ? timed_ev(hd, DIT_TIME_GEMM) : nullptr;
+  HIPCHK(gemm(hd->cfg.dtype, A, lda, W, ldw, M, N, K, e, hd->stream, ev));
+  timed_done(hd, DIT_TIME_GEMM, ev, 2.0 * M * N * K);
   return DIT_OK;
 }
-// The pair of slot (>= 0) is stamped by the timed launch itself (see run_attention).
-void timed_end(dit_handle* h, int slot, double flop) {
-  if (slot >= 0) h->flop_acc += flop;
+
+// RMSNorm (+ adaLN modulation when shift/scale are given) of h [n, D] into u, timed as
+// kind DIT_TIME_ELEM (bytes: h read in fp32, u written in the dtype, the two vectors).
+int block_norm(dit_handle* hd, const float* h, int n, const float* shift, const float* scale, void* u) {
+  const dit_config& c = hd->cfg;
+  const hipEvent_t* ev = n > 0 ? timed_ev(hd, DIT_TIME_ELEM) : nullptr;
+  HIPCHK(rmsnorm_mod(c.dtype, h, n, c.D, shift, scale, (float)c.eps, u, hd->stream, ev));
+  timed_done(hd, DIT_TIME_ELEM, ev, (double)n * c.D * (4 + hd->lay.elt) + (shift ? 2.0 * c.D * 4 : 0.0));
+  return DIT_OK;
 }
 
 // Attention launch: picks the key-range split, times the main kernel when timing is on
@@ -384,21 +416,19 @@ int run_attention(dit_handle* hd, int n, const AttnSeg* seg, int ns, bool timed,
   AttnSplit sp = attention_plan(n, c.H, attention_key_tiles(seg, ns), L.part_rows, device_cus());
   sp.opart = hd->X<float>(L.opart);
   sp.ml = hd->X<float>(L.ml);
-  int slot = -1, rc;
-  if (timed && n > 0 && (rc = timed_begin(hd, &slot))) return rc;
+  // timed: the main kernel's dispatch stamps the start, the merge's (if split) the end
+  const hipEvent_t* ev = timed && n > 0 ? timed_ev(hd, DIT_TIME_ATTN) : nullptr;
   const bool cross = kind == ATTN_CROSS;
   const AttnNorm norm{hd->B(l, cross ? DIT_WB_GCQ : DIT_WB_GQ), hd->B(l, cross ? DIT_WB_GCK : DIT_WB_GK),
                       (double)attention_q_scale(c.dh)};
-  const hipError_t err = attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp,
-                                   true, hd->stream, kind, &norm, slot >= 0 ? &hd->ev[2 * slot] : nullptr);
-  if (err != hipSuccess && slot >= 0) --hd->ev_used;  // its events were never stamped
-  HIPCHK(err);
-  if (timed) {
+  HIPCHK(attention(c.dtype, c.dh, c.H, hd->X(L.q), c.D, hd->X(L.o), c.D, n, c.D, seg, ns, sp, true, hd->stream,
+                   kind, &norm, ev));
+  HIPCHK(attention_combine(c.dtype, c.dh, c.H, n, sp, hd->X(L.o), c.D, hd->stream, ev ? ev[1] : nullptr));
+  if (ev) {
     double nkv = 0;
     for (int i = 0; i < ns; ++i) nkv += seg[i].n;
-    timed_end(hd, slot, 4.0 * n * nkv * c.D);
+    timed_done(hd, DIT_TIME_ATTN, ev, 4.0 * n * nkv * c.D);
   }
-  HIPCHK(attention_combine(c.dtype, c.dh, c.H, n, sp, hd->X(L.o), c.D, hd->stream));
   return DIT_OK;
 }
 
@@ -467,11 +497,10 @@ int qkv_project(dit_handle* hd, int l, int n, RopeGrid g, void* q_out, void* k_o
     e.D = D; e.kpad = round64(n); e.rope = 1;
     e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.log2_theta = (float)std::log2(c.rope_theta);
     e.g = g;
-    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
-    return DIT_OK;
+    return block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e);
   }
   e.kind = EPI_BIAS;
-  HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e, s));
+  if (int rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_QKV_W), D, n, 3 * D, D, e)) return rc;
   HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, q_out ? big : nullptr, big + (size_t)D * L.elt,
                      big + (size_t)2 * D * L.elt, 3 * D, hd->B(l, DIT_WB_GQ), hd->B(l, DIT_WB_GK), 1, g,
                      (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh), q_out, k_out, vt_out, cap, s));
@@ -505,7 +534,7 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     if (!tab)
       HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec,
                               mod + (size_t)l * 6 * D, s));
-    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
+    if (int rc = block_norm(hd, h, n, m + 0 * D, m + 1 * D, hd->X(L.u))) return rc;
     if (int rc = qkv_project(hd, l, n, g, last ? nullptr : hd->X(L.q), hd->S(kdst[l]), hd->S(vdst[l]), cap))
       return rc;
     if (last) {
@@ -522,16 +551,16 @@ int context_pass_run(dit_handle* hd, const float* z, int n, RopeGrid g, const st
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
     e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
-    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));
+    if ((rc = block_gemm(hd, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e))) return rc;
+    if ((rc = block_norm(hd, h, n, m + 3 * D, m + 4 * D, hd->X(L.u)))) return rc;
     e = GemmEpi{};
     e.kind = EPI_GELU; e.bias = hd->B(l, DIT_WB_FC1_B); e.out = hd->X(L.big); e.ldo = F;
-    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
+    if ((rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e))) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
     e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
-    if (int rc = block_end(hd, l)) return rc;
+    if ((rc = block_gemm(hd, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e))) return rc;
+    if ((rc = block_end(hd, l))) return rc;
   }
   return DIT_OK;
 }
@@ -600,7 +629,8 @@ int dit_create(const dit_config* cfg, const void* const* weights, void* state, s
 
 int dit_destroy(dit_handle* h) {
   if (!h) return DIT_OK;
-  for (auto& e : h->ev) (void)hipEventDestroy(e);
+  for (auto& t : h->tm)
+    for (auto& e : t.ev) (void)hipEventDestroy(e);
   if (h->st.copy) {
     (void)hipStreamSynchronize(h->st.copy);
     for (auto& e : h->st.ready) (void)hipEventDestroy(e);
@@ -836,7 +866,7 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
       HIPCHK(block_modulation(c.dtype, D, hd->B(l, DIT_WB_MOD_W), hd->B(l, DIT_WB_MOD_B), cvec,
                               mod + (size_t)l * 6 * D, s));
     // self-attention
-    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 0 * D, m + 1 * D, (float)c.eps, hd->X(L.u), s));
+    if (int rc = block_norm(hd, h, n, m + 0 * D, m + 1 * D, hd->X(L.u))) return rc;
     if (int rc = qkv_project(hd, l, n, g, hd->X(L.q), hd->X(L.kc), hd->X(L.vtc), L.cap_tok)) return rc;
     AttnSeg seg[ATTN_MAX_SEGS];
     int ns = 0;
@@ -857,10 +887,10 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_O_B); e.out = h; e.ldo = D; e.gate = m + 2 * D;
     e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e, s));
+    if ((rc = block_gemm(hd, hd->X(L.o), D, hd->B(l, DIT_WB_O_W), D, n, D, D, e))) return rc;
     // audio cross-attention
     if (cross) {
-      HIPCHK(rmsnorm_mod(c.dtype, h, n, D, nullptr, nullptr, (float)c.eps, hd->X(L.u), s));
+      if ((rc = block_norm(hd, h, n, nullptr, nullptr, hd->X(L.u)))) return rc;
       // the audio keys and values: held, or from this step's audio
       AttnSeg aseg{hd->S(L.kaud[l]), hd->S(L.vaud[l]), hd->n_aud, L.cap_audio};
       void* uta = L.fold ? hd->S(L.uta[l]) : nullptr;
@@ -877,15 +907,15 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
         e.kind = EPI_QKNORM_X; e.gq = hd->B(l, DIT_WB_GCQ); e.D = D;
         e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
         e.xk = aseg.k; e.xn = aseg.n; e.p_out = hd->X(L.o); e.ldp = HK;
-        HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+        if ((rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e))) return rc;
       } else {
         if (gemm_qknorm_fits(c.dtype, n, D, c.dh)) {  // q-norm in the GEMM epilogue (no RoPE)
           e.kind = EPI_QKNORM; e.gq = hd->B(l, DIT_WB_GCQ); e.q_out = hd->X(L.q); e.D = D;
           e.q_scale = attention_q_scale(c.dh); e.eps = (float)c.eps; e.g = g;
-          HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+          if ((rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e))) return rc;
         } else {
           e.kind = EPI_BIAS;
-          HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e, s));
+          if ((rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_CQ_W), D, n, D, D, e))) return rc;
           HIPCHK(qknorm_rope(c.dtype, c.dh, c.H, n, big, nullptr, nullptr, D, hd->B(l, DIT_WB_GCQ),
                              nullptr, 0, g, (float)c.eps, (float)c.rope_theta, attention_q_scale(c.dh),
                              hd->X(L.q), nullptr, nullptr, L.cap_tok, s));
@@ -900,28 +930,34 @@ int chunk_pass(dit_handle* hd, float* x, const float* cond, const float* audio, 
       e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_CO_B); e.out = h; e.ldo = D; e.gate = nullptr;
       e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
       if (uta)  // h += P U^T + b_co
-        HIPCHK(gemm(c.dtype, hd->X(L.o), HK, uta, HK, n, D, HK, e, s));
+        rc = block_gemm(hd, hd->X(L.o), HK, uta, HK, n, D, HK, e);
       else
-        HIPCHK(gemm(c.dtype, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e, s));
+        rc = block_gemm(hd, hd->X(L.o), D, hd->B(l, DIT_WB_CO_W), D, n, D, D, e);
+      if (rc) return rc;
     }
     // MLP
-    HIPCHK(rmsnorm_mod(c.dtype, h, n, D, m + 3 * D, m + 4 * D, (float)c.eps, hd->X(L.u), s));
+    if ((rc = block_norm(hd, h, n, m + 3 * D, m + 4 * D, hd->X(L.u)))) return rc;
     e = GemmEpi{};
     e.kind = EPI_GELU; e.bias = hd->B(l, DIT_WB_FC1_B); e.out = hd->X(L.big); e.ldo = F;
-    HIPCHK(gemm(c.dtype, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e, s));
+    if ((rc = block_gemm(hd, hd->X(L.u), D, hd->B(l, DIT_WB_FC1_W), D, n, F, D, e))) return rc;
     e = GemmEpi{};
     e.kind = EPI_RESID; e.bias = hd->B(l, DIT_WB_FC2_B); e.out = h; e.ldo = D; e.gate = m + 5 * D;
     e.ws = hd->X<float>(L.opart); e.ws_floats = (long long)L.part_rows * D;
-    HIPCHK(gemm(c.dtype, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e, s));
-    if (int rc = block_end(hd, l)) return rc;
+    if ((rc = block_gemm(hd, hd->X(L.big), F, hd->B(l, DIT_WB_FC2_W), F, n, D, F, e))) return rc;
+    if ((rc = block_end(hd, l))) return rc;
   }
   // final layer + Euler
   if (final_layer_fits(c.dtype, D, c.c_p)) {
+    // bytes: h read (fp32), x read and written, v written, the weights and vectors
+    const hipEvent_t* ev = timed_ev(hd, DIT_TIME_ELEM);
     HIPCHK(final_layer(h, n, D, fmod, fmod + D, (float)c.eps, hd->W(DIT_W_FIN_W), hd->W(DIT_W_FIN_B),
-                       (float)(t_next - t), x, v_out, s));
+                       (float)(t_next - t), x, v_out, s, ev));
+    timed_done(hd, DIT_TIME_ELEM, ev,
+               (double)n * D * 4 + (double)n * c.c_p * 4 * (v_out ? 3 : 2) + (double)c.c_p * (D + 1) * L.elt +
+                   2.0 * D * 4);
     return DIT_OK;
   }
-  HIPCHK(rmsnorm_mod(c.dtype, h, n, D, fmod, fmod + D, (float)c.eps, hd->X(L.u), s));
+  if (int rc = block_norm(hd, h, n, fmod, fmod + D, hd->X(L.u))) return rc;
   e = GemmEpi{};
   e.kind = EPI_EULER; e.bias = hd->W(DIT_W_FIN_B); e.out = x; e.ldo = c.c_p; e.v_out = v_out;
   e.dt = (float)(t_next - t);
@@ -992,27 +1028,43 @@ const char* dit_last_error(void) { return g_err.c_str(); }
 
 int dit_timing_enable(dit_handle* h, int enable) {
   if (!h) return fail(DIT_EINVAL, "handle is NULL");
-  h->timing = enable != 0;
-  h->ev_used = 0;
-  h->flop_acc = 0.0;
+  if (enable < 0 || enable >= (1 << DIT_TIME_KINDS)) return fail(DIT_EINVAL, "enable mask %d", enable);
+  for (int k = 0; k < DIT_TIME_KINDS; ++k) {
+    dit_handle::Timing& t = h->tm[k];
+    t.on = false;
+    t.used = 0;
+    t.work = 0.0;
+    if (!(enable & (1 << k))) continue;
+    // Timing-only events, created here (not inside a timed region): no system-scope
+    // fence when they complete (it would write back and invalidate the caches around
+    // the timed launch).  Elapsed times are read after hipEventSynchronize, which needs
+    // no memory ordering with the timed work.
+    while (t.ev.size() < 2 * (size_t)MAX_EVENT_PAIRS) {
+      hipEvent_t e;
+      HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
+      t.ev.push_back(e);
+    }
+    t.on = true;
+  }
   return DIT_OK;
 }
 
-int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_flop) {
+int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_work) {
   if (!h || !count || !total_ms) return fail(DIT_EINVAL, "NULL argument");
-  if (kind != DIT_TIME_ATTN) return fail(DIT_EINVAL, "kind %d", kind);
+  if (kind < 0 || kind >= DIT_TIME_KINDS) return fail(DIT_EINVAL, "kind %d", kind);
+  dit_handle::Timing& t = h->tm[kind];
   double ms = 0.0;
-  for (int i = 0; i < h->ev_used; ++i) {
-    HIPCHK(hipEventSynchronize(h->ev[2 * i + 1]));
+  for (int i = 0; i < t.used; ++i) {
+    HIPCHK(hipEventSynchronize(t.ev[2 * (size_t)i + 1]));
     float f = 0.f;
-    HIPCHK(hipEventElapsedTime(&f, h->ev[2 * i], h->ev[2 * i + 1]));
+    HIPCHK(hipEventElapsedTime(&f, t.ev[2 * (size_t)i], t.ev[2 * (size_t)i + 1]));
     ms += f;
   }
-  *count = h->ev_used;
+  *count = t.used;
   *total_ms = ms;
-  if (total_flop) *total_flop = h->flop_acc;
-  h->ev_used = 0;
-  h->flop_acc = 0.0;
+  if (total_work) *total_work = t.work;
+  t.used = 0;
+  t.work = 0.0;
   return DIT_OK;
 }
 

@@ -455,23 +455,19 @@ __global__ __launch_bounds__(256) void bnd_reuse_v_kernel(const T* __restrict__ 
 }  // namespace
 
 hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shift,
-                       const float* scale, float eps, void* out, hipStream_t s) {
+                       const float* scale, float eps, void* out, hipStream_t s, const hipEvent_t* ev) {
   if (n <= 0) return hipSuccess;
   if (D % 256 || D > 4096) return hipErrorInvalidValue;
   if (D == 1536 || D == 3072) {
-    dim3 g2((n + 7) / 8);
-#define RMS2(T, IT) rmsnorm_mod2_kernel<T, IT><<<g2, 256, 0, s>>>(h, n, shift, scale, eps, (T*)out)
+    const dim3 g2((n + 7) / 8), b(256);
+#define RMS2(T, IT) return launch_k(rmsnorm_mod2_kernel<T, IT>, g2, b, s, ev, h, n, shift, scale, eps, (T*)out)
     if (dtype == BF16) { if (D == 1536) RMS2(bf16, 6); else RMS2(bf16, 12); }
     else { if (D == 1536) RMS2(float, 6); else RMS2(float, 12); }
 #undef RMS2
-    return hipGetLastError();
   }
-  dim3 grid((n + 3) / 4);
-  if (dtype == BF16)
-    rmsnorm_mod_kernel<bf16><<<grid, 256, 0, s>>>(h, n, D, shift, scale, eps, (bf16*)out);
-  else
-    rmsnorm_mod_kernel<float><<<grid, 256, 0, s>>>(h, n, D, shift, scale, eps, (float*)out);
-  return hipGetLastError();
+  const dim3 grid((n + 3) / 4), b(256);
+  if (dtype == BF16) return launch_k(rmsnorm_mod_kernel<bf16>, grid, b, s, ev, h, n, D, shift, scale, eps, (bf16*)out);
+  return launch_k(rmsnorm_mod_kernel<float>, grid, b, s, ev, h, n, D, shift, scale, eps, (float*)out);
 }
 
 hipError_t qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const void* k_in,

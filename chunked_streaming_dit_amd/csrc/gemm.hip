@@ -430,20 +430,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const T* __restrict__ A, int 
 
 template <class T, int BM, int BN>
 hipError_t launch_t(const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-                    const GemmEpi& e, hipStream_t s) {
+                    const GemmEpi& e, hipStream_t s, const hipEvent_t* ev) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(256);
   const T* a = reinterpret_cast<const T*>(A);
   const T* w = reinterpret_cast<const T*>(W);
+#define GK(EP) launch_k(gemm_kernel<T, BM, BN, EP>, grid, block, s, ev, a, lda, w, ldw, M, N, K, e)
   switch (e.kind) {
-    case EPI_BIAS: gemm_kernel<T, BM, BN, EPI_BIAS><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_RESID: gemm_kernel<T, BM, BN, EPI_RESID><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_F32: gemm_kernel<T, BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_EULER: gemm_kernel<T, BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_BIAS: return GK(EPI_BIAS);
+    case EPI_GELU: return GK(EPI_GELU);
+    case EPI_RESID: return GK(EPI_RESID);
+    case EPI_F32: return GK(EPI_F32);
+    case EPI_EULER: return GK(EPI_EULER);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+#undef GK
 }
 
 
@@ -611,47 +612,44 @@ __global__ __launch_bounds__(256) void splitk_resid_kernel(const float* __restri
 
 template <int BM, int BN>
 hipError_t launch_lds(const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-                      const GemmEpi& e, hipStream_t s) {
+                      const GemmEpi& e, hipStream_t s, const hipEvent_t* ev) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid(tiles), block(LDS_THREADS);
   const bf16* a = reinterpret_cast<const bf16*>(A);
   const bf16* w = reinterpret_cast<const bf16*>(W);
+#define LK(EP) launch_k(gemm_lds_kernel<BM, BN, EP>, grid, block, s, ev, a, lda, w, ldw, M, N, K, e)
   switch (e.kind) {
-    case EPI_BIAS: gemm_lds_kernel<BM, BN, EPI_BIAS><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_GELU: gemm_lds_kernel<BM, BN, EPI_GELU><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_RESID: gemm_lds_kernel<BM, BN, EPI_RESID><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_F32: gemm_lds_kernel<BM, BN, EPI_F32><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_EULER: gemm_lds_kernel<BM, BN, EPI_EULER><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
-    case EPI_QKNORM: gemm_lds_kernel<BM, BN, EPI_QKNORM><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e); break;
+    case EPI_BIAS: return LK(EPI_BIAS);
+    case EPI_GELU: return LK(EPI_GELU);
+    case EPI_RESID: return LK(EPI_RESID);
+    case EPI_F32: return LK(EPI_F32);
+    case EPI_EULER: return LK(EPI_EULER);
+    case EPI_QKNORM: return LK(EPI_QKNORM);
     case EPI_QKNORM_X:
-      if constexpr (BM <= 192) {
-        gemm_lds_kernel<BM, BN, EPI_QKNORM_X><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e);
-        break;
-      } else {
-        return hipErrorInvalidValue;
-      }
+      if constexpr (BM <= 192) return LK(EPI_QKNORM_X);
+      else return hipErrorInvalidValue;
     case EPI_PARTIAL:
       grid.x = tiles * e.ksplit;
-      gemm_lds_kernel<BM, BN, EPI_PARTIAL><<<grid, block, 0, s>>>(a, lda, w, ldw, M, N, K, e);
-      break;
+      return LK(EPI_PARTIAL);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+#undef LK
 }
 
 // EPI_RESID with the K range split into parts (see GemmEpi::ws): partial products of
 // 128 x 256 tiles into ws, then the residual epilogue over their sum.
 hipError_t gemm_resid_splitk(const void* A, int lda, const void* W, int ldw, int M, int N, int K, int parts,
-                             const GemmEpi& e, hipStream_t s) {
+                             const GemmEpi& e, hipStream_t s, const hipEvent_t* ev) {
   GemmEpi ep = e;
   ep.kind = EPI_PARTIAL;
   ep.ksplit = parts;
-  hipError_t err = launch_lds<128, 256>(A, lda, W, ldw, M, N, K, ep, s);
+  const hipEvent_t ev0[2] = {ev ? ev[0] : nullptr, nullptr}, ev1[2] = {nullptr, ev ? ev[1] : nullptr};
+  hipError_t err = launch_lds<128, 256>(A, lda, W, ldw, M, N, K, ep, s, ev0);
   if (err != hipSuccess) return err;
   const long long n4 = (long long)M * N / 4;
-  splitk_resid_kernel<bf16><<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(
-      e.ws, parts, M, N, reinterpret_cast<const bf16*>(e.bias), e.gate, reinterpret_cast<float*>(e.out), e.ldo);
-  return hipGetLastError();
+  return launch_k(splitk_resid_kernel<bf16>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, ev1,
+                  (const float*)e.ws, parts, M, N, reinterpret_cast<const bf16*>(e.bias), e.gate,
+                  reinterpret_cast<float*>(e.out), e.ldo);
 }
 
 
@@ -889,7 +887,7 @@ bool gemm_qknorm_fits(int dtype, int M, int N, int dh) {
 }
 
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-                const GemmEpi& e, hipStream_t s) {
+                const GemmEpi& e, hipStream_t s, const hipEvent_t* ev) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (e.kind == EPI_QKNORM && (!gemm_qknorm_fits(dtype, M, N, 128) || e.D % 256 || (N != e.D && N != 3 * e.D)))
     return hipErrorInvalidValue;
@@ -916,21 +914,21 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
       if (e.kind == EPI_RESID && e.ws && t128 < 160 && K >= 4096 && K % 64 == 0) {
         int parts = (int)std::min<long long>(4, 256 / t128);
         while (parts > 1 && (long long)parts * M * N > e.ws_floats) --parts;
-        if (parts > 1) return gemm_resid_splitk(A, lda, W, ldw, M, N, K, parts, e, s);
+        if (parts > 1) return gemm_resid_splitk(A, lda, W, ldw, M, N, K, parts, e, s, ev);
       }
       if (e.kind != EPI_QKNORM && e.kind != EPI_QKNORM_X && ((M + best - 1) / best) * (N / 256) < 160) {
-        if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
-        return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
+        if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s, ev);
+        return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s, ev);
       }
       if (best == 256 && e.kind == EPI_QKNORM_X) best = 192;  // its LDS holds a 192-row q tile at most
-      if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s);
-      if (best == 192) return launch_lds<192, 256>(A, lda, W, ldw, M, N, K, e, s);
-      return launch_lds<128, 256>(A, lda, W, ldw, M, N, K, e, s);
+      if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s, ev);
+      if (best == 192) return launch_lds<192, 256>(A, lda, W, ldw, M, N, K, e, s, ev);
+      return launch_lds<128, 256>(A, lda, W, ldw, M, N, K, e, s, ev);
     }
-    if (M >= 512 && N >= 512) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s);
-    return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
+    if (M >= 512 && N >= 512) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s, ev);
+    return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s, ev);
   }
-  return launch_t<float, 64, 64>(A, lda, W, ldw, M, N, K, e, s);
+  return launch_t<float, 64, 64>(A, lda, W, ldw, M, N, K, e, s, ev);
 }
 
 bool patch_embed_fits(int dtype, int c_p, int c_c, int N) {
@@ -959,19 +957,21 @@ bool final_layer_fits(int dtype, int D, int c_p) {
 }
 
 hipError_t final_layer(const float* h, int n, int D, const float* shift, const float* scale, float eps,
-                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s) {
+                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s,
+                       const hipEvent_t* ev) {
   if (n <= 0) return hipSuccess;
   dim3 grid((n + FL_BM - 1) / FL_BM), block(FL_THREADS);
   const bf16* w = reinterpret_cast<const bf16*>(W);
   const bf16* bb = reinterpret_cast<const bf16*>(b);
+#define FK(KD) launch_k(final_layer_kernel<KD>, grid, block, s, ev, h, n, shift, scale, eps, w, bb, dt, x, v_out)
   switch (D) {
-    case 256: final_layer_kernel<1><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
-    case 512: final_layer_kernel<2><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
-    case 1024: final_layer_kernel<4><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
-    case 1536: final_layer_kernel<6><<<grid, block, 0, s>>>(h, n, shift, scale, eps, w, bb, dt, x, v_out); break;
+    case 256: return FK(1);
+    case 512: return FK(2);
+    case 1024: return FK(4);
+    case 1536: return FK(6);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+#undef FK
 }
 
 }  // namespace dit

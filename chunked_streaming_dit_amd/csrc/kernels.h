@@ -1,9 +1,22 @@
 // Host-side launchers of the device kernels (internal to libditchunk).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 namespace dit {
+
+// Launch a kernel.  With ev (a start/stop event pair, either entry may be null) the
+// dispatch itself stamps the kernel's start into ev[0] and its end into ev[1]
+// (hipExtLaunchKernelGGL): timing without marker packets between launches.
+template <typename... Args, typename F = void (*)(Args...)>
+inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, hipStream_t s, const hipEvent_t* ev, Args... args) {
+  if (ev && (ev[0] || ev[1]))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev[0], ev[1], 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 enum Dtype { F32 = 0, BF16 = 1 };
 
@@ -62,9 +75,25 @@ struct GemmEpi {
   int ldp;
 };
 // Whether gemm() can fuse EPI_QKNORM for this launch (else: EPI_BIAS + qknorm_rope).
+// 32-bit operand offsets.  The LDS-staged GEMM forms each lane's offset into A and W as
+// rows x row pitch in 32-bit integers (elements, then bytes), and the attention kernel
+// forms the V^T offset of a head's rows (D x key capacity) in 32 bits.  Callers keep every
+// GEMM operand (rows x pitch) under GEMM_MAX_ELEMS elements and every V^T buffer under
+// VT_MAX_BYTES bytes; the host entry points reject larger shapes.
+constexpr long long GEMM_MAX_ELEMS = (1LL << 31) - 64;
+constexpr long long VT_MAX_BYTES = 1LL << 31;
+
+// ---------------------------------------------------------------- measured ceilings
+// The dense bf16 MFMA loop (flop: its algorithmic MFMA work) and the plain copy of
+// probe.hip; sink holds PROBE_SINK_FLOATS floats (one per thread of the MFMA grid).
+constexpr int PROBE_SINK_FLOATS = 512 * 256;
+hipError_t probe_mfma(const void* data, int iters, float* sink, double* flop, hipStream_t s);
+hipError_t probe_copy(const void* src, void* dst, long long bytes, hipStream_t s);
+
 bool gemm_qknorm_fits(int dtype, int M, int N, int dh);
+// ev: optional start/stop pair stamped by the first and the last kernel of the GEMM.
 hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M, int N, int K,
-                const GemmEpi& e, hipStream_t s);
+                const GemmEpi& e, hipStream_t s, const hipEvent_t* ev = nullptr);
 
 // ---------------------------------------------------------------- attention
 // K/V segment in the attention layout:
@@ -117,8 +146,11 @@ hipError_t attention(int dtype, int dh, int H, const void* q, int ldq, void* o, 
                      const hipEvent_t* ev = nullptr);
 // log2(e) / sqrt(dh): the q scale of the exp2-domain logits.
 inline float attention_q_scale(int dh) { return (float)(1.4426950408889634 / __builtin_sqrt((double)dh)); }
+// Whether a launch of nq queries with split sp splits any q-tile (then attention_combine
+// launches its merge; with events, attention stamps only the start and the merge the end).
+bool attention_splits(int nq, const AttnSplit& sp);
 hipError_t attention_combine(int dtype, int dh, int H, int nq, const AttnSplit& sp, void* o, int ldo,
-                             hipStream_t s);
+                             hipStream_t s, hipEvent_t stop = nullptr);
 // One short key segment (1..64 keys, bf16, dh = 128): the exact softmax over one tile,
 // o[nq, ldo] per head, in a kernel whose whole grid is resident at once.
 bool short_attention_fits(int dtype, int dh, int nseg, const AttnSeg* segs);
@@ -140,7 +172,7 @@ int device_cus();
 // ---------------------------------------------------------------- elementwise
 // out[n, D] (dtype) = RMSNorm(h) * (1 + scale) + shift  (shift/scale NULL: plain RMSNorm)
 hipError_t rmsnorm_mod(int dtype, const float* h, int n, int D, const float* shift,
-                       const float* scale, float eps, void* out, hipStream_t s);
+                       const float* scale, float eps, void* out, hipStream_t s, const hipEvent_t* ev = nullptr);
 
 // Per-head QK-norm (+ optional 3D RoPE) and K/V repacking.
 //   q_in/k_in/v_in: [n, ld_in] dtype (any may be NULL); gq/gk [dh] dtype.
@@ -169,7 +201,8 @@ bool patch_embed_fits(int dtype, int c_p, int c_c, int N);
 // fp32.  final_layer_fits: the shapes it takes (bf16, c_p = 64, D in 256/512/1024/1536).
 bool final_layer_fits(int dtype, int D, int c_p);
 hipError_t final_layer(const float* h, int n, int D, const float* shift, const float* scale, float eps,
-                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s);
+                       const void* W, const void* b, float dt, float* x, float* v_out, hipStream_t s,
+                       const hipEvent_t* ev = nullptr);
 hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
                        RopeGrid g, const void* W, const void* bias, float* out, int N, hipStream_t s);
 

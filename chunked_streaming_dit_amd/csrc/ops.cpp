@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -42,6 +43,8 @@ int gemm_args(int dtype, const void* A, const void* W, const void* b, int M, int
   if (M < 0 || N < 1 || K < 1) return fail(DIT_ESHAPE, "M=%d N=%d K=%d", M, N, K);
   if (K % 64) return fail(DIT_ESHAPE, "K=%d must be a multiple of 64", K);
   if (N % 4) return fail(DIT_ESHAPE, "N=%d must be a multiple of 4", N);
+  if ((long long)M * K >= GEMM_MAX_ELEMS || (long long)N * K >= GEMM_MAX_ELEMS)
+    return fail(DIT_ESHAPE, "M=%d N=%d K=%d: each operand must hold fewer than 2^31 elements", M, N, K);
   return DIT_OK;
 }
 
@@ -133,10 +136,15 @@ int ditk_attention_probs(int H, const void* q, int nq, const void* k, int n, int
                 "short_attention_probs");
 }
 
-int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
-                   const void* const* k, const void* const* vt, const int* n, const int* cap,
-                   int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
-                   const void* gk, double q_fold, void* o, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch of ditk_attention.
+int attention_entry(int dtype, int dh, int H, const void* q, int nq, int nseg, const void* const* k,
+                    const void* const* vt, const int* n, const int* cap, int nsplit, float* partial,
+                    int unsplit_rows, int q_prescaled, const void* gq, const void* gk,
+                    double q_fold, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if ((gq != nullptr) != (gk != nullptr)) return fail(DIT_EINVAL, "gq and gk must both be given or both NULL");
   if (gq && !(q_fold > 0 && std::isfinite(q_fold))) return fail(DIT_EINVAL, "q_fold must be finite and > 0");
@@ -150,6 +158,8 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
     if (n[i] < 0 || cap[i] % 64 || cap[i] < (n[i] + 63) / 64 * 64)
       return fail(DIT_ESHAPE, "segment %d: n=%d cap=%d", i, n[i], cap[i]);
     if (n[i] > 0 && (!k[i] || !vt[i])) return fail(DIT_EINVAL, "segment %d NULL", i);
+    if ((long long)H * dh * cap[i] * (dtype == DIT_BF16 ? 2 : 4) >= VT_MAX_BYTES)
+      return fail(DIT_ESHAPE, "segment %d: V^T [%d, %d] must stay under 2^31 bytes", i, H * dh, cap[i]);
     seg[i] = AttnSeg{k[i], vt[i], n[i], cap[i]};
     total += n[i];
   }
@@ -159,9 +169,9 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
     return fail(DIT_EINVAL, "unsplit_rows=%d: must be >= 0 and a multiple of %d or >= nq=%d", unsplit_rows,
                 ATTN_QTILE, nq);
   if (unsplit_rows >= nq) nsplit = 1;  // nothing left to split
+  const int D = H * dh;
   if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   if (nq == 0) return DIT_OK;
-  const int D = H * dh;
   if (nsplit == 1 && short_attention_fits(dtype, dh, nseg, seg))
     return hipchk(short_attention(dh, H, q, D, o, D, nq, seg[0], q_prescaled != 0, (hipStream_t)stream),
                   "short_attention");
@@ -172,6 +182,18 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                   "attention");
   if (rc) return rc;
   return hipchk(attention_combine(dtype, dh, H, nq, sp, o, D, (hipStream_t)stream), "attention_combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
+                   const void* const* k, const void* const* vt, const int* n, const int* cap,
+                   int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
+                   const void* gk, double q_fold, void* o, void* stream) {
+  return attention_entry(dtype, dh, H, q, nq, nseg, k, vt, n, cap, nsplit, partial, unsplit_rows,
+                         q_prescaled, gq, gk, q_fold, o, stream);
 }
 
 int ditk_modulation(int dtype, int D, int L, double t, const void* const* w, float* mod_out,
@@ -205,6 +227,25 @@ int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* con
   RopeGrid g{grid.t0, grid.frames, grid.h, grid.w};
   return hipchk(patch_input(dtype, x, n, c_p, cond, c_c, cond_mode, g, xin, (hipStream_t)stream),
                 "patch_input");
+}
+
+static_assert(DITK_PROBE_SINK_FLOATS == PROBE_SINK_FLOATS, "probe sink size");
+
+int ditk_probe_mfma(const void* data, int iters, float* sink, long long sink_floats, double* flop,
+                    void* stream) {
+  if (!data || !sink || !flop) return fail(DIT_EINVAL, "NULL argument");
+  if (iters < 1) return fail(DIT_EINVAL, "iters=%d must be >= 1", iters);
+  if (sink_floats < DITK_PROBE_SINK_FLOATS)
+    return fail(DIT_EWORKSPACE, "sink of %lld floats < %d", sink_floats, DITK_PROBE_SINK_FLOATS);
+  return hipchk(probe_mfma(data, iters, sink, flop, (hipStream_t)stream), "probe_mfma");
+}
+
+int ditk_probe_copy(const void* src, void* dst, long long bytes, void* stream) {
+  if (bytes < 0 || bytes % 16) return fail(DIT_EINVAL, "bytes=%lld must be a non-negative multiple of 16", bytes);
+  if (bytes == 0) return DIT_OK;
+  if (!src || !dst) return fail(DIT_EINVAL, "NULL argument");
+  if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return fail(DIT_EINVAL, "src, dst must be 16-byte aligned");
+  return hipchk(probe_copy(src, dst, bytes, (hipStream_t)stream), "probe_copy");
 }
 
 int ditk_patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,

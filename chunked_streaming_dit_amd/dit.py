@@ -136,9 +136,18 @@ class DitChunk:
         self._h = h
 
     def close(self) -> None:
+        """Release the handle.  Teardown order: weight streaming is switched off (its
+        copies finish), the device is synchronised, the handle is destroyed, and only
+        then are the ring and the pinned host blocks released, so that no copy or kernel
+        can still touch memory that is being freed."""
         if getattr(self, "_h", None):
+            if getattr(self, "_stream_keep", None) is not None:
+                C.lib().dit_weight_stream(self._h, None, None, 0, 0)
+            torch.cuda.synchronize(self.device)
             C.lib().dit_destroy(self._h)
             self._h = None
+        self._stream_keep = None
+        self._ring = None
 
     def __del__(self):
         try:
@@ -150,9 +159,11 @@ class DitChunk:
         """Stream the block weights from pinned host tensors (names "blk{l}.<entry>",
         shapes and dtype of the weight table) through a device ring of nslot block slots
         (dit_weight_stream); None switches back to the resident weights."""
-        # work already enqueued may still read the ring (or, on the library's copy
-        # stream, write it) that this call releases; a first ring needs no wait, so the
-        # prefetch of its first blocks overlaps work still running
+        # Work already enqueued may still read the ring (or, on the library's copy
+        # stream, write it) when streaming is switched off or moves to other host
+        # blocks: synchronise first.  The ring itself stays allocated across switches, so
+        # switching streaming on again (the hand-over between two stages) needs no wait
+        # and the prefetch of the first blocks overlaps the work still running.
         if getattr(self, "_stream_keep", None) is not None or host_blocks is None:
             torch.cuda.synchronize(self.device)
         if host_blocks is None:
@@ -172,9 +183,18 @@ class DitChunk:
                 raise ValueError(f"{nm} must be a contiguous pinned host tensor of {dt}")
             keep.append(t)
             ptrs[i] = t.data_ptr()
-        ring = torch.empty(nslot * self.cfg.block_weight_bytes(), dtype=torch.uint8, device=self.device)
+        need = nslot * self.cfg.block_weight_bytes()
+        ring = getattr(self, "_ring", None)
+        if ring is None or ring.numel() < need:
+            # A new ring comes from torch's caching allocator, which may hand back memory
+            # that kernels still enqueued on torch's stream were using; the library's copy
+            # stream would not wait for them, so synchronise once before copying into it.
+            self._ring = None
+            ring = torch.empty(need, dtype=torch.uint8, device=self.device)
+            torch.cuda.synchronize(self.device)
+            self._ring = ring
         C.check(C.lib().dit_weight_stream(self._h, ptrs, ring.data_ptr(), ring.numel(), nslot))
-        self._stream_keep = (keep, ring)
+        self._stream_keep = keep
 
     def ref_kv_precompute(self, ref: torch.Tensor, g: C.DitGrid) -> None:
         _dev(ref, "ref", torch.float32)
@@ -222,15 +242,19 @@ class DitChunk:
         C.check(fn(self._h, x.data_ptr(), _ptr(cond), _ptr(audio), M, g, float(t), float(t_next),
                    _ptr(v_out)))
 
-    def timing_enable(self, on: bool = True) -> None:
-        C.check(C.lib().dit_timing_enable(self._h, 1 if on else 0))
+    def timing_enable(self, on=True) -> None:
+        """Time kernel launches with dispatch-stamped events (dit_timing_enable): True or
+        a mask of 1 << DIT_TIME_* kinds (True: self-attention only); False: none."""
+        mask = (1 if on else 0) if isinstance(on, bool) else int(on)
+        C.check(C.lib().dit_timing_enable(self._h, mask))
 
-    def timing_read(self) -> Tuple[int, float, float]:
-        """(launches, summed ms, summed algorithmic flop) of self-attention since the last read."""
+    def timing_read(self, kind: int = C.DIT_TIME_ATTN) -> Tuple[int, float, float]:
+        """(launches, summed ms, summed work) of a timing kind since the last read: work is
+        algorithmic flop for DIT_TIME_ATTN and DIT_TIME_GEMM, bytes for DIT_TIME_ELEM."""
         n = ctypes.c_int()
         ms = ctypes.c_double()
         fl = ctypes.c_double()
-        C.check(C.lib().dit_timing_read(self._h, C.DIT_TIME_ATTN, ctypes.byref(n), ctypes.byref(ms),
+        C.check(C.lib().dit_timing_read(self._h, int(kind), ctypes.byref(n), ctypes.byref(ms),
                                         ctypes.byref(fl)))
         return n.value, ms.value, fl.value
 

@@ -21,9 +21,17 @@ def chunk_config(cfg, max_tokens=None, max_ref=None, max_bnd=None, max_audio=Non
                        eps=cfg.eps, rope_theta=cfg.rope_theta)
 
 
-def upload_weights(P: Dict[str, np.ndarray], dtype: str, device) -> Dict[str, torch.Tensor]:
-    """float32 arrays (bf16-exact for bf16 workloads) -> device tensors of the compute dtype."""
+def upload_weights(P, dtype: str, device) -> Dict[str, torch.Tensor]:
+    """float32 arrays (bf16-exact for bf16 workloads) -> device tensors of the compute dtype.
+    A mapping that holds bf16 bit patterns (``bits``: name -> uint16 array) is uploaded
+    as those bits."""
     td = torch_dtype(dtype)
+    bits = getattr(P, "bits", None)
+    if bits is not None:
+        if td != torch.bfloat16:
+            raise ValueError("bf16 bit patterns need the bf16 compute dtype")
+        return {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).to(device).view(torch.bfloat16)
+                for k, v in bits.items()}
     return {k: torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device).to(td)
             for k, v in P.items()}
 

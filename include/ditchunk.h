@@ -155,7 +155,13 @@ enum {
 /* Number of entries of the weight table for this config (0 if the config is invalid). */
 int dit_weight_count(const dit_config* cfg);
 
-/* Bytes of the resident state: per block, K and V of max_ref reference tokens, of
+/* Capacity limit (checked with the config): the kernels address activation and V^T
+ * buffers with 32-bit offsets, so the token capacity cap = max(max_tokens, max_ref,
+ * max_bnd) rounded up to 64 must keep [cap, max(3 D, mlp_ratio D)] under 2^31 elements
+ * and [D, cap] of the dtype under 2^31 bytes (e.g. cap < 174763 at D = 3072, mlp_ratio 4);
+ * a larger config is invalid (DIT_EINVAL from dit_create, 0 from the size queries).
+ *
+ * Bytes of the resident state: per block, K and V of max_ref reference tokens, of
  * max_bnd boundary tokens, of max_bnd interpolation-anchor tokens and (d_a > 0) of
  * max_audio audio tokens (each rounded up to 64 tokens); (d_a > 0) the held audio
  * features [max_audio rounded up to 64, d_a]; for bf16 with dh = 128 and max_audio <= 64
@@ -206,9 +212,12 @@ int dit_destroy(dit_handle* h);
  * current block computes; with nslot == L every block is copied once and stays.  The
  * global weight entries stay as given to dit_create, and results equal those of the
  * resident table bit for bit.
- * The call itself starts copying the first nslot blocks at once, so enabling streaming
- * while earlier passes still run (on the resident weights, or another model) overlaps
- * the transfer with them; the ring must therefore not be read by work still enqueued.
+ * The call itself starts copying the first nslot blocks at once, on the copy stream,
+ * without waiting for the handle's stream, so enabling streaming while earlier passes
+ * still run (on the resident weights, or another model) overlaps the transfer with
+ * them; the ring's memory must therefore not be read or written by any work still
+ * enqueued (on any stream) when the call is made, e.g. a ring freshly taken from a
+ * stream-ordered allocator is safe only after that allocator's pending work is done.
  * dit_weight_stream(h, NULL, NULL, 0, 0) switches back to the table of dit_create.
  * Before freeing the ring or the host memory, synchronise the device (the copies run
  * on the library's stream).  After a call that failed with DIT_EHIP the next pass
@@ -319,17 +328,29 @@ int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_st
 /* Message of the last failure on this thread ("" if none). */
 const char* dit_last_error(void);
 
-/* Kernel timing on the handle's stream.  While enabled, the self-attention kernel of
- * each attention launch of dit_chunk_step, ref_kv_precompute, boundary_kv_carry and
- * interp_anchor_kv is timed by a pair of HIP events that its dispatch stamps with the
- * kernel's start and end (hipExtLaunchKernel: no marker packets between launches;
- * events created lazily, at most 4096 pairs per window).
- * dit_timing_read synchronises those events and returns the count and the summed
- * milliseconds of the window, then opens a new window.
- * kind: DIT_TIME_ATTN (self-attention launches). */
-enum { DIT_TIME_ATTN = 0, DIT_TIME_KINDS };
+/* Kernel timing on the handle's stream.  While a kind is enabled, each of its launches is
+ * timed by a pair of HIP events that the dispatches themselves stamp with the kernels'
+ * start and end (hipExtLaunchKernel: no marker packets between launches), at most 4096
+ * pairs per window:
+ *   DIT_TIME_ATTN  the self-attention of every pass (dit_chunk_step, ref_kv_precompute,
+ *                  boundary_kv_carry, interp_anchor_kv), from the start of the main
+ *                  kernel to the end of the merge of its key-range parts when the launch
+ *                  is split; work = the method's 4 n_q n_kv D flop;
+ *   DIT_TIME_GEMM  the Linears of the blocks (QKV with its QK-norm/RoPE epilogue,
+ *                  out-projection, cross-attention q and out, MLP in and out, each with
+ *                  its fused epilogue); work = 2 M N K flop;
+ *   DIT_TIME_ELEM  the RMSNorm (+ adaLN) passes and the final layer (norm, Linear and
+ *                  Euler update); work = the bytes they must move (fp32 h read, their
+ *                  outputs written, x read and written, weights and vectors).
+ * dit_timing_enable(h, mask): bit k of mask enables kind k (1: self-attention only; 0:
+ * none) and opens a new window; it creates the events (once per kind), so a timed region
+ * that follows does not include their creation.
+ * dit_timing_read(h, kind, ...) synchronises that kind's events and returns its launch
+ * count, summed milliseconds and summed work, then opens a new window for that kind.
+ * Errors: EINVAL (NULL handle or output, mask or kind out of range), EHIP. */
+enum { DIT_TIME_ATTN = 0, DIT_TIME_GEMM = 1, DIT_TIME_ELEM = 2, DIT_TIME_KINDS };
 int dit_timing_enable(dit_handle* h, int enable);
-int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_flop);
+int dit_timing_read(dit_handle* h, int kind, int* count, double* total_ms, double* total_work);
 
 #ifdef __cplusplus
 }

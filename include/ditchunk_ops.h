@@ -26,7 +26,8 @@ enum { DITK_ACT_NONE = 0, DITK_ACT_GELU = 1, DITK_OUT_F32 = 2 };
 /* out[M, N] = act(A W^T + b): A [M, K], W [N, K], b [N] (dtype).  act DITK_ACT_NONE
  * or DITK_ACT_GELU (tanh form) store dtype; DITK_OUT_F32 stores fp32 without
  * activation.  The Linear layers of the DiT block (QKV, cross q/k/v, FC1, patch embed).
- * K must be a multiple of 64; N a multiple of 4. */
+ * K must be a multiple of 64; N a multiple of 4; A [M, K] and W [N, K] must each hold
+ * fewer than 2^31 elements (32-bit operand offsets); DIT_ESHAPE otherwise. */
 int ditk_linear(int dtype, const void* A, const void* W, const void* b, int M, int N, int K,
                 int act, void* out, void* hip_stream);
 
@@ -64,7 +65,8 @@ int ditk_qknorm_rope(int dtype, int dh, int H, int n, const void* q_in, const vo
 
 /* o[nq, H*dh] = softmax(q k^T / sqrt(dh)) v per head, keys the concatenation of nseg
  * (1..4) segments given in the layout of ditk_qknorm_rope (k[i] [cap[i], H*dh],
- * vt[i] [H*dh, cap[i]], n[i] valid keys).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
+ * vt[i] [H*dh, cap[i]], n[i] valid keys; each V^T must be under 2^31 bytes, DIT_ESHAPE
+ * otherwise).  q [nq, H*dh] (dtype).  fp32 needs dh = 64.
  * nsplit (1..8) splits the key tiles into contiguous parts computed by separate
  * workgroups and merged afterwards; nsplit > 1 needs partial: fp32 scratch of
  * nsplit * nq * (H*dh + 2*H) floats (NULL allowed when nothing is split).
@@ -128,6 +130,25 @@ int ditk_patch_input(int dtype, const float* x, int n, int c_p, const float* con
 int ditk_patch_embed(const float* x, int n, int c_p, const float* cond, int c_c, int cond_mode,
                      dit_grid grid, const void* w, const void* b, float* out, int D,
                      void* hip_stream);
+
+/* Measured ceilings for the roofline figures (the spec peaks assume clocks and power a
+ * real workload may not get):
+ * ditk_probe_mfma: a dense bf16 MFMA loop, no memory traffic, 2 workgroups of 4 waves per
+ *   CU on 256 CUs' worth of workgroups (512), each wave alternating two operand sets with
+ *   unrelated bit patterns over independent accumulators for `iters` iterations.
+ *   data: 4096 bytes of bf16 (device; random values give realistic operand toggling);
+ *   sink: DITK_PROBE_SINK_FLOATS floats (device, written); *flop (host): the MFMA flop
+ *   the launch performs.  Time it on the stream to get the sustained MFMA rate.
+ * ditk_probe_copy: dst[0, bytes) = src[0, bytes), a plain grid-stride 16-byte copy
+ *   (bytes a multiple of 16, both 16-byte aligned); with a buffer far larger than the
+ *   caches it measures sustained HBM bandwidth (2 x bytes moved), and with a known size
+ *   it calibrates the HBM traffic counters.
+ * Errors: EINVAL (NULL, iters < 1, bad size or alignment), EWORKSPACE (sink too small),
+ * EHIP. */
+#define DITK_PROBE_SINK_FLOATS (512 * 256)
+int ditk_probe_mfma(const void* data, int iters, float* sink, long long sink_floats, double* flop,
+                    void* hip_stream);
+int ditk_probe_copy(const void* src, void* dst, long long bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

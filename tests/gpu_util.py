@@ -1,7 +1,22 @@
-"""Shared helpers of the GPU tests: device, uploads, the parity metric."""
+"""Shared helpers of the GPU tests: device, uploads, the parity metric, the goldens."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name: str):
+    """The oracle's stored values of a full-size workload (tests/golden/<name>.npz, written
+    by tests/golden/make_goldens.py from the oracle alone) and its metadata."""
+    path = os.path.join(GOLDEN_DIR, name + ".npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (python tests/golden/make_goldens.py {name})")
+    d = np.load(path)
+    return {k: d[k] for k in d.files if k != "meta"}, json.loads(str(d["meta"]))
 
 
 def device():

@@ -76,6 +76,49 @@ def test_bad_config_rejected(field, value):
     assert C.last_error()
 
 
+@pytest.mark.parametrize("D,H,mlp,max_tokens", [(4096, 32, 8, 70000), (3072, 24, 4, 180000),
+                                                 (4096, 32, 4, 140000)])
+def test_config_beyond_32bit_operand_offsets_rejected(D, H, mlp, max_tokens):
+    """A token capacity whose activations [cap, max(3D, mlp D)] reach 2^31 elements, or
+    whose V^T [D, cap] reaches 2^31 bytes, is an error (the kernels address those
+    operands with 32-bit offsets); the large chunk's own capacity is accepted."""
+    cs = _cs(5, D=D, H=H, mlp_ratio=mlp, max_tokens=max_tokens)
+    assert C.lib().dit_state_bytes(ctypes.byref(cs)) == 0
+    assert "2^31" in C.last_error()
+    ok = _cs(5)
+    assert C.lib().dit_state_bytes(ctypes.byref(ok)) > 0
+    ok.max_tokens = 65536
+    assert C.lib().dit_workspace_bytes(ctypes.byref(ok)) > 0
+
+
+def test_ops_beyond_32bit_operand_offsets_rejected():
+    lib = C.lib()
+    # A [M, K] of 2^31 elements
+    assert lib.ditk_linear(C.DIT_BF16, FAKE, FAKE, FAKE, 1 << 18, 256, 8192, 0, FAKE, None) == C.DIT_ESHAPE
+    assert lib.ditk_linear_residual(C.DIT_BF16, FAKE, FAKE, FAKE, None, 1 << 18, 256, 8192, FAKE, None, 0,
+                                    None) == C.DIT_ESHAPE
+    # V^T [H*dh, cap] of 2^31 bytes
+    P = ctypes.c_void_p
+    k = (P * 1)(FAKE)
+    n = (ctypes.c_int * 1)(1 << 19)
+    cap = (ctypes.c_int * 1)(1 << 19)
+    rc = lib.ditk_attention(C.DIT_BF16, 128, 16, FAKE, 256, 1, k, k, n, cap, 1, None, 0, 1, None, None, 0.0,
+                            FAKE, None)
+    assert rc == C.DIT_ESHAPE and "2^31" in C.last_error()
+
+
+def test_probe_validation():
+    lib = C.lib()
+    fl = ctypes.c_double()
+    assert lib.ditk_probe_mfma(None, 10, FAKE, C.DITK_PROBE_SINK_FLOATS, ctypes.byref(fl), None) == C.DIT_EINVAL
+    assert lib.ditk_probe_mfma(FAKE, 0, FAKE, C.DITK_PROBE_SINK_FLOATS, ctypes.byref(fl), None) == C.DIT_EINVAL
+    assert lib.ditk_probe_mfma(FAKE, 10, FAKE, C.DITK_PROBE_SINK_FLOATS - 1, ctypes.byref(fl),
+                               None) == C.DIT_EWORKSPACE
+    assert lib.ditk_probe_copy(FAKE, FAKE, 24, None) == C.DIT_EINVAL
+    assert lib.ditk_probe_copy(FAKE + 8, FAKE, 32, None) == C.DIT_EINVAL
+    assert lib.ditk_probe_copy(None, None, 0, None) == C.DIT_OK
+
+
 def _handle(cid=1):
     cs = _cs(cid)
     lib = C.lib()

@@ -1,18 +1,21 @@
 """Parity and properties at the workloads' full sizes, through the C ABI.
 
-- Streaming sequence (6 chunks of the base shape): oracle parity of the first
-  step of chunk 0 (no boundary) and of chunk 1 (boundary K/V carried from the GPU's
-  chunk-0 latent); a resumed handle reproduces a chunk bit for bit; device memory
-  does not grow with the number of chunks.
-- The base chunk job exactly as the benchmark launches it (4 blocks, modulation table,
-  held audio K/V, 8 steps): the first step's velocity on all 7800 tokens against the
-  oracle, and the job repeated bit for bit.
-- Super-resolution and large base chunks: the launch shapes of the full workloads
-  (tokens, keys, hidden size, heads, audio) with one block, the oracle evaluated on
-  sampled query rows (first, last and ragged-tail tiles plus random rows); and the
-  full-depth models run end to end with a zero final projection, where the velocity
-  must equal the final bias exactly (closed-form Euler trajectory), and repeat
-  bit for bit.
+Full depth against the oracle's stored values (tests/golden/<workload>.npz, written by
+tests/golden/make_goldens.py from the float64 oracle alone), on the sampled token rows
+stored with them (the first 64 rows, the last 64, 256 seeded ones):
+- base low-res chunk, run exactly as the benchmark launches it (4 blocks, modulation
+  table, reference and boundary passes, held audio K/V): v of all 8 steps and dx; the
+  first step's v also on all 7800 tokens against the live oracle; the job repeated bit
+  for bit;
+- streaming sequence (6 chunks of the base shape, each boundary from the GPU's own
+  previous chunk): every chunk's first- and last-step v and dx; a resumed handle
+  reproduces a chunk bit for bit; device memory does not grow with the chunks;
+- super-resolution chunk (2 blocks, 4 steps): v of every step and dx;
+- large base chunk (30 blocks, hidden 3072, one step): v and dx, with the launch
+  sequence of the benchmark (held audio K/V).
+Also: one block at each workload's full launch shape with the oracle on sampled query
+rows, the interpolation and boundary-by-reuse chunks at the base shape, and the
+full-depth models with a zero final projection (closed-form velocity).
 Tolerance as elsewhere: max-abs-normalised error <= 2e-2 for bf16.
 """
 import dataclasses
@@ -24,7 +27,7 @@ import torch
 import oracle as O
 import synth
 from synth import Grid
-from tests.gpu_util import TOL, device, rel_err, run_standalone_gpu, to_np
+from tests.gpu_util import TOL, device, golden, rel_err, run_standalone_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -35,9 +38,9 @@ def _handle(cfg, P, dev):
     return DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
 
 
-def _run_chunk(h, cfg, x, audio, prev, v0=None):
+def _run_chunk(h, cfg, x, audio, prev, v0=None, v_last=None):
     """Boundary from prev (None: first chunk), then the chunk's Euler steps on x in
-    place; v0 (optional) receives the first step's velocity."""
+    place; v0 / v_last (optional) receive the first / last step's velocity."""
     from chunked_streaming_dit_amd.workload import grid_of
     g = cfg.chunk
     if prev is None:
@@ -46,28 +49,40 @@ def _run_chunk(h, cfg, x, audio, prev, v0=None):
         h.boundary_kv_carry(prev, grid_of(g))
     ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
     for k in range(cfg.steps):
-        h.step(x, ts[k], ts[k + 1], grid_of(g), audio=audio, v_out=v0 if k == 0 else None)
+        v = v0 if k == 0 else (v_last if k == cfg.steps - 1 else None)
+        h.step(x, ts[k], ts[k + 1], grid_of(g), audio=audio, v_out=v)
+
+
+def _check_rows(what, gpu_rows, want, tol):
+    """max-abs-normalised error of sampled rows against the stored oracle values."""
+    err = rel_err(gpu_rows, want)
+    print(f"{what}: err {err:.2e}")
+    assert err <= tol, (what, err)
+    return err
 
 
 def test_config3_stream_full_size():
     from chunked_streaming_dit_amd.workload import f32, grid_of
     dev = device()
+    gold, _ = golden("stream")
+    rows = gold["rows"]
     cfg = synth.STREAM_6_CHUNKS
     g = cfg.chunk
-    P = synth.make_weights(cfg)
+    P = synth.make_weights(cfg, threads=16)
     chunks = [synth.make_inputs(cfg, c) for c in range(cfg.n_chunks)]
     h = _handle(cfg, P, dev)
     # every device buffer of the session exists before the first chunk
     xs = [f32(inp["x_init"], dev) for inp in chunks]
     auds = [f32(inp["audio"], dev) for inp in chunks]
-    v_first = [torch.empty_like(xs[0]) for _ in range(2)]
+    v_first = [torch.empty_like(xs[0]) for _ in range(cfg.n_chunks)]
+    v_last = [torch.empty_like(xs[0]) for _ in range(cfg.n_chunks)]
     x_resume = f32(chunks[3]["x_init"], dev)
     h.ref_kv_precompute(f32(chunks[0]["ref"], dev), grid_of(cfg.ref))
     torch.cuda.synchronize()
     mem = []
     prev = None
     for c in range(cfg.n_chunks):
-        _run_chunk(h, cfg, xs[c], auds[c], prev, v_first[c] if c < 2 else None)
+        _run_chunk(h, cfg, xs[c], auds[c], prev, v_first[c], v_last[c])
         torch.cuda.synchronize()
         mem.append((torch.cuda.memory_allocated(dev), torch.cuda.max_memory_allocated(dev)))
         prev = xs[c]
@@ -83,30 +98,25 @@ def test_config3_stream_full_size():
     torch.cuda.synchronize()
     assert torch.equal(x_resume, xs[3])
 
-    # oracle: first step of chunk 0 (reference only) and of chunk 1 (boundary from the
-    # GPU's chunk-0 final latent)
-    pos = O.grid_positions(0, g.frames, g.h, g.w)
-    ref_kv = O.ref_context(P, cfg, chunks[0]["ref"], cfg.ref)
-    vo0 = O.dit_velocity(P, cfg, chunks[0]["x_init"], cfg.t_start, pos, [[kv] for kv in ref_kv],
-                         chunks[0]["audio"])
-    e0 = rel_err(to_np(v_first[0]), vo0)
-    x0_gpu = to_np(xs[0])
-    bkv = O.bnd_context(P, cfg, ref_kv, O.last_frame(x0_gpu, g.frames, g.h, g.w), g.h, g.w)
-    vo1 = O.dit_velocity(P, cfg, chunks[1]["x_init"], cfg.t_start, pos,
-                         [[ref_kv[l], bkv[l]] for l in range(cfg.L)], chunks[1]["audio"])
-    e1 = rel_err(to_np(v_first[1]), vo1)
-    print(f"stream: chunk0 v err {e0:.2e}, chunk1 v err {e1:.2e}")
-    assert e0 <= TOL["bf16"] and e1 <= TOL["bf16"], (e0, e1)
+    # every chunk against the oracle's stream (whose boundaries are its own chunks' finals)
+    tol = TOL["bf16"]
+    for c in range(cfg.n_chunks):
+        _check_rows(f"stream chunk {c} first-step v", to_np(v_first[c])[rows], gold["v_first"][c], tol)
+        _check_rows(f"stream chunk {c} last-step v", to_np(v_last[c])[rows], gold["v_last"][c], tol)
+        dx = to_np(xs[c]) - chunks[c]["x_init"].astype(np.float64)
+        _check_rows(f"stream chunk {c} dx", dx[rows], gold["dx"][c], tol)
 
 
-def test_bench_launch_configuration_first_step():
-    """The base chunk job exactly as bench.py runs it (4 blocks, modulation table for the
-    schedule and t = 0, reference and boundary passes, held audio K/V, 8 Euler steps):
-    the first step's velocity on every token against the oracle, and the whole job's
-    result repeatable bit for bit."""
+def test_base_chunk_as_benchmarked():
+    """The base chunk job exactly as bench.py --workload base runs it (4 blocks, modulation
+    table for the schedule and t = 0, reference and boundary passes, held audio K/V, 8
+    Euler steps): every step's velocity and dx on the stored sampled rows, the first step's
+    velocity on every token against the live oracle, and the job repeatable bit for bit."""
     from chunked_streaming_dit_amd import AUDIO_HELD
     from chunked_streaming_dit_amd.workload import f32, grid_of
     dev = device()
+    gold, _ = golden("base")
+    rows = gold["rows"]
     cfg = synth.BASE_CHUNK
     g = cfg.chunk
     P = synth.make_weights(cfg, threads=16)
@@ -114,7 +124,7 @@ def test_bench_launch_configuration_first_step():
     h = _handle(cfg, P, dev)
     ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / cfg.steps for k in range(cfg.steps + 1)]
     ref, bnd, audio = f32(inp["ref"], dev), f32(inp["bnd"], dev), f32(inp["audio"], dev)
-    v0 = torch.empty((cfg.N, cfg.C_p), device=dev)
+    vs = [torch.empty((cfg.N, cfg.C_p), device=dev) for _ in range(cfg.steps)]
     xs = []
     for rep in range(2):
         h.modulation_table(ts[:-1] + [0.0])
@@ -123,19 +133,70 @@ def test_bench_launch_configuration_first_step():
         h.audio_kv_precompute(audio)
         x = f32(inp["x_init"], dev)
         for k in range(cfg.steps):
-            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=AUDIO_HELD, v_out=v0 if k == 0 and rep == 0 else None)
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=AUDIO_HELD, v_out=vs[k] if rep == 0 else None)
         torch.cuda.synchronize()
         xs.append(to_np(x))
     h.close()
     assert np.array_equal(xs[0], xs[1])
     assert np.isfinite(xs[0]).all()
+    tol = TOL["bf16"]
+    for k in range(cfg.steps):
+        _check_rows(f"base chunk step {k} v", to_np(vs[k])[rows], gold["v"][k], tol)
+    _check_rows("base chunk dx", (xs[0] - inp["x_init"])[rows], gold["dx"], tol)
     ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
     bkv = O.bnd_context(P, cfg, ref_kv, inp["bnd"], cfg.bnd.h, cfg.bnd.w)
     vo = O.dit_velocity(P, cfg, inp["x_init"], ts[0], O.grid_positions(0, g.frames, g.h, g.w),
                         [[ref_kv[l], bkv[l]] for l in range(cfg.L)], inp["audio"])
-    err = rel_err(to_np(v0), vo)
-    print(f"bench launch configuration: first-step v err {err:.2e} over {cfg.N} tokens")
-    assert err <= TOL["bf16"], err
+    _check_rows(f"base chunk first-step v over all {cfg.N} tokens (live oracle)", to_np(vs[0]), vo, tol)
+
+
+def test_super_res_full_depth_trajectory():
+    """The super-resolution chunk at full size and depth (31200 tokens conditioned on the
+    nearest-2x upsampled low-resolution latent, keys 6240 + 6240 + 31200, 2 blocks, 4
+    Euler steps 1 -> 0): every step's velocity and dx on the stored sampled rows."""
+    dev = device()
+    gold, _ = golden("sr")
+    rows = gold["rows"]
+    cfg = synth.SUPER_RES
+    P = synth.make_weights(cfg, threads=16)
+    inp = synth.make_inputs(cfg, 0)
+    x, vs, h = run_standalone_gpu(cfg, P, inp, dev)
+    h.close()
+    tol = TOL["bf16"]
+    for k in range(cfg.steps):
+        _check_rows(f"super-resolution step {k} v", vs[k][rows], gold["v"][k], tol)
+    _check_rows("super-resolution dx", (x - inp["x_init"])[rows], gold["dx"], tol)
+
+
+@pytest.mark.timeout(600)
+def test_large_chunk_full_depth_step():
+    """The large base chunk at full size and depth (32760 tokens, keys 1560 + 1560 +
+    32760, 200 audio tokens, 30 blocks, hidden 3072, 24 heads), with the benchmark's
+    launch sequence (reference and boundary passes, the chunk's audio K/V held, one
+    step 1 -> 0.875): v and dx on the stored sampled rows.  The weights are the seeded
+    catalogue's (10.5 GB of bf16, generated on the host)."""
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    gold, _ = golden("large")
+    rows = gold["rows"]
+    cfg = synth.LARGE_CHUNK
+    P = synth.make_weights(cfg, threads=16, compact=True)
+    inp = synth.make_inputs(cfg, 0)
+    W = upload_weights(P, cfg.dtype, dev)
+    del P
+    h = DitChunk(chunk_config(cfg), W, dev)
+    h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+    h.audio_kv_precompute(f32(inp["audio"], dev))
+    x = f32(inp["x_init"], dev)
+    v = torch.empty_like(x)
+    h.step(x, cfg.t_start, cfg.t_end, grid_of(cfg.chunk), audio=AUDIO_HELD, v_out=v)
+    torch.cuda.synchronize()
+    h.close()
+    tol = TOL["bf16"]
+    _check_rows("large chunk v", to_np(v)[rows], gold["v"][0], tol)
+    _check_rows("large chunk dx", (to_np(x) - inp["x_init"])[rows], gold["dx"], tol)
 
 
 def _sample_rows(n, seed):

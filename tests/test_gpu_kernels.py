@@ -71,6 +71,60 @@ def test_linear_residual(dtype, M, N, K, ws, gated):
     assert rel_err(to_np(h) - h0, ref - h0) <= TOL[dtype] / 4
 
 
+def _rows(M, seed):
+    r = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(64), np.arange(M - 64, M), r.choice(M, 384, replace=False)]))
+
+
+# The block Linears at the workloads' launch shapes: these grids take the LDS-staged
+# large-tile kernel (256/192/128 x 256 tiles) with each fused epilogue.  Rows are
+# independent, so the oracle runs on sampled rows (first and last 64 and 384 more).
+@pytest.mark.parametrize("M,N,K,act", [
+    (7800, 4608, 1536, 0),    # base chunk QKV (bias)
+    (7800, 6144, 1536, 1),    # base chunk MLP in (GELU)
+    (7800, 1536, 1536, 2),    # fp32 output
+    (32760, 9216, 3072, 0),   # large chunk QKV
+    (32760, 12288, 3072, 1),  # large chunk MLP in
+    (31200, 6144, 1536, 1)])  # super-resolution MLP in
+def test_linear_large_tiles(M, N, K, act):
+    dev = device()
+    r = np.random.default_rng(M + N + K + act)
+    A, W, b = _arr(r, (M, K), "bf16"), _arr(r, (N, K), "bf16", K ** -0.5), _arr(r, (N,), "bf16", 0.5)
+    out = torch.empty((M, N), device=dev, dtype=torch.float32 if act == 2 else torch.bfloat16)
+    ops.linear(_dev(A, "bf16", dev), _dev(W, "bf16", dev), _dev(b, "bf16", dev), act, out, "bf16")
+    rows = _rows(M, N)
+    ref = O.linear(A[rows].astype(np.float64), W.astype(np.float64), b.astype(np.float64))
+    if act == 1:
+        ref = O.gelu_tanh(ref)
+    torch.cuda.synchronize()
+    err = rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), ref)
+    print(f"linear {M}x{N}x{K} act {act}: err {err:.2e}")
+    assert err <= TOL["bf16"] / 4
+
+
+@pytest.mark.parametrize("M,N,K", [(7800, 1536, 6144), (7800, 1536, 1536), (32760, 3072, 12288),
+                                   (32760, 3072, 3072)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_linear_residual_large_tiles(M, N, K, gated):
+    """The gated residual Linears (out-projection, MLP out) at the launch shapes of the
+    base and large chunks: unsplit large-tile kernel, residual epilogue."""
+    dev = device()
+    r = np.random.default_rng(M + N + K + gated)
+    A, W, b = _arr(r, (M, K), "bf16"), _arr(r, (N, K), "bf16", K ** -0.5), _arr(r, (N,), "bf16", 0.5)
+    h0 = r.standard_normal((M, N)).astype(np.float32)
+    gate = r.standard_normal(N).astype(np.float32) if gated else None
+    h = torch.from_numpy(h0).to(dev)
+    ops.linear_residual(_dev(A, "bf16", dev), _dev(W, "bf16", dev), _dev(b, "bf16", dev),
+                        None if gate is None else torch.from_numpy(gate).to(dev), h, "bf16")
+    rows = _rows(M, N + K)
+    y = O.linear(A[rows].astype(np.float64), W.astype(np.float64), b.astype(np.float64))
+    upd = y if gate is None else gate * y
+    torch.cuda.synchronize()
+    err = rel_err(to_np(h[torch.from_numpy(rows).to(dev)]) - h0[rows], upd)
+    print(f"linear_residual {M}x{N}x{K} gated {gated}: err {err:.2e}")
+    assert err <= TOL["bf16"] / 4
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("n,D", [(1, 256), (37, 256), (301, 1536), (5, 3072)])
 @pytest.mark.parametrize("mod", [False, True])
@@ -437,3 +491,26 @@ def test_zero_rows(dtype):
     torch.cuda.synchronize()
     assert bool((k == 3.0).all()) and bool((vt == 5.0).all()) and bool((x == 2.0).all())
     assert bool((W == 1.0).all()) and bool((b == 1.0).all())
+
+
+def test_probes():
+    """The measured-ceiling probes: the copy copies (bit for bit, ragged tail included),
+    and the MFMA loop reports its flop and leaves finite sums."""
+    import ctypes
+
+    from chunked_streaming_dit_amd import _lib as C
+    dev = device()
+    st = torch.cuda.current_stream().cuda_stream
+    src = torch.randn(1000003 * 4 + 4, device=dev)
+    dst = torch.zeros_like(src)
+    nbytes = (src.numel() * 4) // 16 * 16
+    C.check(C.lib().ditk_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, st))
+    torch.cuda.synchronize()
+    assert torch.equal(src[:nbytes // 4], dst[:nbytes // 4])
+    data = torch.randn(2048, device=dev).to(torch.bfloat16)
+    sink = torch.full((C.DITK_PROBE_SINK_FLOATS,), float("nan"), device=dev)
+    fl = ctypes.c_double()
+    C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 10, sink.data_ptr(), sink.numel(), ctypes.byref(fl), st))
+    torch.cuda.synchronize()
+    assert fl.value == 512 * 4 * 10 * 2 * 4 * 2.0 * 32 * 32 * 16
+    assert torch.isfinite(sink).all()

@@ -254,6 +254,46 @@ def test_config2_full_size_first_step():
     _check(synth.BASE_CHUNK, steps=1)
 
 
+def test_gemm_and_elementwise_timing_counts_every_launch():
+    """dit_timing kinds DIT_TIME_GEMM and DIT_TIME_ELEM (with DIT_TIME_ATTN on as well):
+    every block Linear and every RMSNorm pass / final layer of the passes is counted with
+    its 2 M N K flop or its bytes, with positive durations; results are unchanged bit for
+    bit.  (MINI_BF16: bf16, dh 128, 7 audio tokens, so the cross-attention is folded:
+    its out-projection has K = H*64; its q Linear carries the softmax epilogue.)"""
+    from chunked_streaming_dit_amd.workload import upload_weights
+    cfg = MINI_BF16
+    dev = device()
+    P = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, 0)
+    W = upload_weights(P, cfg.dtype, dev)
+    x_ref, v_ref, h = run_standalone_gpu(cfg, P, inp, dev, weights=W)
+    h.timing_enable(7)
+    x, vs, _ = run_standalone_gpu(cfg, P, inp, dev, handle=h)
+    n_att = h.timing_read(0)[0]
+    ng, msg, fg = h.timing_read(1)
+    ne, mse, be = h.timing_read(2)
+    h.timing_enable(False)
+    h.close()
+    D, L, F, HK, N = cfg.D, cfg.L, cfg.F, cfg.H * 64, cfg.chunk.n
+    ctx_n = [cfg.ref.n, cfg.bnd.n]
+    # context pass: QKV, out, MLP in, MLP out for blocks 0..L-2, QKV only for the last
+    g_ctx = sum((L - 1) * (2 * n * 3 * D * D + 2 * n * D * D + 4 * n * F * D) + 2 * n * 3 * D * D for n in ctx_n)
+    g_step = L * (2 * N * 3 * D * D + 2 * N * D * D + 2 * N * D * D + 2 * N * D * HK + 4 * N * F * D)
+    assert n_att == 2 * (L - 1) + cfg.steps * L
+    assert ng == 2 * (4 * (L - 1) + 1) + cfg.steps * L * 6
+    assert fg == g_ctx + cfg.steps * g_step
+    elt = 2
+    e_ctx = sum((L - 1) * 2 * (n * D * (4 + elt) + 2 * D * 4) + n * D * (4 + elt) + 2 * D * 4 for n in ctx_n)
+    e_norms = L * (2 * (N * D * (4 + elt) + 2 * D * 4) + N * D * (4 + elt))
+    e_final = N * D * 4 + N * 64 * 4 * 3 + 64 * (D + 1) * elt + 2 * D * 4
+    assert ne == 2 * (2 * (L - 1) + 1) + cfg.steps * (3 * L + 1)
+    assert be == e_ctx + cfg.steps * (e_norms + e_final)
+    assert msg > 0 and mse > 0
+    assert np.array_equal(x, x_ref)
+    for a, b in zip(vs, v_ref):
+        assert np.array_equal(a, b)
+
+
 def test_attention_timing_counts_every_launch():
     """dit_timing: with timing on, every self-attention launch of a chunk (the context
     passes run blocks 0..L-2, the steps all L blocks) is counted with its 4 n_q n_kv D
