@@ -130,8 +130,8 @@ def copy_probe(reps: int = 3) -> None:
 
 def ceilings() -> dict:
     """Measured ceilings on this board, in the same process: the library's dense bf16
-    MFMA loop (operands with changing bits, no memory traffic; about 0.2 s) and its plain
-    copy of 1 GiB (HBM bandwidth, 2 x bytes moved), each timed with HIP events."""
+    MFMA loop (operands with changing bits, no memory traffic) and its plain copy of
+    1 GiB (HBM bandwidth, 2 x bytes moved), each timed with HIP events."""
     import ctypes
 
     import torch
@@ -153,8 +153,10 @@ def ceilings() -> dict:
         b.synchronize()
         return a.elapsed_time(b)
 
-    C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 20000, sink.data_ptr(), sink.numel(), ctypes.byref(flop), st))
-    ms = timed(lambda: C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 400000, sink.data_ptr(), sink.numel(),
+    # about 0.5 s of warm-up, then about 0.5 s timed: long enough for the board's clock
+    # and power management to settle, as it does over the bench's timed steps
+    C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 2000000, sink.data_ptr(), sink.numel(), ctypes.byref(flop), st))
+    ms = timed(lambda: C.check(C.lib().ditk_probe_mfma(data.data_ptr(), 2000000, sink.data_ptr(), sink.numel(),
                                                         ctypes.byref(flop), st)))
     mfma = flop.value / (ms * 1e-3) / 1e12
     nbytes = 1 << 30
@@ -168,12 +170,15 @@ def ceilings() -> dict:
     return {"mfma_bf16_ceiling_tflops": mfma, "hbm_copy_ceiling_gbs": gbs}
 
 
-def _counter_means(path: str, counter: str, match) -> tuple:
+def _counter_means(path: str, counter: str, match, largest_grid: bool = False) -> tuple:
     """(mean counter value, dispatches) over the dispatches of a rocprofv3 counter CSV
-    whose kernel name satisfies match."""
+    whose kernel name satisfies match (largest_grid: only those of the largest grid)."""
     import csv
-    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    if largest_grid and rows:
+        g = max(int(r["Grid_Size"]) for r in rows)
+        rows = [r for r in rows if int(r["Grid_Size"]) == g]
+    vals = [float(r["Counter_Value"]) for r in rows]
     if not vals:
         raise SystemExit(f"bench.py: no {counter} rows matched in {path}")
     return sum(vals) / len(vals), len(vals)
@@ -186,15 +191,21 @@ def _is_self_attention(name: str) -> bool:
     return re.search(r"attn_kernel(<[^<>]*,\s*0>|I\w*Li0EE)", name) is not None
 
 
-def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv) -> dict:
+# The timed region's self-attention launches: the large-chunk bench times only the
+# denoising step's launches (the largest grid; its context passes run before), the base
+# chunk job times its context passes too.
+TRAFFIC_LARGEST_GRID = {"large": True, "base": False}
+
+
+def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, largest_grid=False) -> dict:
     """HBM bytes per self-attention launch from four rocprofv3 --pmc runs (FETCH_SIZE and
     WRITE_SIZE, in KiB per dispatch, over the bench and over copy_probe), each counter
     scaled so that the copy reads COPY_PROBE_BYTES and writes COPY_PROBE_BYTES."""
     kib = COPY_PROBE_BYTES / 1024
     cf, _ = _counter_means(copy_fetch_csv, "FETCH_SIZE", lambda n: "copy" in n.lower())
     cw, _ = _counter_means(copy_write_csv, "WRITE_SIZE", lambda n: "copy" in n.lower())
-    f, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_self_attention)
-    w, nw = _counter_means(write_csv, "WRITE_SIZE", _is_self_attention)
+    f, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_self_attention, largest_grid)
+    w, nw = _counter_means(write_csv, "WRITE_SIZE", _is_self_attention, largest_grid)
     sf, sw = kib / cf, kib / cw
     return {
         "attention_src_sha256_16": _src_hash(ATTN_SRC),
@@ -204,6 +215,7 @@ def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv) -> dict
         "fetch_scale": sf,
         "write_scale": sw,
         "dispatches": [nf, nw],
+        "largest_grid_only": bool(largest_grid),
     }
 
 
@@ -691,7 +703,7 @@ def main() -> int:
     if args.reduce_traffic:
         if args.workload not in TRAFFIC_FILES:
             raise SystemExit(f"bench.py: no traffic file for workload {args.workload}")
-        d = reduce_traffic(*args.reduce_traffic)
+        d = reduce_traffic(*args.reduce_traffic, largest_grid=TRAFFIC_LARGEST_GRID[args.workload])
         with open(TRAFFIC_FILES[args.workload], "w") as fh:
             json.dump(d, fh, indent=1)
             fh.write("\n")

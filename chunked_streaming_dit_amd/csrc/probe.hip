@@ -43,11 +43,23 @@ __global__ __launch_bounds__(64 * PROBE_WAVES) void probe_mfma_kernel(const bf16
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// dst[i] = src[i] over n 16-byte chunks, grid-stride.
+// dst[i] = src[i] over n 16-byte chunks: each thread moves COPY_UNROLL chunks per round
+// (all loads issued before the stores, so that many requests are in flight), grid-stride
+// over rounds; the ragged end is handled one chunk at a time.
+constexpr int COPY_UNROLL = 4;
 __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                          long long n) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+  const long long per_round = (long long)gridDim.x * blockDim.x * COPY_UNROLL;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long full = n / per_round * per_round;
+  for (long long base = 0; base < full; base += per_round) {
+    u32x4 v[COPY_UNROLL];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) v[u] = src[base + t + (long long)u * gridDim.x * blockDim.x];
+#pragma unroll
+    for (int u = 0; u < COPY_UNROLL; ++u) dst[base + t + (long long)u * gridDim.x * blockDim.x] = v[u];
+  }
+  for (long long i = full + t; i < n; i += (long long)gridDim.x * blockDim.x) dst[i] = src[i];
 }
 
 }  // namespace
