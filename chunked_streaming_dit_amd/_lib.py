@@ -78,6 +78,8 @@ _SIGS = {
     "ditk_qknorm_rope": (I, [I, I, I, I, P, P, P, I, P, P, I, DitGrid, Dbl, Dbl, Dbl, P, P, P, I, P]),
     "ditk_attention": (I, [I, I, I, P, I, I, ctypes.POINTER(P), ctypes.POINTER(P),
                            ctypes.POINTER(I), ctypes.POINTER(I), I, P, I, I, P, P, Dbl, P, P]),
+    "ditk_attention_noalloc": (I, [I, I, I, P, I, I, ctypes.POINTER(P), ctypes.POINTER(P),
+                                   ctypes.POINTER(I), ctypes.POINTER(I), I, I, I, P, P, Dbl, P, P]),
     "ditk_attention_probs": (I, [I, P, I, P, I, I, I, P, P]),
     "ditk_modulation": (I, [I, I, I, Dbl, ctypes.POINTER(P), P, P, P, P]),
     "ditk_patch_input": (I, [I, P, I, I, P, I, I, DitGrid, P, P]),

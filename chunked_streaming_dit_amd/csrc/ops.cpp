@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "ditchunk.h"
@@ -140,10 +141,41 @@ int ditk_attention_probs(int H, const void* q, int nq, const void* k, int n, int
 
 namespace {
 
-// Validation and launch of ditk_attention.
+// The allocation-free attention's split scratch: a file-scope device array, one copy per
+// GPU, kept until the process ends.  Host code must not pass `scratch` itself to a kernel
+// (on the host it names a stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr long long NOALLOC_SCRATCH_FLOATS = DITK_NOALLOC_SCRATCH_BYTES / 4;
+__device__ __align__(256) float scratch[NOALLOC_SCRATCH_FLOATS];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the calling thread's current device.
+int scratch_on_current_device(float** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+    return fail(DIT_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DIT_EHIP, "device %d beyond the %d supported", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DIT_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch[dev];
+  return DIT_OK;
+}
+
+// Validation and launch shared by ditk_attention (partial from the caller) and
+// ditk_attention_noalloc (noalloc: the split scratch is the device's `scratch`, taken
+// only after every check has passed, and bounded by its size).
 int attention_entry(int dtype, int dh, int H, const void* q, int nq, int nseg, const void* const* k,
                     const void* const* vt, const int* n, const int* cap, int nsplit, float* partial,
-                    int unsplit_rows, int q_prescaled, const void* gq, const void* gk,
+                    bool noalloc, int unsplit_rows, int q_prescaled, const void* gq, const void* gk,
                     double q_fold, void* o, void* stream) {
   if (!dtype_ok(dtype)) return fail(DIT_EINVAL, "dtype %d", dtype);
   if ((gq != nullptr) != (gk != nullptr)) return fail(DIT_EINVAL, "gq and gk must both be given or both NULL");
@@ -170,8 +202,13 @@ int attention_entry(int dtype, int dh, int H, const void* q, int nq, int nseg, c
                 ATTN_QTILE, nq);
   if (unsplit_rows >= nq) nsplit = 1;  // nothing left to split
   const int D = H * dh;
-  if (nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
+  if (noalloc && nsplit > 1 && (long long)nsplit * nq * (D + 2LL * H) > NOALLOC_SCRATCH_FLOATS)
+    return fail(DIT_EWORKSPACE, "split scratch of %d x %d x (%d + 2 x %d) floats exceeds the %lld of the "
+                "allocation-free scratch", nsplit, nq, D, H, NOALLOC_SCRATCH_FLOATS);
+  if (!noalloc && nsplit > 1 && !partial) return fail(DIT_EINVAL, "partial is NULL with nsplit=%d", nsplit);
   if (nq == 0) return DIT_OK;
+  if (noalloc && nsplit > 1)
+    if (int rc = scratch_on_current_device(&partial)) return rc;
   if (nsplit == 1 && short_attention_fits(dtype, dh, nseg, seg))
     return hipchk(short_attention(dh, H, q, D, o, D, nq, seg[0], q_prescaled != 0, (hipStream_t)stream),
                   "short_attention");
@@ -192,7 +229,15 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    const void* const* k, const void* const* vt, const int* n, const int* cap,
                    int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
                    const void* gk, double q_fold, void* o, void* stream) {
-  return attention_entry(dtype, dh, H, q, nq, nseg, k, vt, n, cap, nsplit, partial, unsplit_rows,
+  return attention_entry(dtype, dh, H, q, nq, nseg, k, vt, n, cap, nsplit, partial, false, unsplit_rows,
+                         q_prescaled, gq, gk, q_fold, o, stream);
+}
+
+int ditk_attention_noalloc(int dtype, int dh, int H, const void* q, int nq, int nseg,
+                           const void* const* k, const void* const* vt, const int* n, const int* cap,
+                           int nsplit, int unsplit_rows, int q_prescaled, const void* gq, const void* gk,
+                           double q_fold, void* o, void* stream) {
+  return attention_entry(dtype, dh, H, q, nq, nseg, k, vt, n, cap, nsplit, nullptr, true, unsplit_rows,
                          q_prescaled, gq, gk, q_fold, o, stream);
 }
 

@@ -91,6 +91,25 @@ int ditk_attention(int dtype, int dh, int H, const void* q, int nq, int nseg,
                    int nsplit, float* partial, int unsplit_rows, int q_prescaled, const void* gq,
                    const void* gk, double q_fold, void* o, void* hip_stream);
 
+/* Allocation-free ditk_attention, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results as ditk_attention, without `partial`; the key-range split's
+ * partials live in a device array of the library, DITK_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per GPU, held until the process ends.  The call allocates and frees nothing.
+ *   - A split (nsplit > 1 with rows to split) needs nsplit * nq * (H*dh + 2*H) floats of
+ *     that array: more is DIT_EWORKSPACE (checked before any HIP call).
+ *   - The array used is the one of the calling thread's current device, whose address is
+ *     looked up on the first call on that device; hip_stream must belong to that device.
+ *   - Every call on one GPU shares the array, which keeps the last call's contents (each
+ *     call writes every partial it reads): calls that can overlap on one GPU (other
+ *     streams, other threads) race; serialise them.
+ * Errors: those of ditk_attention, EWORKSPACE, EHIP (symbol lookup failed). */
+#define DITK_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int ditk_attention_noalloc(int dtype, int dh, int H, const void* q, int nq, int nseg,
+                           const void* const* k, const void* const* vt, const int* n, const int* cap,
+                           int nsplit, int unsplit_rows, int q_prescaled, const void* gq, const void* gk,
+                           double q_fold, void* o, void* hip_stream);
+
 /* The softmax probabilities of one short key segment (bf16, dh = 128, 1..64 keys; the
  * audio cross-attention's shape): p [nq, H*64] (bf16), head h's 64 key columns from
  * h*64, p[i, h*64 + j] = softmax_j(q_i k_j / sqrt(dh)) for j < n and 0 for n <= j < 64.
