@@ -164,6 +164,7 @@ def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
 
 
 QUERY_GROUP = 2048  # query rows per score matrix (bounds memory at full-size workloads)
+HEAD_THREADS = 1    # heads computed concurrently (scripts that run full-size workloads raise it)
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
@@ -171,14 +172,27 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
 
     Every query row is its own softmax over all m keys, so the rows are taken
     QUERY_GROUP at a time: the arithmetic of each row is the same, only the size of
-    the score matrix held at once changes."""
+    the score matrix held at once changes.  Heads are independent; with HEAD_THREADS > 1
+    they are computed by that many threads (one BLAS thread each), with the same
+    arithmetic per head."""
     n, H, dh = q.shape
     out = np.empty((n, H, dh), dtype=np.float64)
-    for hh in range(H):
+
+    def head(hh: int) -> None:
         for r0 in range(0, n, QUERY_GROUP):
             r1 = min(n, r0 + QUERY_GROUP)
             s = (q[r0:r1, hh, :] @ k[:, hh, :].T) / np.sqrt(dh)
             out[r0:r1, hh, :] = softmax(s, axis=1) @ v[:, hh, :]
+
+    if HEAD_THREADS > 1 and H > 1:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1), ThreadPoolExecutor(min(HEAD_THREADS, H)) as ex:
+            list(ex.map(head, range(H)))
+    else:
+        for hh in range(H):
+            head(hh)
     return out
 
 

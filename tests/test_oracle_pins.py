@@ -63,6 +63,20 @@ def test_p2_softmax_rows_sum_to_one_and_match_scipy():
     assert (p >= 0).all()
 
 
+def test_attention_heads_in_threads_and_query_groups_change_nothing(monkeypatch):
+    """The oracle's attention with heads computed by several threads and queries taken in
+    groups smaller than the query count gives the same result as one head and one group
+    at a time (each row's arithmetic is the same)."""
+    r = _rng(5)
+    q, k, v = r.standard_normal((37, 5, 8)), r.standard_normal((23, 5, 8)), r.standard_normal((23, 5, 8))
+    want = O.attention(q, k, v)
+    import oracle.dit as OD
+    monkeypatch.setattr(OD, "HEAD_THREADS", 3)
+    monkeypatch.setattr(OD, "QUERY_GROUP", 8)
+    got = O.attention(q, k, v)
+    assert np.abs(got - want).max() <= 1e-14
+
+
 def test_attention_matches_torch_sdpa_f64():
     r = _rng(3)
     q, k, v = r.standard_normal((6, 3, 4)), r.standard_normal((11, 3, 4)), r.standard_normal((11, 3, 4))
