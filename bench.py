@@ -41,6 +41,8 @@ Other workloads (--workload):
   reuse    base chunk jobs whose boundary is carried by reuse (no boundary pass)
   sr, sr1  super-resolution chunk jobs (31200 tokens, 2 blocks, no audio): boundary
            pass + 4 Euler steps (sr) or one step 1 -> 0 (sr1)
+  tiny     the launch-bound fp32 single-block chunk (128 tokens): one step's latency,
+           eager and replayed from a captured HIP graph (value: the graph's rate)
   wstream  the large-chunk step with the block weights streamed from pinned host memory
            through a 2-slot device ring (dit_weight_stream), with the resident step, the
            first (cold) streamed step and the stage hand-over measured in the same process
@@ -509,6 +511,73 @@ def large_main(args) -> int:
     return 0
 
 
+def tiny_main(args) -> int:
+    """tiny: the launch-bound fp32 single-block workload (128 tokens, hidden 256): one
+    denoising step's latency run eagerly and as a captured HIP graph replayed."""
+    import numpy as np
+    import torch
+
+    import synth
+    from chunked_streaming_dit_amd import DitChunk
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+
+    dev = torch.device("cuda", 0)
+    cfg = synth.TINY_FP32
+    P = synth.make_weights(cfg)
+    inp = synth.make_inputs(cfg, 0)
+    s = torch.cuda.Stream(device=dev)
+    reps = max(args.steps, 1) * 20
+    with torch.cuda.stream(s):
+        h = DitChunk(chunk_config(cfg), upload_weights(P, cfg.dtype, dev), dev)
+        h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+        h.boundary_kv_carry(f32(inp["bnd"], dev), grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w)))
+        audio = f32(inp["audio"], dev)
+        x = f32(inp["x_init"], dev)
+        g_chunk = grid_of(cfg.chunk)
+        t0, t1 = cfg.t_start, cfg.t_end
+
+        def timed(fn):
+            out = []
+            for _ in range(reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(s)
+                fn()
+                b.record(s)
+                out.append((a, b))
+            s.synchronize()
+            return float(np.median([a.elapsed_time(b) for a, b in out])) * 1e3
+
+        step = lambda: h.step(x, t0, t1, g_chunk, audio=audio)  # noqa: E731
+        for _ in range(args.warmup * 20 + 1):
+            step()
+        eager_us = timed(step)
+    s.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup * 20 + 1):
+            graph.replay()
+        graph_us = timed(graph.replay)
+    s.synchronize()
+    if not torch.isfinite(x).all():
+        print("bench.py: non-finite output", file=sys.stderr)
+        return 1
+    workload = ("tiny single-block chunk, fp32: 2x8x8 = 128 latent tokens, keys 64 reference + 32 boundary + "
+                "128 chunk, 16 audio tokens of dim 64, 1 DiT block, hidden 256, 4 heads x 64, MLP 4x, one Euler "
+                "step 0.5 -> 0.45; one bench step = one denoising step (median of "
+                f"{reps} event-timed steps), replayed from a captured HIP graph; the eager latency alongside")
+    line = _line("DiT tiny chunk-step latent tokens/sec (fp32, launch-bound; HIP-graph replay), 1 GPU",
+                 cfg.N / (graph_us * 1e-6), args, graph_us * 1e-3, workload,
+                 {"tokens_per_step": cfg.N, "graph_us_per_step": graph_us, "eager_us_per_step": eager_us,
+                  "graph_speedup": eager_us / graph_us}, 0.0, None)
+    line["dtype"] = "f32"
+    line["roofline"] = None
+    print(json.dumps(line), flush=True)
+    h.close()
+    return 0
+
+
 def stream6_main(args) -> int:
     """stream6: whole 6-chunk streaming sessions of the base chunk shape."""
     import numpy as np
@@ -689,7 +758,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="large",
-                    choices=["large", "base", "stream6", "interp", "reuse", "sr", "sr1", "wstream"],
+                    choices=["large", "base", "stream6", "tiny", "interp", "reuse", "sr", "sr1", "wstream"],
                     help="large: one large-chunk denoising step (default, the headline); base: one base "
                          "chunk job; stream6: whole 6-chunk streaming sessions; see the module docstring")
     ap.add_argument("--copy-probe", action="store_true",
@@ -717,6 +786,8 @@ def main() -> int:
         return large_main(args)
     if args.workload == "stream6":
         return stream6_main(args)
+    if args.workload == "tiny":
+        return tiny_main(args)
     return chunk_main(args)
 
 

@@ -110,12 +110,16 @@ def main() -> int:
     ap.add_argument("--threads", type=int, default=0, help="BLAS threads (0: the library default)")
     ap.add_argument("--head-threads", type=int, default=1,
                     help="attention heads computed concurrently by the oracle (same arithmetic)")
+    ap.add_argument("--query-group", type=int, default=0,
+                    help="query rows per score matrix in the oracle's attention (0: its default)")
     args = ap.parse_args()
     if args.threads:
         from threadpoolctl import threadpool_limits
         threadpool_limits(args.threads)
     import oracle.dit
     oracle.dit.HEAD_THREADS = args.head_threads
+    if args.query_group:
+        oracle.dit.QUERY_GROUP = args.query_group
     out = run(args.workload)
     path = os.path.join(HERE, f"{args.workload}.npz")
     np.savez_compressed(path + ".tmp.npz", **out)
