@@ -37,7 +37,7 @@ __all__ = [
     "context_pass", "dit_velocity", "euler", "schedule", "chunk_denoise",
     "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone", "velocity_rows",
     "first_frame", "anchor_context", "interp_stream",
-    "bnd_reuse_context", "stream_reuse",
+    "bnd_reuse_context", "stream_reuse", "mlp",
 ]
 
 Weights = Dict[str, np.ndarray]
@@ -270,10 +270,22 @@ def block_forward(P: Weights, cfg, l: int, h: np.ndarray, mod: Sequence[np.ndarr
         oc = attention(qc, kc, vc).reshape(h.shape[0], D)
         h = h + linear(oc, W(P, p + "co.w"), W(P, p + "co.b"))
     u = modulate(rms_norm(h, eps), sh2, sc2)
-    y = linear(gelu_tanh(linear(u, W(P, p + "fc1.w"), W(P, p + "fc1.b"))),
-               W(P, p + "fc2.w"), W(P, p + "fc2.b"))
-    h = h + g2 * y
+    h = h + g2 * mlp(u, W(P, p + "fc1.w"), W(P, p + "fc1.b"), W(P, p + "fc2.w"), W(P, p + "fc2.b"))
     return h, k, v
+
+
+MLP_ROW_GROUP = 8192  # token rows per MLP hidden matrix (bounds memory at full-size workloads)
+
+
+def mlp(u: np.ndarray, w1: np.ndarray, b1: np.ndarray, w2: np.ndarray, b2: np.ndarray) -> np.ndarray:
+    """The per-token MLP fc2(GELU(fc1(u))).  Each row is its own computation, so rows
+    are taken MLP_ROW_GROUP at a time: only the size of the hidden matrix held at once
+    changes."""
+    y = np.empty((u.shape[0], w2.shape[0]), dtype=np.float64)
+    for r0 in range(0, u.shape[0], MLP_ROW_GROUP):
+        r1 = min(u.shape[0], r0 + MLP_ROW_GROUP)
+        y[r0:r1] = linear(gelu_tanh(linear(u[r0:r1], w1, b1)), w2, b2)
+    return y
 
 
 # ------------------------------------------------------------------ context K/V passes

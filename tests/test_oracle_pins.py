@@ -77,6 +77,25 @@ def test_attention_heads_in_threads_and_query_groups_change_nothing(monkeypatch)
     assert np.abs(got - want).max() <= 1e-14
 
 
+def test_mlp_row_groups_change_nothing(monkeypatch):
+    """The oracle's MLP taken in row groups smaller than the token count (with a ragged
+    last group) gives the same rows as all rows at once, and both are fc2(GELU(fc1(u)))
+    row by row."""
+    r = _rng(6)
+    u = r.standard_normal((29, 12))
+    w1, b1 = r.standard_normal((20, 12)), r.standard_normal(20)
+    w2, b2 = r.standard_normal((12, 20)), r.standard_normal(12)
+    want = O.mlp(u, w1, b1, w2, b2)
+    import oracle.dit as OD
+    monkeypatch.setattr(OD, "MLP_ROW_GROUP", 8)
+    got = O.mlp(u, w1, b1, w2, b2)
+    assert np.abs(got - want).max() <= 1e-13
+    for i in (0, 7, 8, 28):
+        x = u[i] @ w1.T + b1
+        g = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+        assert np.abs(g @ w2.T + b2 - got[i]).max() <= 1e-12
+
+
 def test_attention_matches_torch_sdpa_f64():
     r = _rng(3)
     q, k, v = r.standard_normal((6, 3, 4)), r.standard_normal((11, 3, 4)), r.standard_normal((11, 3, 4))
