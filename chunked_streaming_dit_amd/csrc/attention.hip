@@ -21,6 +21,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "kernels.h"
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   // interleaves (MFMA, LDS read, VALU), so the VALU softmax of one tile runs under the
   // MFMAs of the other.  For the last tile the scores of a (stale) slot are computed and
   // dropped, which keeps the block free of branches; the slot address stays in LDS.
-  auto body = [&](int t, f32x16 (&S)[2], f32x16 (&Snext)[2]) {
+  auto body = [&](int t, f32x16 (&S)[2], f32x16 (&Snext)[2], auto DIRECT) __attribute__((always_inline)) {
     const bool has2 = t + 2 < total, has3 = t + 3 < total;
     // Every wave has finished iteration t-1 (or the prologue's scores of tile tb), so
     // the slots refilled below are no longer read by anyone.  Each wave's own older
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
           }
       }
     }
-    if (!nomax) {  // uniform branch: the running max and its lazy rescale
+    if (!DIRECT && !nomax) {  // uniform branch: the running max and its lazy rescale
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -375,7 +376,7 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
       V pf;
 #pragma unroll
       for (int j = 0; j < VE; ++j)
-        pf[j] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(S[kb][v * VE + j], a.scale, -ms)));
+        pf[j] = from_f<T>(__builtin_amdgcn_exp2f(DIRECT ? S[kb][v * VE + j] : fmaf(S[kb][v * VE + j], a.scale, -ms)));
       l_run = row_sum_add(pf, l_run);
       const int pos = swz<RBV>(l32, (kb * 32 + v * 2 * VE + lg * VE) * SZ / 16);
       V vf[DB];
@@ -395,12 +396,21 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     walk_next(wc);
     sl = sl1;
   };
-  int t = tb;
-  for (; t + 1 < total; t += 2) {
-    body(t, Sc, Sn);
-    body(t + 1, Sn, Sc);
-  }
-  if (t < total) body(t, Sc, Sn);
+  // DIRECT: no running max and q pre-scaled (scale 1), so each weight is exp2 of the raw
+  // score; the general form's fma(s, scale, -m) would be the identity and is left out
+  // (a quarter of the loop's VALU instructions).
+  auto run = [&](auto DIRECT) __attribute__((always_inline)) {
+    int t = tb;
+    for (; t + 1 < total; t += 2) {
+      body(t, Sc, Sn, DIRECT);
+      body(t + 1, Sn, Sc, DIRECT);
+    }
+    if (t < total) body(t, Sc, Sn, DIRECT);
+  };
+  if (nomax && a.scale == 1.f)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // Normalise and store: lane holds query qrow, dh = 32 d + 8 q + 4 lg + [0, 4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
