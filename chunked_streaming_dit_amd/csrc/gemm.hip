@@ -449,9 +449,12 @@ hipError_t launch_t(const void* A, int lda, const void* W, int ldw, int M, int N
 
 
 // bf16 GEMM for large tiles, 8 waves (2 x 4) per workgroup, 2 waves per SIMD.
-// Global -> LDS moves use direct-to-LDS loads (global_load_lds_dwordx4: each wave
-// instruction fills 1 KB = 8 rows of 128 bytes) into a 2-stage ring of unpadded
-// 128-byte rows.  The 16-byte chunk c of row r sits at chunk position
+// Global -> LDS moves use direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds: each
+// wave instruction fills 1 KB = 8 rows of 128 bytes) into a 2-stage ring of unpadded
+// 128-byte rows.  A and W are addressed through buffer resources (base in scalar
+// registers, 32-bit per-lane offsets, the K step as the scalar offset), which measured
+// 1.5-2% faster than 64-bit per-lane addresses; the resource's range check also turns
+// any stray offset into zeros instead of a fault.  The 16-byte chunk c of row r sits at chunk position
 // c ^ ((r >> 1) & 7), so that an MFMA fragment read (consecutive rows, same chunk)
 // spreads over all 64 LDS banks.  Loads for step k+1 are in flight while step k is
 // multiplied; one barrier per 64-wide K step.  Rows past M or N re-read the last valid
@@ -499,15 +502,19 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     else
       off[j] = (unsigned)(min(n0 + r - BM, N - 1) * ldw + chunk * 8) * 2u;
   }
-  const char* Ab = reinterpret_cast<const char*>(A);
-  const char* Wb = reinterpret_cast<const char*>(W);
+  // Raw buffer resources over A and W (stride 0, size in bytes; the third word 0x00020000
+  // is the gfx9-family format field for untyped dword accesses).
+  const unsigned bytes_a = (unsigned)min((size_t)0xffffffffu, (size_t)M * lda * 2);
+  const unsigned bytes_w = (unsigned)min((size_t)0xffffffffu, (size_t)N * ldw * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)bytes_a, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)bytes_w, 0x00020000);
   auto issue = [&](int stage, int k0) {
     char* dst = smem + stage * STAGE + wave * 8 * 128;
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const char* base = (8 * NW * j < BM ? Ab : Wb) + (size_t)k0 * 2;
-      __builtin_amdgcn_global_load_lds((const void*)(base + off[j]), (void*)(dst + j * NW * 8 * 128), 16, 0, 0);
-    }
+    for (int j = 0; j < NLD; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(8 * NW * j < BM ? ra : rw,
+                                               (__attribute__((address_space(3))) void*)(dst + j * NW * 8 * 128), 16,
+                                               (int)off[j], k0 * 2, 0, 0);
   };
 
   // EPI_PARTIAL stores the raw product of its K part as an fp32 tile of ws
