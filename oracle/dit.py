@@ -37,7 +37,7 @@ __all__ = [
     "context_pass", "dit_velocity", "euler", "schedule", "chunk_denoise",
     "last_frame", "stream", "W", "ref_context", "bnd_context", "standalone", "velocity_rows",
     "first_frame", "anchor_context", "interp_stream",
-    "bnd_reuse_context", "stream_reuse", "mlp",
+    "bnd_reuse_context", "stream_reuse", "mlp", "interp_window", "interp_window_stream",
 ]
 
 Weights = Dict[str, np.ndarray]
@@ -522,6 +522,66 @@ def interp_stream(P: Weights, cfg, n_chunks: Sequence[Dict[str, np.ndarray]],
             ctx = [[ref_kv[l], bkv[l], akv[l]] for l in range(cfg.L)]
             ic = i_chunks[k]
             i_out.append(chunk_denoise(P, cfg, ic["x_init"], ctx, ic.get("audio"), cond_of(ic)))
+    return n_out, i_out
+
+
+def interp_window(P: Weights, cfg, ref_kv, z_prev: np.ndarray, z_next: np.ndarray,
+                  ic: Dict[str, np.ndarray], eps: np.ndarray, record: bool = False):
+    """An I-chunk under the window reading of the anchors [bnd].
+
+    reading (the alternative to anchor_context): the anchors are frames of the I-chunk's
+    own generation window [earlier N-chunk's last frame | F new frames | later N-chunk's
+    first frame], at t = -1, 0..F-1, F.  Before every step the two anchor frames are
+    set to their known latents carried to the step's time on the flow-matching path,
+    (1 - t) z + t eps (eps: [2 h w, C_p] fixed noise, earlier anchor first); the window
+    is denoised as one chunk that sees the reference and itself (no boundary segment);
+    at the end the anchor frames, i.e. the model's predictions for them, are dropped.
+    Returns the F new frames (with record, also the per-step window velocities)."""
+    g = cfg.chunk
+    n = g.h * g.w
+    F = g.frames
+    pos = grid_positions(-1, F + 2, g.h, g.w)
+    ctx = [[ref_kv[l]] for l in range(cfg.L)]
+    ts = schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    z0 = np.asarray(z_prev, dtype=np.float64)
+    z1 = np.asarray(z_next, dtype=np.float64)
+    e = np.asarray(eps, dtype=np.float64)
+    x = np.concatenate([np.zeros((n, cfg.C_p)), np.asarray(ic["x_init"], dtype=np.float64),
+                        np.zeros((n, cfg.C_p))], axis=0)
+    vs = []
+    for k in range(cfg.steps):
+        t = float(ts[k])
+        x[:n] = (1.0 - t) * z0 + t * e[:n]
+        x[(F + 1) * n:] = (1.0 - t) * z1 + t * e[n:]
+        v = dit_velocity(P, cfg, x, ts[k], pos, ctx, ic.get("audio"))
+        vs.append(v)
+        x = euler(x, v, ts[k], ts[k + 1])
+    out = x[n:(F + 1) * n]
+    return (out, vs) if record else out
+
+
+def interp_window_stream(P: Weights, cfg, n_chunks: Sequence[Dict[str, np.ndarray]],
+                         i_chunks: Sequence[Dict[str, np.ndarray]], eps: Sequence[np.ndarray],
+                         ref: np.ndarray):
+    """interp_stream() with the I-chunks under the window reading (interp_window): N-chunks
+    as in stream(); I-chunk k, once N_k and N_k+1 are done, from N_k's last frame and
+    N_k+1's first frame with anchor noise eps[k].  Returns (N-chunk finals, I-chunk
+    finals)."""
+    assert cfg.C_c == 0, "the window reading is built for chunks without conditioning"
+    g = cfg.chunk
+    ref_kv = ref_context(P, cfg, ref, cfg.ref)
+    n_out, i_out = [], []
+    for c, inp in enumerate(n_chunks):
+        if c == 0:
+            ctx = [[ref_kv[l]] for l in range(cfg.L)]
+        else:
+            bkv = bnd_context(P, cfg, ref_kv, last_frame(n_out[-1], g.frames, g.h, g.w), g.h, g.w)
+            ctx = [[ref_kv[l], bkv[l]] for l in range(cfg.L)]
+        n_out.append(chunk_denoise(P, cfg, inp["x_init"], ctx, inp.get("audio")))
+        if c >= 1:
+            k = c - 1
+            i_out.append(interp_window(P, cfg, ref_kv, last_frame(n_out[k], g.frames, g.h, g.w),
+                                       first_frame(n_out[k + 1], g.frames, g.h, g.w), i_chunks[k], eps[k]))
     return n_out, i_out
 
 

@@ -290,6 +290,13 @@ def _tokens(cfg: Config, name: str, chunk: int, shape, dtype: str) -> np.ndarray
     return _finish(z, dtype).reshape(shape)
 
 
+def anchor_noise(cfg: Config, chunk: int = 0) -> np.ndarray:
+    """Seeded noise of the two anchor frames of an interpolation window, [2 h w, C_p]
+    float32 (the earlier anchor's frame first)."""
+    g = cfg.chunk
+    return _tokens(cfg, "anchor_eps", chunk, (2 * g.h * g.w, cfg.C_p), "f32")
+
+
 def make_inputs(cfg: Config, chunk: int = 0) -> Dict[str, np.ndarray]:
     """Seeded per-chunk inputs (all float32).
 

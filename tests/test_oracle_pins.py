@@ -503,6 +503,94 @@ def test_interp_stream_schedule_and_anchor_frames(tiny):
 # ---------------------------------------------------------------- boundary by reuse
 
 
+# ---------------------------------------------------------------- I-chunk, window reading
+
+def _window_cfg(steps, t_start):
+    return dataclasses.replace(TINY, bnd=None, steps=steps, t_start=t_start, t_end=0.0)
+
+
+def test_window_velocity_equals_joint_sequence(tiny):
+    """The first step of a window I-chunk: its velocity is the monolithic sequence
+    [ref; window] with the window at t = -1 .. F (one segment seeing itself and the
+    reference) whose anchor frames hold (1 - t) z + t eps; the velocities of the anchor
+    rows exist and are then dropped."""
+    P, inp = tiny
+    cfg = _window_cfg(2, 0.7)
+    g = cfg.chunk
+    n = g.h * g.w
+    z0, z1 = synth.make_inputs(TINY, 5)["bnd"], synth.make_inputs(TINY, 6)["bnd"]
+    eps = synth.anchor_noise(TINY, 3)
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    out, vs = O.interp_window(P, cfg, ref_kv, z0, z1, inp, eps, record=True)
+    t = 0.7
+    z0, z1, e = (a.astype(np.float64) for a in (z0, z1, eps))
+    xw = np.concatenate([(1 - t) * z0 + t * e[:n], inp["x_init"].astype(np.float64), (1 - t) * z1 + t * e[n:]])
+    pos = np.concatenate([O.grid_positions(-1, 1, g.h, g.w), _pos(g), O.grid_positions(g.frames, 1, g.h, g.w)])
+    segs = [(inp["ref"], _pos(cfg.ref), 0, 0.0), (xw, pos, 1, t)]
+    vj = joint_velocity(P, cfg, segs, inp["audio"].astype(np.float64), t)
+    assert vs[0].shape == ((g.frames + 2) * n, cfg.C_p)
+    assert np.abs(vs[0] - vj).max() <= 1e-12 * np.abs(vj).max()
+    assert out.shape == (g.frames * n, cfg.C_p)
+
+
+def test_window_at_t1_sees_only_anchor_noise(tiny):
+    """One step from t = 1: the anchors are pure noise then, so the new frames do not
+    depend on the anchor latents; from t = 0.5 they do."""
+    P, inp = tiny
+    g = TINY.chunk
+    z0, z1 = synth.make_inputs(TINY, 5)["bnd"], synth.make_inputs(TINY, 6)["bnd"]
+    eps = synth.anchor_noise(TINY, 3)
+    for t0, moves in ((1.0, False), (0.5, True)):
+        cfg = _window_cfg(1, t0)
+        ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+        a = O.interp_window(P, cfg, ref_kv, z0, z1, inp, eps)
+        b = O.interp_window(P, cfg, ref_kv, 3.0 * z1, -z0, inp, eps)
+        c = O.interp_window(P, cfg, ref_kv, z0, z1, inp, 2.0 * eps)
+        assert (np.abs(a - b).max() > 1e-9) == moves
+        assert np.abs(a - c).max() > 1e-9
+        assert a.shape == (g.frames * g.h * g.w, cfg.C_p)
+
+
+def test_window_without_attention_is_per_token(tiny):
+    """With every block gated off (the model is then patch embed + final layer, token by
+    token) the new frames equal the plain multi-step pass of the I-chunk's own noise:
+    the window keeps their rows and order, and the anchors do not reach them."""
+    P, inp = tiny
+    cfg = _window_cfg(3, 1.0)
+    P0 = P
+    for l in range(cfg.L):
+        P0 = _gated(P0, l, cfg.D, 0.0, 0.0)
+    z0, z1 = synth.make_inputs(TINY, 5)["bnd"], synth.make_inputs(TINY, 6)["bnd"]
+    eps = synth.anchor_noise(TINY, 3)
+    ref_kv = O.ref_context(P0, cfg, inp["ref"], cfg.ref)
+    got = O.interp_window(P0, cfg, ref_kv, z0, z1, inp, eps)
+    want = O.chunk_denoise(P0, cfg, inp["x_init"], [[ref_kv[l]] for l in range(cfg.L)], inp["audio"])
+    assert np.abs(got - want).max() <= 1e-13 * np.abs(want).max()
+
+
+def test_interp_window_stream_order_and_anchor_frames(tiny):
+    """N0, N1, I0, N2, I1 under the window reading: the N-chunks equal stream(); I_k equals
+    interp_window with N_k's last frame and N_k+1's first frame (rows picked here by their
+    grid coordinates) and its own anchor noise."""
+    P, _ = tiny
+    cfg = _window_cfg(2, 1.0)
+    g = cfg.chunk
+    n_in = [synth.make_inputs(TINY, c) for c in range(3)]
+    i_in = [synth.make_inputs(TINY, 100 + k) for k in range(2)]
+    eps = [synth.anchor_noise(TINY, 100 + k) for k in range(2)]
+    n_out, i_out = O.interp_window_stream(P, cfg, n_in, i_in, eps, n_in[0]["ref"])
+    assert len(n_out) == 3 and len(i_out) == 2
+    for a, b in zip(n_out, O.stream(P, cfg, n_in, n_in[0]["ref"])):
+        assert np.abs(a - b).max() == 0.0
+    pos = _pos(g)
+    ref_kv = O.ref_context(P, cfg, n_in[0]["ref"], cfg.ref)
+    for k in range(2):
+        last = n_out[k][pos[:, 0] == g.frames - 1]
+        first = n_out[k + 1][pos[:, 0] == 0]
+        want = O.interp_window(P, cfg, ref_kv, last, first, i_in[k], eps[k])
+        assert np.abs(i_out[k] - want).max() == 0.0
+
+
 def test_bnd_reuse_special_case_equals_clean_boundary_pass(tiny):
     """A one-frame chunk at t0 = 0 whose reference sits one frame earlier (t = -1), run at
     t = 0 without audio, has the relative positions, visibility, timestep and inputs of a
