@@ -5,4 +5,4 @@ package is its ctypes binding.  The first call into it loads the library and rai
 if it is missing: there is no fallback path.
 """
 from ._lib import DitError, lib  # noqa: F401
-from .dit import AUDIO_HELD, ChunkConfig, DitChunk, fm_euler_step, grid, ops, torch_dtype  # noqa: F401
+from .dit import AUDIO_HELD, ChunkConfig, DitChunk, fm_euler_step, fm_noise_to, grid, ops, torch_dtype  # noqa: F401

@@ -69,6 +69,7 @@ _SIGS = {
     "dit_chunk_step": (I, [P, P, P, P, I, DitGrid, Dbl, Dbl, P]),
     "dit_chunk_step_carry": (I, [P, P, P, P, I, DitGrid, Dbl, Dbl, P]),
     "fm_euler_step": (I, [P, P, Dbl, ctypes.c_longlong, P]),
+    "fm_noise_to": (I, [P, P, P, Dbl, ctypes.c_longlong, P]),
     "dit_last_error": (ctypes.c_char_p, []),
     "dit_timing_enable": (I, [P, I]),
     "dit_timing_read": (I, [P, I, ctypes.POINTER(I), ctypes.POINTER(Dbl), ctypes.POINTER(Dbl)]),

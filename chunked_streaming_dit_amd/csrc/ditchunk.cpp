@@ -1024,6 +1024,17 @@ int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_st
   return DIT_OK;
 }
 
+int fm_noise_to(float* x, const float* z, const float* eps, double t, long long n, void* hip_stream) {
+  if (n < 0) return fail(DIT_EINVAL, "n < 0");
+  if (n == 0) return DIT_OK;
+  if (!x || !z || !eps) return fail(DIT_EINVAL, "x, z or eps is NULL");
+  if (!std::isfinite(t)) return fail(DIT_EINVAL, "t not finite");
+  if (((uintptr_t)x & 15) || ((uintptr_t)z & 15) || ((uintptr_t)eps & 15))
+    return fail(DIT_EINVAL, "x, z, eps must be 16-byte aligned");
+  HIPCHK(noise_to(x, z, eps, (float)(1.0 - t), (float)t, n, static_cast<hipStream_t>(hip_stream)));
+  return DIT_OK;
+}
+
 const char* dit_last_error(void) { return g_err.c_str(); }
 
 int dit_timing_enable(dit_handle* h, int enable) {

@@ -257,6 +257,26 @@ __global__ void patch_input_kernel(const float* __restrict__ x, int n, int c_p,
   }
 }
 
+// x[i] = a z[i] + b e[i] (fp32): a point of the flow-matching path between data z
+// (a = 1 - t) and noise e (b = t).
+__global__ void noise_to_kernel(float* __restrict__ x, const float* __restrict__ z,
+                                const float* __restrict__ e, float a, float b, long long n) {
+  const long long n4 = n / 4;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    const f32x4 zz = reinterpret_cast<const f32x4*>(z)[i];
+    const f32x4 ee = reinterpret_cast<const f32x4*>(e)[i];
+    f32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = fmaf(b, ee[k], a * zz[k]);
+    reinterpret_cast<f32x4*>(x)[i] = r;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
+    const long long i = n4 * 4 + threadIdx.x;
+    x[i] = fmaf(b, e[i], a * z[i]);
+  }
+}
+
 __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dt,
                              long long n) {
   const long long n4 = n / 4;
@@ -503,6 +523,15 @@ hipError_t patch_input(int dtype, const float* x, int n, int c_p, const float* c
     patch_input_kernel<bf16><<<blocks, 256, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g, (bf16*)xin);
   else
     patch_input_kernel<float><<<blocks, 256, 0, s>>>(x, n, c_p, cond, c_c, cond_mode, g, (float*)xin);
+  return hipGetLastError();
+}
+
+hipError_t noise_to(float* x, const float* z, const float* e, float a, float b, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  long long blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  noise_to_kernel<<<(int)blocks, 256, 0, s>>>(x, z, e, a, b, n);
   return hipGetLastError();
 }
 

@@ -208,6 +208,8 @@ hipError_t patch_embed(const float* x, int n, int c_p, const float* cond, int c_
 
 // x[i] += dt * v[i]
 hipError_t euler(float* x, const float* v, float dt, long long n, hipStream_t s);
+// x = a z + b e over n fp32 elements (16-byte aligned pointers).
+hipError_t noise_to(float* x, const float* z, const float* e, float a, float b, long long n, hipStream_t s);
 
 // Boundary by reuse: keys [first, first + n) of a chunk's K [*, H*dh] and V^T
 // [H*dh, cap_src] (layouts of qknorm_rope) become keys [0, n) of a boundary segment

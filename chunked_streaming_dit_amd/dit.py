@@ -13,7 +13,7 @@ import torch
 
 from . import _lib as C
 
-__all__ = ["ChunkConfig", "DitChunk", "grid", "fm_euler_step", "ops", "torch_dtype"]
+__all__ = ["ChunkConfig", "DitChunk", "grid", "fm_euler_step", "fm_noise_to", "ops", "torch_dtype"]
 
 
 def torch_dtype(dtype: str) -> torch.dtype:
@@ -265,6 +265,15 @@ def fm_euler_step(x: torch.Tensor, v: torch.Tensor, dt: float) -> None:
     if x.numel() != v.numel():
         raise ValueError("x and v differ in size")
     C.check(C.lib().fm_euler_step(x.data_ptr(), v.data_ptr(), float(dt), x.numel(), _stream()))
+
+
+def fm_noise_to(x: torch.Tensor, z: torch.Tensor, eps: torch.Tensor, t: float) -> None:
+    """x = (1 - t) z + t eps (fm_noise_to); x may be z or eps."""
+    for a, name in ((x, "x"), (z, "z"), (eps, "eps")):
+        _dev(a, name, torch.float32)
+    if not (x.numel() == z.numel() == eps.numel()):
+        raise ValueError("x, z and eps differ in size")
+    C.check(C.lib().fm_noise_to(x.data_ptr(), z.data_ptr(), eps.data_ptr(), float(t), x.numel(), _stream()))
 
 
 class ops:

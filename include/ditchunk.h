@@ -26,7 +26,9 @@
  *   dit_chunk_step      once per denoising step: v = DiT(x, t), x += (t_next - t) v;
  *   dit_chunk_step_carry  alternatively the chunk's last step, which also leaves
  *                       that step's last-frame K/V as the next boundary;
- *   fm_euler_step       the bare Euler update, for callers with their own velocity.
+ *   fm_euler_step       the bare Euler update, for callers with their own velocity;
+ *   fm_noise_to         a point of the flow-matching path (frames held at known
+ *                       latents, e.g. interpolation anchors inside the chunk's window).
  *
  * The block (readings of the pages, which give no internals): tokens are
  * patchified latents [N, c_p] (fp32).  A patch-embed Linear feeds L blocks.
@@ -324,6 +326,19 @@ int dit_chunk_step_carry(dit_handle* h, float* x, const float* cond, const float
 /* x[i] += (float)dt * v[i] for i < n (fp32, device) on hip_stream.
  * Errors: EINVAL (null pointer with n > 0, non-finite dt, n < 0). */
 int fm_euler_step(float* x, const float* v, double dt, long long n, void* hip_stream);
+
+/* x[i] = (float)(1 - t) * z[i] + (float)t * eps[i] for i < n (fp32, device) on hip_stream:
+ * the point at time t of the flow-matching path from data z (t = 0) to noise eps (t = 1)
+ * (HeyGen, "Avatar inference at scale": the generator is trained with flow matching,
+ * section "The underlying model architecture").  It holds frames at known latents
+ * during a pass, as the window reading of the interpolation anchors does: before every
+ * step of an I-chunk whose window is [earlier N-chunk's last frame | F new frames |
+ * later N-chunk's first frame] (grid t0 = -1, F + 2 frames, reference context only),
+ * the two anchor frames are set to their latents at the step's t; the anchors'
+ * predictions are dropped at the end (section "Boundary continuity and chunk
+ * consistency").  x may alias z or eps.  Pointers 16-byte aligned.
+ * Errors: EINVAL (null pointer with n > 0, misalignment, non-finite t, n < 0). */
+int fm_noise_to(float* x, const float* z, const float* eps, double t, long long n, void* hip_stream);
 
 /* Message of the last failure on this thread ("" if none). */
 const char* dit_last_error(void);

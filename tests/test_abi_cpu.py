@@ -213,6 +213,11 @@ def test_euler_and_ops_validation():
     assert lib.fm_euler_step(FAKE, FAKE, float("inf"), 10, None) == C.DIT_EINVAL
     assert lib.fm_euler_step(FAKE, FAKE, 0.1, -1, None) == C.DIT_EINVAL
     assert lib.fm_euler_step(FAKE + 4, FAKE, 0.1, 8, None) == C.DIT_EINVAL
+    assert lib.fm_noise_to(FAKE, FAKE, FAKE, 0.5, 0, None) == C.DIT_OK
+    assert lib.fm_noise_to(FAKE, None, FAKE, 0.5, 8, None) == C.DIT_EINVAL
+    assert lib.fm_noise_to(FAKE, FAKE, FAKE, float("nan"), 8, None) == C.DIT_EINVAL
+    assert lib.fm_noise_to(FAKE, FAKE, FAKE, 0.5, -1, None) == C.DIT_EINVAL
+    assert lib.fm_noise_to(FAKE, FAKE, FAKE + 8, 0.5, 8, None) == C.DIT_EINVAL
     assert lib.ditk_linear(1, FAKE, FAKE, FAKE, 10, 64, 100, 0, FAKE, None) == C.DIT_ESHAPE  # K % 64
     assert lib.ditk_linear(1, FAKE, FAKE, FAKE, 10, 66, 128, 0, FAKE, None) == C.DIT_ESHAPE  # N % 4
     assert lib.ditk_linear(5, FAKE, FAKE, FAKE, 10, 64, 128, 0, FAKE, None) == C.DIT_EINVAL

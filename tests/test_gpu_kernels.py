@@ -12,7 +12,7 @@ import torch
 
 import oracle as O
 import synth
-from chunked_streaming_dit_amd import ChunkConfig, fm_euler_step, grid, ops, torch_dtype
+from chunked_streaming_dit_amd import ChunkConfig, fm_euler_step, fm_noise_to, grid, ops, torch_dtype
 from tests.gpu_util import TOL, device, rel_err, to_np
 
 pytestmark = pytest.mark.gpu
@@ -441,6 +441,29 @@ def test_patch_embed_fused(frames, h, w, D, cc, mode):
     ref = O.linear(O.patch_input(xr, c_rows, cc), Wt.astype(np.float64), b.astype(np.float64))
     torch.cuda.synchronize()
     assert rel_err(to_np(out), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("n", [1, 7, 1003, 40000])
+def test_fm_noise_to(n):
+    """x = (1 - t) z + t eps on ragged sizes, including in place over z; t = 0 and t = 1
+    give z and eps exactly."""
+    dev = device()
+    r = np.random.default_rng(n)
+    z = r.standard_normal(n).astype(np.float32)
+    e = r.standard_normal(n).astype(np.float32)
+    zd, ed = torch.from_numpy(z).to(dev), torch.from_numpy(e).to(dev)
+    for t in (0.0, 0.3, 0.875, 1.0):
+        x = torch.full((n,), float("nan"), device=dev)
+        fm_noise_to(x, zd, ed, t)
+        want = (1.0 - t) * z.astype(np.float64) + t * e.astype(np.float64)
+        assert np.abs(to_np(x) - want).max() <= 1e-6 * max(1.0, np.abs(want).max())
+        if t == 0.0:
+            assert np.array_equal(to_np(x), z)
+        if t == 1.0:
+            assert np.array_equal(to_np(x), e)
+    zi = zd.clone()
+    fm_noise_to(zi, zi, ed, 0.25)
+    assert np.abs(to_np(zi) - (0.75 * z.astype(np.float64) + 0.25 * e)).max() <= 1e-6 * 5
 
 
 @pytest.mark.parametrize("lam", [0.0, -0.7])

@@ -220,6 +220,69 @@ def test_mini_interp_stream(base):
 
 
 @pytest.mark.parametrize("base", ["bf16", "f32"])
+def test_mini_interp_window_stream(base):
+    """N0, N1, I0, N2, I1 with the I-chunks under the window reading: I_k is a window of
+    F + 2 frames at t = -1 .. F whose first and last frames are reset before every step
+    to N_k's last and N_k+1's first frame carried to the step's time (fm_noise_to), seen
+    with the reference only; its F middle frames are kept."""
+    from chunked_streaming_dit_amd import DitChunk, fm_noise_to
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(MINI_BF16 if base == "bf16" else MINI_F32, cid=209 if base == "bf16" else 210,
+                              bnd=None)
+    P = synth.make_weights(cfg)
+    n_in = [synth.make_inputs(cfg, c) for c in range(3)]
+    i_in = [synth.make_inputs(cfg, 100 + k) for k in range(2)]
+    eps = [synth.anchor_noise(cfg, 100 + k) for k in range(2)]
+    n_ref, i_ref = O.interp_window_stream(P, cfg, n_in, i_in, eps, n_in[0]["ref"])
+    g = cfg.chunk
+    hw = g.h * g.w
+    F = g.frames
+    h = DitChunk(chunk_config(cfg, max_tokens=(F + 2) * hw), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(n_in[0]["ref"], dev), grid_of(cfg.ref))
+    ts = O.schedule(cfg.steps, cfg.t_start, cfg.t_end)
+    win = grid_of(Grid(-1, F + 2, g.h, g.w))
+
+    def denoise(inp):
+        x = f32(inp["x_init"], dev)
+        for k in range(cfg.steps):
+            h.step(x, ts[k], ts[k + 1], grid_of(g), audio=f32(inp["audio"], dev))
+        return x
+
+    def window(inp, z0, z1, e):
+        x = torch.zeros(((F + 2) * hw, cfg.C_p), device=dev)
+        x[hw:(F + 1) * hw] = f32(inp["x_init"], dev)
+        ed = f32(e, dev)
+        audio = f32(inp["audio"], dev)
+        for k in range(cfg.steps):
+            fm_noise_to(x[:hw], z0, ed[:hw], ts[k])
+            fm_noise_to(x[(F + 1) * hw:], z1, ed[hw:], ts[k])
+            h.step(x, ts[k], ts[k + 1], win, audio=audio)
+        return x[hw:(F + 1) * hw].clone()
+
+    n_gpu, i_gpu = [], []
+    for c in range(3):
+        if c == 0:
+            h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+        else:
+            h.boundary_kv_carry(n_gpu[-1], grid_of(g))
+        n_gpu.append(denoise(n_in[c]))
+        if c >= 1:
+            k = c - 1
+            h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))  # the window sees the reference only
+            z0 = n_gpu[k][(F - 1) * hw:].contiguous()
+            z1 = n_gpu[k + 1][:hw].contiguous()
+            i_gpu.append(window(i_in[k], z0, z1, eps[k]))
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    for name, got, want, inps in (("N", n_gpu, n_ref, n_in), ("I", i_gpu, i_ref, i_in)):
+        for k, (a, b) in enumerate(zip(got, want)):
+            err = rel_err(a.cpu().numpy() - inps[k]["x_init"], b - inps[k]["x_init"])
+            print(f"{name}{k}: dx err {err:.2e}")
+            assert err <= tol, (name, k, err)
+
+
+@pytest.mark.parametrize("base", ["bf16", "f32"])
 def test_mini_stream_boundary_by_reuse(base):
     """Three chunks, each chunk's last step carrying its last frame's K/V forward as the
     next boundary (dit_chunk_step_carry), against oracle.stream_reuse."""
