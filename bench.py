@@ -38,6 +38,11 @@ Other workloads (--workload):
            latency is reported as the time to the first chunk
   interp   an interpolation chunk of the base shape (boundary and anchor passes, keys
            [reference | boundary | anchor | chunk])
+  iwin     an interpolation chunk of the base shape under the window reading: a window of
+           the chunk's frames between its two anchor frames (10920 tokens, keys 1560
+           reference + 10920 window), both anchors re-noised to each step's time
+           (fm_noise_to) before each of the 8 steps; value = the chunk's 7800 latent
+           tokens x 8 per job / time
   reuse    base chunk jobs whose boundary is carried by reuse (no boundary pass)
   sr, sr1  super-resolution chunk jobs (31200 tokens, 2 blocks, no audio): boundary
            pass + 4 Euler steps (sr) or one step 1 -> 0 (sr1)
@@ -68,6 +73,8 @@ METRIC_STREAM6 = ("DiT streaming sequence generated latent tokens/sec (steady-st
                   "attention TFLOP/s (% bf16 MFMA peak), 1 GPU")
 METRIC_INTERP = ("DiT interpolation-chunk latent tokens/sec and attention TFLOP/s "
                  "(% bf16 MFMA peak), 1 GPU")
+METRIC_IWIN = ("DiT interpolation-chunk (anchor window) latent tokens/sec and attention TFLOP/s "
+               "(% bf16 MFMA peak), 1 GPU")
 METRIC_SR = ("DiT super-resolution chunk latent tokens/sec and attention TFLOP/s "
              "(% bf16 MFMA peak), 1 GPU")
 METRIC_SR1 = ("DiT single-step super-resolution chunk latent tokens/sec and attention TFLOP/s "
@@ -648,11 +655,11 @@ def stream6_main(args) -> int:
 
 
 def chunk_main(args) -> int:
-    """base / interp / reuse / sr / sr1: chunk jobs of the base or super-resolution shape."""
+    """base / interp / iwin / reuse / sr / sr1: chunk jobs of the base or super-resolution shape."""
     import torch
 
     import synth
-    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk
+    from chunked_streaming_dit_amd import AUDIO_HELD, DitChunk, fm_noise_to
     from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
 
     dev = torch.device("cuda", 0)
@@ -661,13 +668,17 @@ def chunk_main(args) -> int:
     P = synth.make_weights(cfg)
     inp = synth.make_inputs(cfg, 0)
     W = upload_weights(P, cfg.dtype, dev)
-    h = DitChunk(chunk_config(cfg), W, dev)
+    iwin = args.workload == "iwin"
+    gc = cfg.chunk
+    hw = gc.h * gc.w
+    F = gc.frames
+    h = DitChunk(chunk_config(cfg, max_tokens=(F + 2) * hw if iwin else None), W, dev)
     ref = f32(inp["ref"], dev)
     bnd = f32(inp["bnd"], dev)
     x0 = f32(inp["x_init"], dev)
     audio = f32(inp["audio"], dev) if cfg.M else None
     cond = f32(inp["cond_lr"], dev) if sr else None
-    x = torch.empty_like(x0)
+    x = torch.empty(((F + 2) * hw, cfg.C_p), device=dev) if iwin else torch.empty_like(x0)
     S = 1 if args.workload == "sr1" else cfg.steps
     ts = [cfg.t_start + (cfg.t_end - cfg.t_start) * k / S for k in range(S + 1)]
     g_chunk = grid_of(cfg.chunk)
@@ -675,7 +686,7 @@ def chunk_main(args) -> int:
     g_prev = grid_of(synth.Grid(0, 1, cfg.bnd.h, cfg.bnd.w))
     interp = args.workload == "interp"
     reuse = args.workload == "reuse"
-    if sr or reuse or interp:
+    if sr or reuse or interp or iwin:
         h.ref_kv_precompute(ref, g_ref)  # once per request, outside the timed region
     if reuse:
         h.boundary_kv_carry(bnd, g_prev)  # the first job's boundary; later ones are carried
@@ -683,6 +694,15 @@ def chunk_main(args) -> int:
         # the neighbouring N-chunks' final latents (seeded stand-ins of the chunk shape)
         x_before = f32(synth.make_inputs(cfg, 1)["x_init"], dev)
         x_after = f32(synth.make_inputs(cfg, 2)["x_init"], dev)
+    if iwin:
+        # the window sees the reference only; the anchors are the neighbouring N-chunks'
+        # last and first frames (seeded stand-ins), their noise drawn once per chunk
+        h.boundary_kv_carry(None, grid_of(synth.Grid(0, 0, 0, 0)))
+        z0 = f32(synth.make_inputs(cfg, 1)["x_init"][(F - 1) * hw:], dev)
+        z1 = f32(synth.make_inputs(cfg, 2)["x_init"][:hw], dev)
+        e = f32(synth.anchor_noise(cfg, 0), dev)
+        g_win = grid_of(synth.Grid(-1, F + 2, gc.h, gc.w))
+        xc = x[hw:(F + 1) * hw]
 
     table = ts[:-1] + [0.0]  # the schedule's timesteps and t = 0 of the context passes
 
@@ -696,12 +716,15 @@ def chunk_main(args) -> int:
         elif not reuse:
             h.ref_kv_precompute(ref, g_ref)
             h.boundary_kv_carry(bnd, g_prev)
-        x.copy_(x0)
+        (xc if iwin else x).copy_(x0)
         if audio is not None:  # the chunk's audio K/V, once per chunk
             h.audio_kv_precompute(audio)
         for k in range(S):
-            h.step(x, ts[k], ts[k + 1], g_chunk, cond=cond, audio=AUDIO_HELD if audio is not None else None,
-                   carry_boundary=reuse and k == S - 1)
+            if iwin:
+                fm_noise_to(x[:hw], z0, e[:hw], ts[k])
+                fm_noise_to(x[(F + 1) * hw:], z1, e[hw:], ts[k])
+            h.step(x, ts[k], ts[k + 1], g_win if iwin else g_chunk, cond=cond,
+                   audio=AUDIO_HELD if audio is not None else None, carry_boundary=reuse and k == S - 1)
 
     for _ in range(args.warmup):
         step()
@@ -734,14 +757,21 @@ def chunk_main(args) -> int:
                     "1560 reference + 1560 boundary + 1560 anchor + 7800 chunk, 50 audio tokens, "
                     "4 blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0; one bench step = "
                     "modulation table + boundary K/V + anchor K/V + audio K/V + 8 denoising steps")
+    if iwin:
+        workload = ("interpolation chunk of the base low-res shape, anchor-window reading: a window "
+                    "of 7 frames (2 anchor + 5 chunk frames, 10920 tokens), keys 1560 reference + 10920 "
+                    "window, 50 audio tokens, 4 blocks, hidden 1536, 12 heads x 128, 8 Euler steps 1 -> 0 "
+                    "with both anchors re-noised to each step's time; one bench step = modulation table "
+                    "+ audio K/V + 8 x (2 anchor re-noisings + denoising step); value counts the 7800 "
+                    "chunk tokens")
     if sr:
         workload = ("super-resolution chunk: 5x60x104 = 31200 latent tokens conditioned on the "
                     "nearest-2x upsample of a 5x30x52 latent (64 + 64 input channels), keys 6240 "
                     "reference + 6240 boundary + 31200 chunk, no audio, 2 DiT blocks, hidden 1536, "
                     f"12 heads x 128, MLP 4x, {S} Euler step{'s' if S > 1 else ''} 1 -> 0; one bench "
                     f"step = modulation table + boundary K/V + {S} denoising step{'s' if S > 1 else ''}")
-    metric = {"interp": METRIC_INTERP, "reuse": METRIC_REUSE, "sr": METRIC_SR, "sr1": METRIC_SR1}.get(
-        args.workload, METRIC)
+    metric = {"interp": METRIC_INTERP, "iwin": METRIC_IWIN, "reuse": METRIC_REUSE, "sr": METRIC_SR,
+              "sr1": METRIC_SR1}.get(args.workload, METRIC)
     line = _line(metric, cfg.N * S / ((t1 - t0) / args.steps), args, ms_per_step, workload, extra, achieved,
                  _traffic(args.workload))
     h.close()
@@ -758,7 +788,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="large",
-                    choices=["large", "base", "stream6", "tiny", "interp", "reuse", "sr", "sr1", "wstream"],
+                    choices=["large", "base", "stream6", "tiny", "interp", "iwin", "reuse", "sr", "sr1", "wstream"],
                     help="large: one large-chunk denoising step (default, the headline); base: one base "
                          "chunk job; stream6: whole 6-chunk streaming sessions; see the module docstring")
     ap.add_argument("--copy-probe", action="store_true",
