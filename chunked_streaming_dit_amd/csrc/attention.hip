@@ -199,10 +199,13 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  // Direct-to-LDS loads (global_load_lds_dwordx4): instruction g = lw + LW i of loader
-  // wave lw fills 1 KB of a slot = rows [RP g, RP g + RP); the lane covers row
-  // RP g + lane/(64/RP) at chunk position lane % (64/RP), i.e. source chunk
-  // swz(row, position).  The other waves issue none (their waits pass at once).
+  // Direct-to-LDS loads (buffer_load_dwordx4 ... lds through a buffer resource whose base
+  // is the tile's first key row or column, so a load needs no per-lane address
+  // arithmetic): instruction g = lw + LW i of loader wave lw fills 1 KB of a slot = rows
+  // [RP g, RP g + RP); the lane covers row RP g + lane/(64/RP) at chunk position
+  // lane % (64/RP), i.e. source chunk swz(row, position).  The other waves issue none
+  // (their waits pass at once).  All offsets lie inside the segment (V^T under 2^31
+  // bytes), below the resource's unlimited size.
   const int lw = wave % LW;
   unsigned koff[NLK];
 #pragma unroll
@@ -212,28 +215,35 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     const int c = swz<RBK>(r, lane % (64 / RPK));
     koff[i] = (unsigned)((r * a.ldk + head * DH) * SZ + c * 16);
   }
-  int vrow[NLV], vchk[NLV];
-#pragma unroll
-  for (int i = 0; i < NLV; ++i) {
-    const int g = lw + LW * i;
-    vrow[i] = RPV * g + lane / (64 / RPV);
-    vchk[i] = swz<RBV>(vrow[i], lane % (64 / RPV)) * 16;
-  }
+  // V^T lane offsets depend on the segment's row pitch: computed when a new pitch comes.
+  unsigned vvoff[NLV];
+  int vcap = -1;
   auto load_k = [&](const Walk& w, int slot) {
     if (wave >= LW) return;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)w.kp, (short)0, -1, 0x00020000);
     char* dst = ks + slot * KTILE + lw * 1024;
 #pragma unroll
     for (int i = 0; i < NLK; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(w.kp + koff[i]), (void*)(dst + i * LW * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + i * LW * 1024), 16,
+                                               (int)koff[i], 0, 0, 0);
   };
   auto load_v = [&](const Walk& w, int slot) {
     if (wave >= LW) return;
+    if (w.cap != vcap) {  // uniform
+      vcap = w.cap;
+#pragma unroll
+      for (int i = 0; i < NLV; ++i) {
+        const int g = lw + LW * i;
+        const int row = RPV * g + lane / (64 / RPV);
+        vvoff[i] = ((unsigned)(head * DH + row) * (unsigned)vcap) * SZ + swz<RBV>(row, lane % (64 / RPV)) * 16;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)w.vp, (short)0, -1, 0x00020000);
     char* dst = vs + slot * VTILE + lw * 1024;
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const unsigned off = ((unsigned)(head * DH + vrow[i]) * (unsigned)w.cap) * SZ + vchk[i];
-      __builtin_amdgcn_global_load_lds((const void*)(w.vp + off), (void*)(dst + i * LW * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < NLV; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + i * LW * 1024), 16,
+                                               (int)vvoff[i], 0, 0, 0);
   };
   // S^T tile from a K slot: 2 blocks of 32 keys x 32 queries.  Lane: query l32,
   // key = 32 kb + 8 (e/4) + 4 lg + e%4 for element e.
@@ -352,10 +362,13 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     // (P^T operand elements [v*VE, v*VE+VE) of S[kb]), their row-sum contribution and
     // DB P V MFMAs with the V^T vector holding the same keys (stored order).  Phase u
     // first requests the K fragments of phase u+1 (scores of tile t+1, KPU fragments per
-    // phase), then exponentiates, then issues its score and P V MFMAs; the scheduling
-    // barrier keeps that order so LDS latency hides under the exponentials.  The row sum
-    // is taken from the converted operand values, i.e. from exactly the weights the MFMA
-    // uses.
+    // phase), then takes the exponentials of unit u+1 while its score MFMAs and the P V
+    // MFMAs of unit u (whose weights the previous phase made) run: no MFMA of a phase
+    // waits for that phase's VALU work (1.2% faster at the large chunk than
+    // exponentiating and multiplying the same unit, interleaved A/B on one board).  The
+    // scheduling barrier keeps each phase's instructions together so LDS latency hides
+    // under the exponentials.  The row sum is taken from the converted operand values,
+    // i.e. from exactly the weights the MFMA uses.
     constexpr int UPK = 16 / VE;       // units per 32-key block
     constexpr int NU = 2 * UPK;        // units (phases) per tile
     constexpr int KPU = 2 * QV / NU;   // score fragments per phase
@@ -372,16 +385,23 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) Snext[kb][r] = 0.f;
+    auto expu = [&](int u) __attribute__((always_inline)) {
+      const int kb = u / UPK, v = u % UPK;
+      V p;
+#pragma unroll
+      for (int j = 0; j < VE; ++j)
+        p[j] = from_f<T>(__builtin_amdgcn_exp2f(DIRECT ? S[kb][v * VE + j] : fmaf(S[kb][v * VE + j], a.scale, -ms)));
+      return p;
+    };
     kread(0, 0);
+    V pcur = expu(0);
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       if (u + 1 < NU) kread(u + 1, (u + 1) & 1);
       const int kb = u / UPK, v = u % UPK;
-      V pf;
-#pragma unroll
-      for (int j = 0; j < VE; ++j)
-        pf[j] = from_f<T>(__builtin_amdgcn_exp2f(DIRECT ? S[kb][v * VE + j] : fmaf(S[kb][v * VE + j], a.scale, -ms)));
-      l_run = row_sum_add(pf, l_run);
+      V pnext;
+      if (u + 1 < NU) pnext = expu(u + 1);
+      l_run = row_sum_add(pcur, l_run);
       const int pos = swz<RBV>(l32, (kb * 32 + v * 2 * VE + lg * VE) * SZ / 16);
       V vf[DB];
 #pragma unroll
@@ -392,8 +412,9 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
         Snext[skb] = mfma32(kf[u & 1][i], qf[st], Snext[skb]);
       }
 #pragma unroll
-      for (int d = 0; d < DB; ++d) O[d] = mfma32(vf[d], pf, O[d]);
+      for (int d = 0; d < DB; ++d) O[d] = mfma32(vf[d], pcur, O[d]);
       __builtin_amdgcn_sched_barrier(0);
+      if (u + 1 < NU) pcur = pnext;
     }
     if (!FIRST) wait_vm_lds<0>();  // this wave's K t+2, t+3 and V t+1, t+2 (issued at t-1)
     walk_next(wc);

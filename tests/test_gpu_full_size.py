@@ -262,6 +262,51 @@ def test_interp_chunk_full_shape_one_block_sampled_rows():
     assert err <= TOL["bf16"], err
 
 
+def test_interp_window_full_shape_one_block_sampled_rows():
+    """An interpolation chunk of the base-chunk shape under the window reading, one
+    block: the window of 7 frames (t = -1 .. 5, 10920 tokens) seen with the reference
+    only, its two anchor frames re-noised to t = 0.75 by fm_noise_to; the oracle
+    evaluates sampled query rows of the velocity (anchor rows, window edges, chunk
+    rows)."""
+    from chunked_streaming_dit_amd import DitChunk, fm_noise_to
+    from chunked_streaming_dit_amd.workload import chunk_config, f32, grid_of, upload_weights
+    dev = device()
+    cfg = dataclasses.replace(synth.BASE_CHUNK, L=1, cid=54, steps=1, bnd=None)
+    P = synth.make_weights(cfg, threads=16)
+    inp = synth.make_inputs(cfg, 0)
+    g = cfg.chunk
+    hw, F = g.h * g.w, g.frames
+    z0 = synth.make_inputs(cfg, 1)["x_init"][(F - 1) * hw:]  # last frame of the earlier chunk
+    z1 = synth.make_inputs(cfg, 2)["x_init"][:hw]  # first frame of the later chunk
+    e = synth.anchor_noise(cfg, 0)
+    t, t_next = 0.75, 0.625
+    h = DitChunk(chunk_config(cfg, max_tokens=(F + 2) * hw), upload_weights(P, cfg.dtype, dev), dev)
+    h.ref_kv_precompute(f32(inp["ref"], dev), grid_of(cfg.ref))
+    h.boundary_kv_carry(None, grid_of(Grid(0, 0, 0, 0)))
+    x = torch.zeros(((F + 2) * hw, cfg.C_p), device=dev)
+    x[hw:(F + 1) * hw] = f32(inp["x_init"], dev)
+    ed = f32(e, dev)
+    fm_noise_to(x[:hw], f32(z0, dev), ed[:hw], t)
+    fm_noise_to(x[(F + 1) * hw:], f32(z1, dev), ed[hw:], t)
+    x_in = to_np(x).copy()
+    v = torch.empty_like(x)
+    h.step(x, t, t_next, grid_of(Grid(-1, F + 2, g.h, g.w)), audio=f32(inp["audio"], dev), v_out=v)
+    torch.cuda.synchronize()
+    vg = to_np(v)
+    h.close()
+    # the oracle's own window input: the path point in float64
+    xo = np.concatenate([(1 - t) * z0.astype(np.float64) + t * e[:hw], inp["x_init"],
+                         (1 - t) * z1.astype(np.float64) + t * e[hw:]])
+    assert np.abs(x_in - xo).max() <= 1e-6 * np.abs(xo).max()
+    ref_kv = O.ref_context(P, cfg, inp["ref"], cfg.ref)
+    n = (F + 2) * hw
+    rows = np.unique(np.concatenate([_sample_rows(n, 54), [hw - 1, hw, (F + 1) * hw - 1, (F + 1) * hw]]))
+    vo = O.velocity_rows(P, cfg, xo, t, O.grid_positions(-1, F + 2, g.h, g.w), [[ref_kv[0]]], inp["audio"], rows)
+    err = rel_err(vg[rows], vo)
+    print(f"interpolation window one-block full shape, {len(rows)} sampled rows: v err {err:.2e}")
+    assert err <= TOL["bf16"], err
+
+
 def test_boundary_by_reuse_full_shape_one_block_sampled_rows():
     """The base-chunk shape with one block: chunk 0's only step carries its last frame's
     K/V (1560 keys) forward; chunk 1's first-step velocity on sampled rows against the
