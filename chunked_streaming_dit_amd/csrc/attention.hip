@@ -86,7 +86,9 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
   char* const ks = smem;
   char* const vs = smem + NSLOT * KTILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform; saying so keeps the loader waves' LDS destinations (M0)
+  // and their branches scalar instead of per-lane values read back with readfirstlane.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lg = lane >> 5;
   // 1-D grid of two parts.  The first qt0 * H workgroups take q-tiles [0, qt0) over the
   // whole key range; the rest take q-tiles [qt0, nqt), each (head, q-tile) split into
