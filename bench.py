@@ -137,6 +137,79 @@ def copy_probe(reps: int = 3) -> None:
     torch.cuda.synchronize()
 
 
+def elementwise_sweep(reps: int = 20) -> int:
+    """HBM-bound kernels of the step swept over sizes up to about 1 GB moved per launch:
+    RMSNorm + modulate (hidden 1536 and 3072, bf16 out), the standalone QK-norm + RoPE +
+    V^T repack (24 heads x 128), the Euler update, the flow-matching re-noise and the
+    plain copy.  Each launch is timed by HIP events over `reps` launches after two
+    untimed ones; bytes are the algorithmic ones (every input read once, every output
+    written once).  Sizes up to a few hundred MB can be served partly by the 256 MB
+    memory-side cache on repeats, so their rates may exceed what HBM alone gives.
+    Prints one JSON line per (kernel, size)."""
+    import torch
+
+    from chunked_streaming_dit_amd import _lib as C
+    from chunked_streaming_dit_amd import fm_euler_step, fm_noise_to, grid, ops
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def timed(fn) -> float:
+        for _ in range(2):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    def emit(kernel, shape, nbytes, us):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(json.dumps({"kernel": kernel, "shape": shape, "bytes": nbytes, "us": round(us, 2),
+                          "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 3)}), flush=True)
+
+    for D in (1536, 3072):
+        for n in (1560, 7800, 32760, 65520) if D == 3072 else (1560, 7800, 32760, 109200):
+            h = torch.randn(n, D, generator=g, device=dev)
+            shift = torch.randn(D, generator=g, device=dev)
+            scale = torch.randn(D, generator=g, device=dev)
+            out = torch.empty(n, D, device=dev, dtype=torch.bfloat16)
+            us = timed(lambda: ops.rmsnorm_modulate(h, shift, scale, 1e-6, out, "bf16"))
+            emit("rmsnorm_modulate", f"{n}x{D} fp32 -> bf16", n * D * 6 + 2 * D * 4, us)
+            del h, out
+    H, dh = 24, 128
+    D = H * dh
+    for frames in (1, 5, 21, 42):
+        n = frames * 1560
+        cap = (n + 63) // 64 * 64
+        qkv = torch.randn(n, 3 * D, generator=g, device=dev).to(torch.bfloat16)
+        gq = torch.ones(dh, device=dev, dtype=torch.bfloat16)
+        gk = torch.ones(dh, device=dev, dtype=torch.bfloat16)
+        qo = torch.empty(cap, D, device=dev, dtype=torch.bfloat16)
+        ko = torch.empty(cap, D, device=dev, dtype=torch.bfloat16)
+        vt = torch.empty(D, cap, device=dev, dtype=torch.bfloat16)
+        gr = grid(0, frames, 30, 52)
+        us = timed(lambda: ops.qknorm_rope("bf16", dh, H, n, qkv, qkv[:, D:], qkv[:, 2 * D:], 3 * D, gq, gk,
+                                           True, gr, 1e-6, 10000.0, qo, ko, vt, cap))
+        emit("qknorm_rope", f"{n} tokens x 3 x {H}x{dh} bf16", n * 3 * D * 2 * 2 + 2 * dh * 2, us)
+        del qkv, qo, ko, vt
+    for n in (1 << 20, 8 << 20, 32 << 20, 89 << 20):
+        x = torch.randn(n, generator=g, device=dev)
+        v = torch.randn(n, generator=g, device=dev)
+        e = torch.randn(n, generator=g, device=dev)
+        us = timed(lambda: fm_euler_step(x, v, -0.125))
+        emit("fm_euler_step", f"{n} fp32", 12 * n, us)
+        us = timed(lambda: fm_noise_to(x, v, e, 0.375))
+        emit("fm_noise_to", f"{n} fp32", 12 * n, us)
+        us = timed(lambda: C.check(C.lib().ditk_probe_copy(v.data_ptr(), x.data_ptr(), 4 * n,
+                                                           torch.cuda.current_stream().cuda_stream)))
+        emit("probe_copy", f"{4 * n} bytes", 8 * n, us)
+        del x, v, e
+    return 0
+
+
 def ceilings() -> dict:
     """Measured ceilings on this board, in the same process: the library's dense bf16
     MFMA loop (operands with changing bits, no memory traffic) and its plain copy of
@@ -791,6 +864,8 @@ def main() -> int:
                     choices=["large", "base", "stream6", "tiny", "interp", "iwin", "reuse", "sr", "sr1", "wstream"],
                     help="large: one large-chunk denoising step (default, the headline); base: one base "
                          "chunk job; stream6: whole 6-chunk streaming sessions; see the module docstring")
+    ap.add_argument("--elementwise-sweep", action="store_true",
+                    help="only sweep the HBM-bound kernels over sizes (one JSON line per size)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 256 MiB calibration copy (for the traffic counters)")
     ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -799,6 +874,8 @@ def main() -> int:
     if args.copy_probe:
         copy_probe()
         return 0
+    if args.elementwise_sweep:
+        return elementwise_sweep()
     if args.reduce_traffic:
         if args.workload not in TRAFFIC_FILES:
             raise SystemExit(f"bench.py: no traffic file for workload {args.workload}")
