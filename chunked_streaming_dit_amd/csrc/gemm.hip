@@ -178,19 +178,29 @@ __device__ __forceinline__ void epilogue_qknorm(const f32x16 (&acc)[MB][NB], con
     const int m0 = mw - mw % BM, ncol0 = nw - c0 - 2 * e.D;  // tile's first token / V column
     constexpr int G = BM / 16;
     bf16* vt = reinterpret_cast<bf16*>(e.vt_out);
-    for (int it = tid; it < 256 * G; it += (int)blockDim.x) {
-      const int col = it / G, grp = it - col * G;
+    // Two lanes per 16-token group of a column, each reading 8 tokens (16 bytes; a wave
+    // reads 1 KB of consecutive LDS, free of bank conflicts).  The group's output order
+    // puts tokens 0-3, 8-11 in its first 16 bytes and 4-7, 12-15 in its second, so the
+    // lanes swap 8 bytes and each stores one half.
+    for (int it = tid; it < 2 * 256 * G; it += (int)blockDim.x) {
+      const int col = it / (2 * G), rem = it - col * 2 * G, grp = rem >> 1, h = rem & 1;
       const int tok0 = m0 + grp * 16;
-      if (tok0 >= e.kpad) continue;
-      typedef bf16 b16 __attribute__((ext_vector_type(16)));
-      b16 o;
+      if (tok0 >= e.kpad) continue;  // the same for both lanes of a group
+      u32x4 raw = ld16(st + col * P + grp * 16 + h * 8);
+      if (tok0 + 16 > M) {  // tokens in [M, kpad) as 0
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int src = u;  // token offset
-        const int pos = 8 * ((src % 8) / 4) + 4 * (src / 8) + src % 4;
-        o[pos] = tok0 + src < M ? st[col * P + grp * 16 + src] : (bf16)0.f;
+        for (int w = 0; w < 4; ++w) {
+          const int t = tok0 + h * 8 + 2 * w;
+          if (t >= M) raw[w] = 0u;
+          else if (t + 1 >= M) raw[w] &= 0xffffu;
+        }
       }
-      *reinterpret_cast<b16*>(vt + (size_t)(ncol0 + col) * e.vcap + tok0) = o;
+      const uint32_t s0 = h ? raw[0] : raw[2], s1 = h ? raw[1] : raw[3];  // half 0 sends 4-7, half 1 sends 8-11
+      const uint32_t r0 = __shfl_xor(s0, 1), r1 = __shfl_xor(s1, 1);
+      u32x4 o;
+      if (h) { o[0] = r0; o[1] = r1; o[2] = raw[2]; o[3] = raw[3]; }  // 4-7 | 12-15
+      else { o[0] = raw[0]; o[1] = raw[1]; o[2] = r0; o[3] = r1; }   // 0-3 | 8-11
+      *reinterpret_cast<u32x4*>(vt + (size_t)(ncol0 + col) * e.vcap + tok0 + h * 8) = o;
     }
     return;
   }
