@@ -440,10 +440,19 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
 
   // Normalise and store: lane holds query qrow, dh = 32 d + 8 q + 4 lg + [0, 4).
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!qvalid) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (nsp == 1) {
-    T* op = reinterpret_cast<T*>(a.o) + (size_t)qrow * a.ldo + head * DH;
+    // The wave's 32 output rows go row-major through LDS (the rings are free once every
+    // wave has passed this barrier), so that each store instruction writes whole rows,
+    // 16 bytes per lane, instead of 8-byte pieces of 32 rows.  Row pitch padded by 16
+    // bytes against bank conflicts.  No wave leaves before the barrier.
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+    lds_barrier();
+    constexpr int OP = DH + 16 / SZ;  // LDS row pitch (elements)
+    constexpr int RB = DH * SZ;       // bytes per output row
+    constexpr int LPR = RB / 16;      // lanes per row
+    static_assert(RB % 16 == 0 && 64 % LPR == 0, "output rows of whole 16-byte pieces");
+    T* ot = reinterpret_cast<T*>(smem) + wave * 32 * OP;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -451,10 +460,20 @@ __global__ __launch_bounds__(64 * AW, 2) void attn_kernel(AttnArgs a) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = O[d][4 * q + r] * inv;
-        store4<T>(op + d * 32 + 8 * q + 4 * lg, v);
+        store4<T>(ot + l32 * OP + d * 32 + 8 * q + 4 * lg, v);
       }
+    const int row0 = qt * BQ + wave * 32;  // the wave's first query
+    char* og = reinterpret_cast<char*>(a.o) + ((size_t)row0 * a.ldo + head * DH) * SZ;
+#pragma unroll
+    for (int k = 0; k < 32 * LPR / 64; ++k) {
+      const int row = (64 / LPR) * k + lane / LPR, ch = lane % LPR;
+      if (row0 + row < a.nq)
+        st16(og + (size_t)row * a.ldo * SZ + ch * 16,
+             ld16(reinterpret_cast<const char*>(ot) + row * OP * SZ + ch * 16));
+    }
     return;
   }
+  if (!qvalid) return;
   const int D = a.H * DH;
   float* op = a.opart + ((size_t)split * a.nq + qrow) * D + head * DH;
 #pragma unroll
