@@ -51,6 +51,9 @@ Other workloads (--workload):
   wstream  the large-chunk step with the block weights streamed from pinned host memory
            through a 2-slot device ring (dit_weight_stream), with the resident step, the
            first (cold) streamed step and the stage hand-over measured in the same process
+Measurement modes besides the workloads: --elementwise-sweep (the HBM-bound kernels over
+sizes), --copy-probe (the counter calibration copy), --gemm-compare (the block-Linear
+GEMMs next to the vendor BLAS on the same shapes, as a reference point for their rate).
 The large-chunk weights are drawn on the GPU (seeded N(0, 1/fan_in), gammas
 1 + 0.1 N(0, 1)) to keep the 6.7 G parameters' set-up short; the other workloads use the
 seeded host catalogue of synth.
@@ -207,6 +210,70 @@ def elementwise_sweep(reps: int = 20) -> int:
                                                            torch.cuda.current_stream().cuda_stream)))
         emit("probe_copy", f"{4 * n} bytes", 8 * n, us)
         del x, v, e
+    return 0
+
+
+GEMM_COMPARE_SHAPES = (
+    # (name, M, N, K, epilogue): the block Linears of the large and of the base chunk
+    ("large QKV (bias)", 32760, 9216, 3072, "bias"),
+    ("large MLP in (bias + GELU)", 32760, 12288, 3072, "gelu"),
+    ("large MLP out (gated residual)", 32760, 3072, 12288, "resid"),
+    ("large out-projection (gated residual)", 32760, 3072, 3072, "resid"),
+    ("base QKV (bias)", 7800, 4608, 1536, "bias"),
+    ("base MLP in (bias + GELU)", 7800, 6144, 1536, "gelu"),
+)
+
+
+def gemm_compare(reps: int = 20, rounds: int = 5) -> int:
+    """The library's block-Linear GEMM (ditk_linear / ditk_linear_residual, bf16, fused
+    epilogue) next to the vendor BLAS on the same operands (torch.nn.functional.linear,
+    which runs hipBLASLt on this stack: bias only, its output written in bf16), timed by
+    HIP events over `reps` launches after three untimed ones, the two alternated for
+    `rounds` rounds (median).  A reference point for the GEMM's rate on this board, not
+    a path of the library.  Prints one JSON line per shape."""
+    import torch
+    import torch.nn.functional as F
+
+    from chunked_streaming_dit_amd import ops
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+
+    def timed(fn) -> float:
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    for name, M, N, K, epi in GEMM_COMPARE_SHAPES:
+        A = torch.randn(M, K, generator=g, device=dev).to(torch.bfloat16)
+        W = (torch.randn(N, K, generator=g, device=dev) / K ** 0.5).to(torch.bfloat16)
+        bias = (0.1 * torch.randn(N, generator=g, device=dev)).to(torch.bfloat16)
+        if epi == "resid":
+            gate = torch.rand(N, generator=g, device=dev)
+            h = torch.zeros(M, N, device=dev)
+            ours = lambda: ops.linear_residual(A, W, bias, gate, h, "bf16")
+        else:
+            out = torch.empty(M, N, device=dev, dtype=torch.bfloat16)
+            act = 1 if epi == "gelu" else 0
+            ours = lambda: ops.linear(A, W, bias, act, out, "bf16")
+        vendor = lambda: F.linear(A, W, bias)
+        t_ours, t_vendor = [], []
+        for _ in range(rounds):
+            t_ours.append(timed(ours))
+            t_vendor.append(timed(vendor))
+        us_o, us_v = sorted(t_ours)[rounds // 2], sorted(t_vendor)[rounds // 2]
+        fl = 2.0 * M * N * K
+        print(json.dumps({"gemm": name, "M": M, "N": N, "K": K, "epilogue": epi,
+                          "library_us": round(us_o, 1), "library_tflops": round(fl / us_o / 1e6, 1),
+                          "vendor_us": round(us_v, 1), "vendor_tflops": round(fl / us_v / 1e6, 1),
+                          "library_over_vendor": round(us_v / us_o, 3)}), flush=True)
+        del A, W, bias
     return 0
 
 
@@ -868,6 +935,8 @@ def main() -> int:
                     help="only sweep the HBM-bound kernels over sizes (one JSON line per size)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the 256 MiB calibration copy (for the traffic counters)")
+    ap.add_argument("--gemm-compare", action="store_true",
+                    help="only time the block-Linear GEMMs next to the vendor BLAS on the same shapes")
     ap.add_argument("--reduce-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write the workload's attention traffic file from rocprofv3 counter CSVs")
     args = ap.parse_args()
@@ -876,6 +945,8 @@ def main() -> int:
         return 0
     if args.elementwise_sweep:
         return elementwise_sweep()
+    if args.gemm_compare:
+        return gemm_compare()
     if args.reduce_traffic:
         if args.workload not in TRAFFIC_FILES:
             raise SystemExit(f"bench.py: no traffic file for workload {args.workload}")
