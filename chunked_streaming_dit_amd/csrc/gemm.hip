@@ -13,6 +13,7 @@
 //     consecutive output columns of one output row: the epilogue reads bias, gate and
 //     the fp32 residual as 16-byte vectors.
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_common.h"
 #include "kernels.h"
@@ -24,6 +25,8 @@ namespace {
 constexpr int ROWB = 128 + 16;  // LDS bytes per staged row (128 data + 16 pad)
 // Wave layout of gemm_lds_kernel (and patch_embed_kernel): 2 x 4 waves.
 constexpr int LDS_WM = 2, LDS_WN = 4, LDS_THREADS = 64 * LDS_WM * LDS_WN;
+// Rows from which bias / GELU launches take gemm_w4_kernel.
+constexpr int W4_MIN_ROWS = 16384;
 
 // Bias of a wave's NB x 32 columns, loaded into registers before the K loop so that its
 // latency hides under it: lane columns n = nw + 32 j + 8 q + 4 lg + {0..3} in [j][q][0..3].
@@ -611,6 +614,223 @@ __global__ __launch_bounds__(LDS_THREADS) void gemm_lds_kernel(const bf16* __res
     epilogue<bf16, MB, NB, EPI>(acc, cols, m0 + wm * WM, n0 + wn * WN, l32, lg, M, N, e);
 }
 
+// Bias columns of a 256-column tile: every column exists, so the loads carry no per-lane
+// condition and all of them are requested before the first wait.
+template <int NB, int EPI>
+__device__ __forceinline__ void cols_load_all(EpiCols<NB, EPI>& c, int nw, int lg, const GemmEpi& e) {
+  const bf16* bias = reinterpret_cast<const bf16*>(e.bias);
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load4<bf16>(bias + nw + j * 32 + 8 * q + 4 * lg, c.b[j][q]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) c.b[j][q][r] = 0.f;
+  }
+}
+
+// bf16 GEMM with a bias or bias + GELU epilogue for long launches (many 256 x 256
+// tiles): 4 waves, one per SIMD, each with a 128 x 128 wave tile whose 256 accumulator
+// registers live in the AGPRs.  Against gemm_lds_kernel's 8 waves of 128 x 64 it reads a
+// third less LDS per MFMA.  K steps of 64 through two LDS stage buffers (separate arrays,
+// so that the compiler knows the transfers into one never alias the fragment reads from
+// the other and may interleave them); every wave moves a quarter of each stage with
+// direct-to-LDS buffer loads (1 KB per instruction, the same row layout and swizzle as
+// gemm_lds_kernel).  The fragments of all four 16-wide sub-steps of a stage are held in
+// registers; the one barrier per K step sits after the second sub-step, when this
+// stage's fragments are all read (so the next stage can be requested into its buffer)
+// and the next stage has landed (so its first two sub-steps can be read under the last
+// two sub-steps' MFMAs).  The next stage's transfers are spread at one per two MFMAs.
+// Same arithmetic and summation order as gemm_lds_kernel: the results are bit for bit
+// the same.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(const bf16* __restrict__ A, int lda,
+                                                       const bf16* __restrict__ W, int ldw,
+                                                       int M, int N, int K, GemmEpi e) {
+  typedef bf16x8 V;
+  constexpr int BM = 256, BN = 256, MB = 4, NB = 4;
+  constexpr int STAGE = (BM + BN) * 128;
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lg = lane >> 5;
+  const int num_m = (M + BM - 1) / BM, num_n = N / BN;
+  int tm, tn;
+  tile_of((int)blockIdx.x, num_m, num_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int NLD = 16;
+  const int lsub = lane >> 3;
+  unsigned off[NLD];
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) {
+    const int r = 8 * (4 * j + (tid >> 6)) + lsub;
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    if (j < 8)
+      off[j] = (unsigned)(min(m0 + r, M - 1) * lda + chunk * 8) * 2u;
+    else
+      off[j] = (unsigned)(min(n0 + r - BM, N - 1) * ldw + chunk * 8) * 2u;
+  }
+  const unsigned bytes_a = (unsigned)min((size_t)0xffffffffu, (size_t)M * lda * 2);
+  const unsigned bytes_w = (unsigned)min((size_t)0xffffffffu, (size_t)N * ldw * 2);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)bytes_a, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)bytes_w, 0x00020000);
+  auto issue = [&](char* sbuf, int k0, int j) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 8 ? ra : rw,
+                                             (__attribute__((address_space(3))) void*)(sbuf + (4 * j + wave) * 1024),
+                                             16, (int)off[j], k0 * 2, 0, 0);
+  };
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int x = (l32 >> 1) & 7;
+  const int a_base = (wm * 128 + l32) * 128;
+  const int w_base = (BM + wn * 128 + l32) * 128;
+  V af[4][MB], wf[4][NB];
+  auto frags = [&](const char* st, int s) __attribute__((always_inline)) {
+    const int coff = ((2 * s + lg) ^ x) << 4;
+#pragma unroll
+    for (int i = 0; i < MB; ++i) af[s][i] = as_vec<V>(ld16(st + a_base + i * 32 * 128 + coff));
+#pragma unroll
+    for (int j = 0; j < NB; ++j) wf[s][j] = as_vec<V>(ld16(st + w_base + j * 32 * 128 + coff));
+  };
+  auto mfmas = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = mfma32(wf[s][j], af[s][i], acc[i][j]);
+  };
+  const int nk = K / 64;
+#pragma unroll
+  for (int j = 0; j < NLD; ++j) issue(smem0, 0, j);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) issue(smem1, 64, j);
+    wait_vm_lds<NLD>();
+  } else {
+    wait_vm_lds<0>();
+  }
+  lds_barrier();
+  frags(smem0, 0);
+  frags(smem0, 1);
+  auto step = [&](char* st, char* nst, int it, auto LOADS) __attribute__((always_inline)) {
+    frags(st, 2);
+    frags(st, 3);
+    mfmas(0);
+#pragma unroll
+    for (int q = 0; q < 2 * (MB + NB); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    mfmas(1);
+    __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_lds<0>();
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    frags(nst, 0);
+    frags(nst, 1);
+    if constexpr (decltype(LOADS)::value) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) issue(st, (it + 2) * 64, j);
+    }
+    mfmas(2);
+    mfmas(3);
+    if constexpr (decltype(LOADS)::value) {
+#pragma unroll
+      for (int q = 0; q < (MB * NB) / 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < (MB * NB) / 2; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2 * (MB + NB); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);
+    }
+  };
+  int it = 0;
+  for (; it + 3 < nk; it += 2) {
+    step(smem0, smem1, it, std::true_type{});
+    step(smem1, smem0, it + 1, std::true_type{});
+  }
+  if (it + 2 < nk) { step(smem0, smem1, it, std::true_type{}); ++it; }
+  char* st = (it & 1) ? smem1 : smem0;
+  char* nst = (it & 1) ? smem0 : smem1;
+  if (it + 1 < nk) { step(st, nst, it, std::false_type{}); ++it; char* t = st; st = nst; nst = t; }
+  frags(st, 2);
+  frags(st, 3);
+  mfmas(0);
+  mfmas(1);
+  mfmas(2);
+  mfmas(3);
+  // Epilogue: bias (+ GELU) in registers, the bf16 tile staged row-major in the two stage
+  // buffers (rows 0-127 in smem0, 128-255 in smem1; 512 bytes per row, the 16-byte chunk c
+  // of row r at c ^ (r & 31)), then stored as whole rows, 16 bytes per lane (measured
+  // +6-7% against each lane storing its 8-byte pieces of 32 rows).
+  EpiCols<NB, EPI> cols;
+  cols_load_all<NB, EPI>(cols, n0 + wn * 128, lg, e);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int r = wm * 128 + i * 32 + l32;
+    char* rowp = (wm ? smem1 : smem0) + (r & 127) * 512;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 128 + j * 32 + 8 * q + 4 * lg;
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] = acc[i][j][4 * q + t] + cols.b[j][q][t];
+          if constexpr (EPI == EPI_GELU) v[t] = gelu_tanh(v[t]);
+        }
+        store4<bf16>(reinterpret_cast<bf16*>(rowp + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2), v);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  lds_barrier();
+#pragma unroll 4
+  for (int k = 0; k < 32; ++k) {
+    const int r = wave * 64 + 2 * k + (lane >> 5), chunk = lane & 31;
+    const int m = m0 + r;
+    const u32x4 val = ld16((r < 128 ? smem0 : smem1) + (r & 127) * 512 + ((chunk ^ (r & 31)) << 4));
+    if (m < M) st16(reinterpret_cast<bf16*>(e.out) + (size_t)m * e.ldo + n0 + chunk * 8, val);
+  }
+}
+
+
+template <int EPI>
+hipError_t launch_w4(const void* A, int lda, const void* W, int ldw, int M, int N, int K, const GemmEpi& e,
+                     hipStream_t s, const hipEvent_t* ev) {
+  const int tiles = ((M + 255) / 256) * (N / 256);
+  return launch_k(gemm_w4_kernel<EPI>, dim3(tiles), dim3(256), s, ev, reinterpret_cast<const bf16*>(A), lda,
+                  reinterpret_cast<const bf16*>(W), ldw, M, N, K, e);
+}
+
 // Split K: h[m, n] += gate[n] (sum_p ws[p, m, n] + b[n]) (gate NULL: 1), one thread per
 // 4 consecutive columns.
 template <class T>
@@ -944,6 +1164,13 @@ hipError_t gemm(int dtype, const void* A, int lda, const void* W, int ldw, int M
       if (e.kind != EPI_QKNORM && e.kind != EPI_QKNORM_X && ((M + best - 1) / best) * (N / 256) < 160) {
         if ((long long)((M + 127) / 128) * ((N + 127) / 128) >= 240) return launch_t<bf16, 128, 128>(A, lda, W, ldw, M, N, K, e, s, ev);
         return launch_t<bf16, 64, 64>(A, lda, W, ldw, M, N, K, e, s, ev);
+      }
+      // Long bias / bias + GELU launches (the large chunk's MLP in): the 4-wave kernel, whose
+      // 256-row tiles and whole-row stores pay off once the grid is many waves deep (on the
+      // base chunk's 7800 rows it measured the same or slower).
+      if ((e.kind == EPI_BIAS || e.kind == EPI_GELU) && M >= W4_MIN_ROWS && K % 64 == 0) {
+        if (e.kind == EPI_BIAS) return launch_w4<EPI_BIAS>(A, lda, W, ldw, M, N, K, e, s, ev);
+        return launch_w4<EPI_GELU>(A, lda, W, ldw, M, N, K, e, s, ev);
       }
       if (best == 256 && e.kind == EPI_QKNORM_X) best = 192;  // its LDS holds a 192-row q tile at most
       if (best == 256) return launch_lds<256, 256>(A, lda, W, ldw, M, N, K, e, s, ev);
