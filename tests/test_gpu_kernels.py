@@ -77,8 +77,9 @@ def _rows(M, seed):
 
 
 # The block Linears at the workloads' launch shapes: these grids take the LDS-staged
-# large-tile kernel (256/192/128 x 256 tiles) with each fused epilogue.  Rows are
-# independent, so the oracle runs on sampled rows (first and last 64 and 384 more).
+# large-tile kernels with each fused epilogue (8 waves on 256/192/128 x 256 tiles; bias and
+# GELU launches of 16384 rows or more, 4 waves on 256 x 256 tiles).  Rows are independent,
+# so the oracle runs on sampled rows (first and last 64 and 384 more).
 @pytest.mark.parametrize("M,N,K,act", [
     (7800, 4608, 1536, 0),    # base chunk QKV (bias)
     (7800, 6144, 1536, 1),    # base chunk MLP in (GELU)
@@ -100,6 +101,28 @@ def test_linear_large_tiles(M, N, K, act):
     err = rel_err(to_np(out[torch.from_numpy(rows).to(dev)]), ref)
     print(f"linear {M}x{N}x{K} act {act}: err {err:.2e}")
     assert err <= TOL["bf16"] / 4
+
+
+# From 16384 rows, bias and GELU launches take the 4-wave kernel; below, the 8-wave one.
+# Both accumulate each output in the same order, so the rows they share are the same bits.
+@pytest.mark.parametrize("act", [0, 1])
+def test_linear_four_wave_kernel_matches_eight_wave_bits(act):
+    dev = device()
+    M, N, K = 16384, 3072, 3072
+    r = np.random.default_rng(7 + act)
+    A, W, b = _arr(r, (M, K), "bf16"), _arr(r, (N, K), "bf16", K ** -0.5), _arr(r, (N,), "bf16", 0.5)
+    Ad, Wd, bd = _dev(A, "bf16", dev), _dev(W, "bf16", dev), _dev(b, "bf16", dev)
+    big = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
+    small = torch.empty((M - 1, N), device=dev, dtype=torch.bfloat16)
+    ops.linear(Ad, Wd, bd, act, big, "bf16")
+    ops.linear(Ad[:M - 1], Wd, bd, act, small, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(big[:M - 1].view(torch.int16), small.view(torch.int16))
+    rows = _rows(M, 11)
+    ref = O.linear(A[rows].astype(np.float64), W.astype(np.float64), b.astype(np.float64))
+    if act == 1:
+        ref = O.gelu_tanh(ref)
+    assert rel_err(to_np(big[torch.from_numpy(rows).to(dev)]), ref) <= TOL["bf16"] / 4
 
 
 @pytest.mark.parametrize("M,N,K", [(7800, 1536, 6144), (7800, 1536, 1536), (32760, 3072, 12288),
