@@ -105,11 +105,13 @@ def test_linear_large_tiles(M, N, K, act):
 
 # From 16384 rows, bias and GELU launches take the 4-wave kernel; below, the 8-wave one.
 # Both accumulate each output in the same order, so the rows they share are the same bits.
-@pytest.mark.parametrize("act", [0, 1])
-def test_linear_four_wave_kernel_matches_eight_wave_bits(act):
+# K = 64, 128, 192 take the kernel's one-, two- and three-stage paths; N >= 768 keeps the
+# grid (64 x N / 256 tiles) above the small-grid cut-off, so both launches stay on these kernels.
+@pytest.mark.parametrize("N,K,act", [(3072, 3072, 0), (3072, 3072, 1), (768, 64, 0), (768, 128, 1), (768, 192, 0)])
+def test_linear_four_wave_kernel_matches_eight_wave_bits(N, K, act):
     dev = device()
-    M, N, K = 16384, 3072, 3072
-    r = np.random.default_rng(7 + act)
+    M = 16384
+    r = np.random.default_rng(7 + act + K)
     A, W, b = _arr(r, (M, K), "bf16"), _arr(r, (N, K), "bf16", K ** -0.5), _arr(r, (N,), "bf16", 0.5)
     Ad, Wd, bd = _dev(A, "bf16", dev), _dev(W, "bf16", dev), _dev(b, "bf16", dev)
     big = torch.empty((M, N), device=dev, dtype=torch.bfloat16)
