@@ -92,6 +92,8 @@ ATTN_SRC = os.path.join(ROOT, "chunked_streaming_dit_amd", "csrc", "attention.hi
 TRAFFIC_FILES = {
     "large": os.path.join(ROOT, "profiles", "attention_large_chunk_traffic.json"),
     "base": os.path.join(ROOT, "profiles", "attention_base_chunk_traffic.json"),
+    "sr": os.path.join(ROOT, "profiles", "attention_sr_chunk_traffic.json"),
+    "sr1": os.path.join(ROOT, "profiles", "attention_sr1_chunk_traffic.json"),
 }
 DIT_TIME_ATTN, DIT_TIME_GEMM, DIT_TIME_ELEM = 0, 1, 2
 
@@ -319,11 +321,15 @@ def ceilings() -> dict:
     return {"mfma_bf16_ceiling_tflops": mfma, "hbm_copy_ceiling_gbs": gbs}
 
 
-def _counter_means(path: str, counter: str, match, largest_grid: bool = False) -> tuple:
+def _counter_means(path: str, counter: str, match, largest_grid: bool = False, skip_first: bool = False) -> tuple:
     """(mean counter value, dispatches) over the dispatches of a rocprofv3 counter CSV
-    whose kernel name satisfies match (largest_grid: only those of the largest grid)."""
+    whose kernel name satisfies match (largest_grid: only those of the largest grid;
+    skip_first: without the first of them in dispatch order)."""
     import csv
     rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    if skip_first:
+        rows = rows[1:]
     if largest_grid and rows:
         g = max(int(r["Grid_Size"]) for r in rows)
         rows = [r for r in rows if int(r["Grid_Size"]) == g]
@@ -341,20 +347,24 @@ def _is_self_attention(name: str) -> bool:
 
 
 # The timed region's self-attention launches: the large-chunk bench times only the
-# denoising step's launches (the largest grid; its context passes run before), the base
-# chunk job times its context passes too.
-TRAFFIC_LARGEST_GRID = {"large": True, "base": False}
+# denoising step's launches (the largest grid; its context passes run before); the base
+# chunk job times all of its launches, reference pass included; a super-resolution job
+# times its boundary pass and steps, while the session's one reference pass (the first
+# self-attention dispatch of the run) lies outside the timed region.
+TRAFFIC_LARGEST_GRID = {"large": True, "base": False, "sr": False, "sr1": False}
+TRAFFIC_SKIP_FIRST = {"sr": True, "sr1": True}
 
 
-def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, largest_grid=False) -> dict:
+def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, largest_grid=False,
+                   skip_first=False) -> dict:
     """HBM bytes per self-attention launch from four rocprofv3 --pmc runs (FETCH_SIZE and
     WRITE_SIZE, in KiB per dispatch, over the bench and over copy_probe), each counter
     scaled so that the copy reads COPY_PROBE_BYTES and writes COPY_PROBE_BYTES."""
     kib = COPY_PROBE_BYTES / 1024
     cf, _ = _counter_means(copy_fetch_csv, "FETCH_SIZE", lambda n: "copy" in n.lower())
     cw, _ = _counter_means(copy_write_csv, "WRITE_SIZE", lambda n: "copy" in n.lower())
-    f, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_self_attention, largest_grid)
-    w, nw = _counter_means(write_csv, "WRITE_SIZE", _is_self_attention, largest_grid)
+    f, nf = _counter_means(fetch_csv, "FETCH_SIZE", _is_self_attention, largest_grid, skip_first)
+    w, nw = _counter_means(write_csv, "WRITE_SIZE", _is_self_attention, largest_grid, skip_first)
     sf, sw = kib / cf, kib / cw
     return {
         "attention_src_sha256_16": _src_hash(ATTN_SRC),
@@ -365,6 +375,7 @@ def reduce_traffic(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, largest
         "write_scale": sw,
         "dispatches": [nf, nw],
         "largest_grid_only": bool(largest_grid),
+        "first_dispatch_skipped": bool(skip_first),
     }
 
 
@@ -950,7 +961,8 @@ def main() -> int:
     if args.reduce_traffic:
         if args.workload not in TRAFFIC_FILES:
             raise SystemExit(f"bench.py: no traffic file for workload {args.workload}")
-        d = reduce_traffic(*args.reduce_traffic, largest_grid=TRAFFIC_LARGEST_GRID[args.workload])
+        d = reduce_traffic(*args.reduce_traffic, largest_grid=TRAFFIC_LARGEST_GRID[args.workload],
+                           skip_first=TRAFFIC_SKIP_FIRST.get(args.workload, False))
         with open(TRAFFIC_FILES[args.workload], "w") as fh:
             json.dump(d, fh, indent=1)
             fh.write("\n")
